@@ -1,0 +1,198 @@
+"""ctypes binding of the fp64 oracle (``mimo_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the benchmark).
+
+Every array argument is converted to a C-contiguous float32 (inputs: bf16 and fp32 values are
+exact in float32) or int32 array; results are float64 numpy arrays.  Errors raise ValueError.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mimo_oracle.c")
+_LIB = os.path.join(_HERE, "libmimo_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (IEEE fp64: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(
+            ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+             _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _CParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("qk_head_dim", ctypes.c_int32),
+        ("v_head_dim", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+        ("layer_kind", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double), ("v_scale", ctypes.c_double),
+        ("softmax_scale", ctypes.c_double),
+    ]
+
+
+@dataclasses.dataclass
+class OracleParams:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    qk_head_dim: int
+    v_head_dim: int
+    rope_dims: int
+    layer_kind: int  # 0 global causal, 1 sliding window
+    window: int
+    rope_theta: float
+    v_scale: float = 1.0
+    softmax_scale: float = 0.0  # 0 -> 1/sqrt(qk_head_dim)
+
+    def c(self) -> _CParams:
+        return _CParams(self.batch, self.num_q_heads, self.num_kv_heads, self.qk_head_dim,
+                        self.v_head_dim, self.rope_dims, self.layer_kind, self.window,
+                        float(self.rope_theta), float(self.v_scale), float(self.softmax_scale))
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            P = ctypes.POINTER
+            f32, f64, i32 = P(ctypes.c_float), P(ctypes.c_double), P(ctypes.c_int32)
+            lib.oracle_rope_omega.argtypes = [ctypes.c_int32, ctypes.c_double, f64]
+            lib.oracle_rope_rotate.argtypes = [f64, f64, ctypes.c_int64, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_double, i32]
+            lib.oracle_prefill.argtypes = [P(_CParams), ctypes.c_int32, f32, f32, f32, i32, f32,
+                                           f64, i32, ctypes.c_int32, f64]
+            lib.oracle_scores.argtypes = [P(_CParams), ctypes.c_int32, f32, f32, i32,
+                                          ctypes.c_int32, ctypes.c_int32, f64]
+            lib.oracle_decode.argtypes = [P(_CParams), f32, f32, f32, i32, f32, f32, i32, i32,
+                                          ctypes.c_int32, f32, f64, f64, i32, ctypes.c_int32]
+            for fn in ("oracle_rope_omega", "oracle_rope_rotate", "oracle_prefill",
+                       "oracle_scores", "oracle_decode"):
+                getattr(lib, fn).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a, ctype):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def omega(rope_dims: int, theta: float) -> np.ndarray:
+    out = np.zeros(max(rope_dims // 2, 1), dtype=np.float64)
+    _check(_load().oracle_rope_omega(rope_dims, theta, _ptr(out, ctypes.c_double)), "omega")
+    return out[: rope_dims // 2]
+
+
+def rotate(x, rope_dims: int, theta: float, positions) -> np.ndarray:
+    """Rotate rows x[..., dim] at positions[...] (same leading shape)."""
+    x = _f64(x)
+    pos = _i32(positions)
+    assert pos.shape == x.shape[:-1]
+    y = np.empty_like(x)
+    n = int(np.prod(x.shape[:-1]))
+    _check(_load().oracle_rope_rotate(_ptr(x, ctypes.c_double), _ptr(y, ctypes.c_double), n,
+                                      x.shape[-1], rope_dims, theta, _ptr(pos, ctypes.c_int32)),
+           "rotate")
+    return y
+
+
+def prefill(p: OracleParams, q, k, v, positions, sinks=None, rows=None, want_k_rot=False):
+    """Attention over S new tokens: q [B,S,Hq,dqk], k [B,S,Hkv,dqk], v [B,S,Hkv,dv],
+    positions [B,S], sinks [Hq] or None.  Returns out [B,S,Hq,dv] (rows not listed are NaN),
+    plus the rotated keys [B,S,Hkv,dqk] when want_k_rot."""
+    q, k, v, sinks = _f32(q), _f32(k), _f32(v), _f32(sinks)
+    pos = _i32(positions)
+    B, S = pos.shape
+    assert q.shape == (B, S, p.num_q_heads, p.qk_head_dim), q.shape
+    assert k.shape == (B, S, p.num_kv_heads, p.qk_head_dim), k.shape
+    assert v.shape == (B, S, p.num_kv_heads, p.v_head_dim), v.shape
+    out = np.full((B, S, p.num_q_heads, p.v_head_dim), np.nan, dtype=np.float64)
+    rows_a = _i32(rows)
+    krot = np.empty(k.shape, dtype=np.float64) if want_k_rot else None
+    cp = p.c()
+    _check(_load().oracle_prefill(
+        ctypes.byref(cp), S, _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+        _ptr(v, ctypes.c_float), _ptr(pos, ctypes.c_int32), _ptr(sinks, ctypes.c_float),
+        _ptr(out, ctypes.c_double), _ptr(rows_a, ctypes.c_int32),
+        0 if rows_a is None else len(rows_a), _ptr(krot, ctypes.c_double)), "prefill")
+    return (out, krot) if want_k_rot else out
+
+
+def scores(p: OracleParams, q, k, positions, b: int, h: int) -> np.ndarray:
+    """Unmasked scaled score matrix [S,S] of sequence b, query head h."""
+    q, k = _f32(q), _f32(k)
+    pos = _i32(positions)
+    S = pos.shape[1]
+    z = np.empty((S, S), dtype=np.float64)
+    cp = p.c()
+    _check(_load().oracle_scores(ctypes.byref(cp), S, _ptr(q, ctypes.c_float),
+                                 _ptr(k, ctypes.c_float), _ptr(pos, ctypes.c_int32), b, h,
+                                 _ptr(z, ctypes.c_double)), "scores")
+    return z
+
+
+def decode(p: OracleParams, q, k_new, v_new, pos, kc=None, vc=None, kpos=None, count=None,
+           sinks=None, batch_rows=None, want_k_rot=False):
+    """One new token per sequence against a position->(rotated key, value) map.
+
+    q [B,Hq,dqk], k_new [B,Hkv,dqk] (raw), v_new [B,Hkv,dv], pos [B];
+    kc [B,Hkv,L,dqk] rotated keys, vc [B,Hkv,L,dv], kpos [B,L], count [B] (or None for L=0).
+    Returns out [B,Hq,dv] (sequences not listed in batch_rows are NaN), plus the rotated new
+    keys [B,Hkv,dqk] when want_k_rot."""
+    q, k_new, v_new, sinks = _f32(q), _f32(k_new), _f32(v_new), _f32(sinks)
+    pos = _i32(pos)
+    B = pos.shape[0]
+    assert q.shape == (B, p.num_q_heads, p.qk_head_dim)
+    assert k_new.shape == (B, p.num_kv_heads, p.qk_head_dim)
+    assert v_new.shape == (B, p.num_kv_heads, p.v_head_dim)
+    if kc is None:
+        L = 0
+        kc_a = vc_a = kpos_a = cnt_a = None
+    else:
+        kc_a, vc_a, kpos_a, cnt_a = _f32(kc), _f32(vc), _i32(kpos), _i32(count)
+        L = kc_a.shape[2]
+        assert kc_a.shape == (B, p.num_kv_heads, L, p.qk_head_dim)
+        assert vc_a.shape == (B, p.num_kv_heads, L, p.v_head_dim)
+        assert kpos_a.shape == (B, L) and cnt_a.shape == (B,)
+    out = np.full((B, p.num_q_heads, p.v_head_dim), np.nan, dtype=np.float64)
+    krot = np.full(k_new.shape, np.nan, dtype=np.float64) if want_k_rot else None
+    br = _i32(batch_rows)
+    cp = p.c()
+    _check(_load().oracle_decode(
+        ctypes.byref(cp), _ptr(q, ctypes.c_float), _ptr(k_new, ctypes.c_float),
+        _ptr(v_new, ctypes.c_float), _ptr(pos, ctypes.c_int32), _ptr(kc_a, ctypes.c_float),
+        _ptr(vc_a, ctypes.c_float), _ptr(kpos_a, ctypes.c_int32), _ptr(cnt_a, ctypes.c_int32), L,
+        _ptr(sinks, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(krot, ctypes.c_double),
+        _ptr(br, ctypes.c_int32), 0 if br is None else len(br)), "decode")
+    return (out, krot) if want_k_rot else out
