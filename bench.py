@@ -1,0 +1,274 @@
+"""Benchmark of the hybrid attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the 48-layer attention-only stack:
+hybrid_layer_pattern = layer 0 global then 5 sliding : 1 global; batch 2; prefill of 16384 tokens
+per layer (each layer writes its KV cache: linear for global layers, 128-slot ring for sliding
+ones), then 256 single-token decode steps through all 48 layers.  Head shapes: 64 query heads,
+QK head dim 192 (64 rotated), V head dim 128; global layers 4 KV heads, theta 5e6, no sink;
+sliding layers 8 KV heads, theta 1e4, window 128, per-head sinks.  Inputs are seeded N(0,1) bf16,
+generated on the device before timing; every layer has its own inputs (seed 4000 + layer).
+
+Output: one JSON line.  `value` is the step's algorithmic TFLOP/s (prefill + decode flops, masked
+pairs not counted, over the measured step time); the per-phase numbers (prefill TFLOP/s, decode
+KV GB/s, each kind separately, with roofline fractions) are in `phases`; `roofline` covers the
+dominant kernel (global-layer prefill) and `cpu_baseline` the fp64 oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+DQK, DV = 192, 128
+
+
+def pairs_visible(S: int, kind: int, W: int) -> int:
+    """Number of (query, key) pairs the mask admits in a prefill of S tokens."""
+    if kind == 0:
+        return S * (S + 1) // 2
+    full = max(0, S - W)
+    head = min(S, W)
+    return head * (head + 1) // 2 + full * W
+
+
+def prefill_counts(B, S, Hq, Hkv, kind, W):
+    flops = B * Hq * pairs_visible(S, kind, W) * 2 * (DQK + DV)
+    io = B * S * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV) * 2       # q, k, v read; out written
+    cached = min(S, W) if kind == 1 else S
+    io += B * cached * Hkv * (DQK + DV) * 2                          # rotated K and V stored
+    return flops, io
+
+
+def decode_counts(B, Hq, Hkv, kind, W, positions):
+    """flops and bytes of one decode step: every visible cached slot read once, q/k/v_new read,
+    out and the appended slot written."""
+    flops = bytes_ = 0
+    for p in positions:
+        cached = min(W - 1, p) if kind == 1 else p
+        flops += Hq * (cached + 1) * 2 * (DQK + DV)
+        bytes_ += Hkv * cached * (DQK + DV) * 2
+    B = len(positions)
+    bytes_ += B * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV + Hkv * (DQK + DV)) * 2
+    return flops, bytes_
+
+
+def cpu_baseline(stack_cfg, seed_base):
+    """The fp64 oracle on a bounded sample of the same workload: sequence 0 of layer 0 (global)
+    over its first 3072 tokens, of layer 1 (sliding) over its first 4096 tokens, and one global
+    decode step at position 3072 against the oracle's own rotated keys."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tests import synth
+
+    ga, swa = synth.GA_PREFILL, synth.SWA_PREFILL
+    S_ga, S_swa = 3072, 4096
+    f = lambda t: t.to(torch.float32).numpy()
+    q, k, v, _ = synth.layer_inputs(ga, seed_base + 0, batch=1, seq=S_ga + 1)
+    q2, k2, v2, s2 = synth.layer_inputs(swa, seed_base + 1, batch=1, seq=S_swa)
+    op_ga = oracle.OracleParams(1, 64, 4, DQK, DV, 64, 0, 0, 5e6, ga.v_scale)
+    op_swa = oracle.OracleParams(1, 64, 8, DQK, DV, 64, 1, 128, 1e4, swa.v_scale)
+    pos_ga = np.arange(S_ga, dtype=np.int32)[None]
+    pos_swa = np.arange(S_swa, dtype=np.int32)[None]
+    qa, ka, va = f(q[:, :S_ga]), f(k[:, :S_ga]), f(v[:, :S_ga])
+    qs, ks, vs, ss = f(q2), f(k2), f(v2), f(s2)
+    t0 = time.perf_counter()
+    _, krot = oracle.prefill(op_ga, qa, ka, va, pos_ga, None, want_k_rot=True)
+    oracle.prefill(op_swa, qs, ks, vs, pos_swa, ss)
+    kc = np.ascontiguousarray(krot.transpose(0, 2, 1, 3)).astype(np.float32)
+    vc = np.ascontiguousarray(va.transpose(0, 2, 1, 3))
+    oracle.decode(op_ga, f(q[:, S_ga]), f(k[:, S_ga]), f(v[:, S_ga]), np.array([S_ga], np.int32),
+                  kc, vc, pos_ga, np.array([S_ga], np.int32), None)
+    dt = time.perf_counter() - t0
+    flops = (prefill_counts(1, S_ga, 64, 4, 0, 0)[0] + prefill_counts(1, S_swa, 64, 8, 1, 128)[0]
+             + decode_counts(1, 64, 4, 0, 128, [S_ga])[0])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"fp64 oracle, sequence 0 only: layer 0 (global) prefill of the first {S_ga} "
+                       f"tokens, layer 1 (sliding) prefill of the first {S_swa} tokens, one global "
+                       f"decode step at position {S_ga}; {flops:.3e} algorithmic flop in "
+                       f"{dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
+              "here (multi-GPU sharding is described, not built); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import global_attention_rope_amd as mimo
+    from tests import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mimo.lib()  # fails loudly when the HIP library is missing
+
+    L, B, S, T = synth.STACK_LAYERS, synth.STACK_BATCH, synth.STACK_SEQ, args.decode_steps
+    pattern = synth.stack_pattern(L)
+    cfg = mimo.HybridAttentionConfig(
+        hidden_size=4096, num_attention_heads=64, num_key_value_heads=4,
+        swa_num_key_value_heads=8, head_dim=DQK, v_head_dim=DV, partial_rotary_factor=1.0 / 3.0,
+        rope_theta=5e6, swa_rope_theta=1e4, sliding_window_size=128, hybrid_layer_pattern=pattern,
+        rope_dims=64)
+    specs = mimo.layer_specs(cfg)
+    Hq = cfg.num_attention_heads
+    seed_base = 4000
+
+    # ---- inputs and state, all resident before timing
+    layers = []
+    for sp in specs:
+        w = synth.SWA_PREFILL if sp.kind == mimo.LAYER_SWA else synth.GA_PREFILL
+        q, k, v, s = synth.layer_inputs(w, seed_base + sp.index, device=dev, batch=B, seq=S)
+        cap = sp.window if sp.kind == mimo.LAYER_SWA else S + T
+        kc = torch.zeros((B, sp.num_kv_heads, cap, DQK), dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros((B, sp.num_kv_heads, cap, DV), dtype=torch.bfloat16, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed_base + 100 + sp.index)
+        dq = torch.randn((T, B, Hq, DQK), generator=g, device=dev).to(torch.bfloat16)
+        dk = torch.randn((T, B, sp.num_kv_heads, DQK), generator=g, device=dev).to(torch.bfloat16)
+        dv = torch.randn((T, B, sp.num_kv_heads, DV), generator=g, device=dev).to(torch.bfloat16)
+        layers.append(dict(spec=sp, p=sp.params(cfg, B), q=q, k=k, v=v,
+                           sinks=s if sp.has_sinks else None, kc=kc, vc=vc, dq=dq, dk=dk, dv=dv))
+    start_pos = torch.zeros(B, dtype=torch.int32, device=dev)
+    dec_pos = [torch.full((B,), S + t, dtype=torch.int32, device=dev) for t in range(T)]
+    out_pf = torch.empty((B, S, Hq, DV), dtype=torch.bfloat16, device=dev)
+    out_dec = torch.empty((B, Hq, DV), dtype=torch.bfloat16, device=dev)
+    ws_pf = torch.empty(max(mimo.prefill_workspace_size(l["p"], S) for l in layers) + 256,
+                        dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(mimo.decode_workspace_size(l["p"], S + T - 1) for l in layers) + 256,
+                         dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ga_events = []
+
+    def step(record):
+        for l in layers:
+            is_ga = l["spec"].kind == mimo.LAYER_GLOBAL
+            if record and is_ga:
+                e0 = ev()
+                e0.record()
+            mimo.prefill(l["p"], l["q"], l["k"], l["v"], start_pos, sinks=l["sinks"], out=out_pf,
+                         k_cache=l["kc"], v_cache=l["vc"], workspace=ws_pf)
+            if record and is_ga:
+                e1 = ev()
+                e1.record()
+                ga_events.append((e0, e1))
+        mid = ev()
+        mid.record()
+        for t in range(T):
+            for l in layers:
+                mimo.decode(l["p"], l["dq"][t], l["dk"][t], l["dv"][t], dec_pos[t], S + T - 1,
+                            l["kc"], l["vc"], sinks=l["sinks"], out=out_dec, workspace=ws_dec)
+        return mid
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    starts, mids, ends = [], [], []
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        e0 = ev()
+        e0.record()
+        mids.append(step(True))
+        e1 = ev()
+        e1.record()
+        starts.append(e0)
+        ends.append(e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+
+    step_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    prefill_ms = sum(a.elapsed_time(b) for a, b in zip(starts, mids)) / args.steps
+    decode_ms = sum(a.elapsed_time(b) for a, b in zip(mids, ends)) / args.steps
+    ga_ms = sum(a.elapsed_time(b) for a, b in ga_events) / len(ga_events)
+
+    # ---- algorithmic work of one step
+    n_ga = sum(1 for sp in specs if sp.kind == mimo.LAYER_GLOBAL)
+    n_swa = L - n_ga
+    f_ga, b_ga = prefill_counts(B, S, Hq, 4, 0, 0)
+    f_swa, b_swa = prefill_counts(B, S, Hq, 8, 1, 128)
+    pf_flops = n_ga * f_ga + n_swa * f_swa
+    dec_f = dec_b = dec_b_ga = dec_b_swa = 0
+    for t in range(T):
+        fg, bg = decode_counts(B, Hq, 4, 0, 128, [S + t] * B)
+        fs, bs = decode_counts(B, Hq, 8, 1, 128, [S + t] * B)
+        dec_f += n_ga * fg + n_swa * fs
+        dec_b_ga += n_ga * bg
+        dec_b_swa += n_swa * bs
+    dec_b = dec_b_ga + dec_b_swa
+    step_flops = pf_flops + dec_f
+    value = step_flops / (step_ms * 1e-3) / 1e12
+    ga_tflops = f_ga / (ga_ms * 1e-3) / 1e12
+    swa_prefill_ms = (prefill_ms - n_ga * ga_ms) / n_swa
+    swa_gbps = b_swa / (swa_prefill_ms * 1e-3) / 1e9
+    dec_gbps = dec_b / (decode_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "attention prefill TFLOP/s and decode KV GB/s (SWA and GA) + % of roofline",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hybrid_stack_48L_b2_s16384_prefill_256_decode",
+                   "layers": L, "global_layers": n_ga, "sliding_layers": n_swa, "batch": B,
+                   "prefill_tokens": S, "decode_steps": T, "num_q_heads": Hq,
+                   "kv_heads_global": 4, "kv_heads_sliding": 8, "qk_head_dim": DQK,
+                   "v_head_dim": DV, "rope_dims": 64, "window": 128,
+                   "theta_global": 5e6, "theta_sliding": 1e4},
+        "phases": {
+            "prefill": {"ms": round(prefill_ms, 3),
+                        "tflops": round(pf_flops / (prefill_ms * 1e-3) / 1e12, 2),
+                        "global_layer_ms": round(ga_ms, 4),
+                        "global_layer_tflops": round(ga_tflops, 2),
+                        "global_frac_mfma_peak": round(ga_tflops / PEAK_BF16_TFLOPS, 4),
+                        "sliding_layer_ms_avg": round(swa_prefill_ms, 4),
+                        "sliding_layer_GBps": round(swa_gbps, 1),
+                        "sliding_frac_hbm_peak": round(swa_gbps / PEAK_HBM_GBPS, 4)},
+            "decode": {"ms": round(decode_ms, 3), "steps": T,
+                       "GBps": round(dec_gbps, 1),
+                       "frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                       "kv_bytes_global": dec_b_ga, "kv_bytes_sliding": dec_b_swa},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(ga_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ga_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "global-layer prefill (key rotation pass + attention kernel), "
+                               f"B{B} S{S}, {f_ga:.4e} flop per call"},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, seed_base)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

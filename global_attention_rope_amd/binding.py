@@ -1,0 +1,213 @@
+"""ctypes binding of ``libmimo_attn.so`` (declared in ``include/mimo_attn.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind the C ABI.
+torch supplies device memory and the current stream.  If the library is not built, loading it
+raises; there is no other execution path.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmimo_attn.so")
+
+MIMO_OK, MIMO_ERR_INVALID_ARG, MIMO_ERR_UNSUPPORTED, MIMO_ERR_WORKSPACE, MIMO_ERR_HIP = 0, -1, -2, -3, -4
+LAYER_GLOBAL, LAYER_SWA = 0, 1
+F32, BF16 = 0, 1
+
+EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_decode",
+           "mimo_attn_decode_workspace_size", "mimo_attn_check_params", "mimo_attn_last_error",
+           "mimo_attn_abi_version")
+
+
+class MimoAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mimo_attn error {code}: {msg}")
+        self.code = code
+
+
+class CParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("qk_head_dim", ctypes.c_int32),
+        ("v_head_dim", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+        ("layer_kind", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double), ("v_scale", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+@dataclasses.dataclass
+class Params:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    qk_head_dim: int
+    v_head_dim: int
+    rope_dims: int
+    layer_kind: int
+    window: int
+    rope_theta: float
+    v_scale: float = 1.0
+    softmax_scale: float = 0.0
+    dtype: int = BF16
+
+    def c(self) -> CParams:
+        return CParams(self.batch, self.num_q_heads, self.num_kv_heads, self.qk_head_dim,
+                       self.v_head_dim, self.rope_dims, self.layer_kind, self.window,
+                       float(self.rope_theta), float(self.v_scale), float(self.softmax_scale),
+                       self.dtype, 0)
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it with `python -m global_attention_rope_amd.build`")
+            L = ctypes.CDLL(path)
+            vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+            P = ctypes.POINTER(CParams)
+            L.mimo_attn_prefill.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+            L.mimo_attn_prefill.restype = ctypes.c_int
+            L.mimo_attn_prefill_workspace_size.argtypes = [P, i32]
+            L.mimo_attn_prefill_workspace_size.restype = sz
+            L.mimo_attn_decode.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+            L.mimo_attn_decode.restype = ctypes.c_int
+            L.mimo_attn_decode_workspace_size.argtypes = [P, i32]
+            L.mimo_attn_decode_workspace_size.restype = sz
+            L.mimo_attn_check_params.argtypes = [P]
+            L.mimo_attn_check_params.restype = ctypes.c_int
+            L.mimo_attn_last_error.argtypes = []
+            L.mimo_attn_last_error.restype = ctypes.c_char_p
+            L.mimo_attn_abi_version.argtypes = []
+            L.mimo_attn_abi_version.restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().mimo_attn_last_error().decode()
+
+
+def _raise(code: int):
+    if code != MIMO_OK:
+        raise MimoAttnError(code, last_error())
+
+
+def check_params(p: Params) -> int:
+    cp = p.c()
+    return lib().mimo_attn_check_params(ctypes.byref(cp))
+
+
+def prefill_workspace_size(p: Params, seq_len: int) -> int:
+    cp = p.c()
+    return int(lib().mimo_attn_prefill_workspace_size(ctypes.byref(cp), seq_len))
+
+
+def decode_workspace_size(p: Params, max_position: int) -> int:
+    cp = p.c()
+    return int(lib().mimo_attn_decode_workspace_size(ctypes.byref(cp), max_position))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _tdtype(p: Params):
+    return torch.bfloat16 if p.dtype == BF16 else torch.float32
+
+
+def prefill(p: Params, q, k, v, start_pos, sinks=None, out=None, k_cache=None, v_cache=None,
+            workspace=None, stream=None):
+    """mimo_attn_prefill on torch device tensors (shapes as in include/mimo_attn.h).
+
+    start_pos: int32 [B] device tensor.  Returns out [B,S,Hq,dv]."""
+    B, S = q.shape[0], q.shape[1]
+    dev, dt = q.device, _tdtype(p)
+    if p.batch != B:
+        raise ValueError(f"params.batch {p.batch} != q.shape[0] {B}")
+    _expect(q, "q", (B, S, p.num_q_heads, p.qk_head_dim), dt, dev)
+    _expect(k, "k", (B, S, p.num_kv_heads, p.qk_head_dim), dt, dev)
+    _expect(v, "v", (B, S, p.num_kv_heads, p.v_head_dim), dt, dev)
+    _expect(start_pos, "start_pos", (B,), torch.int32, dev)
+    if sinks is not None:
+        _expect(sinks, "sinks", (p.num_q_heads,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, S, p.num_q_heads, p.v_head_dim), dtype=dt, device=dev)
+    _expect(out, "out", (B, S, p.num_q_heads, p.v_head_dim), dt, dev)
+    cap = 0
+    if k_cache is not None or v_cache is not None:
+        cap = k_cache.shape[2]
+        _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), dt, dev)
+        _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), dt, dev)
+    need = prefill_workspace_size(p, S)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cp = p.c()
+    _raise(lib().mimo_attn_prefill(ctypes.byref(cp), S, _ptr(q), _ptr(k), _ptr(v), _ptr(start_pos),
+                                   _ptr(sinks), _ptr(out), _ptr(k_cache), _ptr(v_cache), cap,
+                                   _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def decode(p: Params, q, k_new, v_new, positions, max_position: int, k_cache, v_cache,
+           sinks=None, out=None, workspace=None, stream=None):
+    """mimo_attn_decode on torch device tensors.  positions: int32 [B] device tensor."""
+    B = q.shape[0]
+    dev, dt = q.device, _tdtype(p)
+    if p.batch != B:
+        raise ValueError(f"params.batch {p.batch} != q.shape[0] {B}")
+    _expect(q, "q", (B, p.num_q_heads, p.qk_head_dim), dt, dev)
+    _expect(k_new, "k_new", (B, p.num_kv_heads, p.qk_head_dim), dt, dev)
+    _expect(v_new, "v_new", (B, p.num_kv_heads, p.v_head_dim), dt, dev)
+    _expect(positions, "positions", (B,), torch.int32, dev)
+    cap = k_cache.shape[2]
+    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), dt, dev)
+    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), dt, dev)
+    if sinks is not None:
+        _expect(sinks, "sinks", (p.num_q_heads,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, p.num_q_heads, p.v_head_dim), dtype=dt, device=dev)
+    _expect(out, "out", (B, p.num_q_heads, p.v_head_dim), dt, dev)
+    need = decode_workspace_size(p, max_position)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cp = p.c()
+    _raise(lib().mimo_attn_decode(ctypes.byref(cp), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                  _ptr(positions), max_position, _ptr(k_cache), _ptr(v_cache), cap,
+                                  _ptr(sinks), _ptr(out), _ptr(workspace), wbytes,
+                                  _stream(stream)))
+    return out

@@ -1,0 +1,348 @@
+// abi.hip — the C ABI of libmimo_attn.so: host-side validation, workspace sizing and dispatch.
+//
+// Declarations, argument meaning, layouts, ownership and error behaviour: include/mimo_attn.h.
+// Layer definition: "Add Xiaomi MiMo-V2" (transformers PR 45144), "Additional useful info";
+// "add Xiaomi MiMo v2 (mimo_v2_flash)" (mlxcel issue 842), "Architecture, verified against
+// upstream" and "Implementation plan".
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mimo_attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return MIMO_OK;
+}
+
+constexpr int kBf16Dqk = 192, kBf16Dv = 128, kF32MaxDim = 256, kMaxDecodeGroup = 16;
+
+// Frequencies of the rotated slice: omega_d = theta^(-2d/r), d < r/2.
+void fill_omega(const mimo_attn_params* p, double* omega) {
+    for (int d = 0; d < mimo::kMaxRopeHalfArgs; ++d) omega[d] = 0.0;
+    for (int d = 0; d < p->rope_dims / 2; ++d)
+        omega[d] = pow(p->rope_theta, -2.0 * (double)d / (double)p->rope_dims);
+}
+
+float score_scale(const mimo_attn_params* p) {
+    return p->softmax_scale != 0.0f ? p->softmax_scale : (float)(1.0 / sqrt((double)p->qk_head_dim));
+}
+
+int check(const mimo_attn_params* p) {
+    if (!p) return fail(MIMO_ERR_INVALID_ARG, "params is NULL");
+    if (p->reserved != 0) return fail(MIMO_ERR_INVALID_ARG, "reserved must be 0");
+    if (p->batch < 0) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+    if (p->num_q_heads < 1 || p->num_kv_heads < 1)
+        return fail(MIMO_ERR_INVALID_ARG, "head counts must be >= 1 (Hq %d, Hkv %d)",
+                    p->num_q_heads, p->num_kv_heads);
+    if (p->num_q_heads % p->num_kv_heads)
+        return fail(MIMO_ERR_INVALID_ARG, "num_kv_heads %d does not divide num_q_heads %d",
+                    p->num_kv_heads, p->num_q_heads);
+    if (p->qk_head_dim < 1 || p->v_head_dim < 1)
+        return fail(MIMO_ERR_INVALID_ARG, "head dims must be >= 1 (dqk %d, dv %d)", p->qk_head_dim,
+                    p->v_head_dim);
+    if (p->rope_dims < 0 || p->rope_dims > p->qk_head_dim || (p->rope_dims & 1))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_dims %d must be even and in [0, qk_head_dim %d]",
+                    p->rope_dims, p->qk_head_dim);
+    if (p->rope_dims / 2 > mimo::kMaxRopeHalfArgs)
+        return fail(MIMO_ERR_UNSUPPORTED, "rope_dims %d above %d", p->rope_dims,
+                    2 * mimo::kMaxRopeHalfArgs);
+    if (p->layer_kind != MIMO_LAYER_GLOBAL && p->layer_kind != MIMO_LAYER_SWA)
+        return fail(MIMO_ERR_INVALID_ARG, "layer_kind %d is neither GLOBAL (0) nor SWA (1)",
+                    p->layer_kind);
+    if (p->layer_kind == MIMO_LAYER_SWA && p->window < 1)
+        return fail(MIMO_ERR_INVALID_ARG, "sliding-window layer needs window >= 1 (got %d)",
+                    p->window);
+    if (p->layer_kind == MIMO_LAYER_GLOBAL && p->window != 0)
+        return fail(MIMO_ERR_INVALID_ARG, "global layer needs window == 0 (got %d)", p->window);
+    if (p->rope_dims > 0 && !(p->rope_theta > 0.0 && isfinite(p->rope_theta)))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+    if (!isfinite(p->v_scale)) return fail(MIMO_ERR_INVALID_ARG, "v_scale must be finite");
+    if (!(p->softmax_scale >= 0.0f) || !isfinite(p->softmax_scale))
+        return fail(MIMO_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (p->dtype == MIMO_BF16) {
+        if (p->qk_head_dim != kBf16Dqk || p->v_head_dim != kBf16Dv)
+            return fail(MIMO_ERR_UNSUPPORTED, "bf16 kernels cover (dqk, dv) = (192, 128), got (%d, %d)",
+                        p->qk_head_dim, p->v_head_dim);
+        if (p->rope_dims % 16)
+            return fail(MIMO_ERR_UNSUPPORTED, "bf16 kernels need rope_dims %% 16 == 0 (got %d)",
+                        p->rope_dims);
+    } else if (p->dtype == MIMO_F32) {
+        if (p->qk_head_dim > kF32MaxDim || p->v_head_dim > kF32MaxDim)
+            return fail(MIMO_ERR_UNSUPPORTED, "fp32 kernels cover head dims <= %d", kF32MaxDim);
+    } else {
+        return fail(MIMO_ERR_INVALID_ARG, "dtype %d is neither MIMO_F32 (0) nor MIMO_BF16 (1)",
+                    p->dtype);
+    }
+    return MIMO_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
+    if (p->dtype != MIMO_BF16 || p->layer_kind != MIMO_LAYER_GLOBAL) return 0;
+    return (size_t)p->batch * p->num_kv_heads * (size_t)S * p->qk_head_dim * 2;
+}
+
+// Decode split size: slots per workgroup, a power of two >= 256, large enough to keep the grid
+// (B * Hkv * splits) within 8192 workgroups.
+int decode_chunk(const mimo_attn_params* p, int32_t max_position) {
+    const int64_t n_max = p->layer_kind == MIMO_LAYER_SWA
+                              ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
+                              : (int64_t)max_position + 1;
+    int64_t chunk = 256;
+    while ((int64_t)p->batch * p->num_kv_heads * ((n_max + chunk - 1) / chunk) > 8192) chunk *= 2;
+    if (p->layer_kind == MIMO_LAYER_SWA && n_max <= 1024) chunk = n_max < 1 ? 1 : n_max;
+    return (int)chunk;
+}
+
+int decode_nsplit(const mimo_attn_params* p, int32_t max_position) {
+    const int64_t n_max = p->layer_kind == MIMO_LAYER_SWA
+                              ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
+                              : (int64_t)max_position + 1;
+    const int chunk = decode_chunk(p, max_position);
+    return (int)((n_max + chunk - 1) / chunk);
+}
+
+size_t decode_ws(const mimo_attn_params* p, int32_t max_position) {
+    if (p->dtype != MIMO_BF16) return 0;
+    const int ns = decode_nsplit(p, max_position);
+    if (ns <= 1) return 0;
+    return (size_t)p->batch * p->num_q_heads * (size_t)ns * (p->v_head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_abi_version(void) { return MIMO_ATTN_ABI_VERSION; }
+
+const char* mimo_attn_last_error(void) { return g_err; }
+
+int mimo_attn_check_params(const mimo_attn_params* p) {
+    const int rc = check(p);
+    return rc == MIMO_OK ? ok() : rc;
+}
+
+size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_len) {
+    if (check(p) != MIMO_OK || seq_len < 0) return 0;
+    return prefill_ws(p, seq_len);
+}
+
+size_t mimo_attn_decode_workspace_size(const mimo_attn_params* p, int32_t max_position) {
+    if (check(p) != MIMO_OK || max_position < 0) return 0;
+    return decode_ws(p, max_position);
+}
+
+int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q, const void* k,
+                      const void* v, const int32_t* start_pos, const float* sinks, void* out,
+                      void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int rc = check(p);
+    if (rc != MIMO_OK) return rc;
+    if (seq_len < 0) return fail(MIMO_ERR_INVALID_ARG, "seq_len %d < 0", seq_len);
+    if (p->batch == 0 || seq_len == 0) return ok();
+    if (!q || !k || !v || !start_pos || !out)
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, start_pos and out must be non-NULL");
+    if ((k_cache == nullptr) != (v_cache == nullptr))
+        return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both be NULL");
+    const bool has_cache = k_cache != nullptr;
+    const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    if (has_cache) {
+        if (cache_capacity < 1) return fail(MIMO_ERR_INVALID_ARG, "cache_capacity must be >= 1");
+        if (swa && cache_capacity != p->window)
+            return fail(MIMO_ERR_INVALID_ARG, "ring cache capacity %d must equal window %d",
+                        cache_capacity, p->window);
+    }
+    if ((int64_t)seq_len * p->num_q_heads * p->batch > ((int64_t)1 << 40))
+        return fail(MIMO_ERR_INVALID_ARG, "problem too large");
+    const size_t need = prefill_ws(p, seq_len);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    hipStream_t st = (hipStream_t)stream;
+
+    mimo::RopeKVArgs ra;
+    memset(&ra, 0, sizeof ra);
+    ra.k = k;
+    ra.v = v;
+    ra.start_pos = start_pos;
+    ra.B = p->batch;
+    ra.S = seq_len;
+    ra.Hkv = p->num_kv_heads;
+    ra.dqk = p->qk_head_dim;
+    ra.dv = p->v_head_dim;
+    ra.rope_dims = p->rope_dims;
+    ra.cap = cache_capacity;
+    ra.ring_window = swa ? p->window : 0;
+    ra.i0 = (swa && has_cache && seq_len > p->window) ? seq_len - p->window : 0;
+    if (has_cache) {
+        ra.k_dst = k_cache;
+        ra.v_dst = v_cache;
+    }
+    fill_omega(p, ra.omega);
+
+    if (p->dtype == MIMO_F32) {
+        mimo::F32PrefillArgs fa;
+        memset(&fa, 0, sizeof fa);
+        fa.q = (const float*)q;
+        fa.k = (const float*)k;
+        fa.v = (const float*)v;
+        fa.start_pos = start_pos;
+        fa.sinks = sinks;
+        fa.out = (float*)out;
+        fa.B = p->batch;
+        fa.S = seq_len;
+        fa.Hq = p->num_q_heads;
+        fa.Hkv = p->num_kv_heads;
+        fa.dqk = p->qk_head_dim;
+        fa.dv = p->v_head_dim;
+        fa.rope_dims = p->rope_dims;
+        fa.window = p->window;
+        fa.layer_kind = p->layer_kind;
+        fa.score_scale = score_scale(p);
+        fa.v_scale = p->v_scale;
+        fill_omega(p, fa.omega);
+        rc = hip_status(mimo::launch_prefill_f32(fa, st), "prefill (fp32)");
+        if (rc != MIMO_OK || !has_cache) return rc;
+        return hip_status(mimo::launch_rope_kv_f32(ra, st), "cache store (fp32)");
+    }
+
+    mimo::PrefillArgs pa;
+    memset(&pa, 0, sizeof pa);
+    pa.q = (const uint16_t*)q;
+    pa.v = (const uint16_t*)v;
+    pa.start_pos = start_pos;
+    pa.sinks = sinks;
+    pa.out = (uint16_t*)out;
+    pa.B = p->batch;
+    pa.S = seq_len;
+    pa.Hq = p->num_q_heads;
+    pa.Hkv = p->num_kv_heads;
+    pa.rope_dims = p->rope_dims;
+    pa.window = p->window;
+    pa.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
+    pa.v_scale = p->v_scale;
+    fill_omega(p, pa.omega);
+    const int64_t dqk = p->qk_head_dim;
+    if (swa) {
+        // raw K read straight from the input and rotated while it is staged
+        pa.k = (const uint16_t*)k;
+        pa.k_sb = (int64_t)seq_len * p->num_kv_heads * dqk;
+        pa.k_sh = dqk;
+        pa.k_sj = (int64_t)p->num_kv_heads * dqk;
+        pa.k_pos_off = 0;
+        rc = hip_status(mimo::launch_prefill_bf16(pa, true, sinks != nullptr, true, st),
+                        "prefill (bf16, sliding)");
+        if (rc != MIMO_OK || !has_cache) return rc;
+        return hip_status(mimo::launch_rope_kv_bf16(ra, st), "ring cache store (bf16)");
+    }
+    // global: rotate K once into the workspace (and the linear cache), then attend
+    ra.k_ws = workspace;
+    rc = hip_status(mimo::launch_rope_kv_bf16(ra, st), "key rotation (bf16)");
+    if (rc != MIMO_OK) return rc;
+    pa.k = (const uint16_t*)workspace;
+    pa.k_sb = (int64_t)p->num_kv_heads * seq_len * dqk;
+    pa.k_sh = (int64_t)seq_len * dqk;
+    pa.k_sj = dqk;
+    pa.k_pos_off = 0;
+    return hip_status(mimo::launch_prefill_bf16(pa, false, sinks != nullptr, false, st),
+                      "prefill (bf16, global)");
+}
+
+int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,
+                     const void* v_new, const int32_t* positions, int32_t max_position,
+                     void* k_cache, void* v_cache, int32_t cache_capacity, const float* sinks,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check(p);
+    if (rc != MIMO_OK) return rc;
+    if (max_position < 0) return fail(MIMO_ERR_INVALID_ARG, "max_position %d < 0", max_position);
+    if (p->batch == 0) return ok();
+    if (!q || !k_new || !v_new || !positions || !k_cache || !v_cache || !out)
+        return fail(MIMO_ERR_INVALID_ARG,
+                    "q, k_new, v_new, positions, k_cache, v_cache and out must be non-NULL");
+    const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    if (swa && cache_capacity != p->window)
+        return fail(MIMO_ERR_INVALID_ARG, "ring cache capacity %d must equal window %d",
+                    cache_capacity, p->window);
+    if (!swa && (int64_t)cache_capacity <= (int64_t)max_position)
+        return fail(MIMO_ERR_INVALID_ARG, "linear cache capacity %d must exceed max_position %d",
+                    cache_capacity, max_position);
+    hipStream_t st = (hipStream_t)stream;
+    if (p->dtype == MIMO_F32) {
+        mimo::F32DecodeArgs fa;
+        memset(&fa, 0, sizeof fa);
+        fa.q = (const float*)q;
+        fa.k_new = (const float*)k_new;
+        fa.v_new = (const float*)v_new;
+        fa.positions = positions;
+        fa.k_cache = (float*)k_cache;
+        fa.v_cache = (float*)v_cache;
+        fa.sinks = sinks;
+        fa.out = (float*)out;
+        fa.B = p->batch;
+        fa.Hq = p->num_q_heads;
+        fa.Hkv = p->num_kv_heads;
+        fa.dqk = p->qk_head_dim;
+        fa.dv = p->v_head_dim;
+        fa.rope_dims = p->rope_dims;
+        fa.window = p->window;
+        fa.layer_kind = p->layer_kind;
+        fa.cap = cache_capacity;
+        fa.max_position = max_position;
+        fa.score_scale = score_scale(p);
+        fa.v_scale = p->v_scale;
+        fill_omega(p, fa.omega);
+        return hip_status(mimo::launch_decode_f32(fa, st), "decode (fp32)");
+    }
+    if (p->num_q_heads / p->num_kv_heads > kMaxDecodeGroup)
+        return fail(MIMO_ERR_UNSUPPORTED, "bf16 decode packs at most %d query heads per KV head",
+                    kMaxDecodeGroup);
+    const size_t need = decode_ws(p, max_position);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    mimo::DecodeArgs da;
+    memset(&da, 0, sizeof da);
+    da.q = (const uint16_t*)q;
+    da.k_new = (const uint16_t*)k_new;
+    da.v_new = (const uint16_t*)v_new;
+    da.positions = positions;
+    da.k_cache = (uint16_t*)k_cache;
+    da.v_cache = (uint16_t*)v_cache;
+    da.sinks = sinks;
+    da.out = (uint16_t*)out;
+    da.partial = (float*)workspace;
+    da.B = p->batch;
+    da.Hq = p->num_q_heads;
+    da.Hkv = p->num_kv_heads;
+    da.rope_dims = p->rope_dims;
+    da.window = p->window;
+    da.cap = cache_capacity;
+    da.max_position = max_position;
+    da.chunk = decode_chunk(p, max_position);
+    da.nsplit = decode_nsplit(p, max_position);
+    da.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
+    da.v_scale = p->v_scale;
+    fill_omega(p, da.omega);
+    return hip_status(mimo::launch_decode_bf16(da, swa, sinks != nullptr, st), "decode (bf16)");
+}
+
+}  // extern "C"

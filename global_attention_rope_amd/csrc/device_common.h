@@ -1,0 +1,82 @@
+// device_common.h — types and small device helpers shared by the gfx950 kernels of this library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+
+// Largest rotated width the kernels accept (frequencies are passed by value in kernel args).
+constexpr int kMaxRopeHalf = 128;
+
+// cos/sin of pos * omega.  The angle is formed and reduced to [-pi, pi] in fp64 (positions reach
+// tens of thousands of radians), then evaluated in fp32.
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, double omega, float& c, float& s) {
+    const double a = (double)pos * omega;
+    const double red = a - rint(a * kInvTwoPi) * kTwoPi;
+    sincosf((float)red, &s, &c);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Unpack 8 bf16 held in a 16-byte word into fp32.
+__device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f[2 * t] = __uint_as_float(w[t] << 16);
+        f[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+    u32x4 w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(f[2 * t], f[2 * t + 1]);
+    return w;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// D = A(32x16) * B(16x32) + C, bf16 operands, fp32 accumulate.
+//   A: lane l holds row (l % 32), k = 8 * (l / 32) + [0, 8).
+//   B: lane l holds column (l % 32), k = 8 * (l / 32) + [0, 8).
+//   C/D: lane l holds column (l % 32), rows 8 * (i / 4) + 4 * (l / 32) + (i % 4), i in [0, 16).
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A(16x32) * B(32x16) + C, bf16 operands, fp32 accumulate.
+//   A: lane l holds row (l % 16), k = 8 * (l / 16) + [0, 8).
+//   B: lane l holds column (l % 16), k = 8 * (l / 16) + [0, 8).
+//   C/D: lane l holds column (l % 16), rows 4 * (l / 16) + i, i in [0, 4).
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace mimo

@@ -1,0 +1,102 @@
+// kernels.h — argument blocks and launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value
+
+// Rotate K (first rope_dims dims) once per token i in [i0, S) of each sequence b (position
+// start_pos[b] + i) and store it
+//   * into k_ws [B,Hkv,S,dqk] at row i, when k_ws is set (rotated-K scratch of a prefill);
+//   * with V into the cache k_dst [B,Hkv,cap,dqk] / v_dst [B,Hkv,cap,dv], when k_dst is set, at
+//     slot position % ring_window (ring_window > 0) or slot position (linear; a token whose slot
+//     falls outside [0, cap) is not stored).
+struct RopeKVArgs {
+    const void* k;       // [B,S,Hkv,dqk]
+    const void* v;       // [B,S,Hkv,dv]
+    const int32_t* start_pos;
+    void* k_ws;          // [B,Hkv,S,dqk] or null
+    void* k_dst;         // [B,Hkv,cap,dqk] or null
+    void* v_dst;         // [B,Hkv,cap,dv], set iff k_dst is
+    int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, ring_window;
+    double omega[kMaxRopeHalfArgs];
+};
+
+// bf16 prefill.  K rows are read from k + b*k_sb + g*k_sh + (j + (k_pos_off ? start_pos[b] : 0))*k_sj
+// (element strides); when rot_k they are raw input rows rotated in the kernel, otherwise they are
+// already rotated.  V rows come from the input v [B,S,Hkv,128].
+struct PrefillArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* start_pos;
+    const float* sinks;
+    uint16_t* out;
+    int64_t k_sb, k_sh, k_sj;
+    int32_t k_pos_off;
+    int32_t B, S, Hq, Hkv, rope_dims, window;
+    float score_scale_log2;
+    float v_scale;
+    double omega[kMaxRopeHalfArgs];
+};
+
+// bf16 decode (split-K over cache slots).
+struct DecodeArgs {
+    const uint16_t* q;       // [B,Hq,192]
+    const uint16_t* k_new;   // [B,Hkv,192]
+    const uint16_t* v_new;   // [B,Hkv,128]
+    const int32_t* positions;
+    uint16_t* k_cache;       // [B,Hkv,cap,192]
+    uint16_t* v_cache;       // [B,Hkv,cap,128]
+    const float* sinks;
+    uint16_t* out;           // [B,Hq,128]
+    float* partial;          // [B,Hq,nsplit,130] (split mode)
+    int32_t B, Hq, Hkv, rope_dims, window, cap, max_position, chunk, nsplit;
+    float score_scale_log2;
+    float v_scale;
+    double omega[kMaxRopeHalfArgs];
+};
+
+// fp32 vector-ALU kernels for small head dims (dqk, dv <= 256).
+struct F32PrefillArgs {
+    const float* q;
+    const float* k;
+    const float* v;
+    const int32_t* start_pos;
+    const float* sinks;
+    float* out;
+    int32_t B, S, Hq, Hkv, dqk, dv, rope_dims, window, layer_kind;
+    float score_scale;
+    float v_scale;
+    double omega[kMaxRopeHalfArgs];
+};
+
+struct F32DecodeArgs {
+    const float* q;
+    const float* k_new;
+    const float* v_new;
+    const int32_t* positions;
+    float* k_cache;
+    float* v_cache;
+    const float* sinks;
+    float* out;
+    int32_t B, Hq, Hkv, dqk, dv, rope_dims, window, layer_kind, cap, max_position;
+    float score_scale;
+    float v_scale;
+    double omega[kMaxRopeHalfArgs];
+};
+
+hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
+hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, bool swa, bool sink, bool rot_k,
+                               hipStream_t st);
+hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);
+hipError_t launch_prefill_f32(const F32PrefillArgs& a, hipStream_t st);
+hipError_t launch_decode_f32(const F32DecodeArgs& a, hipStream_t st);
+
+// Query rows per prefill workgroup (bf16 kernel).
+int prefill_bf16_block_rows();
+
+}  // namespace mimo

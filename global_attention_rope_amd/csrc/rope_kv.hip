@@ -1,0 +1,129 @@
+// rope_kv.hip — rotate keys once and store them (and V) in cache-layout buffers [B, Hkv, n, d].
+//
+// Partial RoPE (pages: "Add Xiaomi MiMo-V2", "Additional useful info": the leading third of the
+// head dim is rotated; "add Xiaomi MiMo v2 (mimo_v2_flash)", "Architecture, verified against
+// upstream": rotated width int(partial_rotary_factor * head_dim), per-kind theta): pair
+// (d, d + r/2), d < r/2, is turned by position * theta^(-2d/r); dims >= r are copied.
+// Destinations: the rotated-K scratch of a global prefill (row = token index), the linear cache of
+// global layers (slot = position) and the rotating cache of sliding layers (slot = position %
+// window; "add Xiaomi MiMo v2 (mimo_v2_flash)", "Implementation plan").
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mimo {
+namespace {
+
+// Cache slot of a token, or -1 when it is not stored.
+__device__ __forceinline__ int cache_slot(const RopeKVArgs& a, int32_t pos) {
+    if (!a.k_dst || pos < 0) return -1;
+    if (a.ring_window > 0) return pos % a.ring_window;
+    return pos < a.cap ? pos : -1;
+}
+
+// bf16: one thread per 8-element chunk of a K or V row.
+__global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
+    const int kch = a.dqk / 8, vch = a.k_dst ? a.dv / 8 : 0, per_row = kch + vch;
+    const int ntok = a.S - a.i0;
+    const int64_t total = (int64_t)a.B * ntok * a.Hkv * per_row;
+    const int r = a.rope_dims, half = r >> 1;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(e % per_row);
+        const int64_t rowid = e / per_row;
+        const int g = (int)(rowid % a.Hkv);
+        const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
+        const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
+        const int32_t pos = a.start_pos[b] + i;
+        const int slot = cache_slot(a, pos);
+        const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
+        if (c < kch) {
+            const uint16_t* krow = (const uint16_t*)a.k + src_row * a.dqk;
+            const int d0 = c * 8;
+            u32x4 w = *(const u32x4*)(krow + d0);
+            if (d0 < r) {
+                const int pd = d0 < half ? d0 + half : d0 - half;
+                const u32x4 pw = *(const u32x4*)(krow + pd);
+                float x[8], y[8];
+                unpack8(w, x);
+                unpack8(pw, y);
+                const bool lower = d0 < half;
+                const int f0 = lower ? d0 : d0 - half;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    float cs, sn;
+                    rope_cos_sin(pos, a.omega[f0 + t], cs, sn);
+                    x[t] = lower ? (x[t] * cs - y[t] * sn) : (x[t] * cs + y[t] * sn);
+                }
+                w = pack8(x);
+            }
+            if (a.k_ws)
+                *(u32x4*)((uint16_t*)a.k_ws + (((int64_t)b * a.Hkv + g) * a.S + i) * a.dqk + d0) = w;
+            if (slot >= 0)
+                *(u32x4*)((uint16_t*)a.k_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dqk + d0) = w;
+        } else if (slot >= 0) {
+            const int d0 = (c - kch) * 8;
+            *(u32x4*)((uint16_t*)a.v_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d0) =
+                *(const u32x4*)((const uint16_t*)a.v + src_row * a.dv + d0);
+        }
+    }
+}
+
+// fp32: one thread per element.
+__global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
+    const int per_row = a.dqk + (a.k_dst ? a.dv : 0);
+    const int ntok = a.S - a.i0;
+    const int64_t total = (int64_t)a.B * ntok * a.Hkv * per_row;
+    const int r = a.rope_dims, half = r >> 1;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(e % per_row);
+        const int64_t rowid = e / per_row;
+        const int g = (int)(rowid % a.Hkv);
+        const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
+        const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
+        const int32_t pos = a.start_pos[b] + i;
+        const int slot = cache_slot(a, pos);
+        const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
+        if (c < a.dqk) {
+            const float* krow = (const float*)a.k + src_row * a.dqk;
+            float x = krow[c];
+            if (c < r) {
+                const bool lower = c < half;
+                float cs, sn;
+                rope_cos_sin(pos, a.omega[lower ? c : c - half], cs, sn);
+                x = lower ? (x * cs - krow[c + half] * sn) : (x * cs + krow[c - half] * sn);
+            }
+            if (a.k_ws) ((float*)a.k_ws)[(((int64_t)b * a.Hkv + g) * a.S + i) * a.dqk + c] = x;
+            if (slot >= 0) ((float*)a.k_dst)[(((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dqk + c] = x;
+        } else if (slot >= 0) {
+            const int d = c - a.dqk;
+            ((float*)a.v_dst)[(((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d] =
+                ((const float*)a.v)[src_row * a.dv + d];
+        }
+    }
+}
+
+unsigned grid_for(int64_t total) {
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return (unsigned)(blocks > 0 ? blocks : 1);
+}
+
+}  // namespace
+
+hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st) {
+    const int64_t total =
+        (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk / 8 + (a.k_dst ? a.dv / 8 : 0));
+    if (total <= 0 || (!a.k_ws && !a.k_dst)) return hipSuccess;
+    rope_kv_bf16_kernel<<<grid_for(total), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st) {
+    const int64_t total = (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk + (a.k_dst ? a.dv : 0));
+    if (total <= 0 || (!a.k_ws && !a.k_dst)) return hipSuccess;
+    rope_kv_f32_kernel<<<grid_for(total), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace mimo

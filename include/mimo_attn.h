@@ -1,0 +1,149 @@
+/*
+ * mimo_attn.h — C ABI of the MI355X (gfx950) hybrid attention library `libmimo_attn.so`.
+ *
+ * The layer is the attention of the MiMo-V2-Flash decoder as the pages describe it:
+ *   - "Add Xiaomi MiMo-V2" (transformers PR 45144), section "Additional useful info": sliding-
+ *     window (SWA) and global (GA) layers use different RoPE bases and different KV-group counts;
+ *     the V head dim is separate from the QK head dim; values are scaled by
+ *     sqrt(hidden / (num_attention_heads * v_head_dim)); the attention sink is used on SWA layers
+ *     only; partial RoPE rotates the leading third of the QK head dim.
+ *   - Same PR, description: gpt-oss-style attention sinks together with dual theta and dual
+ *     head dims.
+ *   - "feat(models): add Xiaomi MiMo v2 (mimo_v2_flash) text model support" (mlxcel issue 842),
+ *     "Architecture, verified against upstream": the layer kind comes from hybrid_layer_pattern
+ *     (1 = sliding); theta is swa_rope_theta on sliding layers, rope_theta otherwise; the rotated
+ *     width is int(partial_rotary_factor * head_dim); the window is sliding_window_size.
+ *     "Implementation plan": sliding layers keep a rotating KV cache.
+ *
+ * Computed, per query head h of sequence b at position p_i:
+ *   q', k' = q, k with pairs (d, d + r/2), d < r/2, turned by p * theta^(-2d/r); dims >= r as is.
+ *   z_j    = tau * <q'_i, k'_j>, tau = softmax_scale (0 selects 1/sqrt(qk_head_dim)),
+ *            k'_j from KV head h / (Hq / Hkv).
+ *   visible j: 0 <= p_i - p_j (GA); 0 <= p_i - p_j < window (SWA).
+ *   out    = v_scale * sum_j e^{z_j} v_j / (e^{s_h} + sum_j e^{z_j}),  s_h = -inf without sinks.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are caller-owned memory on the current HIP device, dense row-major, with the shapes
+ *     given below.  dtype MIMO_BF16: q/k/v/out/caches are bf16, arithmetic fp32 with bf16 MFMA
+ *     operands.  dtype MIMO_F32: all of them fp32, arithmetic fp32.
+ *   - sinks is fp32 [Hq] or NULL (no sink).  Position arrays are int32 in device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  Nothing is
+ *     synchronised, allocated, freed or printed by the library, and it keeps no global state;
+ *     calls are thread-safe.  Calls that write the same cache or workspace must be ordered by
+ *     the caller (same stream or events).
+ *   - Arguments are checked on the host before anything is enqueued.  On error the function
+ *     returns a negative MIMO_ERR_* code, writes nothing, and mimo_attn_last_error() returns a
+ *     message (thread-local).  MIMO_ERR_HIP means a launch failed; the message holds HIP's text.
+ */
+#ifndef MIMO_ATTN_H
+#define MIMO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIMO_ATTN_ABI_VERSION 1
+
+enum mimo_attn_status {
+    MIMO_OK = 0,
+    MIMO_ERR_INVALID_ARG = -1, /* a null pointer, a bad size or an inconsistent parameter    */
+    MIMO_ERR_UNSUPPORTED = -2, /* a valid layer the compiled kernels do not cover            */
+    MIMO_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_size()       */
+    MIMO_ERR_HIP = -4          /* a HIP launch failed                                        */
+};
+
+enum mimo_attn_layer_kind { /* the value of hybrid_layer_pattern[layer] */
+    MIMO_LAYER_GLOBAL = 0,
+    MIMO_LAYER_SWA = 1
+};
+
+enum mimo_attn_dtype { MIMO_F32 = 0, MIMO_BF16 = 1 };
+
+typedef struct mimo_attn_params {
+    int32_t batch;         /* B >= 1                                                         */
+    int32_t num_q_heads;   /* Hq >= 1                                                        */
+    int32_t num_kv_heads;  /* Hkv >= 1, divides Hq (GQA group = Hq / Hkv)                    */
+    int32_t qk_head_dim;   /* dqk                                                            */
+    int32_t v_head_dim;    /* dv                                                             */
+    int32_t rope_dims;     /* r: even, 0 <= r <= dqk; 0 = no rotation                        */
+    int32_t layer_kind;    /* MIMO_LAYER_GLOBAL or MIMO_LAYER_SWA                            */
+    int32_t window;        /* SWA: >= 1, keys with 0 <= p_q - p_k < window; GLOBAL: 0         */
+    double rope_theta;     /* base of the layer kind, > 0 when r > 0                         */
+    float v_scale;         /* multiplies the output; sqrt(hidden / (Hq * dv)) in the model   */
+    float softmax_scale;   /* 0 selects 1 / sqrt(dqk)                                        */
+    int32_t dtype;         /* MIMO_BF16 or MIMO_F32                                          */
+    int32_t reserved;      /* must be 0                                                      */
+} mimo_attn_params;
+
+/*
+ * Head-dim support.  MIMO_BF16 runs the bf16-MFMA kernels, compiled for (dqk, dv) = (192, 128),
+ * the head shape of both layer kinds at full size.  MIMO_F32 runs fp32 vector kernels for any
+ * dqk <= 256 and dv <= 256 (used for small fp32 layers).  Other combinations return
+ * MIMO_ERR_UNSUPPORTED.
+ */
+
+/*
+ * Prefill: attention of S new tokens per sequence over themselves.
+ *   q [B,S,Hq,dqk], k [B,S,Hkv,dqk], v [B,S,Hkv,dv]; out [B,S,Hq,dv].
+ *   start_pos [B] (device): token i of sequence b sits at position start_pos[b] + i (>= 0).
+ *   Only the S given tokens are attended (no earlier cache content is read).
+ *   Caches (optional; both NULL or both set; bf16 for MIMO_BF16, fp32 for MIMO_F32):
+ *     GLOBAL: linear, k_cache [B,Hkv,cache_capacity,dqk], v_cache [B,Hkv,cache_capacity,dv];
+ *             token i is stored at slot start_pos[b] + i, which must be < cache_capacity
+ *             (checked by the kernel: a token whose slot would be out of range is not stored).
+ *     SWA:    ring, cache_capacity == window; the last min(S, window) tokens are stored at slot
+ *             position % window.
+ *     K is stored rotated, V as given.
+ *   workspace: device scratch of at least mimo_attn_prefill_workspace_size() bytes (may be NULL
+ *   when that size is 0).  Its contents are not needed across calls.
+ */
+int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q, const void* k,
+                      const void* v, const int32_t* start_pos, const float* sinks, void* out,
+                      void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mimo_attn_prefill needs for this layer and seq_len (bf16 global layers keep
+ * their rotated keys there: B * Hkv * seq_len * dqk * 2 bytes; 0 otherwise).  Returns 0 for
+ * invalid parameters. */
+size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_len);
+
+/*
+ * Decode: one new token per sequence against the KV cache, which it also appends to.
+ *   q [B,Hq,dqk], k_new [B,Hkv,dqk], v_new [B,Hkv,dv] (raw: not rotated); out [B,Hq,dv].
+ *   positions [B] (device): tokens already cached for sequence b = position of the new token.
+ *   max_position (host): an upper bound of every positions[b]; it sizes the grid and the
+ *   workspace.  A sequence whose position exceeds it, or whose slot exceeds the linear cache,
+ *   produces a zero output and is not appended.
+ *   GLOBAL: linear cache [B,Hkv,cache_capacity,d], cache_capacity > max_position; the new
+ *           token goes to slot positions[b] and keys 0..positions[b] are attended.
+ *   SWA:    ring cache [B,Hkv,window,d], cache_capacity == window; the new token overwrites
+ *           slot positions[b] % window and the min(window, positions[b] + 1) most recent
+ *           positions are attended.
+ *   The new key is rotated at positions[b] before it is stored and used.
+ *   workspace: at least mimo_attn_decode_workspace_size() bytes, for split-K partial results.
+ */
+int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,
+                     const void* v_new, const int32_t* positions, int32_t max_position,
+                     void* k_cache, void* v_cache, int32_t cache_capacity, const float* sinks,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mimo_attn_decode needs: B * Hq * splits * (dv + 2) * 4 when the cache range is
+ * cut into several splits, else 0.  Returns 0 for invalid parameters. */
+size_t mimo_attn_decode_workspace_size(const mimo_attn_params* p, int32_t max_position);
+
+/* Host-only validation of a parameter block (no device access): MIMO_OK or a negative code. */
+int mimo_attn_check_params(const mimo_attn_params* p);
+
+/* Message of the last error on the calling thread ("" after success). */
+const char* mimo_attn_last_error(void);
+
+/* MIMO_ATTN_ABI_VERSION of the built library. */
+int mimo_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MIMO_ATTN_H */

@@ -37,6 +37,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
@@ -65,6 +68,15 @@ static int check_params(const oracle_params* p) {
 
 static double score_scale(const oracle_params* p) {
     return p->softmax_scale != 0.0 ? p->softmax_scale : 1.0 / sqrt((double)p->qk_head_dim);
+}
+
+/* Threads the oracle's parallel loops use (reported beside its timings). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* Frequencies of the rotated slice: omega_d = theta^(-2d/r), d in [0, r/2). */

@@ -80,6 +80,8 @@ def _load():
                                           ctypes.c_int32, ctypes.c_int32, f64]
             lib.oracle_decode.argtypes = [P(_CParams), f32, f32, f32, i32, f32, f32, i32, i32,
                                           ctypes.c_int32, f32, f64, f64, i32, ctypes.c_int32]
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
             for fn in ("oracle_rope_omega", "oracle_rope_rotate", "oracle_prefill",
                        "oracle_scores", "oracle_decode"):
                 getattr(lib, fn).restype = ctypes.c_int
@@ -106,6 +108,10 @@ def _ptr(a, ctype):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
 
 
 def omega(rope_dims: int, theta: float) -> np.ndarray:

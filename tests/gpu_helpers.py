@@ -1,0 +1,51 @@
+"""Helpers for the GPU parity tests: comparisons and oracle-side views of seeded inputs.
+
+Tolerance for bf16 inputs with fp32 accumulation (absolute 1e-2, relative 2e-2): PASS iff every
+element satisfies |gpu - oracle| <= 1e-2 + 2e-2 * |oracle| (allclose form of the two bounds) and
+the whole tensor satisfies ||gpu - oracle||_2 / ||oracle||_2 <= 2e-2.  The bf16 output alone is
+rounded by up to 2^-9 * |x| (0.0078 at |x| = 4), so a bare max-abs bound of 1e-2 would reject
+correctly rounded large outputs.  fp32 layers: absolute 2e-5, relative 1e-5, same form.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+BF16_MAX_ABS, BF16_REL_L2 = 1e-2, 2e-2
+F32_MAX_ABS, F32_REL_L2 = 2e-5, 1e-5
+
+
+def to_np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def errors(gpu: np.ndarray, ref: np.ndarray):
+    d = gpu.astype(np.float64) - ref
+    max_abs = float(np.abs(d).max()) if d.size else 0.0
+    nrm = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d)) / nrm if nrm > 0 else float(np.linalg.norm(d))
+    return max_abs, rel
+
+
+def assert_close(gpu, ref, fp32=False, what=""):
+    gpu = to_np64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    max_abs, rel = errors(gpu, ref)
+    lim_abs, lim_rel = (F32_MAX_ABS, F32_REL_L2) if fp32 else (BF16_MAX_ABS, BF16_REL_L2)
+    excess = np.abs(gpu - ref) - (lim_abs + lim_rel * np.abs(ref))
+    worst = int(np.argmax(excess)) if excess.size else 0
+    ok_elem = excess.size == 0 or excess.flat[worst] <= 0
+    assert ok_elem and rel <= lim_rel, (
+        f"{what}: worst element {np.unravel_index(worst, gpu.shape)} gpu {gpu.flat[worst]:.5f} "
+        f"oracle {ref.flat[worst]:.5f}; max_abs {max_abs:.3e}, rel_l2 {rel:.3e} "
+        f"(limits abs {lim_abs} + rel {lim_rel})")
+    print(f"  [{what}] max_abs {max_abs:.3e} rel_l2 {rel:.3e}", flush=True)
+    return max_abs, rel
+
+
+def ring_positions(pos: int, window: int) -> np.ndarray:
+    """Position held by each ring slot just before the token at `pos` is appended: the most
+    recent position < pos congruent to the slot (negative: the slot is still empty)."""
+    s = np.arange(window)
+    return pos - 1 - ((pos - 1 - s) % window)

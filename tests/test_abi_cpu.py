@@ -1,0 +1,150 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function include/mimo_attn.h
+declares, and rejects every invalid argument with its code before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import global_attention_rope_amd as mimo
+from global_attention_rope_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mimo_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mimo_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 7
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in mimo_attn.h but not exported"
+    assert set(names) == set(binding.EXPORTS)
+    assert mimo.lib().mimo_attn_abi_version() == 1
+
+
+def _swa(**kw):
+    d = dict(batch=1, num_q_heads=64, num_kv_heads=8, qk_head_dim=192, v_head_dim=128,
+             rope_dims=64, layer_kind=mimo.LAYER_SWA, window=128, rope_theta=1e4,
+             v_scale=0.70710678, dtype=mimo.BF16)
+    d.update(kw)
+    return mimo.Params(**d)
+
+
+def _ga(**kw):
+    d = dict(num_kv_heads=4, layer_kind=mimo.LAYER_GLOBAL, window=0, rope_theta=5e6)
+    d.update(kw)
+    return _swa(**d)
+
+
+@pytest.mark.parametrize("p", [_swa(), _ga(), _swa(rope_dims=0), _ga(rope_dims=192),
+                               _swa(dtype=mimo.F32, qk_head_dim=32, v_head_dim=16, rope_dims=10,
+                                    num_q_heads=4, num_kv_heads=1, window=16),
+                               _ga(batch=0)])
+def test_valid_params(p):
+    assert mimo.check_params(p) == mimo.MIMO_OK, mimo.last_error()
+    assert mimo.last_error() == ""
+
+
+@pytest.mark.parametrize("p,code", [
+    (_swa(rope_dims=63), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(rope_dims=194), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(rope_dims=-2), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(num_kv_heads=7), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(num_kv_heads=0), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(window=0), mimo.MIMO_ERR_INVALID_ARG),
+    (_ga(window=128), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(layer_kind=2), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(rope_theta=0.0), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(rope_theta=float("inf")), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(v_scale=float("nan")), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(softmax_scale=-1.0), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(batch=-1), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(dtype=7), mimo.MIMO_ERR_INVALID_ARG),
+    (_swa(qk_head_dim=128), mimo.MIMO_ERR_UNSUPPORTED),
+    (_swa(v_head_dim=192), mimo.MIMO_ERR_UNSUPPORTED),
+    (_swa(rope_dims=40), mimo.MIMO_ERR_UNSUPPORTED),
+    (_swa(dtype=mimo.F32, qk_head_dim=512), mimo.MIMO_ERR_UNSUPPORTED),
+])
+def test_invalid_params_rejected_with_code_and_message(p, code):
+    assert mimo.check_params(p) == code
+    assert mimo.last_error() != ""
+
+
+def test_reserved_field_must_be_zero():
+    cp = _swa().c()
+    cp.reserved = 1
+    assert mimo.lib().mimo_attn_check_params(ctypes.byref(cp)) == mimo.MIMO_ERR_INVALID_ARG
+    assert mimo.lib().mimo_attn_check_params(None) == mimo.MIMO_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    assert mimo.prefill_workspace_size(_swa(), 4096) == 0
+    assert mimo.prefill_workspace_size(_ga(), 8192) == 1 * 4 * 8192 * 192 * 2
+    assert mimo.prefill_workspace_size(_ga(rope_dims=63), 8192) == 0  # invalid -> 0
+    # the 128-slot ring fits one split: no partials
+    assert mimo.decode_workspace_size(_swa(batch=64), 40000) == 0
+    ws = mimo.decode_workspace_size(_ga(batch=64), 32768)
+    assert ws > 0 and ws % (64 * 64 * 130 * 4) == 0
+    assert mimo.decode_workspace_size(_ga(batch=64), 100) == 0
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    _L = mimo.lib()
+    return _L
+
+
+def _prefill(p, S=16, q=1, k=1, v=1, sp=1, out=1, kc=None, vc=None, cap=0, ws=None, wsb=0):
+    cp = p.c()
+    P = ctypes.c_void_p
+    ptr = lambda x: None if x is None else P(0x1000 * x)  # never dereferenced: rejected first
+    return _lib().mimo_attn_prefill(ctypes.byref(cp), S, ptr(q), ptr(k), ptr(v), ptr(sp), None,
+                                    ptr(out), ptr(kc), ptr(vc), cap, ptr(ws), wsb, None)
+
+
+def _decode(p, maxp=10, q=1, kn=1, vn=1, pos=1, kc=1, vc=1, cap=128, out=1, ws=None, wsb=0):
+    cp = p.c()
+    P = ctypes.c_void_p
+    ptr = lambda x: None if x is None else P(0x1000 * x)
+    return _lib().mimo_attn_decode(ctypes.byref(cp), ptr(q), ptr(kn), ptr(vn), ptr(pos), maxp,
+                                   ptr(kc), ptr(vc), cap, None, ptr(out), ptr(ws), wsb, None)
+
+
+def test_prefill_argument_errors_return_before_any_launch():
+    E = mimo.MIMO_ERR_INVALID_ARG
+    assert _prefill(_swa(rope_dims=5)) == E
+    assert _prefill(_swa(), S=-1) == E
+    assert _prefill(_swa(), q=None) == E
+    assert _prefill(_swa(), out=None) == E
+    assert _prefill(_swa(), sp=None) == E
+    assert _prefill(_swa(), kc=3, vc=None, cap=128) == E
+    assert _prefill(_swa(), kc=3, vc=4, cap=64) == E       # ring capacity != window
+    assert _prefill(_ga(), kc=3, vc=4, cap=0) == E
+    assert _prefill(_ga(), ws=None) == mimo.MIMO_ERR_WORKSPACE
+    assert _prefill(_ga(), S=16, ws=5, wsb=100) == mimo.MIMO_ERR_WORKSPACE
+    assert "workspace" in mimo.last_error()
+    # nothing to do: success without touching any pointer
+    assert _prefill(_swa(), S=0, q=None, k=None, v=None, sp=None, out=None) == mimo.MIMO_OK
+    assert _prefill(_swa(batch=0), q=None) == mimo.MIMO_OK
+
+
+def test_decode_argument_errors_return_before_any_launch():
+    E = mimo.MIMO_ERR_INVALID_ARG
+    assert _decode(_swa(), maxp=-1) == E
+    assert _decode(_swa(), kc=None) == E
+    assert _decode(_swa(), pos=None) == E
+    assert _decode(_swa(), cap=100) == E                   # ring capacity != window
+    assert _decode(_ga(), maxp=500, cap=500) == E          # linear cache too short
+    assert _decode(_ga(batch=64), maxp=32768, cap=40000) == mimo.MIMO_ERR_WORKSPACE
+    assert _decode(_ga(num_q_heads=68, num_kv_heads=2), cap=40) == mimo.MIMO_ERR_UNSUPPORTED
+    assert _decode(_swa(batch=0), q=None) == mimo.MIMO_OK

@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by element.
+
+Small cases span several tiles with ragged tails and the band edges; full-size workloads are
+compared whole where the oracle finishes in seconds, else on sampled rows.  Seeds: 1000 * case +
+layer.  Tolerances in tests/gpu_helpers.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import global_attention_rope_amd as mimo
+import oracle
+from oracle import OracleParams
+from tests import synth
+from tests.gpu_helpers import assert_close, ring_positions, to_np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _wl(kind, B, S, Hq, Hkv, sinks, W=128, theta=None, r=64, dtype=torch.bfloat16, dqk=192,
+        dv=128, hidden=4096):
+    return synth.Workload("case", batch=B, seq=S, num_q_heads=Hq, num_kv_heads=Hkv, qk_head_dim=dqk,
+                          v_head_dim=dv, rope_dims=r,
+                          rope_theta=theta if theta else (1e4 if kind == 1 else 5e6),
+                          layer_kind=kind, window=W if kind == 1 else 0, sinks=sinks,
+                          hidden=hidden, dtype=dtype)
+
+
+def _params(w, batch=None):
+    return mimo.Params(batch=w.batch if batch is None else batch, num_q_heads=w.num_q_heads,
+                       num_kv_heads=w.num_kv_heads, qk_head_dim=w.qk_head_dim,
+                       v_head_dim=w.v_head_dim, rope_dims=w.rope_dims, layer_kind=w.layer_kind,
+                       window=w.window, rope_theta=w.rope_theta, v_scale=w.v_scale,
+                       dtype=mimo.BF16 if w.dtype == torch.bfloat16 else mimo.F32)
+
+
+def _oparams(w, batch=None):
+    return OracleParams(batch=w.batch if batch is None else batch, num_q_heads=w.num_q_heads,
+                        num_kv_heads=w.num_kv_heads, qk_head_dim=w.qk_head_dim,
+                        v_head_dim=w.v_head_dim, rope_dims=w.rope_dims, layer_kind=w.layer_kind,
+                        window=w.window, rope_theta=w.rope_theta, v_scale=w.v_scale)
+
+
+def _f32(t):
+    return None if t is None else t.to("cpu", torch.float32).numpy()
+
+
+def _run_prefill(w, seed, starts, rows=None, with_cache=False, cap=None, q_scale=1.0):
+    q, k, v, s = synth.layer_inputs(w, seed, device=DEV)
+    if q_scale != 1.0:
+        q = q * q_scale  # a power of two: exact in bf16
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    kc = vc = None
+    if with_cache:
+        cap = cap if cap else (w.window if w.layer_kind == 1 else max(starts) + w.seq + 7)
+        kc = torch.full((w.batch, w.num_kv_heads, cap, w.qk_head_dim), 7.0, dtype=w.dtype, device=DEV)
+        vc = torch.full((w.batch, w.num_kv_heads, cap, w.v_head_dim), 7.0, dtype=w.dtype, device=DEV)
+    out = mimo.prefill(_params(w), q, k, v, sp, sinks=s, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    pos = np.stack([np.arange(w.seq, dtype=np.int32) + st for st in starts])
+    ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s), rows=rows,
+                         want_k_rot=with_cache)
+    return (q, k, v, s, out, ref, kc, vc, pos)
+
+
+# ----------------------------------------------------------------------------- prefill
+
+
+def test_tiny_swa_fp32_full():
+    w = synth.TINY_SWA
+    _note(w.name)
+    *_, out, ref, _, _, _ = _run_prefill(w, seed=0, starts=[0])
+    assert_close(out, ref, fp32=True, what=w.name)
+
+
+@pytest.mark.parametrize("case", [
+    dict(kind=1, B=2, S=300, Hq=16, Hkv=2, sinks=True, starts=[0, 1000]),
+    dict(kind=1, B=1, S=77, Hq=8, Hkv=8, sinks=True, starts=[5], W=1),
+    dict(kind=1, B=1, S=260, Hq=8, Hkv=1, sinks=False, starts=[0], W=200),
+    dict(kind=1, B=2, S=130, Hq=8, Hkv=2, sinks=True, starts=[3, 0], W=4096),
+    dict(kind=1, B=1, S=190, Hq=8, Hkv=4, sinks=True, starts=[0], W=65, r=0),
+    dict(kind=0, B=2, S=333, Hq=16, Hkv=1, sinks=False, starts=[0, 20000]),
+    dict(kind=0, B=1, S=129, Hq=8, Hkv=2, sinks=True, starts=[7]),
+    dict(kind=0, B=1, S=1, Hq=4, Hkv=4, sinks=False, starts=[0]),
+    # every dim rotated: q scaled by 1/4 so the softmax is flat enough that bf16 rounding of the
+    # rotated operands (all 192 dims here) stays inside the tolerance on the first rows
+    dict(kind=0, B=1, S=257, Hq=8, Hkv=2, sinks=False, starts=[0], r=192, theta=10.0,
+         q_scale=0.25),
+])
+def test_prefill_bf16_small(case):
+    case = dict(case)
+    starts = case.pop("starts")
+    q_scale = case.pop("q_scale", 1.0)
+    w = _wl(**case)
+    _note(str(case))
+    *_, out, ref, _, _, _ = _run_prefill(w, seed=1000 + w.seq, starts=starts, q_scale=q_scale)
+    assert_close(out, ref, what=str(case))
+
+
+def test_prefill_swa_full_size_all_rows():
+    w = synth.SWA_PREFILL
+    _note(w.name)
+    *_, out, ref, _, _, _ = _run_prefill(w, seed=1000, starts=[0])
+    assert_close(out, ref, what=w.name)
+
+
+def test_prefill_global_full_size_sampled_rows():
+    w = synth.GA_PREFILL
+    _note(w.name)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.seq - 64, w.seq),
+                                     rng.integers(0, w.seq, 128)])).astype(np.int32)
+    *_, out, ref, _, _, _ = _run_prefill(w, seed=2000, starts=[0], rows=rows)
+    assert_close(out[:, rows], ref[:, rows], what=w.name)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_prefill_writes_caches(kind):
+    w = _wl(kind=kind, B=2, S=200, Hq=8, Hkv=2, sinks=kind == 1, W=128)
+    starts = [0, 50]
+    _note(f"cache kind={kind}")
+    q, k, v, s, out, (ref, krot), kc, vc, pos = _run_prefill(w, seed=3000 + kind, starts=starts,
+                                                             with_cache=True)
+    assert_close(out, ref, what="out")
+    kc_h, vc_h = to_np64(kc), to_np64(vc)
+    v_h = to_np64(v)
+    cap = kc.shape[2]
+    for b in range(w.batch):
+        written = set()
+        for i in range(w.seq):
+            p = int(pos[b, i])
+            if kind == 1 and i < w.seq - w.window:
+                continue
+            slot = p % w.window if kind == 1 else p
+            written.add(slot)
+            # rotated key: bf16 rounding of the exact rotation
+            exp = krot[b, i]
+            np.testing.assert_allclose(kc_h[b, :, slot], exp, rtol=2 ** -8, atol=1e-6)
+            # value: copied bit for bit
+            assert np.array_equal(vc_h[b, :, slot], v_h[b, i])
+        untouched = [sl for sl in range(cap) if sl not in written]
+        assert all((kc_h[b, :, sl] == 7.0).all() and (vc_h[b, :, sl] == 7.0).all() for sl in untouched)
+
+
+def test_prefill_deterministic():
+    w = _wl(kind=0, B=1, S=500, Hq=16, Hkv=1, sinks=False)
+    q, k, v, s = synth.layer_inputs(w, 4000, device=DEV)
+    sp = torch.zeros(1, dtype=torch.int32, device=DEV)
+    a = mimo.prefill(_params(w), q, k, v, sp, sinks=s)
+    b = mimo.prefill(_params(w), q, k, v, sp, sinks=s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_prefill_empty_and_invalid_arguments():
+    w = _wl(kind=1, B=1, S=0, Hq=8, Hkv=1, sinks=True)
+    q, k, v, s = synth.layer_inputs(w, 1, device=DEV)
+    sp = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = mimo.prefill(_params(w), q, k, v, sp, sinks=s)
+    assert out.shape[1] == 0
+    bad = _params(w)
+    bad.rope_dims = 63
+    w2 = _wl(kind=1, B=1, S=16, Hq=8, Hkv=1, sinks=True)
+    q, k, v, s = synth.layer_inputs(w2, 1, device=DEV)
+    sentinel = torch.full((1, 16, 8, 128), 3.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mimo.MimoAttnError) as ei:
+        mimo.prefill(bad, q, k, v, sp, sinks=s, out=sentinel)
+    assert ei.value.code == mimo.MIMO_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (sentinel == 3.0).all()  # nothing written on error
+
+
+# ----------------------------------------------------------------------------- decode
+
+
+def _decode_case(w, positions, seed, cap=None):
+    """Random cache state + one decode step on the GPU, and the oracle on the same state."""
+    B = len(positions)
+    swa = w.layer_kind == 1
+    cap = w.window if swa else (cap if cap else max(positions) + 1)
+    q, kn, vn, s, kc, vc = synth.decode_inputs(w, seed, B, cap, device=DEV)
+    kc0, vc0 = _f32(kc), _f32(vc)
+    pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    out = mimo.decode(_params(w, B), q, kn, vn, pos_t, max(positions), kc, vc, sinks=s)
+    torch.cuda.synchronize()
+    if swa:
+        # occupied ring slots only (a slot still empty holds no token), packed first
+        kc_o = np.zeros_like(kc0)
+        vc_o = np.zeros_like(vc0)
+        kpos = np.zeros((B, w.window), np.int32)
+        cnt = np.zeros(B, np.int32)
+        for b, p in enumerate(positions):
+            held = ring_positions(p, w.window)
+            slots = np.nonzero(held >= 0)[0]
+            n = len(slots)
+            kc_o[b, :, :n] = kc0[b, :, slots].transpose(1, 0, 2)
+            vc_o[b, :, :n] = vc0[b, :, slots].transpose(1, 0, 2)
+            kpos[b, :n] = held[slots]
+            cnt[b] = n
+        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(positions),
+                                  kc_o, vc_o, kpos, cnt, _f32(s), want_k_rot=True)
+    else:
+        kpos = np.tile(np.arange(cap, dtype=np.int32), (B, 1))
+        cnt = np.array(positions, np.int32)
+        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(positions),
+                                  kc0, vc0, kpos, cnt, _f32(s), want_k_rot=True)
+    return out, ref, krot, kc, vc, kc0, vc0, vn
+
+
+@pytest.mark.parametrize("case", [
+    dict(kind=0, Hq=16, Hkv=1, sinks=False, positions=[0, 1, 255, 256, 257, 1000, 4097]),
+    dict(kind=0, Hq=8, Hkv=2, sinks=True, positions=[31, 32, 33]),
+    dict(kind=1, Hq=8, Hkv=1, sinks=True, positions=[0, 5, 126, 127, 128, 129, 300, 5000]),
+    dict(kind=1, Hq=16, Hkv=2, sinks=False, positions=[1, 200]),
+])
+def test_decode_bf16_small(case):
+    case = dict(case)
+    positions = case.pop("positions")
+    w = _wl(B=len(positions), S=1, **case)
+    _note(str(case) + str(positions))
+    out, ref, krot, kc, vc, kc0, vc0, vn = _decode_case(w, positions, seed=5000 + len(positions))
+    assert_close(out, ref, what=str(case))
+    # the new token was appended (rotated key, raw value) and nothing else changed
+    kc_h, vc_h = _f32(kc), _f32(vc)
+    vn_h = _f32(vn)
+    for b, p in enumerate(positions):
+        slot = p % w.window if w.layer_kind == 1 else p
+        np.testing.assert_allclose(kc_h[b, :, slot], krot[b], rtol=2 ** -8, atol=1e-6)
+        assert np.array_equal(vc_h[b, :, slot], vn_h[b])
+        kc_h[b, :, slot] = kc0[b, :, slot]
+        vc_h[b, :, slot] = vc0[b, :, slot]
+    assert np.array_equal(kc_h, kc0) and np.array_equal(vc_h, vc0)
+
+
+def test_decode_fp32_tiny():
+    w = synth.Workload("tiny_dec", batch=3, seq=1, num_q_heads=4, num_kv_heads=1, qk_head_dim=32,
+                       v_head_dim=16, rope_dims=10, rope_theta=1e4, layer_kind=1, window=16,
+                       sinks=True, hidden=64, dtype=torch.float32)
+    out, ref, *_ = _decode_case(w, [3, 15, 40], seed=6000)
+    assert_close(out, ref, fp32=True, what="fp32 decode")
+
+
+def test_decode_full_size_global_sampled_sequences():
+    """64 sequences with cached lengths uniform in [1024, 32768], linear caches; the oracle checks
+    a sample of sequences (shortest, longest and random ones)."""
+    w = _wl(kind=0, B=synth.DECODE_BATCH, S=1, Hq=64, Hkv=4, sinks=False)
+    lengths = synth.decode_lengths(3)
+    positions = lengths.tolist()
+    B, cap = len(positions), max(positions) + 1
+    _note(f"decode GA full B={B} cap={cap}")
+    q, kn, vn, s, kc, vc = synth.decode_inputs(w, 7000, B, cap, device=DEV)
+    pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    out = mimo.decode(_params(w, B), q, kn, vn, pos_t, max(positions), kc, vc, sinks=s)
+    torch.cuda.synchronize()
+    order = np.argsort(positions)
+    sample = sorted({int(order[0]), int(order[-1]), 5, 17, 42})
+    for b in sample:
+        L = positions[b]
+        kcb = kc[b:b + 1, :, :L].to("cpu", torch.float32).numpy()
+        vcb = vc[b:b + 1, :, :L].to("cpu", torch.float32).numpy()
+        ref = oracle.decode(_oparams(w, 1), _f32(q[b:b + 1]), _f32(kn[b:b + 1]), _f32(vn[b:b + 1]),
+                            np.array([L]), kcb, vcb, np.arange(L, dtype=np.int32)[None],
+                            np.array([L]), None)
+        assert_close(out[b:b + 1], ref, what=f"seq {b} len {L}")
+
+
+def test_decode_full_size_swa_all_sequences():
+    w = _wl(kind=1, B=synth.DECODE_BATCH, S=1, Hq=64, Hkv=8, sinks=True)
+    positions = synth.decode_lengths(4).tolist()
+    _note("decode SWA full")
+    out, ref, *_ = _decode_case(w, positions, seed=8000)
+    assert_close(out, ref, what="swa decode full")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_prefill_then_decode_matches_longer_prefill(kind):
+    """prefill(S) writing the cache, then one decode step == row S of prefill(S + 1)."""
+    S = 300
+    w = _wl(kind=kind, B=2, S=S + 1, Hq=16, Hkv=2, sinks=kind == 1)
+    q, k, v, s = synth.layer_inputs(w, 9000 + kind, device=DEV)
+    starts = [0, 11]
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    cap = w.window if kind == 1 else S + 20
+    kc = torch.zeros((2, w.num_kv_heads, cap, 192), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros((2, w.num_kv_heads, cap, 128), dtype=torch.bfloat16, device=DEV)
+    wS = _wl(kind=kind, B=2, S=S, Hq=16, Hkv=2, sinks=kind == 1)
+    mimo.prefill(_params(wS), q[:, :S].contiguous(), k[:, :S].contiguous(), v[:, :S].contiguous(),
+                 sp, sinks=s, k_cache=kc, v_cache=vc)
+    pos = torch.tensor([S + st for st in starts], dtype=torch.int32, device=DEV)
+    dec = mimo.decode(_params(wS), q[:, S].contiguous(), k[:, S].contiguous(), v[:, S].contiguous(),
+                      pos, max(starts) + S, kc, vc, sinks=s)
+    full = mimo.prefill(_params(w), q, k, v, sp, sinks=s)
+    torch.cuda.synchronize()
+    posn = np.stack([np.arange(S + 1, dtype=np.int32) + st for st in starts])
+    ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), posn, _f32(s),
+                         rows=np.array([S], np.int32))
+    assert_close(dec, ref[:, S], what="decode after prefill")
+    assert_close(full[:, S], ref[:, S], what="longer prefill")
