@@ -63,9 +63,9 @@ def decode_counts(B, Hq, Hkv, kind, W, positions):
 
 
 def cpu_baseline(stack_cfg, seed_base):
-    """The fp64 oracle on a bounded sample of the same workload: sequence 0 of layer 0 (global)
-    over its first 3072 tokens, of layer 1 (sliding) over its first 4096 tokens, and one global
-    decode step at position 3072 against the oracle's own rotated keys."""
+    """The fp64 oracle on a bounded sample of the same workload (about 15 s of host work): sequence
+    0 of layer 0 (global) over its first 6144 tokens, of layer 1 (sliding) over its first 4096
+    tokens, and one global decode step at position 6144 against the oracle's own rotated keys."""
     import numpy as np
     import torch
 
@@ -73,7 +73,7 @@ def cpu_baseline(stack_cfg, seed_base):
     from tests import synth
 
     ga, swa = synth.GA_PREFILL, synth.SWA_PREFILL
-    S_ga, S_swa = 3072, 4096
+    S_ga, S_swa = 6144, 4096
     f = lambda t: t.to(torch.float32).numpy()
     q, k, v, _ = synth.layer_inputs(ga, seed_base + 0, batch=1, seq=S_ga + 1)
     q2, k2, v2, s2 = synth.layer_inputs(swa, seed_base + 1, batch=1, seq=S_swa)

@@ -31,11 +31,13 @@ int ok() {
 
 constexpr int kBf16Dqk = 192, kBf16Dv = 128, kF32MaxDim = 256, kMaxDecodeGroup = 16;
 
-// Frequencies of the rotated slice: omega_d = theta^(-2d/r), d < r/2.
-void fill_omega(const mimo_attn_params* p, double* omega) {
-    for (int d = 0; d < mimo::kMaxRopeHalfArgs; ++d) omega[d] = 0.0;
+// Frequencies of the rotated slice, omega_d = theta^(-2d/r) for d < r/2, in revolutions per
+// position (omega_d / 2pi) as the kernels take them.
+void fill_omega(const mimo_attn_params* p, double* omega_rev) {
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int d = 0; d < mimo::kMaxRopeHalfArgs; ++d) omega_rev[d] = 0.0;
     for (int d = 0; d < p->rope_dims / 2; ++d)
-        omega[d] = pow(p->rope_theta, -2.0 * (double)d / (double)p->rope_dims);
+        omega_rev[d] = pow(p->rope_theta, -2.0 * (double)d / (double)p->rope_dims) / two_pi;
 }
 
 float score_scale(const mimo_attn_params* p) {
@@ -102,13 +104,16 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
 }
 
 // Decode split size: slots per workgroup, a power of two >= 256, large enough to keep the grid
-// (B * Hkv * splits) within 8192 workgroups.
+// (B * Hkv * splits) within 8192 workgroups and the splits per sequence within what the combine
+// kernel merges.
 int decode_chunk(const mimo_attn_params* p, int32_t max_position) {
     const int64_t n_max = p->layer_kind == MIMO_LAYER_SWA
                               ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
                               : (int64_t)max_position + 1;
     int64_t chunk = 256;
-    while ((int64_t)p->batch * p->num_kv_heads * ((n_max + chunk - 1) / chunk) > 8192) chunk *= 2;
+    while ((int64_t)p->batch * p->num_kv_heads * ((n_max + chunk - 1) / chunk) > 8192 ||
+           (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
+        chunk *= 2;
     if (p->layer_kind == MIMO_LAYER_SWA && n_max <= 1024) chunk = n_max < 1 ? 1 : n_max;
     return (int)chunk;
 }
@@ -197,7 +202,7 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
         ra.k_dst = k_cache;
         ra.v_dst = v_cache;
     }
-    fill_omega(p, ra.omega);
+    fill_omega(p, ra.omega_rev);
 
     if (p->dtype == MIMO_F32) {
         mimo::F32PrefillArgs fa;
@@ -219,7 +224,7 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
         fa.layer_kind = p->layer_kind;
         fa.score_scale = score_scale(p);
         fa.v_scale = p->v_scale;
-        fill_omega(p, fa.omega);
+        fill_omega(p, fa.omega_rev);
         rc = hip_status(mimo::launch_prefill_f32(fa, st), "prefill (fp32)");
         if (rc != MIMO_OK || !has_cache) return rc;
         return hip_status(mimo::launch_rope_kv_f32(ra, st), "cache store (fp32)");
@@ -240,7 +245,7 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     pa.window = p->window;
     pa.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
     pa.v_scale = p->v_scale;
-    fill_omega(p, pa.omega);
+    fill_omega(p, pa.omega_rev);
     const int64_t dqk = p->qk_head_dim;
     if (swa) {
         // raw K read straight from the input and rotated while it is staged
@@ -309,7 +314,7 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
         fa.max_position = max_position;
         fa.score_scale = score_scale(p);
         fa.v_scale = p->v_scale;
-        fill_omega(p, fa.omega);
+        fill_omega(p, fa.omega_rev);
         return hip_status(mimo::launch_decode_f32(fa, st), "decode (fp32)");
     }
     if (p->num_q_heads / p->num_kv_heads > kMaxDecodeGroup)
@@ -341,7 +346,7 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
     da.nsplit = decode_nsplit(p, max_position);
     da.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
     da.v_scale = p->v_scale;
-    fill_omega(p, da.omega);
+    fill_omega(p, da.omega_rev);
     return hip_status(mimo::launch_decode_bf16(da, swa, sinks != nullptr, st), "decode (bf16)");
 }
 

@@ -18,7 +18,7 @@ __device__ __forceinline__ void rotate_f32(const float* x, float* y, int dim, in
     const int half = r >> 1;
     for (int d = 0; d < half; ++d) {
         float c, s;
-        rope_cos_sin(pos, omega[d], c, s);
+        rope_cos_sin_rev(pos, omega[d], c, s);
         y[d] = x[d] * c - x[d + half] * s;
         y[d + half] = x[d + half] * c + x[d] * s;
     }
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const F32PrefillArgs a)
     const int32_t p0 = a.start_pos[b];
     float qr[MAXD], kr[MAXD], acc[MAXD];
     rotate_f32(a.q + (((int64_t)b * a.S + i) * a.Hq + h) * a.dqk, qr, a.dqk, a.rope_dims, p0 + i,
-               a.omega);
+               a.omega_rev);
     for (int e = 0; e < a.dv; ++e) acc[e] = 0.0f;
     const bool swa = a.layer_kind == 1;
     const int lo = swa ? max(0, i - a.window + 1) : 0;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const F32PrefillArgs a)
     float m = sink, l = a.sinks ? 1.0f : 0.0f;  // the sink: logit s_h, no value
     for (int j = lo; j <= i; ++j) {
         const int64_t row = ((int64_t)b * a.S + j) * a.Hkv + g;
-        rotate_f32(a.k + row * a.dqk, kr, a.dqk, a.rope_dims, p0 + j, a.omega);
+        rotate_f32(a.k + row * a.dqk, kr, a.dqk, a.rope_dims, p0 + j, a.omega_rev);
         float z = 0.0f;
         for (int d = 0; d < a.dqk; ++d) z = fmaf(qr[d], kr[d], z);
         z *= a.score_scale;
@@ -72,8 +72,8 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const F32DecodeArgs a) {
     const int slot_new = swa ? pos % a.window : pos;
     const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.cap;
     float qr[MAXD], kn[MAXD], acc[MAXD];
-    rotate_f32(a.q + ((int64_t)b * a.Hq + h) * a.dqk, qr, a.dqk, a.rope_dims, pos, a.omega);
-    rotate_f32(a.k_new + ((int64_t)b * a.Hkv + g) * a.dqk, kn, a.dqk, a.rope_dims, pos, a.omega);
+    rotate_f32(a.q + ((int64_t)b * a.Hq + h) * a.dqk, qr, a.dqk, a.rope_dims, pos, a.omega_rev);
+    rotate_f32(a.k_new + ((int64_t)b * a.Hkv + g) * a.dqk, kn, a.dqk, a.rope_dims, pos, a.omega_rev);
     const float* vn = a.v_new + ((int64_t)b * a.Hkv + g) * a.dv;
     for (int e = 0; e < a.dv; ++e) acc[e] = 0.0f;
     float m = -INFINITY, l = 0.0f;

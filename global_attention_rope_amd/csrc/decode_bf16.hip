@@ -4,17 +4,21 @@
 // decoupled V dim, value rescale, SWA-only sink); "add Xiaomi MiMo v2 (mimo_v2_flash)", section
 // "Implementation plan" (sliding layers keep a rotating cache of the window).
 //
-// Per (sequence b, KV head g, split s) one workgroup:
-//   * rotates the query heads of group g (<= 16) at the new token's position and keeps Q^T as the
+// Per (sequence b, KV head g, split s) one workgroup of 4 waves:
+//   * each wave issues the loads of its first 32-slot tile (K straight into MFMA operand layout,
+//     V as coalesced 16-byte rows) before anything else, so their latency overlaps the query
+//     rotation;
+//   * the query heads of group g (<= 16) are rotated at the new token's position and kept as the
 //     B operand of v_mfma_f32_16x16x32_bf16 (heads are the 16-wide N dimension);
 //   * the split that owns the new token's slot rotates k_new, stores it and v_new into the cache
 //     (linear: slot = position; ring: slot = position % window) and substitutes them for that
-//     slot in its own tile loads, so no workgroup reads a slot another one is writing;
-//   * each wave streams 32-slot tiles: S^T = K * Q^T (rotated keys come from the cache), online
-//     softmax per head in the log2 domain, O^T += V^T * P^T;
-//   * the four waves are merged through LDS; with one split the sink is folded in and the bf16
-//     output is written, otherwise (max, sum, O) partials go to the workspace and a combine kernel
-//     merges the splits and adds the sink exactly once.
+//     slot, so no workgroup reads a slot another one is writing;
+//   * per tile: S^T = K * Q^T, online softmax per head in the log2 domain, V staged in a per-wave
+//     LDS tile and read transposed with ds_read_b64_tr_b16, O^T += V^T * P^T; the next tile's
+//     loads are in flight meanwhile;
+//   * the waves are merged through LDS; with one split the sink is folded in and the bf16 output
+//     written, otherwise (max, sum, O) partials go to the workspace and the combine kernel merges
+//     the splits and adds the sink exactly once.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,9 +30,14 @@ constexpr int DV = 128;
 constexpr int NW = 4;
 constexpr int TILE = 32;                 // slots per wave iteration
 constexpr int PSTRIDE = DV + 2;          // floats per partial record: O[128], m, l
+constexpr int VT_PITCH = DV + 16;        // bf16 per V row in the per-wave LDS tile (288 bytes)
+constexpr int KREG = 2 * (DQK / 32);     // 16-byte K operand loads per lane per tile (12)
+constexpr int VREG = TILE * DV / 8 / 64; // 16-byte V loads per lane per tile (8)
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ u32x4 rotate8_dec(const u32x4& w, const u32x4& pw, int d0, int half,
-                                             int32_t pos, const double* omega) {
+                                             int32_t pos, const double* om) {
     float x[8], y[8];
     unpack8(w, x);
     unpack8(pw, y);
@@ -37,19 +46,27 @@ __device__ __forceinline__ u32x4 rotate8_dec(const u32x4& w, const u32x4& pw, in
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         float c, s;
-        rope_cos_sin(pos, omega[f0 + t], c, s);
+        rope_cos_sin_rev(pos, om[f0 + t], c, s);
         x[t] = lower ? (x[t] * c - y[t] * s) : (x[t] * c + y[t] * s);
     }
     return pack8(x);
 }
 
+struct LdsDecode {
+    uint16_t Qs[16 * DQK];
+    uint16_t Kn[DQK];
+    uint16_t Vn[DV];
+    double om[kMaxRopeHalf];
+    float red_m[NW][16], red_l[NW][16];
+    union {
+        uint16_t vt[NW][TILE * VT_PITCH];     // per-wave V tiles
+        float red_o[NW][16][DV + 1];          // wave merge, after the slot loop
+    } u;
+};
+
 template <bool SWA, bool SINK, bool SPLIT>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[16 * DQK];
-    __shared__ __attribute__((aligned(16))) uint16_t Kn[DQK];
-    __shared__ __attribute__((aligned(16))) uint16_t Vn[DV];
-    __shared__ float red_m[NW][16], red_l[NW][16];
-    __shared__ float red_o[NW][16][DV + 1];
+    __shared__ __attribute__((aligned(16))) LdsDecode sm;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -72,7 +89,35 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     const bool own_new = slot_new >= k_begin && slot_new < k_end;
     const int r = a.rope_dims, half = r >> 1;
     const int64_t cache_row0 = ((int64_t)b * a.Hkv + g) * a.cap;
+    const uint16_t* kc = a.k_cache + cache_row0 * DQK;
+    const uint16_t* vc = a.v_cache + cache_row0 * DV;
 
+    // ---- tile loads (slots >= k_end and the new token's slot read as zero here)
+    u32x4 kreg[KREG], vreg[VREG];
+    auto fetch = [&](int t0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int j = t0 + kb * 16 + l16;
+            const bool ok = j < k_end && j != slot_new;
+#pragma unroll
+            for (int c = 0; c < DQK / 32; ++c)
+                kreg[kb * (DQK / 32) + c] =
+                    ok ? *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < VREG; ++it) {
+            const int e = lane + 64 * it;
+            const int row = e / (DV / 8), col = e % (DV / 8);
+            const int j = t0 + row;
+            vreg[it] = (j < k_end && j != slot_new) ? *(const u32x4*)(vc + (int64_t)j * DV + col * 8)
+                                                    : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    int t0 = k_begin + wave * TILE;
+    if (t0 < k_end) fetch(t0);
+
+    for (int f = tid; f < half; f += 256) sm.om[f] = a.omega_rev[f];
+    __syncthreads();
     // ---- rotated queries of this group -> LDS (heads >= G are zero).
     for (int c = tid; c < 16 * (DQK / 8); c += 256) {
         const int hh = c / (DQK / 8), col = c % (DQK / 8);
@@ -83,10 +128,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             if (col * 8 < r) {
                 const int d0 = col * 8;
                 const int pd = d0 < half ? d0 + half : d0 - half;
-                wv = rotate8_dec(wv, *(const u32x4*)(qrow + pd), d0, half, pos, a.omega);
+                wv = rotate8_dec(wv, *(const u32x4*)(qrow + pd), d0, half, pos, sm.om);
             }
         }
-        *(u32x4*)(Qs + hh * DQK + col * 8) = wv;
+        *(u32x4*)(sm.Qs + hh * DQK + col * 8) = wv;
     }
     // ---- the new token: rotate, keep in LDS, append to the cache.
     if (own_new && tid < DQK / 8 + DV / 8) {
@@ -96,14 +141,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             u32x4 wv = *(const u32x4*)(krow + d0);
             if (d0 < r) {
                 const int pd = d0 < half ? d0 + half : d0 - half;
-                wv = rotate8_dec(wv, *(const u32x4*)(krow + pd), d0, half, pos, a.omega);
+                wv = rotate8_dec(wv, *(const u32x4*)(krow + pd), d0, half, pos, sm.om);
             }
-            *(u32x4*)(Kn + d0) = wv;
+            *(u32x4*)(sm.Kn + d0) = wv;
             *(u32x4*)(a.k_cache + (cache_row0 + slot_new) * DQK + d0) = wv;
         } else {
             const int d0 = (tid - DQK / 8) * 8;
             const u32x4 wv = *(const u32x4*)(a.v_new + ((int64_t)b * a.Hkv + g) * DV + d0);
-            *(u32x4*)(Vn + d0) = wv;
+            *(u32x4*)(sm.Vn + d0) = wv;
             *(u32x4*)(a.v_cache + (cache_row0 + slot_new) * DV + d0) = wv;
         }
     }
@@ -111,43 +156,56 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 
     bf16x8 Qb[DQK / 32];
 #pragma unroll
-    for (int c = 0; c < DQK / 32; ++c) Qb[c] = *(const bf16x8*)(Qs + l16 * DQK + 32 * c + 8 * gq);
+    for (int c = 0; c < DQK / 32; ++c) Qb[c] = *(const bf16x8*)(sm.Qs + l16 * DQK + 32 * c + 8 * gq);
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 O[DV / 16];
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db) O[db] = f32x4{};
+    uint16_t* vt = sm.u.vt[wave];
 
-    const uint16_t* kc = a.k_cache + cache_row0 * DQK;
-    const uint16_t* vc = a.v_cache + cache_row0 * DV;
-
-    for (int t0 = k_begin + wave * TILE; t0 < k_end; t0 += NW * TILE) {
+    for (; t0 < k_end; t0 += NW * TILE) {
+        // the new token's slot comes from LDS
+        if (own_new) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (t0 + kb * 16 + l16 == slot_new) {
+#pragma unroll
+                    for (int c = 0; c < DQK / 32; ++c)
+                        kreg[kb * (DQK / 32) + c] = *(const u32x4*)(sm.Kn + 32 * c + 8 * gq);
+                }
+#pragma unroll
+            for (int it = 0; it < VREG; ++it) {
+                const int e = lane + 64 * it;
+                if (t0 + e / (DV / 8) == slot_new) vreg[it] = *(const u32x4*)(sm.Vn + (e % (DV / 8)) * 8);
+            }
+        }
+        // V rows -> this wave's LDS tile
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < VREG; ++it) {
+            const int e = lane + 64 * it;
+            *(u32x4*)(vt + (e / (DV / 8)) * VT_PITCH + (e % (DV / 8)) * 8) = vreg[it];
+        }
         // S^T (16 slots x 16 heads) for the two 16-slot blocks of the tile.
         f32x4 Sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int j = t0 + kb * 16 + l16;
-            u32x4 kw[DQK / 32];
-#pragma unroll
-            for (int c = 0; c < DQK / 32; ++c) {
-                u32x4 wv = u32x4{0u, 0u, 0u, 0u};
-                if (j < k_end) {
-                    wv = (j == slot_new) ? *(const u32x4*)(Kn + 32 * c + 8 * gq)
-                                         : *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq);
-                }
-                kw[c] = wv;
-            }
             f32x4 acc = f32x4{};
 #pragma unroll
-            for (int c = 0; c < DQK / 32; ++c) acc = mfma16x16x32(as_bf16x8(kw[c]), Qb[c], acc);
+            for (int c = 0; c < DQK / 32; ++c)
+                acc = mfma16x16x32(as_bf16x8(kreg[kb * (DQK / 32) + c]), Qb[c], acc);
             Sacc[kb] = acc;
         }
+        const int t_cur = t0;
+        if (t0 + NW * TILE < k_end) fetch(t0 + NW * TILE);
+
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = t0 + kb * 16 + 4 * gq + i;
+                const int j = t_cur + kb * 16 + 4 * gq + i;
                 const float sc = j < k_end ? Sacc[kb][i] * a.score_scale_log2 : -INFINITY;
                 Sacc[kb][i] = sc;
                 mx = fmaxf(mx, sc);
@@ -157,14 +215,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = fast_exp2(m_run - m_use);
         m_run = m_new;
         float psum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = exp2f(Sacc[kb][i] - m_use);
+                const float p = fast_exp2(Sacc[kb][i] - m_use);
                 Sacc[kb][i] = p;
                 psum += p;
             }
@@ -177,37 +235,34 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                                           pack_bf16x2(Sacc[0][2], Sacc[0][3]),
                                           pack_bf16x2(Sacc[1][0], Sacc[1][1]),
                                           pack_bf16x2(Sacc[1][2], Sacc[1][3])});
-        int jt[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) jt[t] = t0 + (t < 4 ? 4 * gq + t : 16 + 4 * gq + (t - 4));
+        __builtin_amdgcn_wave_barrier();
+        // V^T operand: lane j of group gq points at V[key0 + j/4][16db + 4(j%4)] and receives
+        // V[key0 + t][16db + j], t < 4, with key0 = 4gq (first read) and 16 + 4gq (second).
 #pragma unroll
         for (int db = 0; db < DV / 16; ++db) {
-            const int d = db * 16 + l16;
-            uint16_t e[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int j = jt[t];
-                e[t] = j < k_end ? (j == slot_new ? Vn[d] : vc[(int64_t)j * DV + d]) : (uint16_t)0;
-            }
-            const u32x4 vw = u32x4{(uint32_t)e[0] | ((uint32_t)e[1] << 16),
-                                   (uint32_t)e[2] | ((uint32_t)e[3] << 16),
-                                   (uint32_t)e[4] | ((uint32_t)e[5] << 16),
-                                   (uint32_t)e[6] | ((uint32_t)e[7] << 16)};
-            O[db] = mfma16x16x32(as_bf16x8(vw), Pb, O[db]);
+            const int col = db * 16 + 4 * (l16 & 3);
+            const int row = 4 * gq + (l16 >> 2);
+            const bf16x4 v0 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vt + row * VT_PITCH + col));
+            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(vt + (row + 16) * VT_PITCH + col));
+            const bf16x8 A = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            O[db] = mfma16x16x32(A, Pb, O[db]);
         }
     }
 
-    // ---- merge the waves of the workgroup.
+    // ---- merge the waves of the workgroup (the V tiles are dead now; red_o reuses them).
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    __syncthreads();
     if (gq == 0) {
-        red_m[wave][l16] = m_run;
-        red_l[wave][l16] = l_run;
+        sm.red_m[wave][l16] = m_run;
+        sm.red_l[wave][l16] = l_run;
     }
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red_o[wave][l16][db * 16 + 4 * gq + i] = O[db][i];
+        for (int i = 0; i < 4; ++i) sm.u.red_o[wave][l16][db * 16 + 4 * gq + i] = O[db][i];
     __syncthreads();
 
     for (int e = tid; e < 16 * DV; e += 256) {
@@ -215,16 +270,16 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         if (hh >= G) continue;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][hh]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.red_m[w][hh]);
         const int h = g * G + hh;
         if (SPLIT) {
             const float Mu = (M == -INFINITY) ? 0.0f : M;
             float L = 0.0f, acc = 0.0f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const float f = exp2f(red_m[w][hh] - Mu);
-                L += red_l[w][hh] * f;
-                acc += red_o[w][hh][d] * f;
+                const float f = fast_exp2(sm.red_m[w][hh] - Mu);
+                L += sm.red_l[w][hh] * f;
+                acc += sm.u.red_o[w][hh][d] * f;
             }
             float* rec = a.partial + (((int64_t)b * a.Hq + h) * a.nsplit + s) * PSTRIDE;
             rec[d] = acc;
@@ -236,12 +291,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
             const float Ms = fmaxf(M, sk);
             const float Mu = (Ms == -INFINITY) ? 0.0f : Ms;
-            float L = SINK ? exp2f(sk - Mu) : 0.0f, acc = 0.0f;
+            float L = SINK ? fast_exp2(sk - Mu) : 0.0f, acc = 0.0f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const float f = exp2f(red_m[w][hh] - Mu);
-                L += red_l[w][hh] * f;
-                acc += red_o[w][hh][d] * f;
+                const float f = fast_exp2(sm.red_m[w][hh] - Mu);
+                L += sm.red_l[w][hh] * f;
+                acc += sm.u.red_o[w][hh][d] * f;
             }
             const float o = L > 0.0f ? a.v_scale * acc / L : 0.0f;
             a.out[((int64_t)b * a.Hq + h) * DV + d] = f32_to_bf16_bits(o);
@@ -250,8 +305,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 }
 
 // Merge the splits of one (sequence, query head); the sink joins the denominator once here.
+// 128 threads: first the split weights (one thread per split), then one thread per output dim.
 template <bool SWA, bool SINK>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a) {
+    __shared__ float wgt[1024];
+    __shared__ float red[128];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int32_t pos = a.positions[b];
     uint16_t* o = a.out + ((int64_t)b * a.Hq + h) * DV;
@@ -261,18 +319,47 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
         return;
     }
     const int n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
-    const int ns = (n_valid + a.chunk - 1) / a.chunk;
+    const int ns = (n_valid + a.chunk - 1) / a.chunk;   // <= nsplit <= 1024 (host checks)
     const float* rec = a.partial + ((int64_t)b * a.Hq + h) * a.nsplit * PSTRIDE;
     const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
     float M = sk;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[s * PSTRIDE + DV]);
-    const float Mu = (M == -INFINITY) ? 0.0f : M;
-    float L = SINK ? exp2f(sk - Mu) : 0.0f, acc = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-        const float f = exp2f(rec[s * PSTRIDE + DV] - Mu);
-        L += rec[s * PSTRIDE + DV + 1] * f;
-        acc += rec[s * PSTRIDE + d] * f;
+    for (int s = d; s < ns; s += 128) {
+        const float m = rec[(int64_t)s * PSTRIDE + DV];
+        wgt[s] = m;
+        M = fmaxf(M, m);
     }
+    red[d] = M;
+    __syncthreads();
+    for (int off = 64; off > 0; off >>= 1) {
+        if (d < off) red[d] = fmaxf(red[d], red[d + off]);
+        __syncthreads();
+    }
+    M = red[0];
+    const float Mu = (M == -INFINITY) ? 0.0f : M;
+    __syncthreads();
+    float Lp = 0.0f;
+    for (int s = d; s < ns; s += 128) {
+        const float f = fast_exp2(wgt[s] - Mu);
+        wgt[s] = f;
+        Lp += rec[(int64_t)s * PSTRIDE + DV + 1] * f;
+    }
+    red[d] = Lp;
+    __syncthreads();
+    for (int off = 64; off > 0; off >>= 1) {
+        if (d < off) red[d] += red[d + off];
+        __syncthreads();
+    }
+    const float L = red[0] + (SINK ? fast_exp2(sk - Mu) : 0.0f);
+    float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+        acc0 += rec[(int64_t)(s + 0) * PSTRIDE + d] * wgt[s + 0];
+        acc1 += rec[(int64_t)(s + 1) * PSTRIDE + d] * wgt[s + 1];
+        acc2 += rec[(int64_t)(s + 2) * PSTRIDE + d] * wgt[s + 2];
+        acc3 += rec[(int64_t)(s + 3) * PSTRIDE + d] * wgt[s + 3];
+    }
+    for (; s < ns; ++s) acc0 += rec[(int64_t)s * PSTRIDE + d] * wgt[s];
+    const float acc = (acc0 + acc1) + (acc2 + acc3);
     o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
 }
 
@@ -292,8 +379,11 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int decode_max_splits() { return 1024; }
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st) {
     if (a.B == 0) return hipSuccess;
+    if (a.nsplit > decode_max_splits()) return hipErrorInvalidConfiguration;
     if (swa) return sink ? launch_typed<true, true>(a, st) : launch_typed<true, false>(a, st);
     return sink ? launch_typed<false, true>(a, st) : launch_typed<false, false>(a, st);
 }

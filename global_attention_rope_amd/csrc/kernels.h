@@ -5,7 +5,7 @@
 
 namespace mimo {
 
-constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value
+constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value, in revolutions
 
 // Rotate K (first rope_dims dims) once per token i in [i0, S) of each sequence b (position
 // start_pos[b] + i) and store it
@@ -21,7 +21,7 @@ struct RopeKVArgs {
     void* k_dst;         // [B,Hkv,cap,dqk] or null
     void* v_dst;         // [B,Hkv,cap,dv], set iff k_dst is
     int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, ring_window;
-    double omega[kMaxRopeHalfArgs];
+    double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
 // bf16 prefill.  K rows are read from k + b*k_sb + g*k_sh + (j + (k_pos_off ? start_pos[b] : 0))*k_sj
@@ -39,7 +39,7 @@ struct PrefillArgs {
     int32_t B, S, Hq, Hkv, rope_dims, window;
     float score_scale_log2;
     float v_scale;
-    double omega[kMaxRopeHalfArgs];
+    double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
 // bf16 decode (split-K over cache slots).
@@ -56,7 +56,7 @@ struct DecodeArgs {
     int32_t B, Hq, Hkv, rope_dims, window, cap, max_position, chunk, nsplit;
     float score_scale_log2;
     float v_scale;
-    double omega[kMaxRopeHalfArgs];
+    double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
 // fp32 vector-ALU kernels for small head dims (dqk, dv <= 256).
@@ -70,7 +70,7 @@ struct F32PrefillArgs {
     int32_t B, S, Hq, Hkv, dqk, dv, rope_dims, window, layer_kind;
     float score_scale;
     float v_scale;
-    double omega[kMaxRopeHalfArgs];
+    double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
 struct F32DecodeArgs {
@@ -85,7 +85,7 @@ struct F32DecodeArgs {
     int32_t B, Hq, Hkv, dqk, dv, rope_dims, window, layer_kind, cap, max_position;
     float score_scale;
     float v_scale;
-    double omega[kMaxRopeHalfArgs];
+    double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
@@ -98,5 +98,8 @@ hipError_t launch_decode_f32(const F32DecodeArgs& a, hipStream_t st);
 
 // Query rows per prefill workgroup (bf16 kernel).
 int prefill_bf16_block_rows();
+
+// Largest number of decode splits per sequence the combine kernel merges.
+int decode_max_splits();
 
 }  // namespace mimo

@@ -7,16 +7,21 @@
 //   partial RoPE on the first r dims, GQA head h -> KV head h / (Hq / Hkv), optional sink s_h.
 //
 // Shape of the computation (qk head dim 192, v head dim 128):
-//   * one workgroup = 4 waves = 128 query rows of one query head; each wave owns 32 rows;
+//   * one workgroup = 4 waves = 128 query rows of one query head; each wave owns 32 rows; two
+//     workgroups share a CU (<= 256 registers per lane);
 //   * scores are formed transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16: the MFMA
 //     result column is the query, so every lane holds whole columns of S^T for "its" query and
 //     the softmax row statistics need one exchange between lane l and l+32;
 //   * rotated Q (bf16) lives in registers as the B operand for the whole kernel; the RoPE of Q is
 //     applied while it is loaded;
-//   * K tiles (64 keys x 192) are staged in LDS with a 400-byte row pitch (conflict-free 16-byte
-//     reads); for sliding-window layers the raw K is rotated while it is staged;
-//   * V tiles are staged transposed (V^T, 128 x 64 keys, 136-byte pitch) so that O^T = V^T * P^T
-//     takes P^T straight from the score registers, with the key order of the score layout;
+//   * K tiles (64 keys x 192, 400-byte LDS rows: conflict-free 16-byte reads) and V tiles (64 keys
+//     x 128, 320-byte rows) are staged row-major; the next tile is fetched into registers while
+//     the current one is computed;
+//   * for sliding-window layers the raw K rows are rotated in LDS right after staging (one thread
+//     per pair of 8-dim chunks); global layers read keys rotated once by the cache-store pass;
+//   * O^T = V^T * P^T takes P^T straight from the score registers; the V^T operand comes from
+//     the row-major tile with ds_read_b64_tr_b16 (4 keys x 1 dv column per lane per read), in the
+//     key order of the score layout;
 //   * online softmax in the log2 domain; the sink enters as the initial running maximum and a
 //     running sum of 1 (it is one extra logit that carries no value);
 //   * tiles outside the causal/window band are skipped; only tiles crossing the band edges are
@@ -36,31 +41,35 @@ constexpr int NWAVES = 4;
 constexpr int QPW = 32;              // query rows per wave
 constexpr int BM = NWAVES * QPW;     // query rows per workgroup
 constexpr int K_PITCH = DQK + 8;     // bf16 per K row in LDS (400 bytes)
-constexpr int VT_PITCH = BN + 4;     // bf16 per V^T row in LDS (136 bytes)
+constexpr int V_PITCH = DV + 32;     // bf16 per V row in LDS (320 bytes)
 constexpr int KCH = DQK / 16;        // 16-wide k chunks of the QK contraction
+constexpr int K_LOADS = BN * DQK / 8 / 256;   // 16-byte K chunks per thread per tile (6)
+constexpr int V_LOADS = BN * DV / 8 / 256;    // 16-byte V chunks per thread per tile (4)
 
-// Rotate 8 consecutive dims [d0, d0+8) of a row held in w, given the 8 partner dims in pw
-// (d0 +- r/2), at position pos.  r/2 is a multiple of 8 so the block never straddles r/2.
-__device__ __forceinline__ u32x4 rotate8(const u32x4& w, const u32x4& pw, int d0, int half,
-                                         int32_t pos, const double* omega) {
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Rotate the 8 dims held in lo (dims f0..f0+7 < r/2) against their partners hi (dims + r/2).
+__device__ __forceinline__ void rotate_pair8(u32x4& lo, u32x4& hi, int32_t pos, const double* om) {
     float x[8], y[8];
-    unpack8(w, x);
-    unpack8(pw, y);
-    const bool lower = d0 < half;
-    const int f0 = lower ? d0 : d0 - half;
+    unpack8(lo, x);
+    unpack8(hi, y);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         float c, s;
-        rope_cos_sin(pos, omega[f0 + t], c, s);
-        x[t] = lower ? (x[t] * c - y[t] * s) : (x[t] * c + y[t] * s);
+        rope_cos_sin_rev(pos, om[t], c, s);
+        const float xl = x[t], xh = y[t];
+        x[t] = xl * c - xh * s;
+        y[t] = xh * c + xl * s;
     }
-    return pack8(x);
+    lo = pack8(x);
+    hi = pack8(y);
 }
 
 template <bool SWA, bool SINK, bool ROTK>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * K_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VT_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * V_PITCH];
+    __shared__ __attribute__((aligned(16))) double om_s[kMaxRopeHalf];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -84,6 +93,9 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
     const int32_t p0 = a.start_pos[b];
     const int r = a.rope_dims, half = r >> 1;
 
+    for (int f = tid; f < half; f += 256) om_s[f] = a.omega_rev[f];
+    __syncthreads();
+
     const int q_first = qblk * BM + wave * QPW;              // this wave's first query row
     const int q_last = min(q_first + QPW, S) - 1;            // last valid row (< q_first if none)
     const int blk_first = qblk * BM;
@@ -95,17 +107,21 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
         const int qi = q_first + l32;
         const bool qok = qi < S;
         const uint16_t* qrow = a.q + (((int64_t)b * S + (qok ? qi : S - 1)) * Hq + h) * DQK;
+        u32x4 qw[KCH];
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int d0 = 16 * c + 8 * g;
-            u32x4 wv = *(const u32x4*)(qrow + d0);
             if (d0 < r) {
-                const int pd = d0 < half ? d0 + half : d0 - half;
-                const u32x4 pw = *(const u32x4*)(qrow + pd);
-                wv = rotate8(wv, pw, d0, half, p0 + qi, a.omega);
+                const bool lower = d0 < half;
+                u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
+                u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
+                rotate_pair8(lo, hi, p0 + qi, om_s + (lower ? d0 : d0 - half));
+                qw[c] = lower ? lo : hi;
             }
-            if (!qok) wv = u32x4{0u, 0u, 0u, 0u};
-            Qb[c] = as_bf16x8(wv);
+            if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
+            Qb[c] = as_bf16x8(qw[c]);
         }
     }
 
@@ -118,53 +134,64 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
 
     const int kt_lo = SWA ? max(0, blk_first - a.window + 1) / BN : 0;
     const int kt_hi = blk_last / BN;
-    const int64_t kbase = (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+    const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
     const int32_t koff = a.k_pos_off ? p0 : 0;
+    const uint16_t* vbase = a.v + (int64_t)b * S * a.Hkv * DV + (int64_t)kvh * DV;
+    const int64_t v_sj = (int64_t)a.Hkv * DV;
 
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-        const int j0 = kt * BN;
-        // ---- stage K (rotated when ROTK) into LDS: 64 rows x 24 chunks of 8.
+    u32x4 kreg[K_LOADS], vreg[V_LOADS];
+    auto fetch = [&](int j0) {
 #pragma unroll
-        for (int it = 0; it < (BN * DQK / 8) / 256; ++it) {
+        for (int it = 0; it < K_LOADS; ++it) {
             const int cidx = tid + it * 256;
             const int row = cidx / (DQK / 8), col = cidx % (DQK / 8);
             const int j = j0 + row;
-            u32x4 wv = u32x4{0u, 0u, 0u, 0u};
-            if (j < S) {
-                const uint16_t* krow = a.k + kbase + (int64_t)(j + koff) * a.k_sj;
-                wv = *(const u32x4*)(krow + col * 8);
-                if (ROTK && col * 8 < r) {
-                    const int d0 = col * 8;
-                    const int pd = d0 < half ? d0 + half : d0 - half;
-                    const u32x4 pw = *(const u32x4*)(krow + pd);
-                    wv = rotate8(wv, pw, d0, half, p0 + j, a.omega);
-                }
-            }
-            *(u32x4*)(Ks + row * K_PITCH + col * 8) = wv;
+            kreg[it] = j < S ? *(const u32x4*)(kbase + (int64_t)(j + koff) * a.k_sj + col * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
         }
-        // ---- stage V^T into LDS: thread = (dv pair, group of 16 keys).
-        {
-            const int dp = tid & 63, kg = tid >> 6;
-            uint32_t vals[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int j = j0 + kg * 16 + t;
-                vals[t] = j < S ? *(const uint32_t*)(a.v + (((int64_t)b * S + j) * a.Hkv + kvh) * DV +
-                                                     2 * dp)
-                                : 0u;
-            }
-            uint16_t* r0 = Vt + (2 * dp) * VT_PITCH + kg * 16;
-            uint16_t* r1 = r0 + VT_PITCH;
+        for (int it = 0; it < V_LOADS; ++it) {
+            const int cidx = tid + it * 256;
+            const int row = cidx / (DV / 8), col = cidx % (DV / 8);
+            const int j = j0 + row;
+            vreg[it] = j < S ? *(const u32x4*)(vbase + (int64_t)j * v_sj + col * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    fetch(kt_lo * BN);
+
+    const int q_l = q_first + l32;   // this lane's query row
+    const int qsel = lane >> 4, jsel = lane & 15;   // ds_read_tr lane roles
+
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+        const int j0 = kt * BN;
+        // ---- registers -> LDS
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t a0 = vals[4 * t], a1 = vals[4 * t + 1], a2 = vals[4 * t + 2],
-                               a3 = vals[4 * t + 3];
-                *(u32x2*)(r0 + 4 * t) = u32x2{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-                *(u32x2*)(r1 + 4 * t) =
-                    u32x2{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-            }
+        for (int it = 0; it < K_LOADS; ++it) {
+            const int cidx = tid + it * 256;
+            *(u32x4*)(Ks + (cidx / (DQK / 8)) * K_PITCH + (cidx % (DQK / 8)) * 8) = kreg[it];
+        }
+#pragma unroll
+        for (int it = 0; it < V_LOADS; ++it) {
+            const int cidx = tid + it * 256;
+            *(u32x4*)(Vs + (cidx / (DV / 8)) * V_PITCH + (cidx % (DV / 8)) * 8) = vreg[it];
         }
         __syncthreads();
+        if (ROTK && r > 0) {
+            // rotate raw keys in place: one thread per (row, 8-dim chunk below r/2)
+            const int per_row = half / 8;
+            for (int e = tid; e < BN * per_row; e += 256) {
+                const int row = e / per_row, c8 = (e % per_row) * 8;
+                uint16_t* kr = Ks + row * K_PITCH;
+                u32x4 lo = *(const u32x4*)(kr + c8);
+                u32x4 hi = *(const u32x4*)(kr + c8 + half);
+                rotate_pair8(lo, hi, p0 + j0 + row, om_s + c8);
+                *(u32x4*)(kr + c8) = lo;
+                *(u32x4*)(kr + c8 + half) = hi;
+            }
+            __syncthreads();
+        }
+        if (kt < kt_hi) fetch(j0 + BN);   // next tile in flight during the compute below
 
         // ---- does this wave see any key of the tile?
         const bool wave_live = q_first <= q_last && j0 <= q_last &&
@@ -182,7 +209,6 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
                     Sacc[kb] = mfma32x32x16(A, Qb[c], Sacc[kb]);
                 }
             }
-            const int qi = q_first + l32;
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -191,7 +217,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
                     float s = Sacc[kb][i] * a.score_scale_log2;
                     if (!full) {
                         const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                        const bool ok = j <= qi && j < S && (!SWA || qi - j < a.window);
+                        const bool ok = j <= q_l && j < S && (!SWA || q_l - j < a.window);
                         s = ok ? s : -INFINITY;
                     }
                     Sacc[kb][i] = s;
@@ -201,21 +227,23 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m_run, mx);
             const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = exp2f(m_run - m_use);
+            const float alpha = fast_exp2(m_run - m_use);
             m_run = m_new;
             float psum = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = exp2f(Sacc[kb][i] - m_use);
+                    const float p = fast_exp2(Sacc[kb][i] - m_use);
                     Sacc[kb][i] = p;
                     psum += p;
                 }
             }
             l_run = l_run * alpha + psum;
+            if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
+                for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
+            }
 
             // P^T operands: 16-key chunk c = registers 8*(c%2) .. +8 of block c/2.
             bf16x8 Pb[4];
@@ -229,15 +257,20 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
                 Pb[c] = as_bf16x8(pw);
             }
             // O^T += V^T * P^T.  k-slot t of lane group g is key 16c + 4g + t (t < 4) or
-            // 16c + 8 + 4g + (t - 4) (t >= 4), matching the score register order.
+            // 16c + 8 + 4g + (t - 4) (t >= 4), matching the score register order.  Each
+            // ds_read_b64_tr_b16 hands lane i of a 16-lane group V[key0 + t][dv0 + i], t < 4,
+            // when lane i points at V[key0 + i/4][dv0 + 4*(i%4)].
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
+                const int key0 = 16 * c + 4 * (qsel >> 1) + (jsel >> 2);
 #pragma unroll
                 for (int db = 0; db < DV / 32; ++db) {
-                    const uint16_t* vr = Vt + (db * 32 + l32) * VT_PITCH + 16 * c + 4 * g;
-                    const u32x2 lo = *(const u32x2*)vr;
-                    const u32x2 hi = *(const u32x2*)(vr + 8);
-                    const bf16x8 A = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    const int col = db * 32 + 16 * (qsel & 1) + 4 * (jsel & 3);
+                    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4*)(Vs + key0 * V_PITCH + col));
+                    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4*)(Vs + (key0 + 8) * V_PITCH + col));
+                    const bf16x8 A = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
                     O[db] = mfma32x32x16(A, Pb[c], O[db]);
                 }
             }
@@ -248,9 +281,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
     // ---- epilogue: out = v_scale * O / l, bf16.
     const float lt = l_run + __shfl_xor(l_run, 32);
     const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-    const int qi = q_first + l32;
-    if (qi < S) {
-        uint16_t* orow = a.out + (((int64_t)b * S + qi) * Hq + h) * DV;
+    if (q_l < S) {
+        uint16_t* orow = a.out + (((int64_t)b * S + q_l) * Hq + h) * DV;
 #pragma unroll
         for (int db = 0; db < DV / 32; ++db) {
 #pragma unroll

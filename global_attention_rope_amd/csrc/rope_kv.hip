@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     float cs, sn;
-                    rope_cos_sin(pos, a.omega[f0 + t], cs, sn);
+                    rope_cos_sin_rev(pos, a.omega_rev[f0 + t], cs, sn);
                     x[t] = lower ? (x[t] * cs - y[t] * sn) : (x[t] * cs + y[t] * sn);
                 }
                 w = pack8(x);
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
             if (c < r) {
                 const bool lower = c < half;
                 float cs, sn;
-                rope_cos_sin(pos, a.omega[lower ? c : c - half], cs, sn);
+                rope_cos_sin_rev(pos, a.omega_rev[lower ? c : c - half], cs, sn);
                 x = lower ? (x * cs - krow[c + half] * sn) : (x * cs + krow[c - half] * sn);
             }
             if (a.k_ws) ((float*)a.k_ws)[(((int64_t)b * a.Hkv + g) * a.S + i) * a.dqk + c] = x;
