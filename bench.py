@@ -14,6 +14,10 @@ KV GB/s, each kind separately, with roofline fractions) are in `phases`; `roofli
 dominant kernel (global-layer prefill) and `cpu_baseline` the fp64 oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+
+Single-layer workloads for profiling (not the bench line): --workload swa_prefill (batch 1, 4096
+tokens, sliding), ga_prefill (batch 1, 8192 tokens, global), decode (batch 64, cached lengths
+uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one).
 """
 from __future__ import annotations
 
@@ -108,6 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="stack",
+                    choices=["stack", "swa_prefill", "ga_prefill", "decode"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -123,6 +129,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mimo.lib()  # fails loudly when the HIP library is missing
+    if args.workload != "stack":
+        single_layer(args, dev)
+        return
 
     L, B, S, T = synth.STACK_LAYERS, synth.STACK_BATCH, synth.STACK_SEQ, args.decode_steps
     pattern = synth.stack_pattern(L)
@@ -268,6 +277,65 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, seed_base)
     print(json.dumps(result), flush=True)
+
+
+def single_layer(args, dev):
+    """Time one layer configuration on its own (profiling aid); prints one JSON line."""
+    import torch
+
+    import global_attention_rope_amd as mimo
+    from tests import synth
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    res = {"workload": args.workload, "steps": args.steps}
+    if args.workload in ("swa_prefill", "ga_prefill"):
+        w = synth.SWA_PREFILL if args.workload == "swa_prefill" else synth.GA_PREFILL
+        q, k, v, s = synth.layer_inputs(w, 1000 if w.layer_kind else 2000, device=dev)
+        p = mimo.Params(w.batch, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims,
+                        w.layer_kind, w.window, w.rope_theta, w.v_scale)
+        sp = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+        out = torch.empty((w.batch, w.seq, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(mimo.prefill_workspace_size(p, w.seq) + 256, dtype=torch.uint8, device=dev)
+        ms = timed(lambda: mimo.prefill(p, q, k, v, sp, sinks=s, out=out, workspace=ws), args.steps)
+        f, b = prefill_counts(w.batch, w.seq, w.num_q_heads, w.num_kv_heads, w.layer_kind,
+                              w.window)
+        b -= w.batch * (min(w.seq, w.window) if w.layer_kind else w.seq) * w.num_kv_heads * (DQK + DV) * 2
+        res.update(ms=ms, tflops=f / ms / 1e9, GBps=b / ms / 1e6, flop=f, bytes=b,
+                   frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS, frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
+    else:
+        lengths = synth.decode_lengths(3).tolist()
+        B = len(lengths)
+        for name, heads in (("global", synth.GA_HEADS), ("sliding", synth.SWA_HEADS)):
+            w = synth.Workload(name, B, 1, dtype=torch.bfloat16, **heads)
+            swa = w.layer_kind == 1
+            cap = w.window if swa else max(lengths) + 1
+            q, kn, vn, s, kc, vc = synth.decode_inputs(w, 7000 + w.layer_kind, B, cap, device=dev)
+            p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims, w.layer_kind,
+                            w.window, w.rope_theta, w.v_scale)
+            pos = torch.tensor(lengths, dtype=torch.int32, device=dev)
+            out = torch.empty((B, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mimo.decode_workspace_size(p, max(lengths)) + 256, dtype=torch.uint8,
+                             device=dev)
+            # the same step repeated: the appended slot is rewritten with the same values
+            ms = timed(lambda: mimo.decode(p, q, kn, vn, pos, max(lengths), kc, vc, sinks=s,
+                                           out=out, workspace=ws), args.steps)
+            f, b = decode_counts(B, w.num_q_heads, w.num_kv_heads, w.layer_kind, w.window, lengths)
+            res[name] = dict(ms=ms, GBps=b / ms / 1e6, bytes=b, tflops=f / ms / 1e9,
+                             frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -268,8 +268,7 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     pa.k_sh = (int64_t)seq_len * dqk;
     pa.k_sj = dqk;
     pa.k_pos_off = 0;
-    return hip_status(mimo::launch_prefill_bf16(pa, false, sinks != nullptr, false, st),
-                      "prefill (bf16, global)");
+    return hip_status(mimo::launch_prefill_ga_bf16(pa, sinks != nullptr, st), "prefill (bf16, global)");
 }
 
 int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,

@@ -43,8 +43,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Unpack 8 bf16 held in a 16-byte word into fp32.

@@ -92,12 +92,14 @@ hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool swa, bool sink, bool rot_k,
                                hipStream_t st);
+hipError_t launch_prefill_ga_bf16(const PrefillArgs& a, bool sink, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);
 hipError_t launch_prefill_f32(const F32PrefillArgs& a, hipStream_t st);
 hipError_t launch_decode_f32(const F32DecodeArgs& a, hipStream_t st);
 
-// Query rows per prefill workgroup (bf16 kernel).
+// Query rows per prefill workgroup (bf16 kernels: sliding-window / global).
 int prefill_bf16_block_rows();
+int prefill_ga_block_rows();
 
 // Largest number of decode splits per sequence the combine kernel merges.
 int decode_max_splits();

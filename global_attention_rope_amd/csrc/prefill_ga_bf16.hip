@@ -1,0 +1,328 @@
+// prefill_ga_bf16.hip — causal (global-layer) prefill on gfx950 bf16 MFMA.
+//
+// Computes, for a global layer (pages: "Add Xiaomi MiMo-V2", section "Additional useful info";
+// "add Xiaomi MiMo v2 (mimo_v2_flash)", section "Architecture, verified against upstream"):
+//   out[b,i,h,:] = v_scale * sum_{p_j <= p_i} e^{z_ij} v_j / (e^{s_h} + sum e^{z_ij}),
+//   z_ij = tau * <rot(q_i), k'_j>, k'_j the keys already rotated by the key-rotation pass,
+//   GQA head h -> KV head h / (Hq / Hkv), optional sink s_h (the model passes none here).
+//
+// Shape of the computation (qk head dim 192, v head dim 128):
+//   * one workgroup = 8 waves = 256 query rows of one query head (one workgroup per CU, two waves
+//     per SIMD); each wave owns 32 rows and keeps its rotated Q^T (bf16) in registers;
+//   * K (64 x 192) and V (64 x 128) tiles stream through a 3-stage LDS ring filled by
+//     global_load_lds_dwordx4 (memory -> LDS without registers): tile t+2 is in flight while
+//     tile t is computed; one barrier per tile;
+//   * LDS layouts are unpadded and XOR-swizzled at 16-byte granularity so that the MFMA operand
+//     reads are conflict-free: K chunk c of row r sits at c ^ ((r >> 1) & 7); V chunk c of row r at
+//     c ^ ((r & 3) << 2);
+//   * S^T = K * Q^T with v_mfma_f32_32x32x16_bf16 (each lane owns one query column), online
+//     softmax in the log2 domain with a lazily raised running maximum (the maximum is only moved
+//     when a tile exceeds it by more than 2^8, so the O rescale is rare; the result is exact because
+//     numerator and denominator share the reference), O^T += V^T * P^T with V^T read by
+//     ds_read_b64_tr_b16;
+//   * the wave index is made scalar so tile skipping and the diagonal masking are uniform branches;
+//   * workgroups are ordered heavy-first and grouped so that the workgroups the dispatcher sends to
+//     one XCD in a row share a KV head (its K/V stay hot in that XCD's L2).
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mimo {
+namespace {
+
+constexpr int DQK = 192;
+constexpr int DV = 128;
+constexpr int BN = 64;                       // keys per tile
+constexpr int NW = 8;                        // waves per workgroup
+constexpr int QPW = 32;                      // query rows per wave
+constexpr int BM = NW * QPW;                 // query rows per workgroup
+constexpr int STAGES = 3;
+constexpr int K_TILE = BN * DQK * 2;         // bytes
+constexpr int V_TILE = BN * DV * 2;
+constexpr int K_DMA = K_TILE / 1024 / NW;    // 1-KiB DMA instructions per wave per tile (3)
+constexpr int V_DMA = V_TILE / 1024 / NW;    // (2)
+constexpr int KCH = DQK / 16;
+constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyond 2^8
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ void block_sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.  Issued as
+// inline asm so that the compiler does not track these LDS writes: it would otherwise wait for
+// every outstanding load before each transposed LDS read.  Completion is ordered explicitly with
+// wait_vmcnt + block_sync_lds; the instruction has no register results.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void rotate_pair8_kernarg(u32x4& lo, u32x4& hi, int32_t pos,
+                                                     const double* om) {
+    float x[8], y[8];
+    unpack8(lo, x);
+    unpack8(hi, y);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        float c, s;
+        rope_cos_sin_rev(pos, om[t], c, s);
+        const float xl = x[t], xh = y[t];
+        x[t] = xl * c - xh * s;
+        y[t] = xh * c + xl * s;
+    }
+    lo = pack8(x);
+    hi = pack8(y);
+}
+
+template <bool SINK>
+__global__ __launch_bounds__(512) void prefill_ga_kernel(const PrefillArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * (K_TILE + V_TILE)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+    const int S = a.S, Hq = a.Hq;
+    const int nqblk = (S + BM - 1) / BM;
+    const int total = a.B * Hq * nqblk;
+
+    // ---- work item: XCD-grouped, heavy-first
+    const int id = blockIdx.x;
+    int w = id;
+    {
+        const int xcd = id & 7, slot = id >> 3, grp = slot >> 3;
+        if ((grp + 1) * 64 <= total) w = grp * 64 + xcd * 8 + (slot & 7);
+    }
+    const int h = w % Hq;
+    const int b = (w / Hq) % a.B;
+    const int qblk = nqblk - 1 - w / (Hq * a.B);
+    const int kvh = h / (Hq / a.Hkv);
+    const int32_t p0 = a.start_pos[b];
+    const int r = a.rope_dims, half = r >> 1;
+
+    const int q_first = qblk * BM + wave * QPW;          // this wave's first row (scalar)
+    const int q_last = min(q_first + QPW, S) - 1;        // its last valid row
+    const int blk_last = min(qblk * BM + BM, S) - 1;
+    const int n_tiles = blk_last / BN + 1;
+
+    // ---- DMA source mapping: LDS 16-byte slot P of this wave's instruction i holds
+    //      K row P / 24, logical chunk (P % 24) ^ swizzle; V row P / 16, chunk (P % 16) ^ swizzle.
+    const uint16_t* kslice = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+    const uint16_t* vslice = a.v + ((int64_t)b * S * a.Hkv + kvh) * DV;
+    const int64_t v_sj = (int64_t)a.Hkv * DV;
+    int k_row[K_DMA], k_off[K_DMA], v_row[V_DMA], v_off[V_DMA];
+#pragma unroll
+    for (int i = 0; i < K_DMA; ++i) {
+        const int P = (wave * K_DMA + i) * 64 + lane;
+        const int row = P / (DQK / 8), phys = P % (DQK / 8);
+        k_row[i] = row;
+        k_off[i] = (phys ^ ((row >> 1) & 7)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < V_DMA; ++i) {
+        const int P = (wave * V_DMA + i) * 64 + lane;
+        const int row = P / (DV / 8), phys = P % (DV / 8);
+        v_row[i] = row;
+        v_off[i] = (phys ^ ((row & 3) << 2)) * 8;
+    }
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8_t*)smem;
+    auto issue = [&](int t, auto stage_c) {
+        constexpr int ST = decltype(stage_c)::value;
+        const int j0 = t * BN;
+        const uint32_t kst = lds0 + ST * K_TILE;
+        const uint32_t vst = lds0 + STAGES * K_TILE + ST * V_TILE;
+#pragma unroll
+        for (int i = 0; i < K_DMA; ++i) {
+            const int j = min(j0 + k_row[i], S - 1);
+            dma16(kslice + (int64_t)j * a.k_sj + k_off[i], kst + (wave * K_DMA + i) * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < V_DMA; ++i) {
+            const int j = min(j0 + v_row[i], S - 1);
+            dma16(vslice + (int64_t)j * v_sj + v_off[i], vst + (wave * V_DMA + i) * 1024);
+        }
+    };
+    issue(0, std::integral_constant<int, 0>{});
+    if (n_tiles > 1) issue(1, std::integral_constant<int, 1>{});
+
+    // ---- Q^T operands, rotated, in registers
+    bf16x8 Qb[KCH];
+    {
+        const int qi = q_first + l32;
+        const bool qok = qi < S;
+        const uint16_t* qrow = a.q + (((int64_t)b * S + (qok ? qi : S - 1)) * Hq + h) * DQK;
+        u32x4 qw[KCH];
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int d0 = 16 * c + 8 * g;
+            if (d0 < r) {
+                const bool lower = d0 < half;
+                u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
+                u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
+                rotate_pair8_kernarg(lo, hi, p0 + qi, a.omega_rev + (lower ? d0 : d0 - half));
+                qw[c] = lower ? lo : hi;
+            }
+            if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
+            Qb[c] = as_bf16x8(qw[c]);
+        }
+    }
+
+    // ---- per-lane LDS read offsets (bytes, within a stage)
+    const int swz = (l32 >> 1) & 7;
+    int k_rd[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) k_rd[x] = l32 * (DQK * 2) + 16 * ((2 * x + g) ^ swz);
+    const int qsel = lane >> 4, jsel = lane & 15;
+    const int vrow = 4 * (qsel >> 1) + (jsel >> 2);
+    int v_rd[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+        v_rd[db] = vrow * (DV * 2) +
+                   16 * (4 * (db ^ ((jsel >> 2) & 3)) + 2 * (qsel & 1) + ((jsel & 3) >> 1)) +
+                   8 * (jsel & 1);
+
+    const float sink_l2 = SINK ? a.sinks[h] * kLog2e : -INFINITY;
+    float m_run = SINK ? sink_l2 : -INFINITY;
+    float l_run = (SINK && g == 0) ? 1.0f : 0.0f;
+    f32x16 O[DV / 32];
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db) O[db] = f32x16{};
+    const float sc = a.score_scale_log2;
+    const int q_l = q_first + l32;
+
+    auto compute = [&](int t, auto stage_c) {
+        constexpr int ST = decltype(stage_c)::value;
+        const int j0 = t * BN;
+        if (q_first > q_last || j0 > q_last) return;   // nothing visible for this wave (uniform)
+        const bool full = j0 + BN - 1 <= q_first;        // every key visible to every row
+        const uint8_t* kst = smem + ST * K_TILE;
+        const uint8_t* vst = smem + STAGES * K_TILE + ST * V_TILE;
+
+        f32x16 S0 = f32x16{}, S1 = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const uint8_t* kp = kst + k_rd[c & 3] + (c >> 2) * 128;
+            const bf16x8 A0 = *(const bf16x8*)(kp);
+            const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
+            S0 = mfma32x32x16(A0, Qb[c], S0);
+            S1 = mfma32x32x16(A1, Qb[c], S1);
+        }
+        float mx = -INFINITY;
+        if (!full) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = j0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                S0[i] = (j <= q_l) ? S0[i] : -INFINITY;
+                S1[i] = (j + 32 <= q_l) ? S1[i] : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+        // lazily raised reference maximum
+        const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
+        const float m_new = raise ? fmaxf(m_run, mx) : m_run;
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        if (__any(raise)) {
+            const float alpha = fast_exp2(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
+        }
+        m_run = m_new;
+        float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            S0[i] = fast_exp2(__builtin_fmaf(S0[i], sc, -m_use));
+            S1[i] = fast_exp2(__builtin_fmaf(S1[i], sc, -m_use));
+            ps0 += S0[i];
+            ps1 += S1[i];
+        }
+        l_run += ps0 + ps1;
+
+        // P^T operands: 16-key chunk c = registers 8*(c%2) .. +8 of block c/2
+        bf16x8 Pb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f32x16& Sx = (c >> 1) ? S1 : S0;
+            const int o = 8 * (c & 1);
+            Pb[c] = as_bf16x8(u32x4{pack_bf16x2(Sx[o], Sx[o + 1]), pack_bf16x2(Sx[o + 2], Sx[o + 3]),
+                                    pack_bf16x2(Sx[o + 4], Sx[o + 5]), pack_bf16x2(Sx[o + 6], Sx[o + 7])});
+        }
+        // O^T += V^T * P^T: k-slot t of lane group g is key 16c + 4g + t (t < 4) or
+        // 16c + 8 + 4g + (t - 4); ds_read_b64_tr_b16 hands lane i of a 16-lane group
+        // V[key0 + t][dv0 + i] when it points at V[key0 + i/4][dv0 + 4(i%4)].
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int db = 0; db < DV / 32; ++db) {
+                const uint8_t* vp = vst + v_rd[db] + 16 * c * (DV * 2);
+                const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+                const bf16x4 v1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * DV * 2));
+                O[db] = mfma32x32x16(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), Pb[c],
+                                     O[db]);
+            }
+        }
+    };
+
+    // ---- main loop: tile t lives in stage t % 3; tile t + 1 may be in flight while waiting
+    auto step = [&](int t, auto stage_c) {
+        constexpr int ST = decltype(stage_c)::value;
+        if (t + 1 < n_tiles) wait_vmcnt<K_DMA + V_DMA>();
+        else wait_vmcnt<0>();
+        block_sync_lds();   // tile t is in LDS for every wave; stage (t + 2) % 3 is free
+        if (t + 2 < n_tiles) issue(t + 2, std::integral_constant<int, (ST + 2) % 3>{});
+        compute(t, stage_c);
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+        if (t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2>{});
+    }
+
+    // ---- epilogue: out = v_scale * O / l, bf16
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+    if (q_l < S) {
+        uint16_t* orow = a.out + (((int64_t)b * S + q_l) * Hq + h) * DV;
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int d = db * 32 + 8 * ii + 4 * g;
+                *(u32x2*)(orow + d) =
+                    u32x2{pack_bf16x2(O[db][4 * ii] * inv, O[db][4 * ii + 1] * inv),
+                          pack_bf16x2(O[db][4 * ii + 2] * inv, O[db][4 * ii + 3] * inv)};
+            }
+        }
+    }
+}
+
+}  // namespace
+
+int prefill_ga_block_rows() { return BM; }
+
+hipError_t launch_prefill_ga_bf16(const PrefillArgs& a, bool sink, hipStream_t st) {
+    const int nqblk = (a.S + BM - 1) / BM;
+    const int64_t total = (int64_t)a.B * a.Hq * nqblk;
+    if (total == 0) return hipSuccess;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (a.k_sj != DQK) return hipErrorInvalidValue;   // keys must be contiguous rotated rows
+    const dim3 grid((unsigned)total), block(NW * 64);
+    if (sink) prefill_ga_kernel<true><<<grid, block, 0, st>>>(a);
+    else prefill_ga_kernel<false><<<grid, block, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace mimo
