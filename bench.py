@@ -17,7 +17,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N] [-
 
 Single-layer workloads for profiling (not the bench line): --workload swa_prefill (batch 1, 4096
 tokens, sliding), ga_prefill (batch 1, 8192 tokens, global), decode (batch 64, cached lengths
-uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one).
+uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one), copy
+(a 2 GiB device-to-device copy: the known-size reference for HBM byte counters).
 """
 from __future__ import annotations
 
@@ -113,7 +114,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="stack",
-                    choices=["stack", "swa_prefill", "ga_prefill", "decode"])
+                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "copy"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -301,7 +302,13 @@ def single_layer(args, dev):
         return e0.elapsed_time(e1) / n
 
     res = {"workload": args.workload, "steps": args.steps}
-    if args.workload in ("swa_prefill", "ga_prefill"):
+    if args.workload == "copy":
+        nbytes = 2 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ms = timed(lambda: dst.copy_(src), args.steps)
+        res.update(ms=ms, bytes_read=nbytes, bytes_written=nbytes, GBps=2 * nbytes / ms / 1e6)
+    elif args.workload in ("swa_prefill", "ga_prefill"):
         w = synth.SWA_PREFILL if args.workload == "swa_prefill" else synth.GA_PREFILL
         q, k, v, s = synth.layer_inputs(w, 1000 if w.layer_kind else 2000, device=dev)
         p = mimo.Params(w.batch, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims,

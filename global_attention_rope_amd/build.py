@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmimo_attn.so")
-SOURCES = ["abi.hip", "prefill_bf16.hip", "prefill_ga_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip"]
+SOURCES = ["abi.hip", "prefill_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip"]
 ARCH = "gfx950"
 
 

@@ -98,8 +98,9 @@ int hip_status(hipError_t e, const char* what) {
     return fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// bf16 prefill keeps the keys rotated once in [B, Hkv, S, dqk] (both layer kinds).
 size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
-    if (p->dtype != MIMO_BF16 || p->layer_kind != MIMO_LAYER_GLOBAL) return 0;
+    if (p->dtype != MIMO_BF16) return 0;
     return (size_t)p->batch * p->num_kv_heads * (size_t)S * p->qk_head_dim * 2;
 }
 
@@ -197,7 +198,8 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     ra.rope_dims = p->rope_dims;
     ra.cap = cache_capacity;
     ra.ring_window = swa ? p->window : 0;
-    ra.i0 = (swa && has_cache && seq_len > p->window) ? seq_len - p->window : 0;
+    // the ring only keeps the last `window` tokens
+    ra.cache_i0 = (swa && seq_len > p->window) ? seq_len - p->window : 0;
     if (has_cache) {
         ra.k_dst = k_cache;
         ra.v_dst = v_cache;
@@ -227,6 +229,7 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
         fill_omega(p, fa.omega_rev);
         rc = hip_status(mimo::launch_prefill_f32(fa, st), "prefill (fp32)");
         if (rc != MIMO_OK || !has_cache) return rc;
+        ra.i0 = ra.cache_i0;
         return hip_status(mimo::launch_rope_kv_f32(ra, st), "cache store (fp32)");
     }
 
@@ -246,29 +249,16 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     pa.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
     pa.v_scale = p->v_scale;
     fill_omega(p, pa.omega_rev);
-    const int64_t dqk = p->qk_head_dim;
-    if (swa) {
-        // raw K read straight from the input and rotated while it is staged
-        pa.k = (const uint16_t*)k;
-        pa.k_sb = (int64_t)seq_len * p->num_kv_heads * dqk;
-        pa.k_sh = dqk;
-        pa.k_sj = (int64_t)p->num_kv_heads * dqk;
-        pa.k_pos_off = 0;
-        rc = hip_status(mimo::launch_prefill_bf16(pa, true, sinks != nullptr, true, st),
-                        "prefill (bf16, sliding)");
-        if (rc != MIMO_OK || !has_cache) return rc;
-        return hip_status(mimo::launch_rope_kv_bf16(ra, st), "ring cache store (bf16)");
-    }
-    // global: rotate K once into the workspace (and the linear cache), then attend
+    // rotate K once into the workspace (and store the cache), then attend
     ra.k_ws = workspace;
     rc = hip_status(mimo::launch_rope_kv_bf16(ra, st), "key rotation (bf16)");
     if (rc != MIMO_OK) return rc;
+    const int64_t dqk = p->qk_head_dim;
     pa.k = (const uint16_t*)workspace;
     pa.k_sb = (int64_t)p->num_kv_heads * seq_len * dqk;
     pa.k_sh = (int64_t)seq_len * dqk;
     pa.k_sj = dqk;
-    pa.k_pos_off = 0;
-    return hip_status(mimo::launch_prefill_ga_bf16(pa, sinks != nullptr, st), "prefill (bf16, global)");
+    return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "prefill (bf16)");
 }
 
 int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,

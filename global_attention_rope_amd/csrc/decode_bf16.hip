@@ -6,8 +6,8 @@
 //
 // Per (sequence b, KV head g, split s) one workgroup of 4 waves:
 //   * each wave issues the loads of its first 32-slot tile (K straight into MFMA operand layout,
-//     V as coalesced 16-byte rows) before anything else, so their latency overlaps the query
-//     rotation;
+//     V as coalesced 16-byte rows) early — on sliding layers before the position is even read —
+//     so their latency overlaps the query rotation;
 //   * the query heads of group g (<= 16) are rotated at the new token's position and kept as the
 //     B operand of v_mfma_f32_16x16x32_bf16 (heads are the 16-wide N dimension);
 //   * the split that owns the new token's slot rotates k_new, stores it and v_new into the cache
@@ -15,10 +15,10 @@
 //     slot, so no workgroup reads a slot another one is writing;
 //   * per tile: S^T = K * Q^T, online softmax per head in the log2 domain, V staged in a per-wave
 //     LDS tile and read transposed with ds_read_b64_tr_b16, O^T += V^T * P^T; the next tile's
-//     loads are in flight meanwhile;
+//     loads are in flight meanwhile (two waves per SIMD keep ~160 KB per CU in flight);
 //   * the waves are merged through LDS; with one split the sink is folded in and the bf16 output
 //     written, otherwise (max, sum, O) partials go to the workspace and the combine kernel merges
-//     the splits and adds the sink exactly once.
+//     the splits in one pass (running maximum) and adds the sink exactly once.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -56,7 +56,6 @@ struct LdsDecode {
     uint16_t Qs[16 * DQK];
     uint16_t Kn[DQK];
     uint16_t Vn[DV];
-    double om[kMaxRopeHalf];
     float red_m[NW][16], red_l[NW][16];
     union {
         uint16_t vt[NW][TILE * VT_PITCH];     // per-wave V tiles
@@ -69,9 +68,40 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, gq = lane >> 4;
     const int G = a.Hq / a.Hkv;
+    const int k_begin = s * a.chunk;
+    const int64_t cache_row0 = ((int64_t)b * a.Hkv + g) * a.cap;
+    const uint16_t* kc = a.k_cache + cache_row0 * DQK;
+    const uint16_t* vc = a.v_cache + cache_row0 * DV;
+
+    // ---- slot loads into registers, one tile ahead of the one being computed.  Slots past
+    //      `limit` are not loaded; slots past the visible range and the new token's slot are fixed
+    //      up when used.
+    u32x4 kA[KREG], vA[VREG];
+    auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0, int limit) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int j = t0 + kb * 16 + l16;
+#pragma unroll
+            for (int c = 0; c < DQK / 32; ++c)
+                kr[kb * (DQK / 32) + c] = j < limit ? *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq)
+                                                    : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < VREG; ++it) {
+            const int e = lane + 64 * it;
+            const int j = t0 + e / (DV / 8);
+            vr[it] = j < limit ? *(const u32x4*)(vc + (int64_t)j * DV + (e % (DV / 8)) * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    const int stride = NW * TILE;
+    int t0 = k_begin + wave * TILE;
+    if (SWA) fetch(kA, vA, t0, a.cap);  // every ring slot is in bounds: start before the position is known
+
     const int32_t pos = a.positions[b];
     const bool pos_ok = pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap);
     if (!pos_ok) {
@@ -83,41 +113,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     }
     const int n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
     const int slot_new = SWA ? pos % a.window : pos;
-    const int k_begin = s * a.chunk;
     if (k_begin >= n_valid) return;
     const int k_end = min(n_valid, k_begin + a.chunk);
     const bool own_new = slot_new >= k_begin && slot_new < k_end;
     const int r = a.rope_dims, half = r >> 1;
-    const int64_t cache_row0 = ((int64_t)b * a.Hkv + g) * a.cap;
-    const uint16_t* kc = a.k_cache + cache_row0 * DQK;
-    const uint16_t* vc = a.v_cache + cache_row0 * DV;
+    if (!SWA) fetch(kA, vA, t0, k_end);
 
-    // ---- tile loads (slots >= k_end and the new token's slot read as zero here)
-    u32x4 kreg[KREG], vreg[VREG];
-    auto fetch = [&](int t0) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int j = t0 + kb * 16 + l16;
-            const bool ok = j < k_end && j != slot_new;
-#pragma unroll
-            for (int c = 0; c < DQK / 32; ++c)
-                kreg[kb * (DQK / 32) + c] =
-                    ok ? *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int it = 0; it < VREG; ++it) {
-            const int e = lane + 64 * it;
-            const int row = e / (DV / 8), col = e % (DV / 8);
-            const int j = t0 + row;
-            vreg[it] = (j < k_end && j != slot_new) ? *(const u32x4*)(vc + (int64_t)j * DV + col * 8)
-                                                    : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    int t0 = k_begin + wave * TILE;
-    if (t0 < k_end) fetch(t0);
-
-    for (int f = tid; f < half; f += 256) sm.om[f] = a.omega_rev[f];
-    __syncthreads();
     // ---- rotated queries of this group -> LDS (heads >= G are zero).
     for (int c = tid; c < 16 * (DQK / 8); c += 256) {
         const int hh = c / (DQK / 8), col = c % (DQK / 8);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             if (col * 8 < r) {
                 const int d0 = col * 8;
                 const int pd = d0 < half ? d0 + half : d0 - half;
-                wv = rotate8_dec(wv, *(const u32x4*)(qrow + pd), d0, half, pos, sm.om);
+                wv = rotate8_dec(wv, *(const u32x4*)(qrow + pd), d0, half, pos, a.omega_rev);
             }
         }
         *(u32x4*)(sm.Qs + hh * DQK + col * 8) = wv;
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             u32x4 wv = *(const u32x4*)(krow + d0);
             if (d0 < r) {
                 const int pd = d0 < half ? d0 + half : d0 - half;
-                wv = rotate8_dec(wv, *(const u32x4*)(krow + pd), d0, half, pos, sm.om);
+                wv = rotate8_dec(wv, *(const u32x4*)(krow + pd), d0, half, pos, a.omega_rev);
             }
             *(u32x4*)(sm.Kn + d0) = wv;
             *(u32x4*)(a.k_cache + (cache_row0 + slot_new) * DQK + d0) = wv;
@@ -163,52 +164,55 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db) O[db] = f32x4{};
     uint16_t* vt = sm.u.vt[wave];
+    const float sc = a.score_scale_log2;
 
-    for (; t0 < k_end; t0 += NW * TILE) {
-        // the new token's slot comes from LDS
-        if (own_new) {
+    // consume the tile held in (kr, vr) at slot t, refilling the registers with the next tile as
+    // soon as the scores are formed
+    auto consume = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
+        if (own_new && slot_new >= t && slot_new < t + TILE) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                if (t0 + kb * 16 + l16 == slot_new) {
+                if (t + kb * 16 + l16 == slot_new) {
 #pragma unroll
                     for (int c = 0; c < DQK / 32; ++c)
-                        kreg[kb * (DQK / 32) + c] = *(const u32x4*)(sm.Kn + 32 * c + 8 * gq);
+                        kr[kb * (DQK / 32) + c] = *(const u32x4*)(sm.Kn + 32 * c + 8 * gq);
                 }
 #pragma unroll
             for (int it = 0; it < VREG; ++it) {
                 const int e = lane + 64 * it;
-                if (t0 + e / (DV / 8) == slot_new) vreg[it] = *(const u32x4*)(sm.Vn + (e % (DV / 8)) * 8);
+                if (t + e / (DV / 8) == slot_new) vr[it] = *(const u32x4*)(sm.Vn + (e % (DV / 8)) * 8);
             }
         }
-        // V rows -> this wave's LDS tile
+        // V rows -> this wave's LDS tile (rows past the visible range as zeros)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int it = 0; it < VREG; ++it) {
             const int e = lane + 64 * it;
-            *(u32x4*)(vt + (e / (DV / 8)) * VT_PITCH + (e % (DV / 8)) * 8) = vreg[it];
+            const int row = e / (DV / 8);
+            *(u32x4*)(vt + row * VT_PITCH + (e % (DV / 8)) * 8) =
+                (t + row < k_end) ? vr[it] : u32x4{0u, 0u, 0u, 0u};
         }
-        // S^T (16 slots x 16 heads) for the two 16-slot blocks of the tile.
+        // S^T (16 slots x 16 heads) for the two 16-slot blocks of the tile
         f32x4 Sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             f32x4 acc = f32x4{};
 #pragma unroll
             for (int c = 0; c < DQK / 32; ++c)
-                acc = mfma16x16x32(as_bf16x8(kreg[kb * (DQK / 32) + c]), Qb[c], acc);
+                acc = mfma16x16x32(as_bf16x8(kr[kb * (DQK / 32) + c]), Qb[c], acc);
             Sacc[kb] = acc;
         }
-        const int t_cur = t0;
-        if (t0 + NW * TILE < k_end) fetch(t0 + NW * TILE);
+        fetch(kr, vr, t + stride, k_end);
 
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = t_cur + kb * 16 + 4 * gq + i;
-                const float sc = j < k_end ? Sacc[kb][i] * a.score_scale_log2 : -INFINITY;
-                Sacc[kb][i] = sc;
-                mx = fmaxf(mx, sc);
+                const int j = t + kb * 16 + 4 * gq + i;
+                const float v = j < k_end ? Sacc[kb][i] * sc : -INFINITY;
+                Sacc[kb][i] = v;
+                mx = fmaxf(mx, v);
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -230,14 +234,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         l_run = l_run * alpha + psum;
 #pragma unroll
         for (int db = 0; db < DV / 16; ++db) O[db] *= alpha;
-        // P^T: k-slot t of lane group gq is slot 4gq + t (t < 4) or 16 + 4gq + (t - 4).
+        // P^T: k-slot t' of lane group gq is slot 4gq + t' (t' < 4) or 16 + 4gq + (t' - 4).
         const bf16x8 Pb = as_bf16x8(u32x4{pack_bf16x2(Sacc[0][0], Sacc[0][1]),
                                           pack_bf16x2(Sacc[0][2], Sacc[0][3]),
                                           pack_bf16x2(Sacc[1][0], Sacc[1][1]),
                                           pack_bf16x2(Sacc[1][2], Sacc[1][3])});
         __builtin_amdgcn_wave_barrier();
         // V^T operand: lane j of group gq points at V[key0 + j/4][16db + 4(j%4)] and receives
-        // V[key0 + t][16db + j], t < 4, with key0 = 4gq (first read) and 16 + 4gq (second).
+        // V[key0 + t'][16db + j], t' < 4, with key0 = 4gq (first read) and 16 + 4gq (second).
 #pragma unroll
         for (int db = 0; db < DV / 16; ++db) {
             const int col = db * 16 + 4 * (l16 & 3);
@@ -249,7 +253,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             const bf16x8 A = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
             O[db] = mfma16x16x32(A, Pb, O[db]);
         }
-    }
+    };
+    for (; t0 < k_end; t0 += stride) consume(kA, vA, t0);
 
     // ---- merge the waves of the workgroup (the V tiles are dead now; red_o reuses them).
     l_run += __shfl_xor(l_run, 16);
@@ -304,12 +309,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     }
 }
 
-// Merge the splits of one (sequence, query head); the sink joins the denominator once here.
-// 128 threads: first the split weights (one thread per split), then one thread per output dim.
+// Merge the splits of one (sequence, query head); the sink joins the denominator once, here.  One
+// thread per output dim; the records of up to 32 splits are loaded in one round trip, then merged
+// against their common maximum (chunks of 32 are chained with a running maximum).
 template <bool SWA, bool SINK>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a) {
-    __shared__ float wgt[1024];
-    __shared__ float red[128];
+    constexpr int CH = 32;
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int32_t pos = a.positions[b];
     uint16_t* o = a.out + ((int64_t)b * a.Hq + h) * DV;
@@ -319,47 +324,35 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
         return;
     }
     const int n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
-    const int ns = (n_valid + a.chunk - 1) / a.chunk;   // <= nsplit <= 1024 (host checks)
+    const int ns = (n_valid + a.chunk - 1) / a.chunk;   // every one of these splits wrote a record
     const float* rec = a.partial + ((int64_t)b * a.Hq + h) * a.nsplit * PSTRIDE;
-    const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
-    float M = sk;
-    for (int s = d; s < ns; s += 128) {
-        const float m = rec[(int64_t)s * PSTRIDE + DV];
-        wgt[s] = m;
-        M = fmaxf(M, m);
+    float M = SINK ? a.sinks[h] * kLog2e : -INFINITY;
+    float L = SINK ? 1.0f : 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += CH) {
+        float m[CH], l[CH], x[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const bool ok = s0 + i < ns;
+            const float* r = rec + (int64_t)(s0 + i) * PSTRIDE;
+            m[i] = ok ? r[DV] : -INFINITY;
+            l[i] = ok ? r[DV + 1] : 0.0f;
+            x[i] = ok ? r[d] : 0.0f;
+        }
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, m[i]);
+        const float Mu = (Mc == -INFINITY) ? 0.0f : Mc;
+        const float f = fast_exp2(M - Mu);
+        L *= f;
+        acc *= f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float wgt = fast_exp2(m[i] - Mu);
+            L += l[i] * wgt;
+            acc += x[i] * wgt;
+        }
+        M = Mc;
     }
-    red[d] = M;
-    __syncthreads();
-    for (int off = 64; off > 0; off >>= 1) {
-        if (d < off) red[d] = fmaxf(red[d], red[d + off]);
-        __syncthreads();
-    }
-    M = red[0];
-    const float Mu = (M == -INFINITY) ? 0.0f : M;
-    __syncthreads();
-    float Lp = 0.0f;
-    for (int s = d; s < ns; s += 128) {
-        const float f = fast_exp2(wgt[s] - Mu);
-        wgt[s] = f;
-        Lp += rec[(int64_t)s * PSTRIDE + DV + 1] * f;
-    }
-    red[d] = Lp;
-    __syncthreads();
-    for (int off = 64; off > 0; off >>= 1) {
-        if (d < off) red[d] += red[d + off];
-        __syncthreads();
-    }
-    const float L = red[0] + (SINK ? fast_exp2(sk - Mu) : 0.0f);
-    float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
-    int s = 0;
-    for (; s + 4 <= ns; s += 4) {
-        acc0 += rec[(int64_t)(s + 0) * PSTRIDE + d] * wgt[s + 0];
-        acc1 += rec[(int64_t)(s + 1) * PSTRIDE + d] * wgt[s + 1];
-        acc2 += rec[(int64_t)(s + 2) * PSTRIDE + d] * wgt[s + 2];
-        acc3 += rec[(int64_t)(s + 3) * PSTRIDE + d] * wgt[s + 3];
-    }
-    for (; s < ns; ++s) acc0 += rec[(int64_t)s * PSTRIDE + d] * wgt[s];
-    const float acc = (acc0 + acc1) + (acc2 + acc3);
     o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
 }
 

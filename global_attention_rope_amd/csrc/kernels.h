@@ -10,9 +10,9 @@ constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value, in re
 // Rotate K (first rope_dims dims) once per token i in [i0, S) of each sequence b (position
 // start_pos[b] + i) and store it
 //   * into k_ws [B,Hkv,S,dqk] at row i, when k_ws is set (rotated-K scratch of a prefill);
-//   * with V into the cache k_dst [B,Hkv,cap,dqk] / v_dst [B,Hkv,cap,dv], when k_dst is set, at
-//     slot position % ring_window (ring_window > 0) or slot position (linear; a token whose slot
-//     falls outside [0, cap) is not stored).
+//   * with V into the cache k_dst [B,Hkv,cap,dqk] / v_dst [B,Hkv,cap,dv], when k_dst is set and
+//     i >= cache_i0, at slot position % ring_window (ring_window > 0) or slot position (linear; a
+//     token whose slot falls outside [0, cap) is not stored).
 struct RopeKVArgs {
     const void* k;       // [B,S,Hkv,dqk]
     const void* v;       // [B,S,Hkv,dv]
@@ -20,13 +20,12 @@ struct RopeKVArgs {
     void* k_ws;          // [B,Hkv,S,dqk] or null
     void* k_dst;         // [B,Hkv,cap,dqk] or null
     void* v_dst;         // [B,Hkv,cap,dv], set iff k_dst is
-    int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, ring_window;
+    int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, cache_i0, ring_window;
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
-// bf16 prefill.  K rows are read from k + b*k_sb + g*k_sh + (j + (k_pos_off ? start_pos[b] : 0))*k_sj
-// (element strides); when rot_k they are raw input rows rotated in the kernel, otherwise they are
-// already rotated.  V rows come from the input v [B,S,Hkv,128].
+// bf16 prefill.  Rotated K rows are read from k + b*k_sb + g*k_sh + j*k_sj (element strides, rows
+// contiguous: k_sj == 192); V rows come from the input v [B,S,Hkv,128].
 struct PrefillArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -35,7 +34,6 @@ struct PrefillArgs {
     const float* sinks;
     uint16_t* out;
     int64_t k_sb, k_sh, k_sj;
-    int32_t k_pos_off;
     int32_t B, S, Hq, Hkv, rope_dims, window;
     float score_scale_log2;
     float v_scale;
@@ -90,16 +88,13 @@ struct F32DecodeArgs {
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
-hipError_t launch_prefill_bf16(const PrefillArgs& a, bool swa, bool sink, bool rot_k,
-                               hipStream_t st);
-hipError_t launch_prefill_ga_bf16(const PrefillArgs& a, bool sink, hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, bool window, bool sink, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);
 hipError_t launch_prefill_f32(const F32PrefillArgs& a, hipStream_t st);
 hipError_t launch_decode_f32(const F32DecodeArgs& a, hipStream_t st);
 
-// Query rows per prefill workgroup (bf16 kernels: sliding-window / global).
-int prefill_bf16_block_rows();
-int prefill_ga_block_rows();
+// Query rows per prefill workgroup (bf16 kernel) for a sliding-window or global layer.
+int prefill_bf16_block_rows(bool window);
 
 // Largest number of decode splits per sequence the combine kernel merges.
 int decode_max_splits();

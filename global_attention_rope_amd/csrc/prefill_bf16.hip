@@ -1,33 +1,37 @@
-// prefill_bf16.hip — flash-style prefill of the hybrid attention layer on gfx950 bf16 MFMA.
+// prefill_bf16.hip — prefill of the hybrid attention layer (global and sliding-window kinds) on
+// gfx950 bf16 MFMA.
 //
-// Computes, for one layer (pages: "Add Xiaomi MiMo-V2", section "Additional useful info";
-// "add Xiaomi MiMo v2 (mimo_v2_flash)", section "Architecture, verified against upstream"):
-//   out[b,i,h,:] = v_scale * sum_j e^{z_ij} v_j / (e^{s_h} + sum_j e^{z_ij})
-//   z_ij = tau * <rot(q_i, p_i), rot(k_j, p_j)>, keys j visible by the causal or window mask,
-//   partial RoPE on the first r dims, GQA head h -> KV head h / (Hq / Hkv), optional sink s_h.
+// Computes (pages: "Add Xiaomi MiMo-V2", section "Additional useful info"; "add Xiaomi MiMo v2
+// (mimo_v2_flash)", section "Architecture, verified against upstream"):
+//   out[b,i,h,:] = v_scale * sum_{j visible} e^{z_ij} v_j / (e^{s_h} + sum e^{z_ij}),
+//   z_ij = tau * <rot(q_i), k'_j>, k'_j the keys already rotated by the key-rotation pass,
+//   visible: p_j <= p_i (global) and additionally p_i - p_j < window (sliding), GQA head
+//   h -> KV head h / (Hq / Hkv), optional sink s_h (sliding layers in the model).
 //
 // Shape of the computation (qk head dim 192, v head dim 128):
-//   * one workgroup = 4 waves = 128 query rows of one query head; each wave owns 32 rows; two
-//     workgroups share a CU (<= 256 registers per lane);
-//   * scores are formed transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16: the MFMA
-//     result column is the query, so every lane holds whole columns of S^T for "its" query and
-//     the softmax row statistics need one exchange between lane l and l+32;
-//   * rotated Q (bf16) lives in registers as the B operand for the whole kernel; the RoPE of Q is
-//     applied while it is loaded;
-//   * K tiles (64 keys x 192, 400-byte LDS rows: conflict-free 16-byte reads) and V tiles (64 keys
-//     x 128, 320-byte rows) are staged row-major; the next tile is fetched into registers while
-//     the current one is computed;
-//   * for sliding-window layers the raw K rows are rotated in LDS right after staging (one thread
-//     per pair of 8-dim chunks); global layers read keys rotated once by the cache-store pass;
-//   * O^T = V^T * P^T takes P^T straight from the score registers; the V^T operand comes from
-//     the row-major tile with ds_read_b64_tr_b16 (4 keys x 1 dv column per lane per read), in the
-//     key order of the score layout;
-//   * online softmax in the log2 domain; the sink enters as the initial running maximum and a
-//     running sum of 1 (it is one extra logit that carries no value);
-//   * tiles outside the causal/window band are skipped; only tiles crossing the band edges are
-//     masked element by element;
-//   * workgroups are ordered heavy-first (late query blocks first on global layers) and grouped so
-//     that the 8 workgroups the dispatcher sends to one XCD in a row share a KV head.
+//   * each wave owns 32 query rows of one query head and keeps their rotated Q^T (bf16) in
+//     registers; global layers: 8 waves on 8 consecutive row blocks of one head, one workgroup per
+//     CU; sliding layers: 4 waves, two workgroups per CU, and when the GQA group is a multiple of 4
+//     the 4 waves take 4 heads of one KV group over the same 32 rows, so every wave computes every
+//     tile of the ~3-tile band and each K/V tile feeds 4 heads;
+//   * K (64 x 192) and V (64 x 128) tiles stream through a 3-stage (global) or 2-stage (sliding)
+//     LDS ring filled by global_load_lds_dwordx4 (memory -> LDS without registers) one or two
+//     tiles ahead of the one being computed; one barrier per tile;
+//   * LDS layouts are unpadded and XOR-swizzled at 16-byte granularity so that the MFMA operand
+//     reads are conflict-free: K chunk c of row r sits at c ^ ((r >> 1) & 7); V chunk c of row r at
+//     c ^ ((r & 3) << 2);
+//   * S^T = K * Q^T with v_mfma_f32_32x32x16_bf16 (each lane owns one query column), online
+//     softmax in the log2 domain with a lazily raised running maximum (the maximum is only moved
+//     when a tile exceeds it by more than 2^8, so the O rescale is rare; the result is exact because
+//     numerator and denominator share the reference), O^T += V^T * P^T with V^T read by
+//     ds_read_b64_tr_b16;
+//   * the wave index is made scalar so tile skipping and the band-edge masking are uniform
+//     branches; sliding-window workgroups only stream the tiles of their band, and each wave only
+//     computes the tiles its own rows can see;
+//   * workgroups are ordered heavy-first and grouped so that the workgroups the dispatcher sends to
+//     one XCD in a row share a KV head (its K/V stay hot in that XCD's L2).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,20 +40,42 @@ namespace {
 
 constexpr int DQK = 192;
 constexpr int DV = 128;
-constexpr int BN = 64;               // keys per tile
-constexpr int NWAVES = 4;
-constexpr int QPW = 32;              // query rows per wave
-constexpr int BM = NWAVES * QPW;     // query rows per workgroup
-constexpr int K_PITCH = DQK + 8;     // bf16 per K row in LDS (400 bytes)
-constexpr int V_PITCH = DV + 32;     // bf16 per V row in LDS (320 bytes)
-constexpr int KCH = DQK / 16;        // 16-wide k chunks of the QK contraction
-constexpr int K_LOADS = BN * DQK / 8 / 256;   // 16-byte K chunks per thread per tile (6)
-constexpr int V_LOADS = BN * DV / 8 / 256;    // 16-byte V chunks per thread per tile (4)
+constexpr int BN = 64;                       // keys per tile
+constexpr int QPW = 32;                      // query rows per wave
+constexpr int K_TILE = BN * DQK * 2;         // bytes
+constexpr int V_TILE = BN * DV * 2;
+constexpr int KCH = DQK / 16;
 
+// Launch shapes.  Global layers: 8 waves (256 rows) and a 3-stage ring, one workgroup per CU.
+// Sliding layers see only ~3 tiles per wave, so pipeline fill and the Q prologue dominate a
+// workgroup's life: 4 waves (128 rows) and a 2-stage ring let two workgroups share a CU and hide
+// each other's latency.
+constexpr int GA_WAVES = 8, GA_STAGES = 3;
+constexpr int SW_WAVES = 4, SW_STAGES = 2;
+constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyond 2^8
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// Rotate the 8 dims held in lo (dims f0..f0+7 < r/2) against their partners hi (dims + r/2).
-__device__ __forceinline__ void rotate_pair8(u32x4& lo, u32x4& hi, int32_t pos, const double* om) {
+__device__ __forceinline__ void block_sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.  Issued as
+// inline asm so that the compiler does not track these LDS writes: it would otherwise wait for
+// every outstanding load before each transposed LDS read.  Completion is ordered explicitly with
+// wait_vmcnt + block_sync_lds; the instruction has no register results.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void rotate_pair8_kernarg(u32x4& lo, u32x4& hi, int32_t pos,
+                                                     const double* om) {
     float x[8], y[8];
     unpack8(lo, x);
     unpack8(hi, y);
@@ -65,43 +91,107 @@ __device__ __forceinline__ void rotate_pair8(u32x4& lo, u32x4& hi, int32_t pos, 
     hi = pack8(y);
 }
 
-template <bool SWA, bool SINK, bool ROTK>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * K_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * V_PITCH];
-    __shared__ __attribute__((aligned(16))) double om_s[kMaxRopeHalf];
+// GROUPED: a workgroup covers NW query heads of one KV group over the same 32 rows (wave w takes
+// head base + w); otherwise it covers NW consecutive 32-row blocks of one query head.
+template <int NW, int STAGES, bool WINDOW, bool SINK, bool GROUPED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
+    const PrefillArgs a) {
+    constexpr int BM = GROUPED ? QPW : NW * QPW;   // query rows per workgroup
+    constexpr int K_DMA = K_TILE / 1024 / NW;      // 1-KiB DMA instructions per wave per tile
+    constexpr int V_DMA = V_TILE / 1024 / NW;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * (K_TILE + V_TILE)];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
     const int S = a.S, Hq = a.Hq;
     const int nqblk = (S + BM - 1) / BM;
-    const int total = a.B * Hq * nqblk;
+    const int hunits = GROUPED ? Hq / NW : Hq;     // head units per (row block, sequence)
+    const int total = a.B * hunits * nqblk;
 
-    // Work item: XCD-grouped, heavy-first.
+    // ---- work item: XCD-grouped (the 8 items one XCD receives in a row share rows and, for
+    //      consecutive heads, a KV head), heavy-first on global layers
     const int id = blockIdx.x;
     int w = id;
     {
         const int xcd = id & 7, slot = id >> 3, grp = slot >> 3;
         if ((grp + 1) * 64 <= total) w = grp * 64 + xcd * 8 + (slot & 7);
     }
-    const int h = w % Hq;
-    const int b = (w / Hq) % a.B;
-    const int qrank = w / (Hq * a.B);
-    const int qblk = SWA ? qrank : (nqblk - 1 - qrank);
-    const int kvh = h / (Hq / a.Hkv);
+    const int hu = w % hunits;
+    const int b = (w / hunits) % a.B;
+    const int qrank = w / (hunits * a.B);
+    const int qblk = WINDOW ? qrank : nqblk - 1 - qrank;   // global: heaviest blocks first
+    const int h = GROUPED ? hu * NW + wave : hu;
+    const int kvh = (GROUPED ? hu * NW : hu) / (Hq / a.Hkv);
     const int32_t p0 = a.start_pos[b];
     const int r = a.rope_dims, half = r >> 1;
 
-    for (int f = tid; f < half; f += 256) om_s[f] = a.omega_rev[f];
-    __syncthreads();
-
-    const int q_first = qblk * BM + wave * QPW;              // this wave's first query row
-    const int q_last = min(q_first + QPW, S) - 1;            // last valid row (< q_first if none)
+    const int W = a.window;
+    const int q_first = qblk * BM + (GROUPED ? 0 : wave * QPW);   // this wave's first row (scalar)
+    const int q_last = min(q_first + QPW, S) - 1;                 // its last valid row
     const int blk_first = qblk * BM;
     const int blk_last = min(blk_first + BM, S) - 1;
+    const int kt_lo = WINDOW ? max(0, blk_first - W + 1) / BN : 0;
+    const int n_tiles = blk_last / BN + 1 - kt_lo;
 
-    // ---- Q^T operands, rotated, in registers.
+    // ---- DMA source mapping: LDS 16-byte slot P of this wave's instruction i holds
+    //      K row P / 24, logical chunk (P % 24) ^ swizzle; V row P / 16, chunk (P % 16) ^ swizzle.
+    const uint16_t* kslice = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+    const uint16_t* vslice = a.v + ((int64_t)b * S * a.Hkv + kvh) * DV;
+    const int64_t v_sj = (int64_t)a.Hkv * DV;
+    int k_row[K_DMA], k_off[K_DMA], v_row[V_DMA], v_off[V_DMA];
+#pragma unroll
+    for (int i = 0; i < K_DMA; ++i) {
+        const int P = (wave * K_DMA + i) * 64 + lane;
+        const int row = P / (DQK / 8), phys = P % (DQK / 8);
+        k_row[i] = row;
+        k_off[i] = (phys ^ ((row >> 1) & 7)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < V_DMA; ++i) {
+        const int P = (wave * V_DMA + i) * 64 + lane;
+        const int row = P / (DV / 8), phys = P % (DV / 8);
+        v_row[i] = row;
+        v_off[i] = (phys ^ ((row & 3) << 2)) * 8;
+    }
+    // per-lane source pointers of tile 0; tile t adds t * BN rows (a scalar offset) except on the
+    // ragged last tile, whose rows past S are clamped to row S - 1 (they are masked anyway)
+    const uint16_t* kp[K_DMA];
+    const uint16_t* vp[V_DMA];
+#pragma unroll
+    for (int i = 0; i < K_DMA; ++i) kp[i] = kslice + (int64_t)(kt_lo * BN + k_row[i]) * DQK + k_off[i];
+#pragma unroll
+    for (int i = 0; i < V_DMA; ++i) vp[i] = vslice + (int64_t)(kt_lo * BN + v_row[i]) * v_sj + v_off[i];
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8_t*)smem;
+    auto issue = [&](int t, auto stage_c) {
+        constexpr int ST = decltype(stage_c)::value;
+        const int j0 = (kt_lo + t) * BN;
+        const uint32_t kst = lds0 + ST * K_TILE;
+        const uint32_t vst = lds0 + STAGES * K_TILE + ST * V_TILE;
+        if (j0 + BN <= S) {
+            const int64_t dk = (int64_t)t * BN * DQK, dv = (int64_t)t * BN * v_sj;
+#pragma unroll
+            for (int i = 0; i < K_DMA; ++i) dma16(kp[i] + dk, kst + (wave * K_DMA + i) * 1024);
+#pragma unroll
+            for (int i = 0; i < V_DMA; ++i) dma16(vp[i] + dv, vst + (wave * V_DMA + i) * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < K_DMA; ++i) {
+                const int j = min(j0 + k_row[i], S - 1);
+                dma16(kslice + (int64_t)j * DQK + k_off[i], kst + (wave * K_DMA + i) * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < V_DMA; ++i) {
+                const int j = min(j0 + v_row[i], S - 1);
+                dma16(vslice + (int64_t)j * v_sj + v_off[i], vst + (wave * V_DMA + i) * 1024);
+            }
+        }
+    };
+    issue(0, std::integral_constant<int, 0>{});
+    if (STAGES == 3 && n_tiles > 1) issue(1, std::integral_constant<int, 1 % STAGES>{});
+
+    // ---- Q^T operands, rotated, in registers
     bf16x8 Qb[KCH];
     {
         const int qi = q_first + l32;
@@ -117,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
                 const bool lower = d0 < half;
                 u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
                 u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
-                rotate_pair8(lo, hi, p0 + qi, om_s + (lower ? d0 : d0 - half));
+                rotate_pair8_kernarg(lo, hi, p0 + qi, a.omega_rev + (lower ? d0 : d0 - half));
                 qw[c] = lower ? lo : hi;
             }
             if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
@@ -125,160 +215,127 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         }
     }
 
+    // ---- per-lane LDS read offsets (bytes, within a stage)
+    const int swz = (l32 >> 1) & 7;
+    int k_rd[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) k_rd[x] = l32 * (DQK * 2) + 16 * ((2 * x + g) ^ swz);
+    const int qsel = lane >> 4, jsel = lane & 15;
+    const int vrow = 4 * (qsel >> 1) + (jsel >> 2);
+    int v_rd[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+        v_rd[db] = vrow * (DV * 2) +
+                   16 * (4 * (db ^ ((jsel >> 2) & 3)) + 2 * (qsel & 1) + ((jsel & 3) >> 1)) +
+                   8 * (jsel & 1);
+
     const float sink_l2 = SINK ? a.sinks[h] * kLog2e : -INFINITY;
     float m_run = SINK ? sink_l2 : -INFINITY;
     float l_run = (SINK && g == 0) ? 1.0f : 0.0f;
     f32x16 O[DV / 32];
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db) O[db] = f32x16{};
+    const float sc = a.score_scale_log2;
+    const int q_l = q_first + l32;
 
-    const int kt_lo = SWA ? max(0, blk_first - a.window + 1) / BN : 0;
-    const int kt_hi = blk_last / BN;
-    const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-    const int32_t koff = a.k_pos_off ? p0 : 0;
-    const uint16_t* vbase = a.v + (int64_t)b * S * a.Hkv * DV + (int64_t)kvh * DV;
-    const int64_t v_sj = (int64_t)a.Hkv * DV;
+    auto compute = [&](int t, auto stage_c) {
+        constexpr int ST = decltype(stage_c)::value;
+        const int j0 = (kt_lo + t) * BN;
+        // nothing visible for this wave (uniform branch)
+        if (q_first > q_last || j0 > q_last || (WINDOW && j0 + BN - 1 <= q_first - W)) return;
+        // every key visible to every row of the wave
+        const bool full = j0 + BN - 1 <= q_first && (!WINDOW || q_last - j0 < W);
+        const uint8_t* kst = smem + ST * K_TILE;
+        const uint8_t* vst = smem + STAGES * K_TILE + ST * V_TILE;
 
-    u32x4 kreg[K_LOADS], vreg[V_LOADS];
-    auto fetch = [&](int j0) {
+        f32x16 S0 = f32x16{}, S1 = f32x16{};
 #pragma unroll
-        for (int it = 0; it < K_LOADS; ++it) {
-            const int cidx = tid + it * 256;
-            const int row = cidx / (DQK / 8), col = cidx % (DQK / 8);
-            const int j = j0 + row;
-            kreg[it] = j < S ? *(const u32x4*)(kbase + (int64_t)(j + koff) * a.k_sj + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < KCH; ++c) {
+            const uint8_t* kp = kst + k_rd[c & 3] + (c >> 2) * 128;
+            const bf16x8 A0 = *(const bf16x8*)(kp);
+            const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
+            S0 = mfma32x32x16(A0, Qb[c], S0);
+            S1 = mfma32x32x16(A1, Qb[c], S1);
+        }
+        float mx = -INFINITY;
+        if (!full) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = j0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                const bool ok0 = j <= q_l && (!WINDOW || q_l - j < W);
+                const bool ok1 = j + 32 <= q_l && (!WINDOW || q_l - j - 32 < W);
+                S0[i] = ok0 ? S0[i] : -INFINITY;
+                S1[i] = ok1 ? S1[i] : -INFINITY;
+            }
         }
 #pragma unroll
-        for (int it = 0; it < V_LOADS; ++it) {
-            const int cidx = tid + it * 256;
-            const int row = cidx / (DV / 8), col = cidx % (DV / 8);
-            const int j = j0 + row;
-            vreg[it] = j < S ? *(const u32x4*)(vbase + (int64_t)j * v_sj + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+        // lazily raised reference maximum
+        const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
+        const float m_new = raise ? fmaxf(m_run, mx) : m_run;
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        if (__any(raise)) {
+            const float alpha = fast_exp2(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
+        }
+        m_run = m_new;
+        float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            S0[i] = fast_exp2(__builtin_fmaf(S0[i], sc, -m_use));
+            S1[i] = fast_exp2(__builtin_fmaf(S1[i], sc, -m_use));
+            ps0 += S0[i];
+            ps1 += S1[i];
+        }
+        l_run += ps0 + ps1;
+
+        // P^T operands: 16-key chunk c = registers 8*(c%2) .. +8 of block c/2
+        bf16x8 Pb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f32x16& Sx = (c >> 1) ? S1 : S0;
+            const int o = 8 * (c & 1);
+            Pb[c] = as_bf16x8(u32x4{pack_bf16x2(Sx[o], Sx[o + 1]), pack_bf16x2(Sx[o + 2], Sx[o + 3]),
+                                    pack_bf16x2(Sx[o + 4], Sx[o + 5]), pack_bf16x2(Sx[o + 6], Sx[o + 7])});
+        }
+        // O^T += V^T * P^T: k-slot t of lane group g is key 16c + 4g + t (t < 4) or
+        // 16c + 8 + 4g + (t - 4); ds_read_b64_tr_b16 hands lane i of a 16-lane group
+        // V[key0 + t][dv0 + i] when it points at V[key0 + i/4][dv0 + 4(i%4)].
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int db = 0; db < DV / 32; ++db) {
+                const uint8_t* vp = vst + v_rd[db] + 16 * c * (DV * 2);
+                const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+                const bf16x4 v1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * DV * 2));
+                O[db] = mfma32x32x16(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), Pb[c],
+                                     O[db]);
+            }
         }
     };
-    fetch(kt_lo * BN);
 
-    const int q_l = q_first + l32;   // this lane's query row
-    const int qsel = lane >> 4, jsel = lane & 15;   // ds_read_tr lane roles
-
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-        const int j0 = kt * BN;
-        // ---- registers -> LDS
-#pragma unroll
-        for (int it = 0; it < K_LOADS; ++it) {
-            const int cidx = tid + it * 256;
-            *(u32x4*)(Ks + (cidx / (DQK / 8)) * K_PITCH + (cidx % (DQK / 8)) * 8) = kreg[it];
-        }
-#pragma unroll
-        for (int it = 0; it < V_LOADS; ++it) {
-            const int cidx = tid + it * 256;
-            *(u32x4*)(Vs + (cidx / (DV / 8)) * V_PITCH + (cidx % (DV / 8)) * 8) = vreg[it];
-        }
-        __syncthreads();
-        if (ROTK && r > 0) {
-            // rotate raw keys in place: one thread per (row, 8-dim chunk below r/2)
-            const int per_row = half / 8;
-            for (int e = tid; e < BN * per_row; e += 256) {
-                const int row = e / per_row, c8 = (e % per_row) * 8;
-                uint16_t* kr = Ks + row * K_PITCH;
-                u32x4 lo = *(const u32x4*)(kr + c8);
-                u32x4 hi = *(const u32x4*)(kr + c8 + half);
-                rotate_pair8(lo, hi, p0 + j0 + row, om_s + c8);
-                *(u32x4*)(kr + c8) = lo;
-                *(u32x4*)(kr + c8 + half) = hi;
-            }
-            __syncthreads();
-        }
-        if (kt < kt_hi) fetch(j0 + BN);   // next tile in flight during the compute below
-
-        // ---- does this wave see any key of the tile?
-        const bool wave_live = q_first <= q_last && j0 <= q_last &&
-                               (!SWA || j0 + BN - 1 > q_first - a.window);
-        if (wave_live) {
-            const bool full = (j0 + BN - 1 <= q_first) && (!SWA || q_last - j0 < a.window);
-            f32x16 Sacc[2];
-            Sacc[0] = f32x16{};
-            Sacc[1] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 A = *(const bf16x8*)(Ks + (kb * 32 + l32) * K_PITCH + 16 * c + 8 * g);
-                    Sacc[kb] = mfma32x32x16(A, Qb[c], Sacc[kb]);
-                }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float s = Sacc[kb][i] * a.score_scale_log2;
-                    if (!full) {
-                        const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                        const bool ok = j <= q_l && j < S && (!SWA || q_l - j < a.window);
-                        s = ok ? s : -INFINITY;
-                    }
-                    Sacc[kb][i] = s;
-                    mx = fmaxf(mx, s);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
-            float psum = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(Sacc[kb][i] - m_use);
-                    Sacc[kb][i] = p;
-                    psum += p;
-                }
-            }
-            l_run = l_run * alpha + psum;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
-            }
-
-            // P^T operands: 16-key chunk c = registers 8*(c%2) .. +8 of block c/2.
-            bf16x8 Pb[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                u32x4 pw;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    pw[t] = pack_bf16x2(Sacc[c >> 1][8 * (c & 1) + 2 * t],
-                                        Sacc[c >> 1][8 * (c & 1) + 2 * t + 1]);
-                Pb[c] = as_bf16x8(pw);
-            }
-            // O^T += V^T * P^T.  k-slot t of lane group g is key 16c + 4g + t (t < 4) or
-            // 16c + 8 + 4g + (t - 4) (t >= 4), matching the score register order.  Each
-            // ds_read_b64_tr_b16 hands lane i of a 16-lane group V[key0 + t][dv0 + i], t < 4,
-            // when lane i points at V[key0 + i/4][dv0 + 4*(i%4)].
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int key0 = 16 * c + 4 * (qsel >> 1) + (jsel >> 2);
-#pragma unroll
-                for (int db = 0; db < DV / 32; ++db) {
-                    const int col = db * 32 + 16 * (qsel & 1) + 4 * (jsel & 3);
-                    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4*)(Vs + key0 * V_PITCH + col));
-                    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4*)(Vs + (key0 + 8) * V_PITCH + col));
-                    const bf16x8 A = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    O[db] = mfma32x32x16(A, Pb[c], O[db]);
-                }
-            }
-        }
-        __syncthreads();
+    // ---- main loop: tile t lives in stage t % STAGES; up to STAGES - 2 later tiles may still be
+    //      in flight while tile t is awaited
+    auto step = [&](int t, auto stage_c) {
+        constexpr int ST = decltype(stage_c)::value;
+        if (STAGES == 3 && t + 1 < n_tiles) wait_vmcnt<K_DMA + V_DMA>();
+        else wait_vmcnt<0>();
+        block_sync_lds();   // tile t is in LDS for every wave; stage (t - 1) % STAGES is free
+        if (t + STAGES - 1 < n_tiles)
+            issue(t + STAGES - 1, std::integral_constant<int, (ST + STAGES - 1) % STAGES>{});
+        compute(t, stage_c);
+    };
+    for (int t = 0; t < n_tiles; t += STAGES) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1 % STAGES>{});
+        if (STAGES == 3 && t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2 % STAGES>{});
     }
 
-    // ---- epilogue: out = v_scale * O / l, bf16.
+    // ---- epilogue: out = v_scale * O / l, bf16
     const float lt = l_run + __shfl_xor(l_run, 32);
     const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
     if (q_l < S) {
@@ -298,25 +355,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
 
 }  // namespace
 
-int prefill_bf16_block_rows() { return BM; }
+int prefill_bf16_block_rows(bool window) { return (window ? SW_WAVES : GA_WAVES) * QPW; }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, bool swa, bool sink, bool rot_k,
-                               hipStream_t st) {
-    const int nqblk = (a.S + BM - 1) / BM;
-    const int64_t total = (int64_t)a.B * a.Hq * nqblk;
+hipError_t launch_prefill_bf16(const PrefillArgs& a, bool window, bool sink, hipStream_t st) {
+    if (a.k_sj != DQK) return hipErrorInvalidValue;   // keys must be contiguous rotated rows
+    const int group = a.Hq / a.Hkv;
+    const bool grouped = window && group % SW_WAVES == 0;
+    const int bm = grouped ? QPW : prefill_bf16_block_rows(window);
+    const int nqblk = (a.S + bm - 1) / bm;
+    const int64_t total = (int64_t)a.B * (grouped ? a.Hq / SW_WAVES : a.Hq) * nqblk;
     if (total == 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)total), block(256);
-    if (swa && !rot_k) return hipErrorInvalidValue;  // sliding layers always rotate K in-kernel
-    if (swa) {
-        if (sink) prefill_bf16_kernel<true, true, true><<<grid, block, 0, st>>>(a);
-        else prefill_bf16_kernel<true, false, true><<<grid, block, 0, st>>>(a);
-    } else if (rot_k) {
-        if (sink) prefill_bf16_kernel<false, true, true><<<grid, block, 0, st>>>(a);
-        else prefill_bf16_kernel<false, false, true><<<grid, block, 0, st>>>(a);
+    const dim3 grid((unsigned)total);
+    if (window) {
+        const dim3 block(SW_WAVES * 64);
+        if (grouped) {
+            if (sink) prefill_kernel<SW_WAVES, SW_STAGES, true, true, true><<<grid, block, 0, st>>>(a);
+            else prefill_kernel<SW_WAVES, SW_STAGES, true, false, true><<<grid, block, 0, st>>>(a);
+        } else {
+            if (sink) prefill_kernel<SW_WAVES, SW_STAGES, true, true, false><<<grid, block, 0, st>>>(a);
+            else prefill_kernel<SW_WAVES, SW_STAGES, true, false, false><<<grid, block, 0, st>>>(a);
+        }
     } else {
-        if (sink) prefill_bf16_kernel<false, true, false><<<grid, block, 0, st>>>(a);
-        else prefill_bf16_kernel<false, false, false><<<grid, block, 0, st>>>(a);
+        const dim3 block(GA_WAVES * 64);
+        if (sink) prefill_kernel<GA_WAVES, GA_STAGES, false, true, false><<<grid, block, 0, st>>>(a);
+        else prefill_kernel<GA_WAVES, GA_STAGES, false, false, false><<<grid, block, 0, st>>>(a);
     }
     return hipGetLastError();
 }

@@ -13,9 +13,9 @@
 namespace mimo {
 namespace {
 
-// Cache slot of a token, or -1 when it is not stored.
-__device__ __forceinline__ int cache_slot(const RopeKVArgs& a, int32_t pos) {
-    if (!a.k_dst || pos < 0) return -1;
+// Cache slot of token i at position pos, or -1 when it is not stored.
+__device__ __forceinline__ int cache_slot(const RopeKVArgs& a, int i, int32_t pos) {
+    if (!a.k_dst || pos < 0 || i < a.cache_i0) return -1;
     if (a.ring_window > 0) return pos % a.ring_window;
     return pos < a.cap ? pos : -1;
 }
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
         const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
         const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
         const int32_t pos = a.start_pos[b] + i;
-        const int slot = cache_slot(a, pos);
+        const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
         if (c < kch) {
             const uint16_t* krow = (const uint16_t*)a.k + src_row * a.dqk;
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
         const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
         const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
         const int32_t pos = a.start_pos[b] + i;
-        const int slot = cache_slot(a, pos);
+        const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
         if (c < a.dqk) {
             const float* krow = (const float*)a.k + src_row * a.dqk;

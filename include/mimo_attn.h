@@ -63,7 +63,7 @@ enum mimo_attn_layer_kind { /* the value of hybrid_layer_pattern[layer] */
 enum mimo_attn_dtype { MIMO_F32 = 0, MIMO_BF16 = 1 };
 
 typedef struct mimo_attn_params {
-    int32_t batch;         /* B >= 1                                                         */
+    int32_t batch;         /* B >= 0 (0: nothing to do)                                      */
     int32_t num_q_heads;   /* Hq >= 1                                                        */
     int32_t num_kv_heads;  /* Hkv >= 1, divides Hq (GQA group = Hq / Hkv)                    */
     int32_t qk_head_dim;   /* dqk                                                            */
@@ -105,9 +105,9 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
                       void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mimo_attn_prefill needs for this layer and seq_len (bf16 global layers keep
- * their rotated keys there: B * Hkv * seq_len * dqk * 2 bytes; 0 otherwise).  Returns 0 for
- * invalid parameters. */
+/* Workspace bytes mimo_attn_prefill needs for this layer and seq_len: bf16 layers keep their keys,
+ * rotated once, there (B * Hkv * seq_len * dqk * 2 bytes); fp32 layers need none (0).  Returns 0
+ * for invalid parameters. */
 size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_len);
 
 /*

@@ -85,7 +85,9 @@ def test_reserved_field_must_be_zero():
 
 
 def test_workspace_sizes():
-    assert mimo.prefill_workspace_size(_swa(), 4096) == 0
+    assert mimo.prefill_workspace_size(_swa(), 4096) == 1 * 8 * 4096 * 192 * 2
+    assert mimo.prefill_workspace_size(_swa(dtype=mimo.F32, qk_head_dim=32, v_head_dim=16, rope_dims=10,
+                                            num_q_heads=4, num_kv_heads=1, window=16), 64) == 0
     assert mimo.prefill_workspace_size(_ga(), 8192) == 1 * 4 * 8192 * 192 * 2
     assert mimo.prefill_workspace_size(_ga(rope_dims=63), 8192) == 0  # invalid -> 0
     # the 128-slot ring fits one split: no partials
@@ -131,6 +133,7 @@ def test_prefill_argument_errors_return_before_any_launch():
     assert _prefill(_swa(), kc=3, vc=4, cap=64) == E       # ring capacity != window
     assert _prefill(_ga(), kc=3, vc=4, cap=0) == E
     assert _prefill(_ga(), ws=None) == mimo.MIMO_ERR_WORKSPACE
+    assert _prefill(_swa(), ws=None) == mimo.MIMO_ERR_WORKSPACE
     assert _prefill(_ga(), S=16, ws=5, wsb=100) == mimo.MIMO_ERR_WORKSPACE
     assert "workspace" in mimo.last_error()
     # nothing to do: success without touching any pointer

@@ -301,3 +301,38 @@ def test_prefill_then_decode_matches_longer_prefill(kind):
                          rows=np.array([S], np.int32))
     assert_close(dec, ref[:, S], what="decode after prefill")
     assert_close(full[:, S], ref[:, S], what="longer prefill")
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_stack_layer_full_size_prefill_then_decode_sampled(layer):
+    """A layer of the 48-layer stack at full size (batch 2, 16384 tokens; layer 0 global, layer 1
+    sliding): prefill writes the cache, then two decode steps; sampled prefill rows and every
+    decode output are checked against the oracle (whose decode cache is its own rotated keys)."""
+    pattern = synth.stack_pattern()
+    heads = synth.SWA_HEADS if pattern[layer] == 1 else synth.GA_HEADS
+    B, S, T = synth.STACK_BATCH, synth.STACK_SEQ, 2
+    w = synth.Workload("stack", B, S + T, dtype=torch.bfloat16, **heads)
+    _note(f"stack layer {layer} kind {w.layer_kind}")
+    q, k, v, s = synth.layer_inputs(w, 4000 + layer, device=DEV)
+    wS = synth.Workload("stack", B, S, dtype=torch.bfloat16, **heads)
+    sp = torch.zeros(B, dtype=torch.int32, device=DEV)
+    cap = w.window if w.layer_kind == 1 else S + T
+    kc = torch.zeros((B, w.num_kv_heads, cap, 192), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros((B, w.num_kv_heads, cap, 128), dtype=torch.bfloat16, device=DEV)
+    out = mimo.prefill(_params(wS), q[:, :S].contiguous(), k[:, :S].contiguous(),
+                       v[:, :S].contiguous(), sp, sinks=s, k_cache=kc, v_cache=vc)
+    decs = []
+    for t in range(T):
+        pos = torch.full((B,), S + t, dtype=torch.int32, device=DEV)
+        decs.append(mimo.decode(_params(wS), q[:, S + t].contiguous(), k[:, S + t].contiguous(),
+                                v[:, S + t].contiguous(), pos, S + T - 1, kc, vc, sinks=s))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(layer)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(S - 8, S),
+                                     rng.integers(0, S, 16)])).astype(np.int32)
+    rows_all = np.concatenate([rows, np.arange(S, S + T, dtype=np.int32)])
+    posn = np.stack([np.arange(S + T, dtype=np.int32)] * B)
+    ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), posn, _f32(s), rows=rows_all)
+    assert_close(out[:, rows], ref[:, rows], what=f"stack layer {layer} prefill rows")
+    for t in range(T):
+        assert_close(decs[t], ref[:, S + t], what=f"stack layer {layer} decode step {t}")
