@@ -9,7 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/mimo_attn.h"
+#include "mimo_attn.h"
 #include "kernels.h"
 
 namespace {
