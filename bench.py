@@ -36,6 +36,34 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 DQK, DV = 192, 128
 
+# HBM bytes per global-layer prefill call, counted by rocprofv3 (FETCH_SIZE and WRITE_SIZE, each
+# scaled by what the counter reads for a copy of known size); valid only for the kernel sources it
+# was taken on, which the summary records as a SHA-256.
+TRAFFIC_PROFILE = os.path.join("profiles", "ga_prefill_b2_s16384_hbm_counters.md")
+TRAFFIC_SOURCES = ["global_attention_rope_amd/csrc/prefill_bf16.hip",
+                   "global_attention_rope_amd/csrc/rope_kv.hip",
+                   "global_attention_rope_amd/csrc/device_common.h",
+                   "global_attention_rope_amd/csrc/kernels.h"]
+
+
+def counted_traffic():
+    """Bytes per call from the committed counter summary, or None when the kernels changed since."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, TRAFFIC_PROFILE)).read()
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+    except OSError:
+        return None
+    m_b = re.search(r"traffic_bytes_per_call:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    if not m_b or not m_h or m_h.group(1) != h.hexdigest():
+        return None
+    return float(m_b.group(1))
+
 
 def pairs_visible(S: int, kind: int, W: int) -> int:
     """Number of (query, key) pairs the mask admits in a prefill of S tokens."""
@@ -270,7 +298,8 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(ga_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ga_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": counted_traffic(),
+                     "traffic_source": TRAFFIC_PROFILE,
                      "kernel": "global-layer prefill (key rotation pass + attention kernel), "
                                f"B{B} S{S}, {f_ga:.4e} flop per call"},
         "wall_s_timed": round(wall, 3),
