@@ -104,18 +104,33 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
     return (size_t)p->batch * p->num_kv_heads * (size_t)S * p->qk_head_dim * 2;
 }
 
-// Decode split size: slots per workgroup, a power of two >= 256, large enough to keep the grid
-// (B * Hkv * splits) within 8192 workgroups and the splits per sequence within what the combine
-// kernel merges.
+// Decode split size: slots per workgroup.
+//  * a sliding ring of at most 1024 slots is one split;
+//  * a small grid (at most two rounds of 256-slot splits on the chip, which holds 512 resident
+//    decode workgroups: 256 CUs x two 4-wave workgroups) is cut into as many splits as fill ONE
+//    round, at least 128 slots each (one 32-slot tile per wave), rounded up to whole tiles — a
+//    second, mostly idle round would cost as much as the first;
+//  * otherwise a power of two >= 256, large enough to keep the grid (B * Hkv * splits) within 8192
+//    workgroups and the splits per sequence within what the combine kernel merges.
+constexpr int64_t kResidentDecodeGroups = 512;
+
 int decode_chunk(const mimo_attn_params* p, int32_t max_position) {
     const int64_t n_max = p->layer_kind == MIMO_LAYER_SWA
                               ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
                               : (int64_t)max_position + 1;
+    if (p->layer_kind == MIMO_LAYER_SWA && n_max <= 1024) return n_max < 1 ? 1 : (int)n_max;
+    const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
+    if (pairs * ((n_max + 255) / 256) <= 2 * kResidentDecodeGroups) {
+        int64_t ns = kResidentDecodeGroups / pairs;
+        if (ns < 1) ns = 1;
+        if (ns > (n_max + 127) / 128) ns = (n_max + 127) / 128;
+        const int64_t chunk = ((n_max + ns - 1) / ns + 31) / 32 * 32;
+        return (int)chunk;
+    }
     int64_t chunk = 256;
-    while ((int64_t)p->batch * p->num_kv_heads * ((n_max + chunk - 1) / chunk) > 8192 ||
+    while (pairs * ((n_max + chunk - 1) / chunk) > 8192 ||
            (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
         chunk *= 2;
-    if (p->layer_kind == MIMO_LAYER_SWA && n_max <= 1024) chunk = n_max < 1 ? 1 : n_max;
     return (int)chunk;
 }
 

@@ -19,6 +19,8 @@
 //   * the waves are merged through LDS; with one split the sink is folded in and the bf16 output
 //     written, otherwise (max, sum, O) partials go to the workspace and the combine kernel merges
 //     the splits in one pass (running maximum) and adds the sink exactly once.
+#include <cstddef>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,37 +35,49 @@ constexpr int PSTRIDE = DV + 2;          // floats per partial record: O[128], m
 constexpr int VT_PITCH = DV + 16;        // bf16 per V row in the per-wave LDS tile (288 bytes)
 constexpr int KREG = 2 * (DQK / 32);     // 16-byte K operand loads per lane per tile (12)
 constexpr int VREG = TILE * DV / 8 / 64; // 16-byte V loads per lane per tile (8)
+constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merge buffer
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ u32x4 rotate8_dec(const u32x4& w, const u32x4& pw, int d0, int half,
-                                             int32_t pos, const double* om) {
+// Rotate 8 consecutive dims d0.. of a row (w) against their partners (pw) with the cos/sin of the
+// row's position per frequency (cs, in LDS).  Dims at or past r read the identity entries
+// (cos 1, sin 0) stored after the table, so every chunk runs the same straight-line code and the
+// table reads of several chunks overlap.
+constexpr int kIdentity = kMaxRopeHalf;   // first of 8 identity entries in the table
+__device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int d0, int half,
+                                            int r, const float2* cs) {
+    const bool lower = d0 < half;
+    const int f0 = d0 < r ? (lower ? d0 : d0 - half) : kIdentity;
+    float4 e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = *(const float4*)(cs + f0 + 2 * i);
     float x[8], y[8];
     unpack8(w, x);
     unpack8(pw, y);
-    const bool lower = d0 < half;
-    const int f0 = lower ? d0 : d0 - half;
+    const float sgn = lower ? -1.0f : 1.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        float c, s;
-        rope_cos_sin_rev(pos, om[f0 + t], c, s);
-        x[t] = lower ? (x[t] * c - y[t] * s) : (x[t] * c + y[t] * s);
+        const float c = (t & 1) ? e[t >> 1].z : e[t >> 1].x;
+        const float sn = (t & 1) ? e[t >> 1].w : e[t >> 1].y;
+        x[t] = __builtin_fmaf(sgn * y[t], sn, x[t] * c);
     }
     return pack8(x);
 }
 
 struct LdsDecode {
-    uint16_t Qs[16 * DQK];
+    float2 cs[kMaxRopeHalf + 8];              // cos/sin of the position per frequency, identity
     uint16_t Kn[DQK];
     uint16_t Vn[DV];
     float red_m[NW][16], red_l[NW][16];
+    float sink[16];
     union {
         uint16_t vt[NW][TILE * VT_PITCH];     // per-wave V tiles
-        float red_o[NW][16][DV + 1];          // wave merge, after the slot loop
+        float red_o[NW][16][RO_PITCH];        // wave merge, after the slot loop
     } u;
 };
 
-template <bool SWA, bool SINK, bool SPLIT>
+// ROT: how many of a lane's 32-dim query chunk rows can hold rotated dims (2 when r <= 64).
+template <bool SWA, bool SINK, bool SPLIT, int ROT>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
 
@@ -77,30 +91,65 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     const uint16_t* kc = a.k_cache + cache_row0 * DQK;
     const uint16_t* vc = a.v_cache + cache_row0 * DV;
 
-    // ---- slot loads into registers, one tile ahead of the one being computed.  Slots past
-    //      `limit` are not loaded; slots past the visible range and the new token's slot are fixed
-    //      up when used.
+    // ---- slot loads into registers, one tile ahead of the one being computed.  Every load is
+    //      unconditional: slots at or past `limit` read slot limit-1 again (a cache hit); slots
+    //      past the visible range and the new token's slot are fixed up when used.
     u32x4 kA[KREG], vA[VREG];
     auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0, int limit) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int j = t0 + kb * 16 + l16;
+            const int j = min(t0 + kb * 16 + l16, limit - 1);
 #pragma unroll
             for (int c = 0; c < DQK / 32; ++c)
-                kr[kb * (DQK / 32) + c] = j < limit ? *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq)
-                                                    : u32x4{0u, 0u, 0u, 0u};
+                kr[kb * (DQK / 32) + c] = *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq);
         }
 #pragma unroll
         for (int it = 0; it < VREG; ++it) {
             const int e = lane + 64 * it;
-            const int j = t0 + e / (DV / 8);
-            vr[it] = j < limit ? *(const u32x4*)(vc + (int64_t)j * DV + (e % (DV / 8)) * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+            const int j = min(t0 + e / (DV / 8), limit - 1);
+            vr[it] = *(const u32x4*)(vc + (int64_t)j * DV + (e % (DV / 8)) * 8);
         }
     };
+    // ---- every load that does not depend on the position goes out first, unconditionally (a
+    //      load under a branch would be waited for at the branch's end): this lane's query chunks
+    //      in B-operand layout (head l16 of the group, dims 32c + 8gq..; lanes past the group's
+    //      heads read its last head, and those copies are never written out) with their rotation
+    //      partners, the new token, the sinks, one frequency per thread and, on sliding layers, the
+    //      first slot tile.
+    const int r = a.rope_dims, half = r >> 1;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + min(l16, G - 1)) * DQK;
+    u32x4 qraw[DQK / 32], qpar[ROT];
+#pragma unroll
+    for (int c = 0; c < DQK / 32; ++c) qraw[c] = *(const u32x4*)(qrow + 32 * c + 8 * gq);
+#pragma unroll
+    for (int c = 0; c < ROT; ++c) {
+        const int d0 = 32 * c + 8 * gq;
+        qpar[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : (d0 < r ? d0 - half : d0)));
+    }
+    const int64_t kv_row = (int64_t)b * a.Hkv + g;
+    const int nd0 = tid < DQK / 8 ? tid * 8 : 0;   // k_new dims of this thread (tid < 24)
+    const uint16_t* nsrc = tid >= DQK / 8 && tid < DQK / 8 + DV / 8
+                               ? a.v_new + kv_row * DV + (tid - DQK / 8) * 8
+                               : a.k_new + kv_row * DQK + nd0;
+    const u32x4 nraw = *(const u32x4*)nsrc;
+    const u32x4 npar = *(const u32x4*)(a.k_new + kv_row * DQK +
+                                       (nd0 < half ? nd0 + half : (nd0 < r ? nd0 - half : nd0)));
+    const float sink_pre = (SINK && !SPLIT) ? a.sinks[g * G + min(tid & 15, G - 1)] : 0.0f;
+    // (kernel arguments count as invariant memory, which the barrier below does not hold in place:
+    //  read the frequencies, which sit in the argument segment, through a pointer the compiler
+    //  cannot trace back to it)
+    const char* kargs = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kargs));
+    const double om = ((const __attribute__((address_space(1))) double*)(
+        kargs + offsetof(DecodeArgs, omega_rev)))[min(tid, kMaxRopeHalf - 1)];
     const int stride = NW * TILE;
     int t0 = k_begin + wave * TILE;
-    if (SWA) fetch(kA, vA, t0, a.cap);  // every ring slot is in bounds: start before the position is known
+    // every ring slot is in bounds; a linear cache's splits past the position would only waste
+    // bandwidth, so those wait for it
+    if (SWA) fetch(kA, vA, t0, a.cap);
+    // keep the loads above here: the compiler would otherwise sink each one next to its use,
+    // behind the position check (emits no instruction and waits for nothing)
+    asm volatile("" ::: "memory");
 
     const int32_t pos = a.positions[b];
     const bool pos_ok = pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap);
@@ -116,48 +165,37 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     if (k_begin >= n_valid) return;
     const int k_end = min(n_valid, k_begin + a.chunk);
     const bool own_new = slot_new >= k_begin && slot_new < k_end;
-    const int r = a.rope_dims, half = r >> 1;
     if (!SWA) fetch(kA, vA, t0, k_end);
 
-    // ---- rotated queries of this group -> LDS (heads >= G are zero).
-    for (int c = tid; c < 16 * (DQK / 8); c += 256) {
-        const int hh = c / (DQK / 8), col = c % (DQK / 8);
-        u32x4 wv = u32x4{0u, 0u, 0u, 0u};
-        if (hh < G) {
-            const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + hh) * DQK;
-            wv = *(const u32x4*)(qrow + col * 8);
-            if (col * 8 < r) {
-                const int d0 = col * 8;
-                const int pd = d0 < half ? d0 + half : d0 - half;
-                wv = rotate8_dec(wv, *(const u32x4*)(qrow + pd), d0, half, pos, a.omega_rev);
-            }
-        }
-        *(u32x4*)(sm.Qs + hh * DQK + col * 8) = wv;
+    // ---- cos/sin of the position per frequency, once per workgroup
+    if (tid < half) {
+        float c, sn;
+        rope_cos_sin_rev(pos, om, c, sn);
+        sm.cs[tid] = make_float2(c, sn);
     }
-    // ---- the new token: rotate, keep in LDS, append to the cache.
-    if (own_new && tid < DQK / 8 + DV / 8) {
-        if (tid < DQK / 8) {
-            const uint16_t* krow = a.k_new + ((int64_t)b * a.Hkv + g) * DQK;
-            const int d0 = tid * 8;
-            u32x4 wv = *(const u32x4*)(krow + d0);
-            if (d0 < r) {
-                const int pd = d0 < half ? d0 + half : d0 - half;
-                wv = rotate8_dec(wv, *(const u32x4*)(krow + pd), d0, half, pos, a.omega_rev);
-            }
-            *(u32x4*)(sm.Kn + d0) = wv;
-            *(u32x4*)(a.k_cache + (cache_row0 + slot_new) * DQK + d0) = wv;
-        } else {
-            const int d0 = (tid - DQK / 8) * 8;
-            const u32x4 wv = *(const u32x4*)(a.v_new + ((int64_t)b * a.Hkv + g) * DV + d0);
-            *(u32x4*)(sm.Vn + d0) = wv;
-            *(u32x4*)(a.v_cache + (cache_row0 + slot_new) * DV + d0) = wv;
-        }
-    }
+    if (tid >= 256 - 8) sm.cs[kIdentity + tid - (256 - 8)] = make_float2(1.0f, 0.0f);
+    if (SINK && !SPLIT && tid < 16) sm.sink[tid] = sink_pre * kLog2e;
     __syncthreads();
 
+    // ---- this lane's rotated query chunks: the B operand of v_mfma_f32_16x16x32_bf16
     bf16x8 Qb[DQK / 32];
 #pragma unroll
-    for (int c = 0; c < DQK / 32; ++c) Qb[c] = *(const bf16x8*)(sm.Qs + l16 * DQK + 32 * c + 8 * gq);
+    for (int c = 0; c < DQK / 32; ++c)
+        Qb[c] = as_bf16x8(c < ROT ? rotate8_cs(qraw[c], qpar[c], 32 * c + 8 * gq, half, r, sm.cs)
+                                  : qraw[c]);
+    // ---- the new token: rotate, keep in LDS, append to the cache (the owning split only).
+    if (own_new) {
+        if (tid < DQK / 8) {
+            const u32x4 wv = rotate8_cs(nraw, npar, nd0, half, r, sm.cs);
+            *(u32x4*)(sm.Kn + nd0) = wv;
+            *(u32x4*)(a.k_cache + (cache_row0 + slot_new) * DQK + nd0) = wv;
+        } else if (tid < DQK / 8 + DV / 8) {
+            const int d0 = (tid - DQK / 8) * 8;
+            *(u32x4*)(sm.Vn + d0) = nraw;
+            *(u32x4*)(a.v_cache + (cache_row0 + slot_new) * DV + d0) = nraw;
+        }
+        __syncthreads();
+    }
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 O[DV / 16];
@@ -202,7 +240,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 acc = mfma16x16x32(as_bf16x8(kr[kb * (DQK / 32) + c]), Qb[c], acc);
             Sacc[kb] = acc;
         }
-        fetch(kr, vr, t + stride, k_end);
+        if (t + stride < k_end) fetch(kr, vr, t + stride, k_end);
 
         float mx = -INFINITY;
 #pragma unroll
@@ -266,56 +304,62 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     }
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.u.red_o[wave][l16][db * 16 + 4 * gq + i] = O[db][i];
+        *(f32x4*)&sm.u.red_o[wave][l16][db * 16 + 4 * gq] = O[db];
     __syncthreads();
 
-    for (int e = tid; e < 16 * DV; e += 256) {
-        const int hh = e / DV, d = e % DV;
-        if (hh >= G) continue;
-        float M = -INFINITY;
+    // one thread per (head, 4 dims): the head's wave weights once, then 4 outputs
+    for (int e4 = tid; e4 < G * (DV / 4); e4 += 256) {
+        const int hh = e4 / (DV / 4), d0 = (e4 % (DV / 4)) * 4;
+        const int h = g * G + hh;
+        float M = SINK && !SPLIT ? sm.sink[hh] : -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.red_m[w][hh]);
-        const int h = g * G + hh;
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        float L = SINK && !SPLIT ? fast_exp2(sm.sink[hh] - Mu) : 0.0f;
+        f32x4 acc = f32x4{};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(sm.red_m[w][hh] - Mu);
+            L += sm.red_l[w][hh] * f;
+            acc += *(const f32x4*)&sm.u.red_o[w][hh][d0] * f;
+        }
         if (SPLIT) {
-            const float Mu = (M == -INFINITY) ? 0.0f : M;
-            float L = 0.0f, acc = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float f = fast_exp2(sm.red_m[w][hh] - Mu);
-                L += sm.red_l[w][hh] * f;
-                acc += sm.u.red_o[w][hh][d] * f;
-            }
             float* rec = a.partial + (((int64_t)b * a.Hq + h) * a.nsplit + s) * PSTRIDE;
-            rec[d] = acc;
-            if (d == 0) {
-                rec[DV] = M;
-                rec[DV + 1] = L;
-            }
+            *(float2*)(rec + d0) = make_float2(acc[0], acc[1]);
+            *(float2*)(rec + d0 + 2) = make_float2(acc[2], acc[3]);
+            if (d0 == 0) *(float2*)(rec + DV) = make_float2(M, L);
         } else {
-            const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
-            const float Ms = fmaxf(M, sk);
-            const float Mu = (Ms == -INFINITY) ? 0.0f : Ms;
-            float L = SINK ? fast_exp2(sk - Mu) : 0.0f, acc = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float f = fast_exp2(sm.red_m[w][hh] - Mu);
-                L += sm.red_l[w][hh] * f;
-                acc += sm.u.red_o[w][hh][d] * f;
-            }
-            const float o = L > 0.0f ? a.v_scale * acc / L : 0.0f;
-            a.out[((int64_t)b * a.Hq + h) * DV + d] = f32_to_bf16_bits(o);
+            const float sc_o = L > 0.0f ? a.v_scale / L : 0.0f;
+            const u32x2 o2 = u32x2{pack_bf16x2(acc[0] * sc_o, acc[1] * sc_o),
+                                   pack_bf16x2(acc[2] * sc_o, acc[3] * sc_o)};
+            *(u32x2*)(a.out + ((int64_t)b * a.Hq + h) * DV + d0) = o2;
         }
     }
 }
 
 // Merge the splits of one (sequence, query head); the sink joins the denominator once, here.  One
-// thread per output dim; the records of up to 32 splits are loaded in one round trip, then merged
-// against their common maximum (chunks of 32 are chained with a running maximum).
+// thread per output dim.  The position, every split's (max, sum) and the first PRE records' values
+// are requested together, before anything waits (records past the last split are read as the last
+// one again): splits the position leaves empty never wrote their records, so those values are
+// masked, never used.  Then the common maximum and the
+// weights go through LDS and each thread sums its dim.
 template <bool SWA, bool SINK>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a) {
-    constexpr int CH = 32;
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    constexpr int PRE = 96, CH = 32;
+    __shared__ float w_s[1024], l_s[1024];
+    __shared__ float red[4];
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, wave = d >> 6;
+    const int nsp = a.nsplit;
+    const float* rec = a.partial + ((int64_t)b * a.Hq + h) * nsp * PSTRIDE;
+    float x[PRE];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) x[i] = rec[(int64_t)min(i, nsp - 1) * PSTRIDE + d];
+    for (int i = d; i < nsp; i += 128) {
+        w_s[i] = rec[(int64_t)i * PSTRIDE + DV];
+        l_s[i] = rec[(int64_t)i * PSTRIDE + DV + 1];
+    }
+    const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
+    asm volatile("" ::: "memory");   // keeps the loads above ahead of the position check
     const int32_t pos = a.positions[b];
     uint16_t* o = a.out + ((int64_t)b * a.Hq + h) * DV;
     const bool pos_ok = pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap);
@@ -324,46 +368,48 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
         return;
     }
     const int n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
-    const int ns = (n_valid + a.chunk - 1) / a.chunk;   // every one of these splits wrote a record
-    const float* rec = a.partial + ((int64_t)b * a.Hq + h) * a.nsplit * PSTRIDE;
-    float M = SINK ? a.sinks[h] * kLog2e : -INFINITY;
-    float L = SINK ? 1.0f : 0.0f, acc = 0.0f;
-    for (int s0 = 0; s0 < ns; s0 += CH) {
-        float m[CH], l[CH], x[CH];
+    const int ns = min(nsp, (n_valid + a.chunk - 1) / a.chunk);   // splits that wrote a record
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int i = d; i < ns; i += 128) mx = fmaxf(mx, w_s[i]);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const bool ok = s0 + i < ns;
-            const float* r = rec + (int64_t)(s0 + i) * PSTRIDE;
-            m[i] = ok ? r[DV] : -INFINITY;
-            l[i] = ok ? r[DV + 1] : 0.0f;
-            x[i] = ok ? r[d] : 0.0f;
-        }
-        float Mc = M;
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if ((d & 63) == 0) red[wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), sk);
+    const float Mu = (M == -INFINITY) ? 0.0f : M;
+    float ls = 0.0f;
+    for (int i = d; i < ns; i += 128) {
+        const float w = fast_exp2(w_s[i] - Mu);
+        w_s[i] = w;
+        ls += w * l_s[i];
+    }
 #pragma unroll
-        for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, m[i]);
-        const float Mu = (Mc == -INFINITY) ? 0.0f : Mc;
-        const float f = fast_exp2(M - Mu);
-        L *= f;
-        acc *= f;
+    for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off);
+    if ((d & 63) == 0) red[2 + wave] = ls;
+    __syncthreads();
+    const float L = red[2] + red[3] + (SINK ? fast_exp2(sk - Mu) : 0.0f);
+    float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const float wgt = fast_exp2(m[i] - Mu);
-            L += l[i] * wgt;
-            acc += x[i] * wgt;
-        }
-        M = Mc;
+    for (int i = 0; i < PRE; ++i) acc += i < ns ? w_s[i] * x[i] : 0.0f;
+    for (int s0 = PRE; s0 < ns; s0 += CH) {
+        float y[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) y[i] = rec[(int64_t)min(s0 + i, ns - 1) * PSTRIDE + d];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) acc += s0 + i < ns ? w_s[s0 + i] * y[i] : 0.0f;
     }
     o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
 }
 
-template <bool SWA, bool SINK>
+template <bool SWA, bool SINK, int ROT>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
     const dim3 grid(a.nsplit, a.Hkv, a.B);
     if (a.nsplit == 1) {
-        decode_bf16_kernel<SWA, SINK, false><<<grid, 256, 0, st>>>(a);
+        decode_bf16_kernel<SWA, SINK, false, ROT><<<grid, 256, 0, st>>>(a);
         return hipGetLastError();
     }
-    decode_bf16_kernel<SWA, SINK, true><<<grid, 256, 0, st>>>(a);
+    decode_bf16_kernel<SWA, SINK, true, ROT><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     decode_combine_kernel<SWA, SINK><<<dim3(a.Hq, a.B), DV, 0, st>>>(a);
@@ -377,8 +423,12 @@ int decode_max_splits() { return 1024; }
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st) {
     if (a.B == 0) return hipSuccess;
     if (a.nsplit > decode_max_splits()) return hipErrorInvalidConfiguration;
-    if (swa) return sink ? launch_typed<true, true>(a, st) : launch_typed<true, false>(a, st);
-    return sink ? launch_typed<false, true>(a, st) : launch_typed<false, false>(a, st);
+    if (a.rope_dims <= 64) {
+        if (swa) return sink ? launch_typed<true, true, 2>(a, st) : launch_typed<true, false, 2>(a, st);
+        return sink ? launch_typed<false, true, 2>(a, st) : launch_typed<false, false, 2>(a, st);
+    }
+    if (swa) return sink ? launch_typed<true, true, 6>(a, st) : launch_typed<true, false, 6>(a, st);
+    return sink ? launch_typed<false, true, 6>(a, st) : launch_typed<false, false, 6>(a, st);
 }
 
 }  // namespace mimo
