@@ -14,6 +14,10 @@ KV GB/s, each kind separately, with roofline fractions) are in `phases`; `roofli
 dominant kernel (global-layer prefill) and `cpu_baseline` the fp64 oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+                      [--eager-decode]
+
+The decode phase replays one HIP graph per step (the 48 decode calls and the position increment,
+captured once before timing); --eager-decode launches them from Python instead.
 
 Single-layer workloads for profiling (not the bench line): --workload swa_prefill (batch 1, 4096
 tokens, sliding), ga_prefill (batch 1, 8192 tokens, global), decode (batch 64, cached lengths
@@ -141,6 +145,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-decode", action="store_true",
+                    help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
                     choices=["stack", "swa_prefill", "ga_prefill", "decode", "copy"])
     args = ap.parse_args()
@@ -183,13 +189,15 @@ def main():
         vc = torch.zeros((B, sp.num_kv_heads, cap, DV), dtype=torch.bfloat16, device=dev)
         g = torch.Generator(device=dev)
         g.manual_seed(seed_base + 100 + sp.index)
-        dq = torch.randn((T, B, Hq, DQK), generator=g, device=dev).to(torch.bfloat16)
-        dk = torch.randn((T, B, sp.num_kv_heads, DQK), generator=g, device=dev).to(torch.bfloat16)
-        dv = torch.randn((T, B, sp.num_kv_heads, DV), generator=g, device=dev).to(torch.bfloat16)
+        # the decoding token's q/k/v buffers of this layer (a serving engine's projection outputs:
+        # fixed addresses, rewritten every step; the values do not change the work)
+        dq = torch.randn((B, Hq, DQK), generator=g, device=dev).to(torch.bfloat16)
+        dk = torch.randn((B, sp.num_kv_heads, DQK), generator=g, device=dev).to(torch.bfloat16)
+        dv = torch.randn((B, sp.num_kv_heads, DV), generator=g, device=dev).to(torch.bfloat16)
         layers.append(dict(spec=sp, p=sp.params(cfg, B), q=q, k=k, v=v,
                            sinks=s if sp.has_sinks else None, kc=kc, vc=vc, dq=dq, dk=dk, dv=dv))
     start_pos = torch.zeros(B, dtype=torch.int32, device=dev)
-    dec_pos = [torch.full((B,), S + t, dtype=torch.int32, device=dev) for t in range(T)]
+    dec_pos = torch.full((B,), S, dtype=torch.int32, device=dev)   # position of the decoding token
     out_pf = torch.empty((B, S, Hq, DV), dtype=torch.bfloat16, device=dev)
     out_dec = torch.empty((B, Hq, DV), dtype=torch.bfloat16, device=dev)
     ws_pf = torch.empty(max(mimo.prefill_workspace_size(l["p"], S) for l in layers) + 256,
@@ -200,6 +208,26 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     ga_events = []
+
+    def decode_step():
+        """One decode step through the 48 layers, then the position advances."""
+        for l in layers:
+            mimo.decode(l["p"], l["dq"], l["dk"], l["dv"], dec_pos, S + T - 1, l["kc"], l["vc"],
+                        sinks=l["sinks"], out=out_dec, workspace=ws_dec)
+        dec_pos.add_(1)
+
+    graph = None
+    if not args.eager_decode:
+        # decode is launch-bound at batch 2 (48 small layers per step): the step is captured once
+        # as a HIP graph and replayed; positions live in device memory, so one graph serves every
+        # step.  Warm up eagerly first (kernel code objects load on first launch).
+        dec_pos.fill_(S)
+        decode_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_step()
+        torch.cuda.synchronize()
 
     def step(record):
         for l in layers:
@@ -215,10 +243,12 @@ def main():
                 ga_events.append((e0, e1))
         mid = ev()
         mid.record()
+        dec_pos.fill_(S)
         for t in range(T):
-            for l in layers:
-                mimo.decode(l["p"], l["dq"][t], l["dk"][t], l["dv"][t], dec_pos[t], S + T - 1,
-                            l["kc"], l["vc"], sinks=l["sinks"], out=out_dec, workspace=ws_dec)
+            if graph is not None:
+                graph.replay()
+            else:
+                decode_step()
         return mid
 
     for _ in range(args.warmup):
@@ -292,6 +322,7 @@ def main():
                         "sliding_layer_GBps": round(swa_gbps, 1),
                         "sliding_frac_hbm_peak": round(swa_gbps / PEAK_HBM_GBPS, 4)},
             "decode": {"ms": round(decode_ms, 3), "steps": T,
+                       "launch": "eager" if graph is None else "hip_graph_per_step",
                        "GBps": round(dec_gbps, 1),
                        "frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
                        "kv_bytes_global": dec_b_ga, "kv_bytes_sliding": dec_b_swa},

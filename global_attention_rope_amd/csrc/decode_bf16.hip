@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     }
     if (tid >= 256 - 8) sm.cs[kIdentity + tid - (256 - 8)] = make_float2(1.0f, 0.0f);
     if (SINK && !SPLIT && tid < 16) sm.sink[tid] = sink_pre * kLog2e;
-    __syncthreads();
+    block_sync_lds();
 
     // ---- this lane's rotated query chunks: the B operand of v_mfma_f32_16x16x32_bf16
     bf16x8 Qb[DQK / 32];
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             *(u32x4*)(sm.Vn + d0) = nraw;
             *(u32x4*)(a.v_cache + (cache_row0 + slot_new) * DV + d0) = nraw;
         }
-        __syncthreads();
+        block_sync_lds();
     }
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // ---- merge the waves of the workgroup (the V tiles are dead now; red_o reuses them).
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    __syncthreads();
+    block_sync_lds();
     if (gq == 0) {
         sm.red_m[wave][l16] = m_run;
         sm.red_l[wave][l16] = l_run;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db)
         *(f32x4*)&sm.u.red_o[wave][l16][db * 16 + 4 * gq] = O[db];
-    __syncthreads();
+    block_sync_lds();
 
     // one thread per (head, 4 dims): the head's wave weights once, then 4 outputs
     for (int e4 = tid; e4 < G * (DV / 4); e4 += 256) {
@@ -369,13 +369,13 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
     }
     const int n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
     const int ns = min(nsp, (n_valid + a.chunk - 1) / a.chunk);   // splits that wrote a record
-    __syncthreads();
+    block_sync_lds();
     float mx = -INFINITY;
     for (int i = d; i < ns; i += 128) mx = fmaxf(mx, w_s[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if ((d & 63) == 0) red[wave] = mx;
-    __syncthreads();
+    block_sync_lds();
     const float M = fmaxf(fmaxf(red[0], red[1]), sk);
     const float Mu = (M == -INFINITY) ? 0.0f : M;
     float ls = 0.0f;
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off);
     if ((d & 63) == 0) red[2 + wave] = ls;
-    __syncthreads();
+    block_sync_lds();
     const float L = red[2] + red[3] + (SINK ? fast_exp2(sk - Mu) : 0.0f);
     float acc = 0.0f;
 #pragma unroll

@@ -29,6 +29,13 @@ __device__ __forceinline__ void rope_cos_sin_rev(int32_t pos, double w_rev, floa
     c = __builtin_amdgcn_cosf(xf);
 }
 
+// Workgroup barrier for LDS traffic only: every wave's LDS accesses have completed, nothing else
+// is waited for.  (__syncthreads also releases global memory, which on gfx950 waits for every
+// outstanding global load and store of the wave.)
+__device__ __forceinline__ void block_sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // 2^x by the hardware exponential (softmax weights; x <= 0 here).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

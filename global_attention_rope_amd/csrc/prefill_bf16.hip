@@ -57,9 +57,6 @@ constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyon
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ void block_sync_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -1,0 +1,75 @@
+"""Decode under HIP graph capture.
+
+A serving loop captures one decode step (the layers' decode calls plus the position advance) and
+replays it; the entry points allocate nothing, set no memory and never synchronise, so they can be
+captured.  Each replay must reproduce the eager calls on the same state bit for bit (the kernels
+are deterministic), with unrelated eager work and synchronisations between the replays, and leave
+the caches exactly as the eager calls leave them.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import global_attention_rope_amd as mimo
+from tests import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _layer(kind, B, P0, R, seed):
+    heads = synth.SWA_HEADS if kind == 1 else synth.GA_HEADS
+    w = synth.Workload("graph", B, 1, dtype=torch.bfloat16, **heads)
+    cap = w.window if kind == 1 else P0 + R
+    q, kn, vn, s, kc, vc = synth.decode_inputs(w, seed, B, cap, device=DEV)
+    p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, w.qk_head_dim, w.v_head_dim, w.rope_dims,
+                    w.layer_kind, w.window, w.rope_theta, w.v_scale)
+    ws = torch.empty(mimo.decode_workspace_size(p, P0 + R - 1) + 256, dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, w.num_q_heads, w.v_head_dim), dtype=torch.bfloat16, device=DEV)
+    return dict(p=p, q=q, kn=kn, vn=vn, s=s, kc=kc, vc=vc, ws=ws, out=out)
+
+
+def test_decode_graph_replays_match_eager():
+    B, P0, R = 2, 3000, 4
+    layers = [_layer(0, B, P0, R, 9100), _layer(1, B, P0, R, 9101)]
+    maxp = P0 + R - 1
+    print(f"[case] graph decode B={B} positions {P0}..{maxp}, global + sliding layer", flush=True)
+
+    def step(pos, caches, outs):
+        for l, (kc, vc), out in zip(layers, caches, outs):
+            mimo.decode(l["p"], l["q"], l["kn"], l["vn"], pos, maxp, kc, vc, sinks=l["s"], out=out,
+                        workspace=l["ws"])
+        pos.add_(1)
+
+    # eager reference on copies of the caches
+    caches_e = [(l["kc"].clone(), l["vc"].clone()) for l in layers]
+    outs_e = [torch.empty_like(l["out"]) for l in layers]
+    pos_e = torch.full((B,), P0, dtype=torch.int32, device=DEV)
+    ref = []
+    for _ in range(R):
+        step(pos_e, caches_e, outs_e)
+        ref.append([o.clone() for o in outs_e])
+    torch.cuda.synchronize()
+
+    # captured step on the original caches
+    caches = [(l["kc"], l["vc"]) for l in layers]
+    outs = [l["out"] for l in layers]
+    pos = torch.full((B,), P0, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(pos, caches, outs)
+    torch.cuda.synchronize()
+    assert int(pos[0]) == P0, "capture must not execute the step"
+    for t in range(R):
+        g.replay()
+        torch.cuda.synchronize()
+        for li, (o, r) in enumerate(zip(outs, ref[t])):
+            assert torch.equal(o, r), f"replay {t} layer {li} differs from the eager call"
+        junk = torch.randn(4096, device=DEV)   # unrelated eager work between replays
+        assert torch.isfinite(junk.sum())
+        torch.cuda.synchronize()
+    assert torch.equal(pos, pos_e)
+    for (kc, vc), (kce, vce) in zip(caches, caches_e):
+        assert torch.equal(kc, kce) and torch.equal(vc, vce)
