@@ -28,8 +28,10 @@
 //   * the wave index is made scalar so tile skipping and the band-edge masking are uniform
 //     branches; sliding-window workgroups only stream the tiles of their band, and each wave only
 //     computes the tiles its own rows can see;
-//   * workgroups are ordered heavy-first and grouped so that the workgroups the dispatcher sends to
-//     one XCD in a row share a KV head (its K/V stay hot in that XCD's L2).
+//   * global layers: workgroups are ordered heavy-first and grouped so that the workgroups the
+//     dispatcher sends to one XCD in a row share a KV head (its K/V stay hot in that XCD's L2);
+//     sliding layers: each XCD walks consecutive row blocks of a few (sequence, head unit) pairs,
+//     so the sliding K/V band is fetched from memory about once.
 #include <type_traits>
 
 #include "device_common.h"
@@ -107,11 +109,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int hunits = GROUPED ? Hq / NW : Hq;     // head units per (row block, sequence)
     const int total = a.B * hunits * nqblk;
 
-    // ---- work item: XCD-grouped (the 8 items one XCD receives in a row share rows and, for
-    //      consecutive heads, a KV head), heavy-first on global layers
+    // ---- work item (XCD-aware order; heavy-first on global layers)
     const int id = blockIdx.x;
     int w = id;
-    {
+    const int pairs = a.B * hunits;                // (sequence, head unit) pairs
+    if (WINDOW && pairs % 8 == 0) {
+        // sliding layers: workgroup ids go round-robin to the 8 XCDs; each XCD walks the row
+        // blocks of its own pairs in order (its pairs interleaved), so the K/V band, which
+        // consecutive row blocks share, stays in that XCD's L2 as it slides
+        const int P = pairs / 8, xcd = id & 7, k = id >> 3;
+        w = (k / P) * pairs + xcd * P + k % P;
+    } else if (!WINDOW) {
         const int xcd = id & 7, slot = id >> 3, grp = slot >> 3;
         if ((grp + 1) * 64 <= total) w = grp * 64 + xcd * 8 + (slot & 7);
     }
@@ -197,18 +205,56 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         u32x4 qw[KCH];
 #pragma unroll
         for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int d0 = 16 * c + 8 * g;
-            if (d0 < r) {
-                const bool lower = d0 < half;
-                u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
-                u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
-                rotate_pair8_kernarg(lo, hi, p0 + qi, a.omega_rev + (lower ? d0 : d0 - half));
-                qw[c] = lower ? lo : hi;
+        if constexpr (GROUPED) {
+            // The NW waves share the 32 rows (one head each): the cos/sin of the rows' positions
+            // per frequency are evaluated once for the workgroup into a table in stage 1, which
+            // no tile uses before the first tile step.
+            static_assert(STAGES == 2, "table lives in stage 1");   // 32 x 97 x 8 B <= K_TILE
+            // (row pitch half + 1 entries: the 32 rows' reads of one frequency hit distinct banks)
+            float2* cs = (float2*)(smem + K_TILE);
+            const int pitch = half + 1;
+            for (int e = tid; e < QPW * half; e += NW * 64) {
+                const int row = e / half, f = e - row * half;
+                float c, sn;
+                rope_cos_sin_rev(p0 + min(q_first + row, S - 1), a.omega_rev[f], c, sn);
+                cs[row * pitch + f] = make_float2(c, sn);
             }
-            if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
-            Qb[c] = as_bf16x8(qw[c]);
+            block_sync_lds();
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int d0 = 16 * c + 8 * g;
+                if (d0 < r) {
+                    const bool lower = d0 < half;
+                    const u32x4 pw = *(const u32x4*)(qrow + (lower ? d0 + half : d0 - half));
+                    const float2* e = cs + l32 * pitch + (lower ? d0 : d0 - half);
+                    float x[8], y[8];
+                    unpack8(qw[c], x);
+                    unpack8(pw, y);
+                    const float sgn = lower ? -1.0f : 1.0f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float2 cst = e[t];
+                        x[t] = __builtin_fmaf(sgn * y[t], cst.y, x[t] * cst.x);
+                    }
+                    qw[c] = pack8(x);
+                }
+                if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
+                Qb[c] = as_bf16x8(qw[c]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int d0 = 16 * c + 8 * g;
+                if (d0 < r) {
+                    const bool lower = d0 < half;
+                    u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
+                    u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
+                    rotate_pair8_kernarg(lo, hi, p0 + qi, a.omega_rev + (lower ? d0 : d0 - half));
+                    qw[c] = lower ? lo : hi;
+                }
+                if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
+                Qb[c] = as_bf16x8(qw[c]);
+            }
         }
     }
 
@@ -219,12 +265,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int x = 0; x < 4; ++x) k_rd[x] = l32 * (DQK * 2) + 16 * ((2 * x + g) ^ swz);
     const int qsel = lane >> 4, jsel = lane & 15;
     const int vrow = 4 * (qsel >> 1) + (jsel >> 2);
+    // (V stages start past 64 KiB on global layers, beyond the 16-bit immediate offset of LDS
+    //  reads: the V stage base is folded into these registers, hidden from the compiler so that
+    //  it does not split it back out into a per-read address add)
     int v_rd[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-        v_rd[db] = vrow * (DV * 2) +
+    for (int db = 0; db < 4; ++db) {
+        v_rd[db] = STAGES * K_TILE + vrow * (DV * 2) +
                    16 * (4 * (db ^ ((jsel >> 2) & 3)) + 2 * (qsel & 1) + ((jsel & 3) >> 1)) +
                    8 * (jsel & 1);
+        asm volatile("" : "+v"(v_rd[db]));
+    }
 
     const float sink_l2 = SINK ? a.sinks[h] * kLog2e : -INFINITY;
     float m_run = SINK ? sink_l2 : -INFINITY;
@@ -243,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         // every key visible to every row of the wave
         const bool full = j0 + BN - 1 <= q_first && (!WINDOW || q_last - j0 < W);
         const uint8_t* kst = smem + ST * K_TILE;
-        const uint8_t* vst = smem + STAGES * K_TILE + ST * V_TILE;
+        const uint8_t* vst = smem + ST * V_TILE;   // + v_rd, which holds the V area's base
 
         f32x16 S0 = f32x16{}, S1 = f32x16{};
 #pragma unroll
@@ -254,25 +305,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             S0 = mfma32x32x16(A0, Qb[c], S0);
             S1 = mfma32x32x16(A1, Qb[c], S1);
         }
-        float mx = -INFINITY;
         if (!full) {
+            // (the empty asm keeps the compiler from if-converting this uniform branch, which
+            //  would run the masking on every tile)
+            asm volatile("");
+            // key j0 + 8(i/4) + 4g + i%4 (+32 in block 1) against row q_l: visible iff
+            // 0 <= q_l - j (< W), i.e. the unsigned difference d - off is below the limit
+            const int d = q_l - j0 - 4 * g;
+            const unsigned lim = WINDOW ? (unsigned)W : 0x80000000u;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int j = j0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                const bool ok0 = j <= q_l && (!WINDOW || q_l - j < W);
-                const bool ok1 = j + 32 <= q_l && (!WINDOW || q_l - j - 32 < W);
-                S0[i] = ok0 ? S0[i] : -INFINITY;
-                S1[i] = ok1 ? S1[i] : -INFINITY;
+                const int off = 8 * (i >> 2) + (i & 3);
+                S0[i] = (unsigned)(d - off) < lim ? S0[i] : -INFINITY;
+                S1[i] = (unsigned)(d - off - 32) < lim ? S1[i] : -INFINITY;
             }
         }
+        // row maximum: two chains of 3-input maxima
+        float ma = fmaxf(S0[0], S1[0]), mb = fmaxf(S0[8], S1[8]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
+        for (int i = 1; i < 8; ++i) {
+            ma = fmaxf(fmaxf(ma, S0[i]), S1[i]);
+            mb = fmaxf(fmaxf(mb, S0[i + 8]), S1[i + 8]);
+        }
+        float mx = fmaxf(ma, mb);
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
         // lazily raised reference maximum
         const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
         const float m_new = raise ? fmaxf(m_run, mx) : m_run;
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         if (__any(raise)) {
+            asm volatile("");   // rare: keep it a branch (see above)
             const float alpha = fast_exp2(m_run - m_use);
             l_run *= alpha;
 #pragma unroll
