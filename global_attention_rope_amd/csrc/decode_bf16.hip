@@ -37,8 +37,6 @@ constexpr int KREG = 2 * (DQK / 32);     // 16-byte K operand loads per lane per
 constexpr int VREG = TILE * DV / 8 / 64; // 16-byte V loads per lane per tile (8)
 constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merge buffer
 
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
 // Rotate 8 consecutive dims d0.. of a row (w) against their partners (pw) with the cos/sin of the
 // row's position per frequency (cs, in LDS).  Dims at or past r read the identity entries
 // (cos 1, sin 0) stored after the table, so every chunk runs the same straight-line code and the
@@ -253,8 +251,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 mx = fmaxf(mx, v);
             }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_lane_pair32(max_lane_pair16(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
@@ -295,8 +292,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     for (; t0 < k_end; t0 += stride) consume(kA, vA, t0);
 
     // ---- merge the waves of the workgroup (the V tiles are dead now; red_o reuses them).
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_lane_pair32(sum_lane_pair16(l_run));
     block_sync_lds();
     if (gq == 0) {
         sm.red_m[wave][l16] = m_run;

@@ -36,6 +36,52 @@ __device__ __forceinline__ void block_sync_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.  Issued as
+// inline asm so that the compiler does not track these LDS writes: it would otherwise wait for
+// every outstanding load before each transposed LDS read.  Completion is ordered explicitly with
+// wait_vmcnt + block_sync_lds; the instruction has no register results.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// Maximum of x over the lane pair (l, l ^ 32), in registers (no LDS round trip).
+__device__ __forceinline__ float max_lane_pair32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Maximum of x over the lane pair (l, l ^ 16), in registers.
+__device__ __forceinline__ float max_lane_pair16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum of x over the lane pair (l, l ^ 16).
+__device__ __forceinline__ float sum_lane_pair16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of x over the lane pair (l, l ^ 32).
+__device__ __forceinline__ float sum_lane_pair32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 2^x by the hardware exponential (softmax weights; x <= 0 here).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

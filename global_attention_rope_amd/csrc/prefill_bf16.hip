@@ -56,22 +56,6 @@ constexpr int GA_WAVES = 8, GA_STAGES = 3;
 constexpr int SW_WAVES = 4, SW_STAGES = 2;
 constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyond 2^8
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.  Issued as
-// inline asm so that the compiler does not track these LDS writes: it would otherwise wait for
-// every outstanding load before each transposed LDS read.  Completion is ordered explicitly with
-// wait_vmcnt + block_sync_lds; the instruction has no register results.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-                 : "memory", "m0");
-}
 
 __device__ __forceinline__ void rotate_pair8_kernarg(u32x4& lo, u32x4& hi, int32_t pos,
                                                      const double* om) {
@@ -327,8 +311,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             ma = fmaxf(fmaxf(ma, S0[i]), S1[i]);
             mb = fmaxf(fmaxf(mb, S0[i + 8]), S1[i + 8]);
         }
-        float mx = fmaxf(ma, mb);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+        const float mx = max_lane_pair32(fmaxf(ma, mb)) * sc;
         // lazily raised reference maximum
         const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
         const float m_new = raise ? fmaxf(m_run, mx) : m_run;
@@ -395,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 
     // ---- epilogue: out = v_scale * O / l, bf16
-    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float lt = sum_lane_pair32(l_run);
     const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
     if (q_l < S) {
         uint16_t* orow = a.out + (((int64_t)b * S + q_l) * Hq + h) * DV;
