@@ -145,11 +145,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // every ring slot is in bounds; a linear cache's splits past the position would only waste
     // bandwidth, so those wait for it
     if (SWA) fetch(kA, vA, t0, a.cap);
-    // keep the loads above here: the compiler would otherwise sink each one next to its use,
-    // behind the position check (emits no instruction and waits for nothing)
-    asm volatile("" ::: "memory");
+    // The position comes by a scalar load, counted apart from the vector loads (lgkmcnt, not
+    // vmcnt): the work that needs only the position and the query (cos/sin table, query and
+    // new-token rotation) runs while the slot tile is still in flight.  The load waits for its
+    // own result in the same statement; the memory clobber keeps the loads above in place (the
+    // compiler would otherwise sink each one next to its use, behind the position check).
+    const int32_t pos = load_scalar_i32(a.positions + b);
 
-    const int32_t pos = a.positions[b];
     const bool pos_ok = pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap);
     if (!pos_ok) {
         if (!SPLIT && s == 0) {  // defined result: zero output, nothing appended
@@ -355,8 +357,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
         l_s[i] = rec[(int64_t)i * PSTRIDE + DV + 1];
     }
     const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
-    asm volatile("" ::: "memory");   // keeps the loads above ahead of the position check
-    const int32_t pos = a.positions[b];
+    const int32_t pos = load_scalar_i32(a.positions + b);   // (also keeps the loads above first)
     uint16_t* o = a.out + ((int64_t)b * a.Hq + h) * DV;
     const bool pos_ok = pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap);
     if (!pos_ok) {

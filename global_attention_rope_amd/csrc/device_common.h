@@ -54,6 +54,15 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// 32-bit load of a workgroup-uniform address through the scalar cache, waited for in the same
+// statement (its counter is the scalar one, so vector loads issued before it stay in flight).
+// The memory clobber also keeps every earlier load ahead of it.
+__device__ __forceinline__ int32_t load_scalar_i32(const int32_t* p) {
+    int32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
 // Maximum of x over the lane pair (l, l ^ 32), in registers (no LDS round trip).
 __device__ __forceinline__ float max_lane_pair32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
