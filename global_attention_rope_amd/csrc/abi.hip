@@ -294,6 +294,10 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
     if (!swa && (int64_t)cache_capacity <= (int64_t)max_position)
         return fail(MIMO_ERR_INVALID_ARG, "linear cache capacity %d must exceed max_position %d",
                     cache_capacity, max_position);
+    // bf16 decode addresses a cache slice through a buffer resource with a 32-bit byte bound
+    if (p->dtype == MIMO_BF16 && (int64_t)cache_capacity * p->qk_head_dim * 2 > 0xffffffffLL)
+        return fail(MIMO_ERR_UNSUPPORTED, "cache_capacity %d: a bf16 cache slice must stay below 4 GiB",
+                    cache_capacity);
     hipStream_t st = (hipStream_t)stream;
     if (p->dtype == MIMO_F32) {
         mimo::F32DecodeArgs fa;

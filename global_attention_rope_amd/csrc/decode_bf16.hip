@@ -89,24 +89,34 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     const uint16_t* kc = a.k_cache + cache_row0 * DQK;
     const uint16_t* vc = a.v_cache + cache_row0 * DV;
 
-    // ---- slot loads into registers, one tile ahead of the one being computed.  Every load is
-    //      unconditional: slots at or past `limit` read slot limit-1 again (a cache hit); slots
-    //      past the visible range and the new token's slot are fixed up when used.
+    // ---- slot loads into registers, one tile ahead of the one being computed, as buffer loads:
+    //      one resource per cache slice, a per-lane byte offset computed once, the tile's slot in
+    //      the scalar offset and the chunk in the immediate (no per-load address arithmetic).
+    //      Slots at or past the capacity read zeros (the resource's bound); slots past the
+    //      visible range and the new token's slot are fixed up when used.
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.cap * (DQK * 2), kBufferFormat);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, a.cap * (DV * 2), kBufferFormat);
+    const int k_lane = (l16 * DQK + 8 * gq) * 2;
+    const int v_lane = ((lane >> 4) * DV + (lane & 15) * 8) * 2;
     u32x4 kA[KREG], vA[VREG];
-    auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0, int limit) {
+    auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int j = min(t0 + kb * 16 + l16, limit - 1);
 #pragma unroll
             for (int c = 0; c < DQK / 32; ++c)
-                kr[kb * (DQK / 32) + c] = *(const u32x4*)(kc + (int64_t)j * DQK + 32 * c + 8 * gq);
+                kr[kb * (DQK / 32) + c] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + 64 * c,
+                                                                 (t0 + kb * 16) * (DQK * 2), 0));
         }
+        // (V row e/16 of the tile, chunk e%16, e = lane + 64 it: 4 rows per instruction)
 #pragma unroll
-        for (int it = 0; it < VREG; ++it) {
-            const int e = lane + 64 * it;
-            const int j = min(t0 + e / (DV / 8), limit - 1);
-            vr[it] = *(const u32x4*)(vc + (int64_t)j * DV + (e % (DV / 8)) * 8);
-        }
+        for (int it = 0; it < VREG; ++it)
+            vr[it] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           vrs, v_lane + (it & 3) * 4 * (DV * 2),
+                           t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2), 0));
     };
     // ---- every load that does not depend on the position goes out first, unconditionally (a
     //      load under a branch would be waited for at the branch's end): this lane's query chunks
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     int t0 = k_begin + wave * TILE;
     // every ring slot is in bounds; a linear cache's splits past the position would only waste
     // bandwidth, so those wait for it
-    if (SWA) fetch(kA, vA, t0, a.cap);
+    if (SWA) fetch(kA, vA, t0);
     // The position comes by a scalar load, counted apart from the vector loads (lgkmcnt, not
     // vmcnt): the work that needs only the position and the query (cos/sin table, query and
     // new-token rotation) runs while the slot tile is still in flight.  The load waits for its
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     if (k_begin >= n_valid) return;
     const int k_end = min(n_valid, k_begin + a.chunk);
     const bool own_new = slot_new >= k_begin && slot_new < k_end;
-    if (!SWA) fetch(kA, vA, t0, k_end);
+    if (!SWA) fetch(kA, vA, t0);
 
     // ---- cos/sin of the position per frequency, once per workgroup
     if (tid < half) {
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 acc = mfma16x16x32(as_bf16x8(kr[kb * (DQK / 32) + c]), Qb[c], acc);
             Sacc[kb] = acc;
         }
-        if (t + stride < k_end) fetch(kr, vr, t + stride, k_end);
+        if (t + stride < k_end) fetch(kr, vr, t + stride);
 
         float mx = -INFINITY;
 #pragma unroll

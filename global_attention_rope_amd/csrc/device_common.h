@@ -54,6 +54,9 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
+constexpr int kBufferFormat = 0x00020000;
+
 // 32-bit load of a workgroup-uniform address through the scalar cache, waited for in the same
 // statement (its counter is the scalar one, so vector loads issued before it stay in flight).
 // The memory clobber also keeps every earlier load ahead of it.

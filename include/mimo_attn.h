@@ -123,6 +123,8 @@ size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_l
  *           slot positions[b] % window and the min(window, positions[b] + 1) most recent
  *           positions are attended.
  *   The new key is rotated at positions[b] before it is stored and used.
+ *   bf16: one cache slice [cache_capacity, dqk] must stay below 4 GiB (cache_capacity <=
+ *   11184810), else MIMO_ERR_UNSUPPORTED.
  *   workspace: at least mimo_attn_decode_workspace_size() bytes, for split-K partial results.
  */
 int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,

@@ -151,3 +151,6 @@ def test_decode_argument_errors_return_before_any_launch():
     assert _decode(_ga(batch=64), maxp=32768, cap=40000) == mimo.MIMO_ERR_WORKSPACE
     assert _decode(_ga(num_q_heads=68, num_kv_heads=2), cap=40) == mimo.MIMO_ERR_UNSUPPORTED
     assert _decode(_swa(batch=0), q=None) == mimo.MIMO_OK
+    # a bf16 cache slice is addressed with a 32-bit byte bound
+    assert _decode(_ga(), maxp=10, cap=12_000_000) == mimo.MIMO_ERR_UNSUPPORTED
+    assert "4 GiB" in mimo.last_error()
