@@ -22,7 +22,8 @@ captured once before timing); --eager-decode launches them from Python instead.
 Single-layer workloads for profiling (not the bench line): --workload swa_prefill (batch 1, 4096
 tokens, sliding), ga_prefill (batch 1, 8192 tokens, global), decode (batch 64, cached lengths
 uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one), copy
-(a 2 GiB device-to-device copy: the known-size reference for HBM byte counters).
+(a 2 GiB device-to-device copy: the known-size reference for HBM byte counters and the
+achievable HBM rate), gemm (8192^3 bf16 matrix product: the achievable matrix-core rate).
 """
 from __future__ import annotations
 
@@ -148,7 +149,7 @@ def main():
     ap.add_argument("--eager-decode", action="store_true",
                     help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
-                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "copy"])
+                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "copy", "gemm"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -362,7 +363,15 @@ def single_layer(args, dev):
         return e0.elapsed_time(e1) / n
 
     res = {"workload": args.workload, "steps": args.steps}
-    if args.workload == "copy":
+    if args.workload == "gemm":
+        # achievable dense bf16 matrix-core rate on this part (hipBLASLt through torch), the
+        # practical ceiling next to the nominal peak
+        n = 8192
+        x = torch.randn((n, n), device=dev).to(torch.bfloat16)
+        y = torch.randn((n, n), device=dev).to(torch.bfloat16)
+        ms = timed(lambda: torch.mm(x, y), args.steps)
+        res.update(ms=ms, tflops=2 * n ** 3 / ms / 1e9)
+    elif args.workload == "copy":
         nbytes = 2 << 30
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -8,6 +8,7 @@ from .oracle import (  # noqa: F401
     OracleParams,
     build,
     decode,
+    extend,
     num_threads,
     omega,
     prefill,

@@ -342,3 +342,107 @@ int oracle_decode(const oracle_params* p, const float* q, const float* k_new, co
     }
     return bad ? ORACLE_EINVAL : ORACLE_OK;
 }
+
+/*
+ * Extend (chunked prefill): S new tokens per sequence against previously cached keys.
+ *   The cache is the position -> (rotated key, value) map of oracle_decode: kc [B,Hkv,L,dqk],
+ *   vc [B,Hkv,L,dv], kpos [B,L], count [B].
+ *   q [B,S,Hq,dqk], k [B,S,Hkv,dqk] (raw, not rotated), v [B,S,Hkv,dv]; start [B]: new token i
+ *   of sequence b sits at position start[b] + i, and its key is rotated there.
+ *   Visible to new token i: the cached entries at positions before start[b] that the mask
+ *   admits (entries at positions >= start[b] are ignored), and the new tokens j <= i that the
+ *   mask admits.  Same definition as prefill, with the cached entries as extra keys.
+ *   out [B,S,Hq,dv]; k_rot_out [B,S,Hkv,dqk] optional (rotated new keys); rows/nrows: optional
+ *   subset of query indices (others untouched).
+ */
+int oracle_extend(const oracle_params* p, int32_t S, const float* q, const float* k,
+                  const float* v, const int32_t* start, const float* kc, const float* vc,
+                  const int32_t* kpos, const int32_t* count, int32_t L, const float* sinks,
+                  double* out, const int32_t* rows, int32_t nrows, double* k_rot_out) {
+    if (check_params(p) != ORACLE_OK || S < 0 || !q || !k || !v || !start || !out || L < 0)
+        return ORACLE_EINVAL;
+    if (L > 0 && (!kc || !vc || !kpos || !count)) return ORACLE_EINVAL;
+    const int32_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+    const int32_t dqk = p->qk_head_dim, dv = p->v_head_dim, r = p->rope_dims;
+    const int32_t group = Hq / Hkv;
+    const int32_t nr = rows ? nrows : S;
+    if (rows)
+        for (int32_t t = 0; t < nrows; ++t)
+            if (rows[t] < 0 || rows[t] >= S) return ORACLE_EINVAL;
+    for (int32_t b = 0; b < B; ++b)
+        if (start[b] < 0 || (L > 0 && (count[b] < 0 || count[b] > L))) return ORACLE_EINVAL;
+    const double tau = score_scale(p);
+    double omega[4096];
+    if (r / 2 > 4096) return ORACLE_EINVAL;
+    oracle_rope_omega(r, p->rope_theta, omega);
+
+    /* rotate every new key once at its own position; widen the new values */
+    const int64_t nk = (int64_t)B * S * Hkv;
+    double* kr = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1) * dqk);
+    double* vd = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1) * dv);
+    if (!kr || !vd) { free(kr); free(vd); return ORACLE_EINVAL; }
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < nk; ++t) {
+        const int64_t b = t / ((int64_t)S * Hkv), s = (t / Hkv) % S;
+        double tmp[4096];
+        for (int32_t d = 0; d < dqk; ++d) tmp[d] = (double)k[t * dqk + d];
+        rotate_row(tmp, kr + t * dqk, dqk, r, omega, (double)(start[b] + s));
+        for (int32_t e = 0; e < dv; ++e) vd[t * dv + e] = (double)v[t * dv + e];
+    }
+    if (k_rot_out) memcpy(k_rot_out, kr, sizeof(double) * (size_t)nk * dqk);
+
+    const int64_t work = (int64_t)B * Hq * nr;
+    int bad = 0;
+    #pragma omp parallel
+    {
+        const int64_t cap = (int64_t)L + S + 1;
+        double* z = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* crow = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * dv);
+        const double** vals = (const double**)malloc(sizeof(double*) * (size_t)cap);
+        double qraw[4096], qrot[4096], kj[4096];
+        if (!z || !crow || !vals) {
+            #pragma omp atomic write
+            bad = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 4)
+            for (int64_t w = 0; w < work; ++w) {
+                const int32_t b = (int32_t)(w / ((int64_t)Hq * nr));
+                const int32_t h = (int32_t)((w / nr) % Hq);
+                const int32_t i = rows ? rows[w % nr] : (int32_t)(w % nr);
+                const int32_t g = h / group;
+                const int64_t pq = (int64_t)start[b] + i;
+                for (int32_t d = 0; d < dqk; ++d)
+                    qraw[d] = (double)q[(((int64_t)b * S + i) * Hq + h) * dqk + d];
+                rotate_row(qraw, qrot, dqk, r, omega, (double)pq);
+                int64_t n = 0;
+                const int32_t cnt = L > 0 ? count[b] : 0;
+                for (int32_t j = 0; j < cnt; ++j) {   /* cached keys */
+                    const int64_t pk = kpos[(int64_t)b * L + j];
+                    if (pk >= start[b] || !visible(p, pq, pk)) continue;
+                    const int64_t off = ((int64_t)b * Hkv + g) * L + j;
+                    for (int32_t d = 0; d < dqk; ++d) kj[d] = (double)kc[off * dqk + d];
+                    z[n] = tau * dot(qrot, kj, dqk);
+                    for (int32_t e = 0; e < dv; ++e) crow[n * dv + e] = (double)vc[off * dv + e];
+                    vals[n] = crow + n * dv;
+                    ++n;
+                }
+                for (int32_t j = 0; j <= i; ++j) {    /* new keys */
+                    if (!visible(p, pq, (int64_t)start[b] + j)) continue;
+                    const int64_t kv = ((int64_t)b * S + j) * Hkv + g;
+                    z[n] = tau * dot(qrot, kr + kv * dqk, dqk);
+                    vals[n] = vd + kv * dv;
+                    ++n;
+                }
+                const double sink = sinks ? (double)sinks[h] : -INFINITY;
+                attend_row(z, vals, n, dv, sink, p->v_scale,
+                           out + (((int64_t)b * S + i) * Hq + h) * dv);
+            }
+        }
+        free(z);
+        free(crow);
+        free(vals);
+    }
+    free(kr);
+    free(vd);
+    return bad ? ORACLE_EINVAL : ORACLE_OK;
+}

@@ -80,10 +80,13 @@ def _load():
                                           ctypes.c_int32, ctypes.c_int32, f64]
             lib.oracle_decode.argtypes = [P(_CParams), f32, f32, f32, i32, f32, f32, i32, i32,
                                           ctypes.c_int32, f32, f64, f64, i32, ctypes.c_int32]
+            lib.oracle_extend.argtypes = [P(_CParams), ctypes.c_int32, f32, f32, f32, i32, f32,
+                                          f32, i32, i32, ctypes.c_int32, f32, f64, i32,
+                                          ctypes.c_int32, f64]
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             for fn in ("oracle_rope_omega", "oracle_rope_rotate", "oracle_prefill",
-                       "oracle_scores", "oracle_decode"):
+                       "oracle_scores", "oracle_decode", "oracle_extend"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -201,4 +204,42 @@ def decode(p: OracleParams, q, k_new, v_new, pos, kc=None, vc=None, kpos=None, c
         _ptr(vc_a, ctypes.c_float), _ptr(kpos_a, ctypes.c_int32), _ptr(cnt_a, ctypes.c_int32), L,
         _ptr(sinks, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(krot, ctypes.c_double),
         _ptr(br, ctypes.c_int32), 0 if br is None else len(br)), "decode")
+    return (out, krot) if want_k_rot else out
+
+
+def extend(p: OracleParams, q, k, v, start, kc=None, vc=None, kpos=None, count=None, sinks=None,
+           rows=None, want_k_rot=False):
+    """Chunked prefill: S new tokens per sequence (positions start[b] + i) against a
+    position->(rotated key, value) map of earlier tokens.
+
+    q [B,S,Hq,dqk], k [B,S,Hkv,dqk] (raw), v [B,S,Hkv,dv], start [B];
+    kc [B,Hkv,L,dqk] rotated keys, vc [B,Hkv,L,dv], kpos [B,L], count [B] (or None for L=0).
+    Returns out [B,S,Hq,dv] (rows not listed are NaN), plus the rotated new keys [B,S,Hkv,dqk]
+    when want_k_rot."""
+    q, k, v, sinks = _f32(q), _f32(k), _f32(v), _f32(sinks)
+    st = _i32(start)
+    B, S = q.shape[0], q.shape[1]
+    assert st.shape == (B,)
+    assert q.shape == (B, S, p.num_q_heads, p.qk_head_dim), q.shape
+    assert k.shape == (B, S, p.num_kv_heads, p.qk_head_dim), k.shape
+    assert v.shape == (B, S, p.num_kv_heads, p.v_head_dim), v.shape
+    if kc is None:
+        L = 0
+        kc_a = vc_a = kpos_a = cnt_a = None
+    else:
+        kc_a, vc_a, kpos_a, cnt_a = _f32(kc), _f32(vc), _i32(kpos), _i32(count)
+        L = kc_a.shape[2]
+        assert kc_a.shape == (B, p.num_kv_heads, L, p.qk_head_dim)
+        assert vc_a.shape == (B, p.num_kv_heads, L, p.v_head_dim)
+        assert kpos_a.shape == (B, L) and cnt_a.shape == (B,)
+    out = np.full((B, S, p.num_q_heads, p.v_head_dim), np.nan, dtype=np.float64)
+    rows_a = _i32(rows)
+    krot = np.empty(k.shape, dtype=np.float64) if want_k_rot else None
+    cp = p.c()
+    _check(_load().oracle_extend(
+        ctypes.byref(cp), S, _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+        _ptr(v, ctypes.c_float), _ptr(st, ctypes.c_int32), _ptr(kc_a, ctypes.c_float),
+        _ptr(vc_a, ctypes.c_float), _ptr(kpos_a, ctypes.c_int32), _ptr(cnt_a, ctypes.c_int32), L,
+        _ptr(sinks, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(rows_a, ctypes.c_int32),
+        0 if rows_a is None else len(rows_a), _ptr(krot, ctypes.c_double)), "extend")
     return (out, krot) if want_k_rot else out

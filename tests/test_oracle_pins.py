@@ -355,6 +355,71 @@ def test_decode_with_empty_cache_returns_scaled_new_value():
     np.testing.assert_array_equal(krot, ref)
 
 
+# ----------------------------------------------------------------------------- extend
+
+
+def _cache_of(krot, v, upto, starts):
+    """position -> (rotated key, value) map of the first `upto` tokens of each sequence."""
+    kc = np.ascontiguousarray(krot[:, :upto].transpose(0, 2, 1, 3)).astype(np.float32)
+    vc = np.ascontiguousarray(_np(v[:, :upto]).transpose(0, 2, 1, 3))
+    kpos = np.stack([np.arange(upto, dtype=np.int32) + s0 for s0 in starts])
+    return kc, vc, kpos, np.full(len(starts), upto, np.int32)
+
+
+@pytest.mark.parametrize("kind,W", [(0, 0), (1, 5), (1, 40)])
+@pytest.mark.parametrize("split", [1, 4, 11])
+def test_extend_equals_the_unsplit_prefill(kind, W, split):
+    """Prefill the first `split` tokens, extend with the rest: the rows of the extension equal
+    those rows of one prefill over the whole sequence (the prefill itself is pinned by SDPA)."""
+    w = _small(kind=kind, W=W)
+    T = w.seq
+    starts = [0, 5]
+    q, k, v, s = synth.layer_inputs(w, seed=131, seq=T)
+    pos = _positions(w.batch, T, starts)
+    P = _params(w)
+    full, krot = oracle.prefill(P, _np(q), _np(k), _np(v), pos, _np(s), want_k_rot=True)
+    kc, vc, kpos, cnt = _cache_of(krot, v, split, starts)
+    ext, krot_new = oracle.extend(P, _np(q[:, split:]), _np(k[:, split:]), _np(v[:, split:]),
+                                  np.array(starts) + split, kc, vc, kpos, cnt, _np(s),
+                                  want_k_rot=True)
+    # float32 cache of fp64 rotated keys: equal within the float rounding of the cached keys
+    np.testing.assert_allclose(ext, full[:, split:], rtol=0, atol=1e-5)
+    np.testing.assert_array_equal(krot_new, krot[:, split:])
+    if kind == 1:
+        # a ring keeps only the last W positions, in any slot order: same answer
+        keep = min(W, split)
+        order = np.random.default_rng(5).permutation(keep)
+        sl = slice(split - keep, split)
+        ext_r = oracle.extend(P, _np(q[:, split:]), _np(k[:, split:]), _np(v[:, split:]),
+                              np.array(starts) + split,
+                              np.ascontiguousarray(kc[:, :, sl][:, :, order]),
+                              np.ascontiguousarray(vc[:, :, sl][:, :, order]),
+                              np.ascontiguousarray(kpos[:, sl][:, order]),
+                              np.full(w.batch, keep, np.int32), _np(s))
+        np.testing.assert_allclose(ext_r, ext, rtol=0, atol=1e-13)
+
+
+def test_extend_with_empty_cache_is_prefill_and_one_token_is_decode():
+    w = _small(kind=1, W=5)
+    q, k, v, s = synth.layer_inputs(w, seed=141)
+    starts = np.array([3, 9], np.int32)
+    P = _params(w)
+    pf = oracle.prefill(P, _np(q), _np(k), _np(v), _positions(w.batch, w.seq, starts), _np(s))
+    ex = oracle.extend(P, _np(q), _np(k), _np(v), starts, sinks=_np(s))
+    np.testing.assert_array_equal(ex, pf)
+    # one new token against a cache: the decode definition
+    kc = np.random.default_rng(7).standard_normal((w.batch, w.num_kv_heads, 6, w.qk_head_dim))
+    vc = np.random.default_rng(8).standard_normal((w.batch, w.num_kv_heads, 6, w.v_head_dim))
+    kpos = np.stack([np.arange(6, dtype=np.int32) + 4, np.arange(6, dtype=np.int32) + 1])
+    cnt = np.array([6, 6], np.int32)
+    st = np.array([10, 7], np.int32)
+    ex1 = oracle.extend(P, _np(q[:, :1]), _np(k[:, :1]), _np(v[:, :1]), st, kc, vc, kpos, cnt,
+                        _np(s))
+    dec = oracle.decode(P, _np(q[:, 0]), _np(k[:, 0]), _np(v[:, 0]), st, kc, vc, kpos, cnt,
+                        _np(s))
+    np.testing.assert_allclose(ex1[:, 0], dec, rtol=0, atol=1e-13)
+
+
 def test_oracle_rejects_invalid_arguments():
     w = _small()
     q, k, v, s = synth.layer_inputs(w, seed=1)
