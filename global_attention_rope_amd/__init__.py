@@ -20,6 +20,8 @@ from .binding import (  # noqa: F401
     check_params,
     decode,
     decode_workspace_size,
+    extend,
+    extend_workspace_size,
     last_error,
     lib,
     prefill,

@@ -20,7 +20,8 @@ MIMO_OK, MIMO_ERR_INVALID_ARG, MIMO_ERR_UNSUPPORTED, MIMO_ERR_WORKSPACE, MIMO_ER
 LAYER_GLOBAL, LAYER_SWA = 0, 1
 F32, BF16 = 0, 1
 
-EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_decode",
+EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_extend",
+           "mimo_attn_extend_workspace_size", "mimo_attn_decode",
            "mimo_attn_decode_workspace_size", "mimo_attn_check_params", "mimo_attn_last_error",
            "mimo_attn_abi_version")
 
@@ -84,6 +85,11 @@ def lib(path: str = LIB_PATH):
             L.mimo_attn_prefill.restype = ctypes.c_int
             L.mimo_attn_prefill_workspace_size.argtypes = [P, i32]
             L.mimo_attn_prefill_workspace_size.restype = sz
+            L.mimo_attn_extend.argtypes = [P, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, sz,
+                                           vp]
+            L.mimo_attn_extend.restype = ctypes.c_int
+            L.mimo_attn_extend_workspace_size.argtypes = [P, i32]
+            L.mimo_attn_extend_workspace_size.restype = sz
             L.mimo_attn_decode.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
             L.mimo_attn_decode.restype = ctypes.c_int
             L.mimo_attn_decode_workspace_size.argtypes = [P, i32]
@@ -115,6 +121,11 @@ def check_params(p: Params) -> int:
 def prefill_workspace_size(p: Params, seq_len: int) -> int:
     cp = p.c()
     return int(lib().mimo_attn_prefill_workspace_size(ctypes.byref(cp), seq_len))
+
+
+def extend_workspace_size(p: Params, seq_len: int) -> int:
+    cp = p.c()
+    return int(lib().mimo_attn_extend_workspace_size(ctypes.byref(cp), seq_len))
 
 
 def decode_workspace_size(p: Params, max_position: int) -> int:
@@ -179,6 +190,42 @@ def prefill(p: Params, q, k, v, start_pos, sinks=None, out=None, k_cache=None, v
     _raise(lib().mimo_attn_prefill(ctypes.byref(cp), S, _ptr(q), _ptr(k), _ptr(v), _ptr(start_pos),
                                    _ptr(sinks), _ptr(out), _ptr(k_cache), _ptr(v_cache), cap,
                                    _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def extend(p: Params, q, k, v, start_pos, max_start: int, k_cache, v_cache, sinks=None, out=None,
+           workspace=None, stream=None):
+    """mimo_attn_extend on torch device tensors: S new tokens per sequence against the cache,
+    which holds each sequence's positions before start_pos[b] and receives the new tokens.
+
+    start_pos: int32 [B] device tensor; max_start: host bound of every start_pos[b].
+    Returns out [B,S,Hq,dv]."""
+    B, S = q.shape[0], q.shape[1]
+    dev, dt = q.device, _tdtype(p)
+    if p.batch != B:
+        raise ValueError(f"params.batch {p.batch} != q.shape[0] {B}")
+    _expect(q, "q", (B, S, p.num_q_heads, p.qk_head_dim), dt, dev)
+    _expect(k, "k", (B, S, p.num_kv_heads, p.qk_head_dim), dt, dev)
+    _expect(v, "v", (B, S, p.num_kv_heads, p.v_head_dim), dt, dev)
+    _expect(start_pos, "start_pos", (B,), torch.int32, dev)
+    if sinks is not None:
+        _expect(sinks, "sinks", (p.num_q_heads,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, S, p.num_q_heads, p.v_head_dim), dtype=dt, device=dev)
+    _expect(out, "out", (B, S, p.num_q_heads, p.v_head_dim), dt, dev)
+    if k_cache is None or v_cache is None:
+        raise ValueError("extend needs k_cache and v_cache")
+    cap = k_cache.shape[2]
+    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), dt, dev)
+    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), dt, dev)
+    need = extend_workspace_size(p, S)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cp = p.c()
+    _raise(lib().mimo_attn_extend(ctypes.byref(cp), S, _ptr(q), _ptr(k), _ptr(v), _ptr(start_pos),
+                                  max_start, _ptr(sinks), _ptr(out), _ptr(k_cache), _ptr(v_cache),
+                                  cap, _ptr(workspace), wbytes, _stream(stream)))
     return out
 
 

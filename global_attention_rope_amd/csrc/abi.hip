@@ -104,6 +104,14 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
     return (size_t)p->batch * p->num_kv_heads * (size_t)S * p->qk_head_dim * 2;
 }
 
+// bf16 extend of a sliding layer lays out [B, Hkv, window + S] rotated K and V rows: the ring's
+// content in position order, then the new tokens.  Global layers attend straight from the cache.
+size_t extend_ws(const mimo_attn_params* p, int32_t S) {
+    if (p->dtype != MIMO_BF16 || p->layer_kind != MIMO_LAYER_SWA) return 0;
+    return (size_t)p->batch * p->num_kv_heads * ((size_t)p->window + S) *
+           (p->qk_head_dim + p->v_head_dim) * 2;
+}
+
 // Decode split size: slots per workgroup.
 //  * a sliding ring of at most 1024 slots is one split;
 //  * a small grid (at most two rounds of 256-slot splits on the chip, which holds 512 resident
@@ -167,6 +175,11 @@ size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_l
     return prefill_ws(p, seq_len);
 }
 
+size_t mimo_attn_extend_workspace_size(const mimo_attn_params* p, int32_t seq_len) {
+    if (check(p) != MIMO_OK || seq_len < 0) return 0;
+    return extend_ws(p, seq_len);
+}
+
 size_t mimo_attn_decode_workspace_size(const mimo_attn_params* p, int32_t max_position) {
     if (check(p) != MIMO_OK || max_position < 0) return 0;
     return decode_ws(p, max_position);
@@ -213,6 +226,8 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     ra.rope_dims = p->rope_dims;
     ra.cap = cache_capacity;
     ra.ring_window = swa ? p->window : 0;
+    ra.ws_rows = seq_len;
+    ra.max_start = -1;
     // the ring only keeps the last `window` tokens
     ra.cache_i0 = (swa && seq_len > p->window) ? seq_len - p->window : 0;
     if (has_cache) {
@@ -263,6 +278,11 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     pa.window = p->window;
     pa.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
     pa.v_scale = p->v_scale;
+    pa.v_sb = (int64_t)seq_len * p->num_kv_heads * p->v_head_dim;   // v [B,S,Hkv,dv]
+    pa.v_sh = p->v_head_dim;
+    pa.v_sj = (int64_t)p->num_kv_heads * p->v_head_dim;
+    pa.kpos_rel = 1;   // key row j is token j
+    pa.max_start = -1;
     fill_omega(p, pa.omega_rev);
     // rotate K once into the workspace (and store the cache), then attend
     ra.k_ws = workspace;
@@ -274,6 +294,129 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     pa.k_sh = (int64_t)seq_len * dqk;
     pa.k_sj = dqk;
     return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "prefill (bf16)");
+}
+
+int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, const void* k,
+                     const void* v, const int32_t* start_pos, int32_t max_start,
+                     const float* sinks, void* out, void* k_cache, void* v_cache,
+                     int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    int rc = check(p);
+    if (rc != MIMO_OK) return rc;
+    if (seq_len < 0) return fail(MIMO_ERR_INVALID_ARG, "seq_len %d < 0", seq_len);
+    if (max_start < 0) return fail(MIMO_ERR_INVALID_ARG, "max_start %d < 0", max_start);
+    if ((int64_t)max_start + seq_len > 0x7fffffffLL)
+        return fail(MIMO_ERR_INVALID_ARG, "max_start %d + seq_len %d overflows int32 positions",
+                    max_start, seq_len);
+    if (p->dtype != MIMO_BF16)
+        return fail(MIMO_ERR_UNSUPPORTED, "extend is compiled for bf16 layers only");
+    const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    if (swa && cache_capacity != p->window)
+        return fail(MIMO_ERR_INVALID_ARG, "ring cache capacity %d must equal window %d",
+                    cache_capacity, p->window);
+    if (!swa && (int64_t)max_start + seq_len > (int64_t)cache_capacity)
+        return fail(MIMO_ERR_INVALID_ARG,
+                    "linear cache capacity %d must hold max_start %d + seq_len %d positions",
+                    cache_capacity, max_start, seq_len);
+    if (p->batch == 0 || seq_len == 0) return ok();
+    if (!q || !k || !v || !start_pos || !out || !k_cache || !v_cache)
+        return fail(MIMO_ERR_INVALID_ARG,
+                    "q, k, v, start_pos, out, k_cache and v_cache must be non-NULL");
+    if ((int64_t)seq_len * p->num_q_heads * p->batch > ((int64_t)1 << 40))
+        return fail(MIMO_ERR_INVALID_ARG, "problem too large");
+    const size_t need = extend_ws(p, seq_len);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t Hkv = p->num_kv_heads, dqk = p->qk_head_dim, dv = p->v_head_dim;
+
+    mimo::RopeKVArgs ra;
+    memset(&ra, 0, sizeof ra);
+    ra.k = k;
+    ra.v = v;
+    ra.start_pos = start_pos;
+    ra.k_dst = k_cache;
+    ra.v_dst = v_cache;
+    ra.B = p->batch;
+    ra.S = seq_len;
+    ra.Hkv = p->num_kv_heads;
+    ra.dqk = p->qk_head_dim;
+    ra.dv = p->v_head_dim;
+    ra.rope_dims = p->rope_dims;
+    ra.cap = cache_capacity;
+    ra.ring_window = swa ? p->window : 0;
+    ra.max_start = max_start;
+    fill_omega(p, ra.omega_rev);
+
+    mimo::PrefillArgs pa;
+    memset(&pa, 0, sizeof pa);
+    pa.q = (const uint16_t*)q;
+    pa.start_pos = start_pos;
+    pa.sinks = sinks;
+    pa.out = (uint16_t*)out;
+    pa.max_start = max_start;
+    pa.B = p->batch;
+    pa.S = seq_len;
+    pa.Hq = p->num_q_heads;
+    pa.Hkv = p->num_kv_heads;
+    pa.rope_dims = p->rope_dims;
+    pa.window = p->window;
+    pa.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
+    pa.v_scale = p->v_scale;
+    fill_omega(p, pa.omega_rev);
+
+    if (swa) {
+        // workspace rows r < W: the ring's positions start - W + r (in position order); rows
+        // W + i: the new tokens, rotated.  The ring itself is refreshed only after it is read.
+        const int64_t rows = (int64_t)p->window + seq_len;
+        uint16_t* kws = (uint16_t*)workspace;
+        uint16_t* vws = kws + (int64_t)p->batch * Hkv * rows * dqk;
+        mimo::RingUnrollArgs ua;
+        memset(&ua, 0, sizeof ua);
+        ua.k_cache = (const uint16_t*)k_cache;
+        ua.v_cache = (const uint16_t*)v_cache;
+        ua.start_pos = start_pos;
+        ua.k_ws = kws;
+        ua.v_ws = vws;
+        ua.B = p->batch;
+        ua.Hkv = p->num_kv_heads;
+        ua.dqk = p->qk_head_dim;
+        ua.dv = p->v_head_dim;
+        ua.W = p->window;
+        ua.ws_rows = (int32_t)rows;
+        ua.max_start = max_start;
+        rc = hip_status(mimo::launch_ring_unroll_bf16(ua, st), "ring unroll (bf16)");
+        if (rc != MIMO_OK) return rc;
+        ra.k_ws = kws;
+        ra.v_ws = vws;
+        ra.ws_rows = (int32_t)rows;
+        ra.ws_row0 = p->window;
+        ra.cache_i0 = seq_len > p->window ? seq_len - p->window : 0;
+        pa.k = kws;
+        pa.v = vws;
+        pa.k_sb = Hkv * rows * dqk;
+        pa.k_sh = rows * dqk;
+        pa.v_sb = Hkv * rows * dv;
+        pa.v_sh = rows * dv;
+        pa.kpos_rel = 1;
+        pa.kpos_off = -p->window;   // key row j sits at position start - W + j
+    } else {
+        // new tokens go to the linear cache first; key row j of the cache is position j
+        pa.k = (const uint16_t*)k_cache;
+        pa.v = (const uint16_t*)v_cache;
+        pa.k_sb = Hkv * cache_capacity * dqk;
+        pa.k_sh = (int64_t)cache_capacity * dqk;
+        pa.v_sb = Hkv * cache_capacity * dv;
+        pa.v_sh = (int64_t)cache_capacity * dv;
+        pa.kpos_rel = 0;
+        pa.kpos_off = 0;
+    }
+    pa.k_sj = dqk;
+    pa.v_sj = dv;
+    rc = hip_status(mimo::launch_rope_kv_bf16(ra, st), "key rotation (bf16)");
+    if (rc != MIMO_OK) return rc;
+    return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "extend (bf16)");
 }
 
 int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,

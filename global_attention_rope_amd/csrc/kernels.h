@@ -9,23 +9,44 @@ constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value, in re
 
 // Rotate K (first rope_dims dims) once per token i in [i0, S) of each sequence b (position
 // start_pos[b] + i) and store it
-//   * into k_ws [B,Hkv,S,dqk] at row i, when k_ws is set (rotated-K scratch of a prefill);
+//   * into k_ws [B,Hkv,ws_rows,dqk] at row ws_row0 + i, when k_ws is set (rotated-K scratch of a
+//     prefill), and V likewise into v_ws [B,Hkv,ws_rows,dv] when v_ws is set;
 //   * with V into the cache k_dst [B,Hkv,cap,dqk] / v_dst [B,Hkv,cap,dv], when k_dst is set and
 //     i >= cache_i0, at slot position % ring_window (ring_window > 0) or slot position (linear; a
 //     token whose slot falls outside [0, cap) is not stored).
+// With max_start >= 0, sequences whose start_pos lies outside [0, max_start] are skipped.
 struct RopeKVArgs {
     const void* k;       // [B,S,Hkv,dqk]
     const void* v;       // [B,S,Hkv,dv]
     const int32_t* start_pos;
-    void* k_ws;          // [B,Hkv,S,dqk] or null
+    void* k_ws;          // [B,Hkv,ws_rows,dqk] or null
+    void* v_ws;          // [B,Hkv,ws_rows,dv] or null
     void* k_dst;         // [B,Hkv,cap,dqk] or null
     void* v_dst;         // [B,Hkv,cap,dv], set iff k_dst is
     int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, cache_i0, ring_window;
+    int32_t ws_rows, ws_row0, max_start;
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
-// bf16 prefill.  Rotated K rows are read from k + b*k_sb + g*k_sh + j*k_sj (element strides, rows
-// contiguous: k_sj == 192); V rows come from the input v [B,S,Hkv,128].
+// Copy the ring cache's W most recent positions before start_pos[b] into workspace rows in
+// position order: row r of [B,Hkv,ws_rows,d] holds position start_pos[b] - W + r (slot
+// position % W); rows of negative positions are left as they are.  With max_start >= 0,
+// sequences whose start_pos lies outside [0, max_start] are skipped.
+struct RingUnrollArgs {
+    const uint16_t* k_cache;   // [B,Hkv,W,dqk]
+    const uint16_t* v_cache;   // [B,Hkv,W,dv]
+    const int32_t* start_pos;
+    uint16_t* k_ws;            // [B,Hkv,ws_rows,dqk]
+    uint16_t* v_ws;            // [B,Hkv,ws_rows,dv]
+    int32_t B, Hkv, dqk, dv, W, ws_rows, max_start;
+};
+
+// bf16 prefill.  Query row i of sequence b sits at position start_pos[b] + i.  Key row j (rotated
+// K at k + b*k_sb + g*k_sh + j*k_sj, V at v + b*v_sb + g*v_sh + j*v_sj; element strides, rows
+// contiguous: k_sj == 192) sits at position kpos0 = (kpos_rel ? start_pos[b] : 0) + kpos_off,
+// plus j; key rows run up to the last query's position, and rows of negative positions hold no
+// token.  With max_start >= 0, a sequence whose start_pos lies outside [0, max_start] gets a
+// zero output.
 struct PrefillArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -34,6 +55,8 @@ struct PrefillArgs {
     const float* sinks;
     uint16_t* out;
     int64_t k_sb, k_sh, k_sj;
+    int64_t v_sb, v_sh, v_sj;
+    int32_t kpos_rel, kpos_off, max_start;
     int32_t B, S, Hq, Hkv, rope_dims, window;
     float score_scale_log2;
     float v_scale;
@@ -87,6 +110,7 @@ struct F32DecodeArgs {
 };
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
+hipError_t launch_ring_unroll_bf16(const RingUnrollArgs& a, hipStream_t st);
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool window, bool sink, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);

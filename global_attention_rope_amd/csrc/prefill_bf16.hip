@@ -116,19 +116,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int32_t p0 = a.start_pos[b];
     const int r = a.rope_dims, half = r >> 1;
 
+    // Key rows: row j sits at position kpos0 + j.  Query row i (position p0 + i) thus meets key
+    // row i + shift at its own position; rows below jmin (negative positions) hold no token, and
+    // the last query row reaches key row nk - 1.  A sequence outside the accepted start range
+    // streams no tiles and gets a zero output.
+    const bool seq_ok = a.max_start < 0 || (unsigned)p0 <= (unsigned)a.max_start;
+    const int32_t kpos0 = (a.kpos_rel ? (seq_ok ? p0 : 0) : 0) + a.kpos_off;
+    const int shift = (seq_ok ? p0 : 0) - kpos0;
+    const int jmin = max(0, -kpos0);
+    const int nk = S + shift;
+
     const int W = a.window;
     const int q_first = qblk * BM + (GROUPED ? 0 : wave * QPW);   // this wave's first row (scalar)
     const int q_last = min(q_first + QPW, S) - 1;                 // its last valid row
     const int blk_first = qblk * BM;
     const int blk_last = min(blk_first + BM, S) - 1;
-    const int kt_lo = WINDOW ? max(0, blk_first - W + 1) / BN : 0;
-    const int n_tiles = blk_last / BN + 1 - kt_lo;
+    const int kt_lo = max(jmin, WINDOW ? blk_first + shift - W + 1 : 0) / BN;
+    const int n_tiles = seq_ok ? (blk_last + shift) / BN + 1 - kt_lo : 0;
 
     // ---- DMA source mapping: LDS 16-byte slot P of this wave's instruction i holds
     //      K row P / 24, logical chunk (P % 24) ^ swizzle; V row P / 16, chunk (P % 16) ^ swizzle.
     const uint16_t* kslice = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-    const uint16_t* vslice = a.v + ((int64_t)b * S * a.Hkv + kvh) * DV;
-    const int64_t v_sj = (int64_t)a.Hkv * DV;
+    const uint16_t* vslice = a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+    const int64_t v_sj = a.v_sj;
     int k_row[K_DMA], k_off[K_DMA], v_row[V_DMA], v_off[V_DMA];
 #pragma unroll
     for (int i = 0; i < K_DMA; ++i) {
@@ -144,8 +154,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         v_row[i] = row;
         v_off[i] = (phys ^ ((row & 3) << 2)) * 8;
     }
-    // per-lane source pointers of tile 0; tile t adds t * BN rows (a scalar offset) except on the
-    // ragged last tile, whose rows past S are clamped to row S - 1 (they are masked anyway)
+    // per-lane source pointers of tile 0; tile t adds t * BN rows (a scalar offset) except on a
+    // tile that reaches past the key rows [jmin, nk): its rows are clamped into that range (they
+    // are masked anyway, and clamping keeps unwritten rows out of the products)
     const uint16_t* kp[K_DMA];
     const uint16_t* vp[V_DMA];
 #pragma unroll
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int j0 = (kt_lo + t) * BN;
         const uint32_t kst = lds0 + ST * K_TILE;
         const uint32_t vst = lds0 + STAGES * K_TILE + ST * V_TILE;
-        if (j0 + BN <= S) {
+        if (j0 >= jmin && j0 + BN <= nk) {
             const int64_t dk = (int64_t)t * BN * DQK, dv = (int64_t)t * BN * v_sj;
 #pragma unroll
             for (int i = 0; i < K_DMA; ++i) dma16(kp[i] + dk, kst + (wave * K_DMA + i) * 1024);
@@ -167,17 +178,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         } else {
 #pragma unroll
             for (int i = 0; i < K_DMA; ++i) {
-                const int j = min(j0 + k_row[i], S - 1);
+                const int j = min(max(j0 + k_row[i], jmin), nk - 1);
                 dma16(kslice + (int64_t)j * DQK + k_off[i], kst + (wave * K_DMA + i) * 1024);
             }
 #pragma unroll
             for (int i = 0; i < V_DMA; ++i) {
-                const int j = min(j0 + v_row[i], S - 1);
+                const int j = min(max(j0 + v_row[i], jmin), nk - 1);
                 dma16(vslice + (int64_t)j * v_sj + v_off[i], vst + (wave * V_DMA + i) * 1024);
             }
         }
     };
-    issue(0, std::integral_constant<int, 0>{});
+    if (n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
     if (STAGES == 3 && n_tiles > 1) issue(1, std::integral_constant<int, 1 % STAGES>{});
 
     // ---- Q^T operands, rotated, in registers
@@ -269,14 +280,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int db = 0; db < DV / 32; ++db) O[db] = f32x16{};
     const float sc = a.score_scale_log2;
     const int q_l = q_first + l32;
+    // row q_l sees key row j iff q_l + shift - j lies in [0, lim): the window (sliding) and the
+    // first key row holding a token both bound it
+    const unsigned lim = (unsigned)max(0, min(WINDOW ? W : 0x7fffffff, q_l + shift - jmin + 1));
 
     auto compute = [&](int t, auto stage_c) {
         constexpr int ST = decltype(stage_c)::value;
         const int j0 = (kt_lo + t) * BN;
         // nothing visible for this wave (uniform branch)
-        if (q_first > q_last || j0 > q_last || (WINDOW && j0 + BN - 1 <= q_first - W)) return;
+        if (q_first > q_last || j0 > q_last + shift || (WINDOW && j0 + BN - 1 <= q_first + shift - W))
+            return;
         // every key visible to every row of the wave
-        const bool full = j0 + BN - 1 <= q_first && (!WINDOW || q_last - j0 < W);
+        const bool full = j0 >= jmin && j0 + BN - 1 <= q_first + shift &&
+                          (!WINDOW || q_last + shift - j0 < W);
         const uint8_t* kst = smem + ST * K_TILE;
         const uint8_t* vst = smem + ST * V_TILE;   // + v_rd, which holds the V area's base
 
@@ -293,10 +309,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             // (the empty asm keeps the compiler from if-converting this uniform branch, which
             //  would run the masking on every tile)
             asm volatile("");
-            // key j0 + 8(i/4) + 4g + i%4 (+32 in block 1) against row q_l: visible iff
-            // 0 <= q_l - j (< W), i.e. the unsigned difference d - off is below the limit
-            const int d = q_l - j0 - 4 * g;
-            const unsigned lim = WINDOW ? (unsigned)W : 0x80000000u;
+            // key j0 + 8(i/4) + 4g + i%4 (+32 in block 1) against row q_l: visible iff the
+            // unsigned difference d - off is below the row's limit
+            const int d = q_l + shift - j0 - 4 * g;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int off = 8 * (i >> 2) + (i & 3);

@@ -4,9 +4,11 @@
 // head dim is rotated; "add Xiaomi MiMo v2 (mimo_v2_flash)", "Architecture, verified against
 // upstream": rotated width int(partial_rotary_factor * head_dim), per-kind theta): pair
 // (d, d + r/2), d < r/2, is turned by position * theta^(-2d/r); dims >= r are copied.
-// Destinations: the rotated-K scratch of a global prefill (row = token index), the linear cache of
-// global layers (slot = position) and the rotating cache of sliding layers (slot = position %
-// window; "add Xiaomi MiMo v2 (mimo_v2_flash)", "Implementation plan").
+// Destinations: the rotated-K (and V) scratch of a prefill or an extend (row = a fixed offset +
+// token index), the linear cache of global layers (slot = position) and the rotating cache of
+// sliding layers (slot = position % window; "add Xiaomi MiMo v2 (mimo_v2_flash)", "Implementation
+// plan").  The ring unroll pass lays the ring's content out by position in front of an extend's
+// new tokens.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -20,9 +22,14 @@ __device__ __forceinline__ int cache_slot(const RopeKVArgs& a, int i, int32_t po
     return pos < a.cap ? pos : -1;
 }
 
+// Sequence b takes part (its start lies in the accepted range, when one is given).
+__device__ __forceinline__ bool start_ok(int32_t start, int32_t max_start) {
+    return max_start < 0 || (unsigned)start <= (unsigned)max_start;
+}
+
 // bf16: one thread per 8-element chunk of a K or V row.
 __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
-    const int kch = a.dqk / 8, vch = a.k_dst ? a.dv / 8 : 0, per_row = kch + vch;
+    const int kch = a.dqk / 8, vch = (a.k_dst || a.v_ws) ? a.dv / 8 : 0, per_row = kch + vch;
     const int ntok = a.S - a.i0;
     const int64_t total = (int64_t)a.B * ntok * a.Hkv * per_row;
     const int r = a.rope_dims, half = r >> 1;
@@ -33,9 +40,12 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
         const int g = (int)(rowid % a.Hkv);
         const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
         const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
-        const int32_t pos = a.start_pos[b] + i;
+        const int32_t start = a.start_pos[b];
+        if (!start_ok(start, a.max_start)) continue;
+        const int32_t pos = start + i;
         const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
+        const int64_t ws_row = ((int64_t)b * a.Hkv + g) * a.ws_rows + a.ws_row0 + i;
         if (c < kch) {
             const uint16_t* krow = (const uint16_t*)a.k + src_row * a.dqk;
             const int d0 = c * 8;
@@ -56,21 +66,22 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
                 }
                 w = pack8(x);
             }
-            if (a.k_ws)
-                *(u32x4*)((uint16_t*)a.k_ws + (((int64_t)b * a.Hkv + g) * a.S + i) * a.dqk + d0) = w;
+            if (a.k_ws) *(u32x4*)((uint16_t*)a.k_ws + ws_row * a.dqk + d0) = w;
             if (slot >= 0)
                 *(u32x4*)((uint16_t*)a.k_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dqk + d0) = w;
-        } else if (slot >= 0) {
+        } else if (slot >= 0 || a.v_ws) {
             const int d0 = (c - kch) * 8;
-            *(u32x4*)((uint16_t*)a.v_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d0) =
-                *(const u32x4*)((const uint16_t*)a.v + src_row * a.dv + d0);
+            const u32x4 w = *(const u32x4*)((const uint16_t*)a.v + src_row * a.dv + d0);
+            if (a.v_ws) *(u32x4*)((uint16_t*)a.v_ws + ws_row * a.dv + d0) = w;
+            if (slot >= 0)
+                *(u32x4*)((uint16_t*)a.v_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d0) = w;
         }
     }
 }
 
 // fp32: one thread per element.
 __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
-    const int per_row = a.dqk + (a.k_dst ? a.dv : 0);
+    const int per_row = a.dqk + ((a.k_dst || a.v_ws) ? a.dv : 0);
     const int ntok = a.S - a.i0;
     const int64_t total = (int64_t)a.B * ntok * a.Hkv * per_row;
     const int r = a.rope_dims, half = r >> 1;
@@ -81,9 +92,12 @@ __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
         const int g = (int)(rowid % a.Hkv);
         const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
         const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
-        const int32_t pos = a.start_pos[b] + i;
+        const int32_t start = a.start_pos[b];
+        if (!start_ok(start, a.max_start)) continue;
+        const int32_t pos = start + i;
         const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
+        const int64_t ws_row = ((int64_t)b * a.Hkv + g) * a.ws_rows + a.ws_row0 + i;
         if (c < a.dqk) {
             const float* krow = (const float*)a.k + src_row * a.dqk;
             float x = krow[c];
@@ -93,13 +107,40 @@ __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
                 rope_cos_sin_rev(pos, a.omega_rev[lower ? c : c - half], cs, sn);
                 x = lower ? (x * cs - krow[c + half] * sn) : (x * cs + krow[c - half] * sn);
             }
-            if (a.k_ws) ((float*)a.k_ws)[(((int64_t)b * a.Hkv + g) * a.S + i) * a.dqk + c] = x;
+            if (a.k_ws) ((float*)a.k_ws)[ws_row * a.dqk + c] = x;
             if (slot >= 0) ((float*)a.k_dst)[(((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dqk + c] = x;
-        } else if (slot >= 0) {
+        } else if (slot >= 0 || a.v_ws) {
             const int d = c - a.dqk;
-            ((float*)a.v_dst)[(((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d] =
-                ((const float*)a.v)[src_row * a.dv + d];
+            const float x = ((const float*)a.v)[src_row * a.dv + d];
+            if (a.v_ws) ((float*)a.v_ws)[ws_row * a.dv + d] = x;
+            if (slot >= 0) ((float*)a.v_dst)[(((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d] = x;
         }
+    }
+}
+
+// bf16 ring unroll: one thread per 16-byte chunk of a K or V row.
+__global__ __launch_bounds__(256) void ring_unroll_bf16_kernel(const RingUnrollArgs a) {
+    const int kch = a.dqk / 8, per_row = kch + a.dv / 8;
+    const int64_t total = (int64_t)a.B * a.Hkv * a.W * per_row;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(e % per_row);
+        const int64_t rowid = e / per_row;
+        const int r = (int)(rowid % a.W);
+        const int64_t bg = rowid / a.W;            // b * Hkv + g
+        const int b = (int)(bg / a.Hkv);
+        const int32_t start = a.start_pos[b];
+        if (!start_ok(start, a.max_start)) continue;
+        const int32_t pos = start - a.W + r;
+        if (pos < 0) continue;
+        const int64_t slot_row = bg * a.W + pos % a.W;
+        const int64_t ws_row = bg * a.ws_rows + r;
+        if (c < kch)
+            *(u32x4*)(a.k_ws + ws_row * a.dqk + 8 * c) =
+                *(const u32x4*)(a.k_cache + slot_row * a.dqk + 8 * c);
+        else
+            *(u32x4*)(a.v_ws + ws_row * a.dv + 8 * (c - kch)) =
+                *(const u32x4*)(a.v_cache + slot_row * a.dv + 8 * (c - kch));
     }
 }
 
@@ -113,16 +154,25 @@ unsigned grid_for(int64_t total) {
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st) {
     const int64_t total =
-        (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk / 8 + (a.k_dst ? a.dv / 8 : 0));
-    if (total <= 0 || (!a.k_ws && !a.k_dst)) return hipSuccess;
+        (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk / 8 + ((a.k_dst || a.v_ws) ? a.dv / 8 : 0));
+    if (total <= 0 || (!a.k_ws && !a.k_dst && !a.v_ws)) return hipSuccess;
     rope_kv_bf16_kernel<<<grid_for(total), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st) {
-    const int64_t total = (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk + (a.k_dst ? a.dv : 0));
-    if (total <= 0 || (!a.k_ws && !a.k_dst)) return hipSuccess;
+    const int64_t total =
+        (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk + ((a.k_dst || a.v_ws) ? a.dv : 0));
+    if (total <= 0 || (!a.k_ws && !a.k_dst && !a.v_ws)) return hipSuccess;
     rope_kv_f32_kernel<<<grid_for(total), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_unroll_bf16(const RingUnrollArgs& a, hipStream_t st) {
+    if (a.dqk % 8 || a.dv % 8) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)a.B * a.Hkv * a.W * (a.dqk / 8 + a.dv / 8);
+    if (total <= 0) return hipSuccess;
+    ring_unroll_bf16_kernel<<<grid_for(total), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

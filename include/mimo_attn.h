@@ -111,6 +111,41 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
 size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_len);
 
 /*
+ * Extend (chunked prefill): S new tokens per sequence against themselves and the tokens already
+ * in the cache, which it also appends to.  The same attention as prefill, with every earlier
+ * position of the sequence visible as well (subject to the window): splitting a prompt into
+ * chunks, each extending the cache the previous chunks left, gives the prompt's prefill result.
+ * (Layer as defined above; the caches are the ones prefill and decode keep, the rotating one of
+ * "add Xiaomi MiMo v2 (mimo_v2_flash)", "Implementation plan", with its sliding prefill mask.)
+ *   q [B,S,Hq,dqk], k [B,S,Hkv,dqk], v [B,S,Hkv,dv] (raw: not rotated); out [B,S,Hq,dv].
+ *   start_pos [B] (device): token i of sequence b sits at position start_pos[b] + i; the cache
+ *   holds that sequence's positions before start_pos[b].
+ *   max_start (host): an upper bound of every start_pos[b] (>= 0).  A sequence whose start_pos
+ *   lies outside [0, max_start] gets a zero output and nothing is stored for it.
+ *   GLOBAL: linear cache [B,Hkv,cache_capacity,d], max_start + S <= cache_capacity; slots
+ *           0..start_pos[b]-1 must hold positions 0..start_pos[b]-1; the new tokens are stored at
+ *           slots start_pos[b] + i before they are attended.
+ *   SWA:    ring cache [B,Hkv,window,d], cache_capacity == window; slot p % window must hold
+ *           position p for the min(window, start_pos[b]) positions p before start_pos[b]; the last
+ *           min(S, window) new tokens are stored at slot position % window.
+ *   K is stored rotated, V as given (as prefill and decode store them).
+ *   bf16 only: MIMO_F32 returns MIMO_ERR_UNSUPPORTED.
+ *   workspace: at least mimo_attn_extend_workspace_size() bytes (may be NULL when that is 0).
+ *   Its contents are not needed across calls.
+ */
+int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, const void* k,
+                     const void* v, const int32_t* start_pos, int32_t max_start,
+                     const float* sinks, void* out, void* k_cache, void* v_cache,
+                     int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Workspace bytes mimo_attn_extend needs: SWA bf16 layers lay the ring's content out in position
+ * order in front of the new tokens' rotated keys and values (B * Hkv * (window + seq_len) *
+ * (dqk + dv) * 2 bytes); GLOBAL layers read the cache in place (0).  Returns 0 for invalid
+ * parameters. */
+size_t mimo_attn_extend_workspace_size(const mimo_attn_params* p, int32_t seq_len);
+
+/*
  * Decode: one new token per sequence against the KV cache, which it also appends to.
  *   q [B,Hq,dqk], k_new [B,Hkv,dqk], v_new [B,Hkv,dv] (raw: not rotated); out [B,Hq,dv].
  *   positions [B] (device): tokens already cached for sequence b = position of the new token.

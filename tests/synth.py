@@ -81,6 +81,15 @@ def layer_inputs(w: Workload, seed: int, device="cpu", batch=None, seq=None):
     return q, k, v, sinks
 
 
+def cache_contents(w: Workload, seed: int, batch: int, cache_capacity: int, device="cpu"):
+    """Cache contents k_cache [B,Hkv,cap,dqk], v_cache [B,Hkv,cap,dv] drawn N(0,1) (the cache
+    holds keys that are already rotated, so any draw is a valid cache state)."""
+    g = _gen(seed, device)
+    k_cache = randn((batch, w.num_kv_heads, cache_capacity, w.qk_head_dim), g, w.dtype, device)
+    v_cache = randn((batch, w.num_kv_heads, cache_capacity, w.v_head_dim), g, w.dtype, device)
+    return k_cache, v_cache
+
+
 def decode_lengths(seed: int, batch: int = DECODE_BATCH, lo: int = DECODE_MIN_LEN,
                    hi: int = DECODE_MAX_LEN) -> torch.Tensor:
     """Tokens already cached per sequence, uniform in [lo, hi] inclusive (host int32)."""

@@ -95,6 +95,10 @@ def test_workspace_sizes():
     ws = mimo.decode_workspace_size(_ga(batch=64), 32768)
     assert ws > 0 and ws % (64 * 64 * 130 * 4) == 0
     assert mimo.decode_workspace_size(_ga(batch=64), 100) == 0
+    # extend: sliding layers lay out window + S rows of K and V; global layers read the cache
+    assert mimo.extend_workspace_size(_swa(batch=2), 1000) == 2 * 8 * (128 + 1000) * (192 + 128) * 2
+    assert mimo.extend_workspace_size(_ga(batch=2), 1000) == 0
+    assert mimo.extend_workspace_size(_swa(), -1) == 0
 
 
 _L = None
@@ -120,6 +124,14 @@ def _decode(p, maxp=10, q=1, kn=1, vn=1, pos=1, kc=1, vc=1, cap=128, out=1, ws=N
     ptr = lambda x: None if x is None else P(0x1000 * x)
     return _lib().mimo_attn_decode(ctypes.byref(cp), ptr(q), ptr(kn), ptr(vn), ptr(pos), maxp,
                                    ptr(kc), ptr(vc), cap, None, ptr(out), ptr(ws), wsb, None)
+
+
+def _extend(p, S=16, q=1, k=1, v=1, sp=1, maxs=100, out=1, kc=1, vc=1, cap=128, ws=None, wsb=0):
+    cp = p.c()
+    P = ctypes.c_void_p
+    ptr = lambda x: None if x is None else P(0x1000 * x)
+    return _lib().mimo_attn_extend(ctypes.byref(cp), S, ptr(q), ptr(k), ptr(v), ptr(sp), maxs,
+                                   None, ptr(out), ptr(kc), ptr(vc), cap, ptr(ws), wsb, None)
 
 
 def test_prefill_argument_errors_return_before_any_launch():
@@ -154,3 +166,24 @@ def test_decode_argument_errors_return_before_any_launch():
     # a bf16 cache slice is addressed with a 32-bit byte bound
     assert _decode(_ga(), maxp=10, cap=12_000_000) == mimo.MIMO_ERR_UNSUPPORTED
     assert "4 GiB" in mimo.last_error()
+
+
+def test_extend_argument_errors_return_before_any_launch():
+    E = mimo.MIMO_ERR_INVALID_ARG
+    assert _extend(_swa(), S=-1) == E
+    assert _extend(_swa(), maxs=-1) == E
+    assert _extend(_swa(), kc=None) == E                   # extend reads the cache
+    assert _extend(_swa(), vc=None) == E
+    assert _extend(_swa(), q=None) == E
+    assert _extend(_swa(), sp=None) == E
+    assert _extend(_swa(), cap=64) == E                    # ring capacity != window
+    assert _extend(_ga(), maxs=100, S=16, cap=115) == E    # linear cache cannot hold 116 positions
+    assert "max_start" in mimo.last_error()
+    assert _extend(_ga(), maxs=0x7ffffff0, S=100, cap=128) == E   # positions overflow int32
+    assert _extend(_swa(), ws=None) == mimo.MIMO_ERR_WORKSPACE
+    assert _extend(_swa(), ws=5, wsb=100) == mimo.MIMO_ERR_WORKSPACE
+    assert _extend(_swa(dtype=mimo.F32, qk_head_dim=32, v_head_dim=16, rope_dims=10,
+                        num_q_heads=4, num_kv_heads=1, window=16), cap=16) == mimo.MIMO_ERR_UNSUPPORTED
+    # nothing to do: success without touching any pointer
+    assert _extend(_swa(), S=0, q=None, k=None, v=None, sp=None, out=None) == mimo.MIMO_OK
+    assert _extend(_ga(batch=0), q=None, cap=116) == mimo.MIMO_OK
