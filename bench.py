@@ -23,7 +23,10 @@ Single-layer workloads for profiling (not the bench line): --workload swa_prefil
 tokens, sliding), ga_prefill (batch 1, 8192 tokens, global), decode (batch 64, cached lengths
 uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one), copy
 (a 2 GiB device-to-device copy: the known-size reference for HBM byte counters and the
-achievable HBM rate), gemm (8192^3 bf16 matrix product: the achievable matrix-core rate).
+achievable HBM rate), gemm (8192^3 bf16 matrix product: the achievable matrix-core rate),
+extend (new tokens against a cache: a 2048-token chunk after 30000 cached positions, global and
+sliding, batch 1; and 4 tokens per sequence after the decode workload's cached lengths, batch 64,
+the shape of multi-token verification).
 """
 from __future__ import annotations
 
@@ -100,6 +103,23 @@ def decode_counts(B, Hq, Hkv, kind, W, positions):
     return flops, bytes_
 
 
+def extend_counts(Hq, Hkv, kind, W, starts, S):
+    """flops and bytes of one extend call: visible (query, key) pairs; q, k, v read, out written,
+    the cached positions any new token sees read once, the new tokens stored (ring: the last W)."""
+    flops = bytes_ = 0
+    for st in starts:
+        if kind == 0:
+            pairs = S * st + S * (S + 1) // 2          # row i sees st + i + 1 keys
+            cached, stored = st, S
+        else:
+            pairs = sum(min(W, st + i + 1) for i in range(S))
+            cached, stored = min(W - 1, st), min(S, W)
+        flops += Hq * pairs * 2 * (DQK + DV)
+        bytes_ += (S * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV)
+                   + Hkv * (cached + stored) * (DQK + DV)) * 2
+    return flops, bytes_
+
+
 def cpu_baseline(stack_cfg, seed_base):
     """The fp64 oracle on a bounded sample of the same workload (about 15 s of host work): sequence
     0 of layer 0 (global) over its first 6144 tokens, of layer 1 (sliding) over its first 4096
@@ -149,7 +169,8 @@ def main():
     ap.add_argument("--eager-decode", action="store_true",
                     help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
-                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "copy", "gemm"])
+                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "extend", "copy",
+                             "gemm"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -391,6 +412,31 @@ def single_layer(args, dev):
         b -= w.batch * (min(w.seq, w.window) if w.layer_kind else w.seq) * w.num_kv_heads * (DQK + DV) * 2
         res.update(ms=ms, tflops=f / ms / 1e9, GBps=b / ms / 1e6, flop=f, bytes=b,
                    frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS, frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
+    elif args.workload == "extend":
+        lengths = synth.decode_lengths(3).tolist()
+        cases = [("global_chunk", synth.GA_HEADS, [30000], 2048),
+                 ("sliding_chunk", synth.SWA_HEADS, [30000], 2048),
+                 ("global_verify4", synth.GA_HEADS, lengths, 4),
+                 ("sliding_verify4", synth.SWA_HEADS, lengths, 4)]
+        for name, heads, starts, S in cases:
+            B = len(starts)
+            w = synth.Workload(name, B, S, dtype=torch.bfloat16, **heads)
+            swa = w.layer_kind == 1
+            cap = w.window if swa else max(starts) + S
+            q, k, v, s = synth.layer_inputs(w, 8000 + w.layer_kind, device=dev)
+            kc, vc = synth.cache_contents(w, 8100 + w.layer_kind, B, cap, device=dev)
+            p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims, w.layer_kind,
+                            w.window, w.rope_theta, w.v_scale)
+            sp = torch.tensor(starts, dtype=torch.int32, device=dev)
+            out = torch.empty((B, S, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mimo.extend_workspace_size(p, S) + 256, dtype=torch.uint8, device=dev)
+            # the same call repeated: the new tokens' slots are rewritten with the same values
+            ms = timed(lambda: mimo.extend(p, q, k, v, sp, max(starts), kc, vc, sinks=s, out=out,
+                                           workspace=ws), args.steps)
+            f, b = extend_counts(w.num_q_heads, w.num_kv_heads, w.layer_kind, w.window, starts, S)
+            res[name] = dict(ms=ms, tflops=f / ms / 1e9, GBps=b / ms / 1e6, flop=f, bytes=b,
+                             frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS,
+                             frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
     else:
         lengths = synth.decode_lengths(3).tolist()
         B = len(lengths)
