@@ -8,6 +8,9 @@ from .oracle import (  # noqa: F401
     OracleParams,
     build,
     decode,
+    decode_fp8,
+    e4m3_decode,
+    e4m3_encode,
     extend,
     num_threads,
     omega,

@@ -267,13 +267,33 @@ int oracle_scores(const oracle_params* p, int32_t S, const float* q, const float
  *   out [B,Hq,dv]; k_new_rot [B,Hkv,dqk] optional, receives the rotated new key.
  *   batch_rows: optional list of sequences to compute (others untouched); NULL = all.
  */
-int oracle_decode(const oracle_params* p, const float* q, const float* k_new, const float* v_new,
-                  const int32_t* pos, const float* kc, const float* vc, const int32_t* kpos,
-                  const int32_t* count, int32_t L, const float* sinks, double* out,
-                  double* k_new_rot, const int32_t* batch_rows, int32_t nbatch_rows) {
+/*
+ * The cache of a decode: either float entries (rotated keys, values) or fp8 e4m3 codes with
+ * one scale per tensor (see the fp8 section below).  For fp8 caches the new token is quantized
+ * the way the cache stores it and attended with its stored value.
+ */
+typedef struct {
+    const float* kf;
+    const float* vf;
+    const uint8_t* k8;
+    const uint8_t* v8;
+    double k_scale, v_scale;   /* fp8: stored value = e4m3(code) * scale */
+    float k_inv, v_inv;        /* fp8: 1 / scale rounded to fp32 */
+} decode_cache;
+
+double oracle_e4m3_value(uint8_t c);
+uint8_t oracle_e4m3_code(float y);
+
+static int decode_core(const oracle_params* p, const float* q, const float* k_new,
+                       const float* v_new, const int32_t* pos, const decode_cache* c,
+                       const int32_t* kpos, const int32_t* count, int32_t L, const float* sinks,
+                       double* out, double* k_new_rot, uint8_t* k_code_new, uint8_t* v_code_new,
+                       const int32_t* batch_rows, int32_t nbatch_rows) {
+    const int fp8 = c->k8 != NULL;
     if (check_params(p) != ORACLE_OK || !q || !k_new || !v_new || !pos || !out || L < 0)
         return ORACLE_EINVAL;
-    if (L > 0 && (!kc || !vc || !kpos || !count)) return ORACLE_EINVAL;
+    if (L > 0 && (!kpos || !count || (fp8 ? (!c->k8 || !c->v8) : (!c->kf || !c->vf))))
+        return ORACLE_EINVAL;
     const int32_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
     const int32_t dqk = p->qk_head_dim, dv = p->v_head_dim, r = p->rope_dims;
     const int32_t group = Hq / Hkv;
@@ -307,29 +327,50 @@ int oracle_decode(const oracle_params* p, const float* q, const float* k_new, co
                 const int32_t h = (int32_t)(w % Hq);
                 const int32_t g = h / group;
                 const int64_t pq = pos[b];
+                const int64_t kv_row = (int64_t)b * Hkv + g;
                 for (int32_t d = 0; d < dqk; ++d) tmp[d] = (double)q[((int64_t)b * Hq + h) * dqk + d];
                 rotate_row(tmp, qrot, dqk, r, omega, (double)pq);
-                for (int32_t d = 0; d < dqk; ++d)
-                    tmp[d] = (double)k_new[((int64_t)b * Hkv + g) * dqk + d];
+                for (int32_t d = 0; d < dqk; ++d) tmp[d] = (double)k_new[kv_row * dqk + d];
                 rotate_row(tmp, knew, dqk, r, omega, (double)pq);
                 if (k_new_rot && h % group == 0)
-                    memcpy(k_new_rot + ((int64_t)b * Hkv + g) * dqk, knew, sizeof(double) * dqk);
+                    memcpy(k_new_rot + kv_row * dqk, knew, sizeof(double) * dqk);
+                if (fp8) {
+                    /* the new key as the cache stores it: fp32 of the rotated key, times the
+                     * fp32 inverse scale, to the nearest code */
+                    for (int32_t d = 0; d < dqk; ++d) {
+                        const uint8_t code = oracle_e4m3_code((float)knew[d] * c->k_inv);
+                        if (k_code_new && h % group == 0) k_code_new[kv_row * dqk + d] = code;
+                        knew[d] = oracle_e4m3_value(code) * c->k_scale;
+                    }
+                }
                 int64_t n = 0;
                 const int32_t cnt = L > 0 ? count[b] : 0;
                 for (int32_t j = 0; j < cnt; ++j) {
                     const int64_t pk = kpos[(int64_t)b * L + j];
                     /* only keys strictly in the past of the new token; it is itself at pq */
                     if (pk >= pq || !visible(p, pq, pk)) continue;
-                    const int64_t off = ((int64_t)b * Hkv + g) * L + j;
-                    for (int32_t d = 0; d < dqk; ++d) kj[d] = (double)kc[off * dqk + d];
+                    const int64_t off = kv_row * L + j;
+                    for (int32_t d = 0; d < dqk; ++d)
+                        kj[d] = fp8 ? oracle_e4m3_value(c->k8[off * dqk + d]) * c->k_scale
+                                    : (double)c->kf[off * dqk + d];
                     z[n] = tau * dot(qrot, kj, dqk);
-                    for (int32_t e = 0; e < dv; ++e) vrows[n * dv + e] = (double)vc[off * dv + e];
+                    for (int32_t e = 0; e < dv; ++e)
+                        vrows[n * dv + e] = fp8 ? oracle_e4m3_value(c->v8[off * dv + e]) * c->v_scale
+                                                : (double)c->vf[off * dv + e];
                     vals[n] = vrows + n * dv;
                     ++n;
                 }
                 z[n] = tau * dot(qrot, knew, dqk);
-                for (int32_t e = 0; e < dv; ++e)
-                    vrows[n * dv + e] = (double)v_new[((int64_t)b * Hkv + g) * dv + e];
+                for (int32_t e = 0; e < dv; ++e) {
+                    const float x = v_new[kv_row * dv + e];
+                    if (fp8) {
+                        const uint8_t code = oracle_e4m3_code(x * c->v_inv);
+                        if (v_code_new && h % group == 0) v_code_new[kv_row * dv + e] = code;
+                        vrows[n * dv + e] = oracle_e4m3_value(code) * c->v_scale;
+                    } else {
+                        vrows[n * dv + e] = (double)x;
+                    }
+                }
                 vals[n] = vrows + n * dv;
                 ++n;
                 const double sink = sinks ? (double)sinks[h] : -INFINITY;
@@ -341,6 +382,99 @@ int oracle_decode(const oracle_params* p, const float* q, const float* k_new, co
         free(vals);
     }
     return bad ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+int oracle_decode(const oracle_params* p, const float* q, const float* k_new, const float* v_new,
+                  const int32_t* pos, const float* kc, const float* vc, const int32_t* kpos,
+                  const int32_t* count, int32_t L, const float* sinks, double* out,
+                  double* k_new_rot, const int32_t* batch_rows, int32_t nbatch_rows) {
+    decode_cache c;
+    memset(&c, 0, sizeof c);
+    c.kf = kc;
+    c.vf = vc;
+    return decode_core(p, q, k_new, v_new, pos, &c, kpos, count, L, sinks, out, k_new_rot, NULL,
+                       NULL, batch_rows, nbatch_rows);
+}
+
+/*
+ * fp8 KV cache.  The pages only hint at quantized storage ("Add Xiaomi MiMo-V2", "Additional
+ * useful info": a garbled note of three dtypes with one quantized); the reading taken here:
+ * the caches hold OCP e4m3 codes with one fp32 scale per cache tensor (K and V), rotated K and
+ * raw V as before.
+ *   e4m3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 holds the
+ *   subnormals m * 2^-9; codes 0x7F and 0xFF are NaN; there are no infinities; the largest
+ *   finite magnitude is 448.
+ *   Stored value of a code: e4m3(code) * scale.
+ *   Code of a value x: y = fp32(x) * fp32(1 / scale) in fp32, clamped to [-448, 448], then the
+ *   nearest e4m3 value, ties to the even mantissa (the sign of y is kept, also for zero).
+ */
+double oracle_e4m3_value(uint8_t c) {
+    const int sgn = c >> 7, E = (c >> 3) & 15, M = c & 7;
+    if (E == 15 && M == 7) return NAN;
+    const double v = E == 0 ? ldexp((double)M, -9) : ldexp((double)(8 + M), E - 10);
+    return sgn ? -v : v;
+}
+
+uint8_t oracle_e4m3_code(float y) {
+    if (isnan(y)) return 0x7F;
+    const uint8_t sgn = signbit(y) ? 0x80 : 0x00;
+    double a = fabs((double)y);
+    if (a > 448.0) a = 448.0;
+    /* spacing of the e4m3 values around a: 2^(e-3) in the binade [2^e, 2^(e+1)), e >= -6;
+     * below 2^-6 the subnormal spacing 2^-9 */
+    int ex = 0;
+    frexp(a, &ex);            /* a = f * 2^ex, f in [0.5, 1) (a > 0) */
+    int e = a > 0.0 ? ex - 1 : -6;
+    if (e < -6) e = -6;
+    const double quantum = ldexp(1.0, e - 3);
+    const double v = nearbyint(a / quantum) * quantum;   /* default rounding: ties to even */
+    if (v == 0.0) return sgn;
+    frexp(v, &ex);
+    const int ev = ex - 1;    /* binade of the rounded value (a carry may have moved it up) */
+    if (ev < -6) return (uint8_t)(sgn | (uint8_t)(v / ldexp(1.0, -9)));   /* subnormal: m */
+    const int mant = (int)((v / ldexp(1.0, ev) - 1.0) * 8.0);
+    return (uint8_t)(sgn | ((ev + 7) << 3) | mant);
+}
+
+/* Array forms: codes of x[i] * inv_scale (fp32 product), and stored values code * scale. */
+int oracle_e4m3_encode(const float* x, int64_t n, float inv_scale, uint8_t* out) {
+    if ((n > 0 && (!x || !out)) || n < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_code(x[i] * inv_scale);
+    return ORACLE_OK;
+}
+
+int oracle_e4m3_decode(const uint8_t* c, int64_t n, double scale, double* out) {
+    if ((n > 0 && (!c || !out)) || n < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_value(c[i]) * scale;
+    return ORACLE_OK;
+}
+
+/*
+ * Decode against fp8 caches: as oracle_decode, with the cache entries given as codes
+ * kc8 [B,Hkv,L,dqk], vc8 [B,Hkv,L,dv] and their scales, and the new token quantized as the
+ * cache stores it before it is attended.  k_code_new [B,Hkv,dqk], v_code_new [B,Hkv,dv]
+ * (optional) receive the new token's codes.  Scales must be finite and > 0.
+ */
+int oracle_decode_fp8(const oracle_params* p, const float* q, const float* k_new,
+                      const float* v_new, const int32_t* pos, const uint8_t* kc8,
+                      const uint8_t* vc8, const int32_t* kpos, const int32_t* count, int32_t L,
+                      double k_scale, double v_scale, const float* sinks, double* out,
+                      double* k_new_rot, uint8_t* k_code_new, uint8_t* v_code_new,
+                      const int32_t* batch_rows, int32_t nbatch_rows) {
+    if (!(k_scale > 0.0 && isfinite(k_scale) && v_scale > 0.0 && isfinite(v_scale)))
+        return ORACLE_EINVAL;
+    static const uint8_t none = 0;
+    decode_cache c;
+    memset(&c, 0, sizeof c);
+    c.k8 = kc8 ? kc8 : &none;   /* (marks the cache as fp8 also when L = 0) */
+    c.v8 = vc8 ? vc8 : &none;
+    c.k_scale = (double)(float)k_scale;
+    c.v_scale = (double)(float)v_scale;
+    c.k_inv = 1.0f / (float)k_scale;
+    c.v_inv = 1.0f / (float)v_scale;
+    if (L > 0 && (!kc8 || !vc8)) return ORACLE_EINVAL;
+    return decode_core(p, q, k_new, v_new, pos, &c, kpos, count, L, sinks, out, k_new_rot,
+                       k_code_new, v_code_new, batch_rows, nbatch_rows);
 }
 
 /*

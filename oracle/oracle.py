@@ -83,10 +83,17 @@ def _load():
             lib.oracle_extend.argtypes = [P(_CParams), ctypes.c_int32, f32, f32, f32, i32, f32,
                                           f32, i32, i32, ctypes.c_int32, f32, f64, i32,
                                           ctypes.c_int32, f64]
+            u8 = P(ctypes.c_uint8)
+            lib.oracle_e4m3_encode.argtypes = [f32, ctypes.c_int64, ctypes.c_float, u8]
+            lib.oracle_e4m3_decode.argtypes = [u8, ctypes.c_int64, ctypes.c_double, f64]
+            lib.oracle_decode_fp8.argtypes = [P(_CParams), f32, f32, f32, i32, u8, u8, i32, i32,
+                                              ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                              f32, f64, f64, u8, u8, i32, ctypes.c_int32]
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             for fn in ("oracle_rope_omega", "oracle_rope_rotate", "oracle_prefill",
-                       "oracle_scores", "oracle_decode", "oracle_extend"):
+                       "oracle_scores", "oracle_decode", "oracle_extend", "oracle_e4m3_encode",
+                       "oracle_e4m3_decode", "oracle_decode_fp8"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -106,6 +113,10 @@ def _i32(a):
 
 def _ptr(a, ctype):
     return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _u8(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
 
 
 def _check(rc, what):
@@ -243,3 +254,62 @@ def extend(p: OracleParams, q, k, v, start, kc=None, vc=None, kpos=None, count=N
         _ptr(sinks, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(rows_a, ctypes.c_int32),
         0 if rows_a is None else len(rows_a), _ptr(krot, ctypes.c_double)), "extend")
     return (out, krot) if want_k_rot else out
+
+
+# ----------------------------------------------------------------------------- fp8 KV cache
+
+
+def e4m3_encode(x, inv_scale: float = 1.0) -> np.ndarray:
+    """e4m3 codes (uint8) of fp32(x) * fp32(inv_scale), clamped to +-448, nearest, ties even."""
+    xa = _f32(x)
+    out = np.empty(xa.shape, dtype=np.uint8)
+    _check(_load().oracle_e4m3_encode(_ptr(xa, ctypes.c_float), xa.size, float(inv_scale),
+                                      _ptr(out, ctypes.c_uint8)), "e4m3_encode")
+    return out
+
+
+def e4m3_decode(codes, scale: float = 1.0) -> np.ndarray:
+    """Stored values code -> e4m3(code) * scale (float64; NaN codes give NaN)."""
+    ca = _u8(codes)
+    out = np.empty(ca.shape, dtype=np.float64)
+    _check(_load().oracle_e4m3_decode(_ptr(ca, ctypes.c_uint8), ca.size, float(scale),
+                                      _ptr(out, ctypes.c_double)), "e4m3_decode")
+    return out
+
+
+def decode_fp8(p: OracleParams, q, k_new, v_new, pos, kc8=None, vc8=None, kpos=None, count=None,
+               k_scale: float = 1.0, v_scale: float = 1.0, sinks=None, batch_rows=None):
+    """decode() against fp8 caches: kc8 [B,Hkv,L,dqk] / vc8 [B,Hkv,L,dv] e4m3 codes with one
+    scale each; the new token is quantized as the cache stores it before it is attended.
+
+    Returns (out [B,Hq,dv], rotated new keys [B,Hkv,dqk] (exact, before quantization),
+    new key codes [B,Hkv,dqk], new value codes [B,Hkv,dv])."""
+    q, k_new, v_new, sinks = _f32(q), _f32(k_new), _f32(v_new), _f32(sinks)
+    pos = _i32(pos)
+    B = pos.shape[0]
+    assert q.shape == (B, p.num_q_heads, p.qk_head_dim)
+    assert k_new.shape == (B, p.num_kv_heads, p.qk_head_dim)
+    assert v_new.shape == (B, p.num_kv_heads, p.v_head_dim)
+    if kc8 is None:
+        L = 0
+        kc_a = vc_a = kpos_a = cnt_a = None
+    else:
+        kc_a, vc_a, kpos_a, cnt_a = _u8(kc8), _u8(vc8), _i32(kpos), _i32(count)
+        L = kc_a.shape[2]
+        assert kc_a.shape == (B, p.num_kv_heads, L, p.qk_head_dim)
+        assert vc_a.shape == (B, p.num_kv_heads, L, p.v_head_dim)
+        assert kpos_a.shape == (B, L) and cnt_a.shape == (B,)
+    out = np.full((B, p.num_q_heads, p.v_head_dim), np.nan, dtype=np.float64)
+    krot = np.full(k_new.shape, np.nan, dtype=np.float64)
+    kcode = np.zeros(k_new.shape, dtype=np.uint8)
+    vcode = np.zeros(v_new.shape, dtype=np.uint8)
+    br = _i32(batch_rows)
+    cp = p.c()
+    _check(_load().oracle_decode_fp8(
+        ctypes.byref(cp), _ptr(q, ctypes.c_float), _ptr(k_new, ctypes.c_float),
+        _ptr(v_new, ctypes.c_float), _ptr(pos, ctypes.c_int32), _ptr(kc_a, ctypes.c_uint8),
+        _ptr(vc_a, ctypes.c_uint8), _ptr(kpos_a, ctypes.c_int32), _ptr(cnt_a, ctypes.c_int32), L,
+        float(k_scale), float(v_scale), _ptr(sinks, ctypes.c_float), _ptr(out, ctypes.c_double),
+        _ptr(krot, ctypes.c_double), _ptr(kcode, ctypes.c_uint8), _ptr(vcode, ctypes.c_uint8),
+        _ptr(br, ctypes.c_int32), 0 if br is None else len(br)), "decode_fp8")
+    return out, krot, kcode, vcode

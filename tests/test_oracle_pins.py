@@ -420,6 +420,125 @@ def test_extend_with_empty_cache_is_prefill_and_one_token_is_decode():
     np.testing.assert_allclose(ex1[:, 0], dec, rtol=0, atol=1e-13)
 
 
+# ----------------------------------------------------------------------------- fp8 KV cache
+# The codes and values are pinned against torch's float8_e4m3fn conversions (a different route
+# than the oracle's bit-level definition); the attention over an fp8 cache against the float
+# decode on the stored values.
+
+
+def _e4m3_torch_values():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _e4m3_torch_codes(y):
+    """torch's nearest-even e4m3 codes of fp32 values, clamped to +-448 first (torch itself turns
+    values that round past 448 into NaN)."""
+    t = torch.from_numpy(np.asarray(y, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_probe_values():
+    vals = _e4m3_torch_values()[:127].astype(np.float32)
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(17)
+    rnd = np.concatenate([rng.standard_normal(4000) * sc for sc in (1e-3, 0.05, 1, 30, 300)])
+    big = np.array([448, 449, 463.9, 464, 464.1, 479, 480, 1e6, np.inf], np.float32)
+    x = np.concatenate([vals, mids, np.nextafter(mids, np.float32(np.inf)),
+                        np.nextafter(mids, np.float32(-np.inf)), rnd.astype(np.float32), big])
+    return np.concatenate([x, -x]).astype(np.float32)
+
+
+def test_e4m3_values_match_torch():
+    mine, ref = oracle.e4m3_decode(np.arange(256, dtype=np.uint8)), _e4m3_torch_values()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.nonzero(np.isnan(ref))[0], [0x7F, 0xFF])
+    # a scale multiplies every stored value
+    np.testing.assert_array_equal(oracle.e4m3_decode(np.arange(127, dtype=np.uint8), 0.375),
+                                  ref[:127] * 0.375)
+
+
+@pytest.mark.parametrize("inv_scale", [1.0, 0.125, 1.0 / 0.37, 3.0])
+def test_e4m3_codes_match_torch_nearest_even(inv_scale):
+    x = _e4m3_probe_values()
+    y = x * np.float32(inv_scale)          # the fp32 product the code is taken of
+    assert np.array_equal(oracle.e4m3_encode(x, np.float32(inv_scale)), _e4m3_torch_codes(y))
+
+
+def test_e4m3_round_trip_error_bound_and_saturation():
+    x = _e4m3_probe_values()
+    x = x[np.isfinite(x)]
+    back = oracle.e4m3_decode(oracle.e4m3_encode(x))
+    a = np.abs(x.astype(np.float64))
+    inside = a <= 448
+    # half a quantum: 2^-4 of the magnitude for normals (3 mantissa bits), 2^-10 for subnormals
+    bound = np.maximum(a * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(back - x)[inside] <= bound[inside] * (1 + 1e-12))
+    assert np.all(np.abs(back[~inside]) == 448) and np.all(np.sign(back[~inside]) == np.sign(x[~inside]))
+    # the grid itself is a fixed point, zero keeps its sign
+    grid = _e4m3_torch_values()[:127]
+    assert np.array_equal(oracle.e4m3_decode(oracle.e4m3_encode(grid)), grid)
+    assert oracle.e4m3_encode(np.array([-0.0], np.float32))[0] == 0x80
+
+
+def _fp8_cache_case(kind, r, seed, L=7, W=5):
+    w = _small(kind=kind, W=W if kind == 1 else 0, Hq=4, Hkv=2, dqk=16, dv=8, r=r)
+    B = w.batch
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, w.num_q_heads, w.qk_head_dim), generator=g)
+    kn = torch.randn((B, w.num_kv_heads, w.qk_head_dim), generator=g).to(torch.bfloat16).float()
+    vn = torch.randn((B, w.num_kv_heads, w.v_head_dim), generator=g).to(torch.bfloat16).float()
+    s = torch.randn((w.num_q_heads,), generator=g) if w.sinks else None
+    kc8 = (torch.randn((B, w.num_kv_heads, L, w.qk_head_dim), generator=g) * 4).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vc8 = (torch.randn((B, w.num_kv_heads, L, w.v_head_dim), generator=g) * 4).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    pos = np.array([L, L + 3], np.int32)
+    kpos = np.stack([np.arange(L, dtype=np.int32) + (p - L) for p in pos])   # positions p-L..p-1
+    kpos = np.ascontiguousarray(kpos[:, np.random.default_rng(seed).permutation(L)])
+    return w, q.numpy(), kn.numpy(), vn.numpy(), None if s is None else s.numpy(), kc8, vc8, pos, kpos
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_decode_fp8_equals_float_decode_on_stored_values(kind):
+    """No rotation (r = 0) and power-of-two scales: every stored value is exact in fp32, so the
+    fp8 decode must equal the float decode given the stored values for the cache and for the new
+    token (quantized by torch's conversion)."""
+    w, q, kn, vn, s, kc8, vc8, pos, kpos = _fp8_cache_case(kind, r=0, seed=61)
+    ks, vs = 0.125, 2.0
+    P = _params(w)
+    cnt = np.full(w.batch, kc8.shape[2], np.int32)
+    out, _, kcode, vcode = oracle.decode_fp8(P, q, kn, vn, pos, kc8, vc8, kpos, cnt, ks, vs, s)
+    tv = _e4m3_torch_values()
+    kst = tv[_e4m3_torch_codes(kn * np.float32(1 / ks))] * ks
+    vst = tv[_e4m3_torch_codes(vn * np.float32(1 / vs))] * vs
+    assert np.array_equal(kcode, _e4m3_torch_codes(kn * np.float32(1 / ks)))
+    assert np.array_equal(vcode, _e4m3_torch_codes(vn * np.float32(1 / vs)))
+    ref = oracle.decode(P, q, kst, vst, pos, (tv[kc8] * ks).astype(np.float32),
+                        (tv[vc8] * vs).astype(np.float32), kpos, cnt, s)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+    # the new token really is the quantized one: the exact one gives another answer
+    exact = oracle.decode(P, q, kn, vn, pos, (tv[kc8] * ks).astype(np.float32),
+                          (tv[vc8] * vs).astype(np.float32), kpos, cnt, s)
+    assert np.abs(exact - out).max() > 1e-4
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_decode_fp8_quantizes_the_rotated_key(kind):
+    """With rotation the new key is rotated first, then rounded to fp32, scaled and coded."""
+    w, q, kn, vn, s, kc8, vc8, pos, kpos = _fp8_cache_case(kind, r=6, seed=62)
+    ks, vs = 0.37, 1.7
+    P = _params(w)
+    cnt = np.full(w.batch, kc8.shape[2], np.int32)
+    _, krot, kcode, vcode = oracle.decode_fp8(P, q, kn, vn, pos, kc8, vc8, kpos, cnt, ks, vs, s)
+    _, krot_ref = oracle.decode(P, q, kn, vn, pos, want_k_rot=True)
+    np.testing.assert_array_equal(krot, krot_ref)
+    inv_k, inv_v = np.float32(1) / np.float32(ks), np.float32(1) / np.float32(vs)
+    assert np.array_equal(kcode, _e4m3_torch_codes(krot.astype(np.float32) * inv_k))
+    assert np.array_equal(vcode, _e4m3_torch_codes(vn * inv_v))
+
+
 def test_oracle_rejects_invalid_arguments():
     w = _small()
     q, k, v, s = synth.layer_inputs(w, seed=1)
