@@ -21,7 +21,8 @@ captured once before timing); --eager-decode launches them from Python instead.
 
 Single-layer workloads for profiling (not the bench line): --workload swa_prefill (batch 1, 4096
 tokens, sliding), ga_prefill (batch 1, 8192 tokens, global), decode (batch 64, cached lengths
-uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one), copy
+uniform in [1024, 32768] for the global layer, full 128-slot rings for the sliding one; with bf16
+and with fp8 e4m3 caches), copy
 (a 2 GiB device-to-device copy: the known-size reference for HBM byte counters and the
 achievable HBM rate), gemm (8192^3 bf16 matrix product: the achievable matrix-core rate),
 extend (new tokens against a cache: a 2048-token chunk after 30000 cached positions, global and
@@ -90,16 +91,16 @@ def prefill_counts(B, S, Hq, Hkv, kind, W):
     return flops, io
 
 
-def decode_counts(B, Hq, Hkv, kind, W, positions):
+def decode_counts(B, Hq, Hkv, kind, W, positions, cache_bytes=2):
     """flops and bytes of one decode step: every visible cached slot read once, q/k/v_new read,
-    out and the appended slot written."""
+    out and the appended slot written (cache_bytes per cache element: 2 bf16, 1 fp8)."""
     flops = bytes_ = 0
     for p in positions:
         cached = min(W - 1, p) if kind == 1 else p
         flops += Hq * (cached + 1) * 2 * (DQK + DV)
-        bytes_ += Hkv * cached * (DQK + DV) * 2
+        bytes_ += Hkv * cached * (DQK + DV) * cache_bytes
     B = len(positions)
-    bytes_ += B * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV + Hkv * (DQK + DV)) * 2
+    bytes_ += B * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV) * 2 + B * Hkv * (DQK + DV) * cache_bytes
     return flops, bytes_
 
 
@@ -440,13 +441,24 @@ def single_layer(args, dev):
     else:
         lengths = synth.decode_lengths(3).tolist()
         B = len(lengths)
-        for name, heads in (("global", synth.GA_HEADS), ("sliding", synth.SWA_HEADS)):
+        for name, heads, fp8 in (("global", synth.GA_HEADS, False),
+                                 ("sliding", synth.SWA_HEADS, False),
+                                 ("global_fp8", synth.GA_HEADS, True),
+                                 ("sliding_fp8", synth.SWA_HEADS, True)):
             w = synth.Workload(name, B, 1, dtype=torch.bfloat16, **heads)
             swa = w.layer_kind == 1
             cap = w.window if swa else max(lengths) + 1
-            q, kn, vn, s, kc, vc = synth.decode_inputs(w, 7000 + w.layer_kind, B, cap, device=dev)
+            if fp8:
+                q, kn, vn, s, _, _ = synth.decode_inputs(w, 7000 + w.layer_kind, B, 1, device=dev)
+                kc, vc = synth.fp8_cache_contents(w, 7100 + w.layer_kind, B, cap, device=dev)
+            else:
+                q, kn, vn, s, kc, vc = synth.decode_inputs(w, 7000 + w.layer_kind, B, cap,
+                                                           device=dev)
             p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims, w.layer_kind,
                             w.window, w.rope_theta, w.v_scale)
+            if fp8:
+                p.cache_dtype = mimo.CACHE_FP8_E4M3
+                p.k_cache_scale, p.v_cache_scale = synth.FP8_K_SCALE, synth.FP8_V_SCALE
             pos = torch.tensor(lengths, dtype=torch.int32, device=dev)
             out = torch.empty((B, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(mimo.decode_workspace_size(p, max(lengths)) + 256, dtype=torch.uint8,
@@ -454,7 +466,8 @@ def single_layer(args, dev):
             # the same step repeated: the appended slot is rewritten with the same values
             ms = timed(lambda: mimo.decode(p, q, kn, vn, pos, max(lengths), kc, vc, sinks=s,
                                            out=out, workspace=ws), args.steps)
-            f, b = decode_counts(B, w.num_q_heads, w.num_kv_heads, w.layer_kind, w.window, lengths)
+            f, b = decode_counts(B, w.num_q_heads, w.num_kv_heads, w.layer_kind, w.window, lengths,
+                                 cache_bytes=1 if fp8 else 2)
             res[name] = dict(ms=ms, GBps=b / ms / 1e6, bytes=b, tflops=f / ms / 1e9,
                              frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
     print(json.dumps(res), flush=True)

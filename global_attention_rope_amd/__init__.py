@@ -6,6 +6,8 @@ this package is its thin Python binding plus the per-layer dispatch from
 """
 from .binding import (  # noqa: F401
     BF16,
+    CACHE_FP8_E4M3,
+    CACHE_SAME,
     EXPORTS,
     F32,
     LAYER_GLOBAL,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libmimo_attn.so")
 MIMO_OK, MIMO_ERR_INVALID_ARG, MIMO_ERR_UNSUPPORTED, MIMO_ERR_WORKSPACE, MIMO_ERR_HIP = 0, -1, -2, -3, -4
 LAYER_GLOBAL, LAYER_SWA = 0, 1
 F32, BF16 = 0, 1
+CACHE_SAME, CACHE_FP8_E4M3 = 0, 2
 
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_extend",
            "mimo_attn_extend_workspace_size", "mimo_attn_decode",
@@ -40,7 +41,8 @@ class CParams(ctypes.Structure):
         ("layer_kind", ctypes.c_int32), ("window", ctypes.c_int32),
         ("rope_theta", ctypes.c_double), ("v_scale", ctypes.c_float),
         ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32), ("k_cache_scale", ctypes.c_float),
+        ("v_cache_scale", ctypes.c_float),
     ]
 
 
@@ -58,12 +60,16 @@ class Params:
     v_scale: float = 1.0
     softmax_scale: float = 0.0
     dtype: int = BF16
+    cache_dtype: int = CACHE_SAME      # CACHE_FP8_E4M3: caches are uint8 e4m3 codes
+    k_cache_scale: float = 1.0
+    v_cache_scale: float = 1.0
 
     def c(self) -> CParams:
         return CParams(self.batch, self.num_q_heads, self.num_kv_heads, self.qk_head_dim,
                        self.v_head_dim, self.rope_dims, self.layer_kind, self.window,
                        float(self.rope_theta), float(self.v_scale), float(self.softmax_scale),
-                       self.dtype, 0)
+                       self.dtype, self.cache_dtype, float(self.k_cache_scale),
+                       float(self.v_cache_scale))
 
 
 _lock = threading.Lock()
@@ -159,6 +165,11 @@ def _tdtype(p: Params):
     return torch.bfloat16 if p.dtype == BF16 else torch.float32
 
 
+def _cdtype(p: Params):
+    """torch dtype of the caches: uint8 codes for fp8 caches, else the layer dtype."""
+    return torch.uint8 if p.cache_dtype == CACHE_FP8_E4M3 else _tdtype(p)
+
+
 def prefill(p: Params, q, k, v, start_pos, sinks=None, out=None, k_cache=None, v_cache=None,
             workspace=None, stream=None):
     """mimo_attn_prefill on torch device tensors (shapes as in include/mimo_attn.h).
@@ -180,8 +191,8 @@ def prefill(p: Params, q, k, v, start_pos, sinks=None, out=None, k_cache=None, v
     cap = 0
     if k_cache is not None or v_cache is not None:
         cap = k_cache.shape[2]
-        _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), dt, dev)
-        _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), dt, dev)
+        _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), _cdtype(p), dev)
+        _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), _cdtype(p), dev)
     need = prefill_workspace_size(p, S)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -216,8 +227,8 @@ def extend(p: Params, q, k, v, start_pos, max_start: int, k_cache, v_cache, sink
     if k_cache is None or v_cache is None:
         raise ValueError("extend needs k_cache and v_cache")
     cap = k_cache.shape[2]
-    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), dt, dev)
-    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), dt, dev)
+    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), _cdtype(p), dev)
+    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), _cdtype(p), dev)
     need = extend_workspace_size(p, S)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -241,8 +252,8 @@ def decode(p: Params, q, k_new, v_new, positions, max_position: int, k_cache, v_
     _expect(v_new, "v_new", (B, p.num_kv_heads, p.v_head_dim), dt, dev)
     _expect(positions, "positions", (B,), torch.int32, dev)
     cap = k_cache.shape[2]
-    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), dt, dev)
-    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), dt, dev)
+    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), _cdtype(p), dev)
+    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), _cdtype(p), dev)
     if sinks is not None:
         _expect(sinks, "sinks", (p.num_q_heads,), torch.float32, dev)
     if out is None:

@@ -40,13 +40,30 @@ void fill_omega(const mimo_attn_params* p, double* omega_rev) {
         omega_rev[d] = pow(p->rope_theta, -2.0 * (double)d / (double)p->rope_dims) / two_pi;
 }
 
+bool fp8_cache(const mimo_attn_params* p) { return p->cache_dtype == MIMO_CACHE_FP8_E4M3; }
+
+// Bytes per cache element.
+int cache_elem_bytes(const mimo_attn_params* p) {
+    return fp8_cache(p) ? 1 : (p->dtype == MIMO_BF16 ? 2 : 4);
+}
+
 float score_scale(const mimo_attn_params* p) {
     return p->softmax_scale != 0.0f ? p->softmax_scale : (float)(1.0 / sqrt((double)p->qk_head_dim));
 }
 
 int check(const mimo_attn_params* p) {
     if (!p) return fail(MIMO_ERR_INVALID_ARG, "params is NULL");
-    if (p->reserved != 0) return fail(MIMO_ERR_INVALID_ARG, "reserved must be 0");
+    if (p->cache_dtype != MIMO_CACHE_SAME && p->cache_dtype != MIMO_CACHE_FP8_E4M3)
+        return fail(MIMO_ERR_INVALID_ARG, "cache_dtype %d is neither MIMO_CACHE_SAME (0) nor "
+                    "MIMO_CACHE_FP8_E4M3 (2)", p->cache_dtype);
+    if (p->cache_dtype == MIMO_CACHE_FP8_E4M3) {
+        if (!(p->k_cache_scale > 0.0f && isfinite(p->k_cache_scale) && p->v_cache_scale > 0.0f &&
+              isfinite(p->v_cache_scale)))
+            return fail(MIMO_ERR_INVALID_ARG, "fp8 caches need finite scales > 0 (k %g, v %g)",
+                        (double)p->k_cache_scale, (double)p->v_cache_scale);
+        if (p->dtype != MIMO_BF16)
+            return fail(MIMO_ERR_UNSUPPORTED, "fp8 caches are compiled for bf16 layers only");
+    }
     if (p->batch < 0) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 0", p->batch);
     if (p->num_q_heads < 1 || p->num_kv_heads < 1)
         return fail(MIMO_ERR_INVALID_ARG, "head counts must be >= 1 (Hq %d, Hkv %d)",
@@ -228,6 +245,9 @@ int mimo_attn_prefill(const mimo_attn_params* p, int32_t seq_len, const void* q,
     ra.ring_window = swa ? p->window : 0;
     ra.ws_rows = seq_len;
     ra.max_start = -1;
+    ra.cache_fp8 = fp8_cache(p);
+    ra.k_inv = fp8_cache(p) ? 1.0f / p->k_cache_scale : 1.0f;
+    ra.v_inv = fp8_cache(p) ? 1.0f / p->v_cache_scale : 1.0f;
     // the ring only keeps the last `window` tokens
     ra.cache_i0 = (swa && seq_len > p->window) ? seq_len - p->window : 0;
     if (has_cache) {
@@ -310,6 +330,8 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
                     max_start, seq_len);
     if (p->dtype != MIMO_BF16)
         return fail(MIMO_ERR_UNSUPPORTED, "extend is compiled for bf16 layers only");
+    if (fp8_cache(p))
+        return fail(MIMO_ERR_UNSUPPORTED, "extend does not read fp8 caches");
     const bool swa = p->layer_kind == MIMO_LAYER_SWA;
     if (swa && cache_capacity != p->window)
         return fail(MIMO_ERR_INVALID_ARG, "ring cache capacity %d must equal window %d",
@@ -438,8 +460,9 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
         return fail(MIMO_ERR_INVALID_ARG, "linear cache capacity %d must exceed max_position %d",
                     cache_capacity, max_position);
     // bf16 decode addresses a cache slice through a buffer resource with a 32-bit byte bound
-    if (p->dtype == MIMO_BF16 && (int64_t)cache_capacity * p->qk_head_dim * 2 > 0xffffffffLL)
-        return fail(MIMO_ERR_UNSUPPORTED, "cache_capacity %d: a bf16 cache slice must stay below 4 GiB",
+    if (p->dtype == MIMO_BF16 &&
+        (int64_t)cache_capacity * p->qk_head_dim * cache_elem_bytes(p) > 0xffffffffLL)
+        return fail(MIMO_ERR_UNSUPPORTED, "cache_capacity %d: a cache slice must stay below 4 GiB",
                     cache_capacity);
     hipStream_t st = (hipStream_t)stream;
     if (p->dtype == MIMO_F32) {
@@ -481,8 +504,8 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
     da.k_new = (const uint16_t*)k_new;
     da.v_new = (const uint16_t*)v_new;
     da.positions = positions;
-    da.k_cache = (uint16_t*)k_cache;
-    da.v_cache = (uint16_t*)v_cache;
+    da.k_cache = k_cache;
+    da.v_cache = v_cache;
     da.sinks = sinks;
     da.out = (uint16_t*)out;
     da.partial = (float*)workspace;
@@ -497,6 +520,14 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
     da.nsplit = decode_nsplit(p, max_position);
     da.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
     da.v_scale = p->v_scale;
+    if (fp8_cache(p)) {
+        // codes are attended as their e4m3 values; the scales multiply scores and output
+        da.cache_fp8 = 1;
+        da.k_inv = 1.0f / p->k_cache_scale;
+        da.v_inv = 1.0f / p->v_cache_scale;
+        da.score_scale_log2 *= p->k_cache_scale;
+        da.v_scale *= p->v_cache_scale;
+    }
     fill_omega(p, da.omega_rev);
     return hip_status(mimo::launch_decode_bf16(da, swa, sinks != nullptr, st), "decode (bf16)");
 }

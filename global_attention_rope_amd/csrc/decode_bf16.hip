@@ -19,7 +19,12 @@
 //   * the waves are merged through LDS; with one split the sink is folded in and the bf16 output
 //     written, otherwise (max, sum, O) partials go to the workspace and the combine kernel merges
 //     the splits in one pass (running maximum) and adds the sink exactly once.
+// fp8 caches (e4m3 codes, one scale per cache tensor): the slot loads are half as wide, codes are
+// turned into their exact bf16 values in registers (K) or on their way into the LDS tile (V), the
+// two scales are folded into the score scale and the output scale, and the new token is coded
+// before it is stored and used.
 #include <cstddef>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -33,8 +38,7 @@ constexpr int NW = 4;
 constexpr int TILE = 32;                 // slots per wave iteration
 constexpr int PSTRIDE = DV + 2;          // floats per partial record: O[128], m, l
 constexpr int VT_PITCH = DV + 16;        // bf16 per V row in the per-wave LDS tile (288 bytes)
-constexpr int KREG = 2 * (DQK / 32);     // 16-byte K operand loads per lane per tile (12)
-constexpr int VREG = TILE * DV / 8 / 64; // 16-byte V loads per lane per tile (8)
+constexpr int KREG = 2 * (DQK / 32);     // K operand loads per lane per tile (12; 8 elements each)
 constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merge buffer
 
 // Rotate 8 consecutive dims d0.. of a row (w) against their partners (pw) with the cos/sin of the
@@ -42,14 +46,14 @@ constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merg
 // (cos 1, sin 0) stored after the table, so every chunk runs the same straight-line code and the
 // table reads of several chunks overlap.
 constexpr int kIdentity = kMaxRopeHalf;   // first of 8 identity entries in the table
-__device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int d0, int half,
-                                            int r, const float2* cs) {
+__device__ __forceinline__ void rotate8_cs_f32(const u32x4& w, const u32x4& pw, int d0, int half,
+                                               int r, const float2* cs, float* x) {
     const bool lower = d0 < half;
     const int f0 = d0 < r ? (lower ? d0 : d0 - half) : kIdentity;
     float4 e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) e[i] = *(const float4*)(cs + f0 + 2 * i);
-    float x[8], y[8];
+    float y[8];
     unpack8(w, x);
     unpack8(pw, y);
     const float sgn = lower ? -1.0f : 1.0f;
@@ -59,12 +63,18 @@ __device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int
         const float sn = (t & 1) ? e[t >> 1].w : e[t >> 1].y;
         x[t] = __builtin_fmaf(sgn * y[t], sn, x[t] * c);
     }
+}
+
+__device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int d0, int half,
+                                            int r, const float2* cs) {
+    float x[8];
+    rotate8_cs_f32(w, pw, d0, half, r, cs, x);
     return pack8(x);
 }
 
 struct LdsDecode {
     float2 cs[kMaxRopeHalf + 8];              // cos/sin of the position per frequency, identity
-    uint16_t Kn[DQK];
+    uint16_t Kn[DQK];                         // the new token (bf16, or e4m3 codes in the first half)
     uint16_t Vn[DV];
     float red_m[NW][16], red_l[NW][16];
     float sink[16];
@@ -75,9 +85,16 @@ struct LdsDecode {
 };
 
 // ROT: how many of a lane's 32-dim query chunk rows can hold rotated dims (2 when r <= 64).
-template <bool SWA, bool SINK, bool SPLIT, int ROT>
+// FP8: the caches hold e4m3 codes.
+template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
+    using elem_t = std::conditional_t<FP8, uint8_t, uint16_t>;
+    using kreg_t = std::conditional_t<FP8, u32x2, u32x4>;   // 8 K elements
+    constexpr int EB = sizeof(elem_t);
+    constexpr int VPL = 16 / EB;                             // V elements per 16-byte load
+    constexpr int VREG = TILE * DV / VPL / 64;               // V loads per lane per tile (8 or 4)
+    constexpr int VCH = DV / VPL;                            // 16-byte chunks per V row
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -86,8 +103,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     const int G = a.Hq / a.Hkv;
     const int k_begin = s * a.chunk;
     const int64_t cache_row0 = ((int64_t)b * a.Hkv + g) * a.cap;
-    const uint16_t* kc = a.k_cache + cache_row0 * DQK;
-    const uint16_t* vc = a.v_cache + cache_row0 * DV;
+    elem_t* const kc = (elem_t*)a.k_cache + cache_row0 * DQK;
+    elem_t* const vc = (elem_t*)a.v_cache + cache_row0 * DV;
 
     // ---- slot loads into registers, one tile ahead of the one being computed, as buffer loads:
     //      one resource per cache slice, a per-lane byte offset computed once, the tile's slot in
@@ -95,28 +112,42 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     //      Slots at or past the capacity read zeros (the resource's bound); slots past the
     //      visible range and the new token's slot are fixed up when used.
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.cap * (DQK * 2), kBufferFormat);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.cap * (DQK * EB), kBufferFormat);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, a.cap * (DV * 2), kBufferFormat);
-    const int k_lane = (l16 * DQK + 8 * gq) * 2;
-    const int v_lane = ((lane >> 4) * DV + (lane & 15) * 8) * 2;
-    u32x4 kA[KREG], vA[VREG];
-    auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
+        __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, a.cap * (DV * EB), kBufferFormat);
+    const int k_lane = (l16 * DQK + 8 * gq) * EB;
+    // (V: lane holds row (lane + 64 it) / VCH of the tile, chunk (lane + 64 it) % VCH)
+    const int v_lane = ((lane / VCH) * DV + (lane % VCH) * VPL) * EB;
+    kreg_t kA[KREG];
+    u32x4 vA[VREG];
+    auto fetch = [&](kreg_t (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int c = 0; c < DQK / 32; ++c)
-                kr[kb * (DQK / 32) + c] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + 64 * c,
-                                                                 (t0 + kb * 16) * (DQK * 2), 0));
+            for (int c = 0; c < DQK / 32; ++c) {
+                if constexpr (FP8)
+                    kr[kb * (DQK / 32) + c] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(krs, k_lane + 32 * c,
+                                                                    (t0 + kb * 16) * DQK, 0));
+                else
+                    kr[kb * (DQK / 32) + c] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + 64 * c,
+                                                                     (t0 + kb * 16) * (DQK * 2), 0));
+            }
         }
-        // (V row e/16 of the tile, chunk e%16, e = lane + 64 it: 4 rows per instruction)
+        // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16)
 #pragma unroll
-        for (int it = 0; it < VREG; ++it)
-            vr[it] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           vrs, v_lane + (it & 3) * 4 * (DV * 2),
-                           t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2), 0));
+        for (int it = 0; it < VREG; ++it) {
+            if constexpr (FP8)
+                vr[it] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane,
+                                                                 t0 * DV + it * (64 / VCH) * DV, 0));
+            else
+                vr[it] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               vrs, v_lane + (it & 3) * 4 * (DV * 2),
+                               t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2), 0));
+        }
     };
     // ---- every load that does not depend on the position goes out first, unconditionally (a
     //      load under a branch would be waited for at the branch's end): this lane's query chunks
@@ -194,15 +225,34 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         Qb[c] = as_bf16x8(c < ROT ? rotate8_cs(qraw[c], qpar[c], 32 * c + 8 * gq, half, r, sm.cs)
                                   : qraw[c]);
     // ---- the new token: rotate, keep in LDS, append to the cache (the owning split only).
+    //      An fp8 cache stores (and the tile loop reads) its codes.
+    elem_t* const Kn = (elem_t*)sm.Kn;
+    elem_t* const Vn = (elem_t*)sm.Vn;
     if (own_new) {
         if (tid < DQK / 8) {
-            const u32x4 wv = rotate8_cs(nraw, npar, nd0, half, r, sm.cs);
-            *(u32x4*)(sm.Kn + nd0) = wv;
-            *(u32x4*)(a.k_cache + (cache_row0 + slot_new) * DQK + nd0) = wv;
+            if constexpr (FP8) {
+                float x[8];
+                rotate8_cs_f32(nraw, npar, nd0, half, r, sm.cs, x);
+                const u32x2 code = e4m3x8_from_f32(x, a.k_inv);
+                *(u32x2*)(Kn + nd0) = code;
+                *(u32x2*)(kc + slot_new * DQK + nd0) = code;
+            } else {
+                const u32x4 wv = rotate8_cs(nraw, npar, nd0, half, r, sm.cs);
+                *(u32x4*)(Kn + nd0) = wv;
+                *(u32x4*)(kc + slot_new * DQK + nd0) = wv;
+            }
         } else if (tid < DQK / 8 + DV / 8) {
             const int d0 = (tid - DQK / 8) * 8;
-            *(u32x4*)(sm.Vn + d0) = nraw;
-            *(u32x4*)(a.v_cache + (cache_row0 + slot_new) * DV + d0) = nraw;
+            if constexpr (FP8) {
+                float x[8];
+                unpack8(nraw, x);
+                const u32x2 code = e4m3x8_from_f32(x, a.v_inv);
+                *(u32x2*)(Vn + d0) = code;
+                *(u32x2*)(vc + slot_new * DV + d0) = code;
+            } else {
+                *(u32x4*)(Vn + d0) = nraw;
+                *(u32x4*)(vc + slot_new * DV + d0) = nraw;
+            }
         }
         block_sync_lds();
     }
@@ -216,29 +266,36 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 
     // consume the tile held in (kr, vr) at slot t, refilling the registers with the next tile as
     // soon as the scores are formed
-    auto consume = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
+    auto consume = [&](kreg_t (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
         if (own_new && slot_new >= t && slot_new < t + TILE) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (t + kb * 16 + l16 == slot_new) {
 #pragma unroll
                     for (int c = 0; c < DQK / 32; ++c)
-                        kr[kb * (DQK / 32) + c] = *(const u32x4*)(sm.Kn + 32 * c + 8 * gq);
+                        kr[kb * (DQK / 32) + c] = *(const kreg_t*)(Kn + 32 * c + 8 * gq);
                 }
 #pragma unroll
             for (int it = 0; it < VREG; ++it) {
                 const int e = lane + 64 * it;
-                if (t + e / (DV / 8) == slot_new) vr[it] = *(const u32x4*)(sm.Vn + (e % (DV / 8)) * 8);
+                if (t + e / VCH == slot_new) vr[it] = *(const u32x4*)(Vn + (e % VCH) * VPL);
             }
         }
-        // V rows -> this wave's LDS tile (rows past the visible range as zeros)
+        // V rows -> this wave's LDS tile as bf16 (rows past the visible range as zeros)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int it = 0; it < VREG; ++it) {
             const int e = lane + 64 * it;
-            const int row = e / (DV / 8);
-            *(u32x4*)(vt + row * VT_PITCH + (e % (DV / 8)) * 8) =
-                (t + row < k_end) ? vr[it] : u32x4{0u, 0u, 0u, 0u};
+            const int row = e / VCH;
+            const bool live = t + row < k_end;
+            uint16_t* dst = vt + row * VT_PITCH + (e % VCH) * VPL;
+            if constexpr (FP8) {
+                const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+                *(u32x4*)dst = live ? bf16x8_from_e4m3x8(u32x2{vr[it][0], vr[it][1]}) : z;
+                *(u32x4*)(dst + 8) = live ? bf16x8_from_e4m3x8(u32x2{vr[it][2], vr[it][3]}) : z;
+            } else {
+                *(u32x4*)dst = live ? vr[it] : u32x4{0u, 0u, 0u, 0u};
+            }
         }
         // S^T (16 slots x 16 heads) for the two 16-slot blocks of the tile
         f32x4 Sacc[2];
@@ -246,8 +303,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
             f32x4 acc = f32x4{};
 #pragma unroll
-            for (int c = 0; c < DQK / 32; ++c)
-                acc = mfma16x16x32(as_bf16x8(kr[kb * (DQK / 32) + c]), Qb[c], acc);
+            for (int c = 0; c < DQK / 32; ++c) {
+                u32x4 kw;
+                if constexpr (FP8) kw = bf16x8_from_e4m3x8(kr[kb * (DQK / 32) + c]);
+                else kw = kr[kb * (DQK / 32) + c];
+                acc = mfma16x16x32(as_bf16x8(kw), Qb[c], acc);
+            }
             Sacc[kb] = acc;
         }
         if (t + stride < k_end) fetch(kr, vr, t + stride);
@@ -409,14 +470,14 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
     o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
 }
 
-template <bool SWA, bool SINK, int ROT>
+template <bool SWA, bool SINK, int ROT, bool FP8>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
     const dim3 grid(a.nsplit, a.Hkv, a.B);
     if (a.nsplit == 1) {
-        decode_bf16_kernel<SWA, SINK, false, ROT><<<grid, 256, 0, st>>>(a);
+        decode_bf16_kernel<SWA, SINK, false, ROT, FP8><<<grid, 256, 0, st>>>(a);
         return hipGetLastError();
     }
-    decode_bf16_kernel<SWA, SINK, true, ROT><<<grid, 256, 0, st>>>(a);
+    decode_bf16_kernel<SWA, SINK, true, ROT, FP8><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     decode_combine_kernel<SWA, SINK><<<dim3(a.Hq, a.B), DV, 0, st>>>(a);
@@ -427,15 +488,20 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
 
 int decode_max_splits() { return 1024; }
 
+template <bool FP8>
+hipError_t launch_kind(const DecodeArgs& a, bool swa, bool sink, hipStream_t st) {
+    if (a.rope_dims <= 64) {
+        if (swa) return sink ? launch_typed<true, true, 2, FP8>(a, st) : launch_typed<true, false, 2, FP8>(a, st);
+        return sink ? launch_typed<false, true, 2, FP8>(a, st) : launch_typed<false, false, 2, FP8>(a, st);
+    }
+    if (swa) return sink ? launch_typed<true, true, 6, FP8>(a, st) : launch_typed<true, false, 6, FP8>(a, st);
+    return sink ? launch_typed<false, true, 6, FP8>(a, st) : launch_typed<false, false, 6, FP8>(a, st);
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st) {
     if (a.B == 0) return hipSuccess;
     if (a.nsplit > decode_max_splits()) return hipErrorInvalidConfiguration;
-    if (a.rope_dims <= 64) {
-        if (swa) return sink ? launch_typed<true, true, 2>(a, st) : launch_typed<true, false, 2>(a, st);
-        return sink ? launch_typed<false, true, 2>(a, st) : launch_typed<false, false, 2>(a, st);
-    }
-    if (swa) return sink ? launch_typed<true, true, 6>(a, st) : launch_typed<true, false, 6>(a, st);
-    return sink ? launch_typed<false, true, 6>(a, st) : launch_typed<false, false, 6>(a, st);
+    return a.cache_fp8 ? launch_kind<true>(a, swa, sink, st) : launch_kind<false>(a, swa, sink, st);
 }
 
 }  // namespace mimo

@@ -132,6 +132,36 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
     return w;
 }
 
+// fp8 KV cache elements: OCP e4m3 codes (the format of gfx950's fp8 conversions).
+// Eight fp32 values times inv, clamped to +-448 (saturation instead of NaN), to their nearest
+// codes (ties to even), packed low byte first.
+__device__ __forceinline__ u32x2 e4m3x8_from_f32(const float* x, float inv) {
+    u32x2 w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(x[4 * h + t] * inv, -448.0f), 448.0f);
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
+        w[h] = (uint32_t)v;
+    }
+    return w;
+}
+
+// Eight e4m3 codes (low byte first) to their exact bf16 values.
+__device__ __forceinline__ u32x4 bf16x8_from_e4m3x8(const u32x2& w) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        r[2 * h] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, false));
+        r[2 * h + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, true));
+    }
+    return r;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
     return __builtin_bit_cast(bf16x8, w);
 }

@@ -25,6 +25,8 @@ struct RopeKVArgs {
     void* v_dst;         // [B,Hkv,cap,dv], set iff k_dst is
     int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, cache_i0, ring_window;
     int32_t ws_rows, ws_row0, max_start;
+    int32_t cache_fp8;   // caches hold e4m3 codes of x * k_inv / v_inv (bf16 kernel only)
+    float k_inv, v_inv;
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
@@ -69,12 +71,14 @@ struct DecodeArgs {
     const uint16_t* k_new;   // [B,Hkv,192]
     const uint16_t* v_new;   // [B,Hkv,128]
     const int32_t* positions;
-    uint16_t* k_cache;       // [B,Hkv,cap,192]
-    uint16_t* v_cache;       // [B,Hkv,cap,128]
+    void* k_cache;           // [B,Hkv,cap,192] bf16, or e4m3 codes (cache_fp8)
+    void* v_cache;           // [B,Hkv,cap,128] bf16, or e4m3 codes (cache_fp8)
     const float* sinks;
     uint16_t* out;           // [B,Hq,128]
     float* partial;          // [B,Hq,nsplit,130] (split mode)
     int32_t B, Hq, Hkv, rope_dims, window, cap, max_position, chunk, nsplit;
+    int32_t cache_fp8;       // caches hold e4m3 codes: the new token is coded with k_inv/v_inv;
+    float k_inv, v_inv;      // the code scales are folded into score_scale_log2 and v_scale
     float score_scale_log2;
     float v_scale;
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)

@@ -46,15 +46,17 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
         const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
         const int64_t ws_row = ((int64_t)b * a.Hkv + g) * a.ws_rows + a.ws_row0 + i;
+        const int64_t slot_row = ((int64_t)b * a.Hkv + g) * a.cap + slot;
         if (c < kch) {
             const uint16_t* krow = (const uint16_t*)a.k + src_row * a.dqk;
             const int d0 = c * 8;
             u32x4 w = *(const u32x4*)(krow + d0);
+            float x[8];
+            unpack8(w, x);
             if (d0 < r) {
                 const int pd = d0 < half ? d0 + half : d0 - half;
                 const u32x4 pw = *(const u32x4*)(krow + pd);
-                float x[8], y[8];
-                unpack8(w, x);
+                float y[8];
                 unpack8(pw, y);
                 const bool lower = d0 < half;
                 const int f0 = lower ? d0 : d0 - half;
@@ -67,14 +69,26 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
                 w = pack8(x);
             }
             if (a.k_ws) *(u32x4*)((uint16_t*)a.k_ws + ws_row * a.dqk + d0) = w;
-            if (slot >= 0)
-                *(u32x4*)((uint16_t*)a.k_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dqk + d0) = w;
+            if (slot >= 0) {
+                // (an fp8 cache codes the fp32 rotated key, not its bf16 rounding)
+                if (a.cache_fp8)
+                    *(u32x2*)((uint8_t*)a.k_dst + slot_row * a.dqk + d0) = e4m3x8_from_f32(x, a.k_inv);
+                else
+                    *(u32x4*)((uint16_t*)a.k_dst + slot_row * a.dqk + d0) = w;
+            }
         } else if (slot >= 0 || a.v_ws) {
             const int d0 = (c - kch) * 8;
             const u32x4 w = *(const u32x4*)((const uint16_t*)a.v + src_row * a.dv + d0);
             if (a.v_ws) *(u32x4*)((uint16_t*)a.v_ws + ws_row * a.dv + d0) = w;
-            if (slot >= 0)
-                *(u32x4*)((uint16_t*)a.v_dst + (((int64_t)b * a.Hkv + g) * a.cap + slot) * a.dv + d0) = w;
+            if (slot >= 0) {
+                if (a.cache_fp8) {
+                    float x[8];
+                    unpack8(w, x);
+                    *(u32x2*)((uint8_t*)a.v_dst + slot_row * a.dv + d0) = e4m3x8_from_f32(x, a.v_inv);
+                } else {
+                    *(u32x4*)((uint16_t*)a.v_dst + slot_row * a.dv + d0) = w;
+                }
+            }
         }
     }
 }

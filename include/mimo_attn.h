@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 1
+#define MIMO_ATTN_ABI_VERSION 2
 
 enum mimo_attn_status {
     MIMO_OK = 0,
@@ -62,6 +62,12 @@ enum mimo_attn_layer_kind { /* the value of hybrid_layer_pattern[layer] */
 
 enum mimo_attn_dtype { MIMO_F32 = 0, MIMO_BF16 = 1 };
 
+/* Element type of the KV caches (params.cache_dtype). */
+enum mimo_attn_cache_dtype {
+    MIMO_CACHE_SAME = 0,     /* the layer dtype (bf16 or fp32 caches)                        */
+    MIMO_CACHE_FP8_E4M3 = 2  /* one-byte OCP e4m3 codes with one fp32 scale per cache tensor */
+};
+
 typedef struct mimo_attn_params {
     int32_t batch;         /* B >= 0 (0: nothing to do)                                      */
     int32_t num_q_heads;   /* Hq >= 1                                                        */
@@ -75,7 +81,9 @@ typedef struct mimo_attn_params {
     float v_scale;         /* multiplies the output; sqrt(hidden / (Hq * dv)) in the model   */
     float softmax_scale;   /* 0 selects 1 / sqrt(dqk)                                        */
     int32_t dtype;         /* MIMO_BF16 or MIMO_F32                                          */
-    int32_t reserved;      /* must be 0                                                      */
+    int32_t cache_dtype;   /* MIMO_CACHE_SAME or MIMO_CACHE_FP8_E4M3 (bf16 layers)           */
+    float k_cache_scale;   /* fp8 caches: stored key = e4m3(code) * k_cache_scale (> 0)      */
+    float v_cache_scale;   /* fp8 caches: stored value = e4m3(code) * v_cache_scale (> 0)    */
 } mimo_attn_params;
 
 /*
@@ -83,6 +91,16 @@ typedef struct mimo_attn_params {
  * the head shape of both layer kinds at full size.  MIMO_F32 runs fp32 vector kernels for any
  * dqk <= 256 and dv <= 256 (used for small fp32 layers).  Other combinations return
  * MIMO_ERR_UNSUPPORTED.
+ *
+ * fp8 KV caches (cache_dtype MIMO_CACHE_FP8_E4M3, bf16 layers; the pages only hint at quantized
+ * storage — "Add Xiaomi MiMo-V2", "Additional useful info", a garbled note of three dtypes with one
+ * quantized — and this is the reading taken): the caches are uint8 arrays of OCP e4m3 codes
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals; 0x7F/0xFF NaN; largest finite
+ * 448) with the shapes of the bf16 caches.  A stored element is written as the e4m3 value nearest
+ * (ties to even) to clamp(x * (1 / scale), -448, 448), x the fp32 rotated key or the value, the
+ * product and 1 / scale in fp32; it is read as e4m3(code) * scale.  Prefill and decode support
+ * fp8 caches; extend returns MIMO_ERR_UNSUPPORTED for them.  Decode attends the new token with its
+ * stored (coded) value, like every other cached token.
  */
 
 /*

@@ -90,6 +90,24 @@ def cache_contents(w: Workload, seed: int, batch: int, cache_capacity: int, devi
     return k_cache, v_cache
 
 
+# fp8 cache scales of the synthetic fp8 workloads (the stored values come out about N(0,1))
+FP8_K_SCALE, FP8_V_SCALE = 1.0 / 16.0, 1.0 / 8.0
+
+
+def fp8_cache_contents(w: Workload, seed: int, batch: int, cache_capacity: int, device="cpu",
+                       k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_SCALE):
+    """fp8 cache contents as uint8 e4m3 codes [B,Hkv,cap,dqk] / [B,Hkv,cap,dv]: N(0,1) draws
+    divided by the scale, turned into codes by torch's float8_e4m3fn conversion (random codes whose
+    stored values are about N(0,1); any code pattern is a valid cache state)."""
+    g = _gen(seed, device)
+    k = torch.randn((batch, w.num_kv_heads, cache_capacity, w.qk_head_dim), generator=g,
+                    dtype=torch.float32, device=device) / k_scale
+    v = torch.randn((batch, w.num_kv_heads, cache_capacity, w.v_head_dim), generator=g,
+                    dtype=torch.float32, device=device) / v_scale
+    code = lambda t: t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return code(k), code(v)
+
+
 def decode_lengths(seed: int, batch: int = DECODE_BATCH, lo: int = DECODE_MIN_LEN,
                    hi: int = DECODE_MAX_LEN) -> torch.Tensor:
     """Tokens already cached per sequence, uniform in [lo, hi] inclusive (host int32)."""

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mimo_attn.h but not exported"
     assert set(names) == set(binding.EXPORTS)
-    assert mimo.lib().mimo_attn_abi_version() == 1
+    assert mimo.lib().mimo_attn_abi_version() == 2
 
 
 def _swa(**kw):
@@ -77,11 +77,29 @@ def test_invalid_params_rejected_with_code_and_message(p, code):
     assert mimo.last_error() != ""
 
 
-def test_reserved_field_must_be_zero():
+def test_cache_dtype_and_scales_are_checked():
+    fp8 = dict(cache_dtype=mimo.CACHE_FP8_E4M3, k_cache_scale=0.05, v_cache_scale=2.0)
+    assert mimo.check_params(_swa(**fp8)) == mimo.MIMO_OK
+    assert mimo.check_params(_ga(**fp8)) == mimo.MIMO_OK
     cp = _swa().c()
-    cp.reserved = 1
+    cp.cache_dtype = 1
     assert mimo.lib().mimo_attn_check_params(ctypes.byref(cp)) == mimo.MIMO_ERR_INVALID_ARG
     assert mimo.lib().mimo_attn_check_params(None) == mimo.MIMO_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert mimo.check_params(_swa(**dict(fp8, k_cache_scale=bad))) == mimo.MIMO_ERR_INVALID_ARG
+        assert mimo.check_params(_swa(**dict(fp8, v_cache_scale=bad))) == mimo.MIMO_ERR_INVALID_ARG
+    # scales are ignored for caches of the layer dtype
+    assert mimo.check_params(_swa(k_cache_scale=0.0)) == mimo.MIMO_OK
+    # fp8 caches belong to bf16 layers
+    assert mimo.check_params(_swa(dtype=mimo.F32, qk_head_dim=32, v_head_dim=16, rope_dims=10,
+                                  num_q_heads=4, num_kv_heads=1, window=16, **fp8)) == \
+        mimo.MIMO_ERR_UNSUPPORTED
+    # extend does not read fp8 caches
+    assert _extend(_swa(**fp8)) == mimo.MIMO_ERR_UNSUPPORTED
+    # an fp8 cache slice may be twice as long as a bf16 one under the 4 GiB bound
+    # (passes the bound, then stops at the missing workspace: nothing is launched)
+    assert _decode(_ga(**fp8), maxp=100_000, cap=12_000_000, ws=None) == mimo.MIMO_ERR_WORKSPACE
+    assert _decode(_ga(**fp8), maxp=10, cap=23_000_000) == mimo.MIMO_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes():
