@@ -136,7 +136,8 @@ size_t extend_ws(const mimo_attn_params* p, int32_t S) {
 //    round, at least 128 slots each (one 32-slot tile per wave), rounded up to whole tiles — a
 //    second, mostly idle round would cost as much as the first;
 //  * otherwise a power of two >= 256, large enough to keep the grid (B * Hkv * splits) within 8192
-//    workgroups and the splits per sequence within what the combine kernel merges.
+//    workgroups and the splits per sequence within what the combine kernel merges; fp8 caches
+//    (half the bytes per slot) take twice the slots per split and half the grid.
 constexpr int64_t kResidentDecodeGroups = 512;
 
 int decode_chunk(const mimo_attn_params* p, int32_t max_position) {
@@ -152,8 +153,9 @@ int decode_chunk(const mimo_attn_params* p, int32_t max_position) {
         const int64_t chunk = ((n_max + ns - 1) / ns + 31) / 32 * 32;
         return (int)chunk;
     }
-    int64_t chunk = 256;
-    while (pairs * ((n_max + chunk - 1) / chunk) > 8192 ||
+    const bool fp8 = fp8_cache(p);
+    int64_t chunk = fp8 ? 512 : 256;
+    while (pairs * ((n_max + chunk - 1) / chunk) > (fp8 ? 4096 : 8192) ||
            (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
         chunk *= 2;
     return (int)chunk;

@@ -38,7 +38,7 @@ constexpr int NW = 4;
 constexpr int TILE = 32;                 // slots per wave iteration
 constexpr int PSTRIDE = DV + 2;          // floats per partial record: O[128], m, l
 constexpr int VT_PITCH = DV + 16;        // bf16 per V row in the per-wave LDS tile (288 bytes)
-constexpr int KREG = 2 * (DQK / 32);     // K operand loads per lane per tile (12; 8 elements each)
+
 constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merge buffer
 
 // Rotate 8 consecutive dims d0.. of a row (w) against their partners (pw) with the cos/sin of the
@@ -90,8 +90,11 @@ template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
     using elem_t = std::conditional_t<FP8, uint8_t, uint16_t>;
-    using kreg_t = std::conditional_t<FP8, u32x2, u32x4>;   // 8 K elements
     constexpr int EB = sizeof(elem_t);
+    // K: 16-byte loads per lane per tile (two 16-slot blocks x 6 bf16 chunks of 8 dims, or
+    // x 3 fp8 chunks of 16 dims; either way a load instruction reads 64 contiguous bytes of each
+    // of 16 slots)
+    constexpr int KREG = FP8 ? 2 * (DQK / 64) : 2 * (DQK / 32);
     constexpr int VPL = 16 / EB;                             // V elements per 16-byte load
     constexpr int VREG = TILE * DV / VPL / 64;               // V loads per lane per tile (8 or 4)
     constexpr int VCH = DV / VPL;                            // 16-byte chunks per V row
@@ -115,25 +118,18 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.cap * (DQK * EB), kBufferFormat);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, a.cap * (DV * EB), kBufferFormat);
-    const int k_lane = (l16 * DQK + 8 * gq) * EB;
+    const int k_lane = (l16 * DQK + (FP8 ? 16 : 8) * gq) * EB;
     // (V: lane holds row (lane + 64 it) / VCH of the tile, chunk (lane + 64 it) % VCH)
     const int v_lane = ((lane / VCH) * DV + (lane % VCH) * VPL) * EB;
-    kreg_t kA[KREG];
-    u32x4 vA[VREG];
-    auto fetch = [&](kreg_t (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
+    u32x4 kA[KREG], vA[VREG];
+    auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int c = 0; c < DQK / 32; ++c) {
-                if constexpr (FP8)
-                    kr[kb * (DQK / 32) + c] = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(krs, k_lane + 32 * c,
-                                                                    (t0 + kb * 16) * DQK, 0));
-                else
-                    kr[kb * (DQK / 32) + c] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + 64 * c,
-                                                                     (t0 + kb * 16) * (DQK * 2), 0));
-            }
+            for (int c = 0; c < KREG / 2; ++c)
+                kr[kb * (KREG / 2) + c] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + 64 * c,
+                                                                 (t0 + kb * 16) * (DQK * EB), 0));
         }
         // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16)
 #pragma unroll
@@ -157,12 +153,17 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     //      first slot tile.
     const int r = a.rope_dims, half = r >> 1;
     const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + min(l16, G - 1)) * DQK;
+    // Dims of MFMA k-chunk c held by lane group gq: 32c + 8gq.. for bf16 caches; for fp8 caches
+    // 64(c/2) + 16gq + 8(c%2).., the order in which one 16-byte load of 16 key codes splits into
+    // two chunks (the dot product does not depend on how its dims are ordered, as long as keys
+    // and queries agree; chunks 0 and 1 still hold dims 0..63)
+    auto qdim = [&](int c) { return FP8 ? 64 * (c >> 1) + 16 * gq + 8 * (c & 1) : 32 * c + 8 * gq; };
     u32x4 qraw[DQK / 32], qpar[ROT];
 #pragma unroll
-    for (int c = 0; c < DQK / 32; ++c) qraw[c] = *(const u32x4*)(qrow + 32 * c + 8 * gq);
+    for (int c = 0; c < DQK / 32; ++c) qraw[c] = *(const u32x4*)(qrow + qdim(c));
 #pragma unroll
     for (int c = 0; c < ROT; ++c) {
-        const int d0 = 32 * c + 8 * gq;
+        const int d0 = qdim(c);
         qpar[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : (d0 < r ? d0 - half : d0)));
     }
     const int64_t kv_row = (int64_t)b * a.Hkv + g;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     bf16x8 Qb[DQK / 32];
 #pragma unroll
     for (int c = 0; c < DQK / 32; ++c)
-        Qb[c] = as_bf16x8(c < ROT ? rotate8_cs(qraw[c], qpar[c], 32 * c + 8 * gq, half, r, sm.cs)
+        Qb[c] = as_bf16x8(c < ROT ? rotate8_cs(qraw[c], qpar[c], qdim(c), half, r, sm.cs)
                                   : qraw[c]);
     // ---- the new token: rotate, keep in LDS, append to the cache (the owning split only).
     //      An fp8 cache stores (and the tile loop reads) its codes.
@@ -266,14 +267,15 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 
     // consume the tile held in (kr, vr) at slot t, refilling the registers with the next tile as
     // soon as the scores are formed
-    auto consume = [&](kreg_t (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
+    auto consume = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
         if (own_new && slot_new >= t && slot_new < t + TILE) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (t + kb * 16 + l16 == slot_new) {
 #pragma unroll
-                    for (int c = 0; c < DQK / 32; ++c)
-                        kr[kb * (DQK / 32) + c] = *(const kreg_t*)(Kn + 32 * c + 8 * gq);
+                    for (int c = 0; c < KREG / 2; ++c)
+                        kr[kb * (KREG / 2) + c] =
+                            *(const u32x4*)(Kn + (FP8 ? 16 : 8) * gq + (64 / EB) * c);
                 }
 #pragma unroll
             for (int it = 0; it < VREG; ++it) {
@@ -305,8 +307,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < DQK / 32; ++c) {
                 u32x4 kw;
-                if constexpr (FP8) kw = bf16x8_from_e4m3x8(kr[kb * (DQK / 32) + c]);
-                else kw = kr[kb * (DQK / 32) + c];
+                if constexpr (FP8) {
+                    const u32x4& w = kr[kb * (KREG / 2) + (c >> 1)];
+                    kw = bf16x8_from_e4m3x8((c & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+                } else {
+                    kw = kr[kb * (KREG / 2) + c];
+                }
                 acc = mfma16x16x32(as_bf16x8(kw), Qb[c], acc);
             }
             Sacc[kb] = acc;
