@@ -430,7 +430,8 @@ def single_layer(args, dev):
                             w.window, w.rope_theta, w.v_scale)
             sp = torch.tensor(starts, dtype=torch.int32, device=dev)
             out = torch.empty((B, S, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(mimo.extend_workspace_size(p, S) + 256, dtype=torch.uint8, device=dev)
+            ws = torch.empty(mimo.extend_workspace_size(p, S, max(starts)) + 256, dtype=torch.uint8,
+                             device=dev)
             # the same call repeated: the new tokens' slots are rewritten with the same values
             ms = timed(lambda: mimo.extend(p, q, k, v, sp, max(starts), kc, vc, sinks=s, out=out,
                                            workspace=ws), args.steps)

@@ -94,7 +94,7 @@ def lib(path: str = LIB_PATH):
             L.mimo_attn_extend.argtypes = [P, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, sz,
                                            vp]
             L.mimo_attn_extend.restype = ctypes.c_int
-            L.mimo_attn_extend_workspace_size.argtypes = [P, i32]
+            L.mimo_attn_extend_workspace_size.argtypes = [P, i32, i32]
             L.mimo_attn_extend_workspace_size.restype = sz
             L.mimo_attn_decode.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
             L.mimo_attn_decode.restype = ctypes.c_int
@@ -129,9 +129,9 @@ def prefill_workspace_size(p: Params, seq_len: int) -> int:
     return int(lib().mimo_attn_prefill_workspace_size(ctypes.byref(cp), seq_len))
 
 
-def extend_workspace_size(p: Params, seq_len: int) -> int:
+def extend_workspace_size(p: Params, seq_len: int, max_start: int) -> int:
     cp = p.c()
-    return int(lib().mimo_attn_extend_workspace_size(ctypes.byref(cp), seq_len))
+    return int(lib().mimo_attn_extend_workspace_size(ctypes.byref(cp), seq_len, max_start))
 
 
 def decode_workspace_size(p: Params, max_position: int) -> int:
@@ -229,7 +229,7 @@ def extend(p: Params, q, k, v, start_pos, max_start: int, k_cache, v_cache, sink
     cap = k_cache.shape[2]
     _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), _cdtype(p), dev)
     _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), _cdtype(p), dev)
-    need = extend_workspace_size(p, S)
+    need = extend_workspace_size(p, S, max_start)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

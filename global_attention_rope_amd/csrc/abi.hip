@@ -121,14 +121,6 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
     return (size_t)p->batch * p->num_kv_heads * (size_t)S * p->qk_head_dim * 2;
 }
 
-// bf16 extend of a sliding layer lays out [B, Hkv, window + S] rotated K and V rows: the ring's
-// content in position order, then the new tokens.  Global layers attend straight from the cache.
-size_t extend_ws(const mimo_attn_params* p, int32_t S) {
-    if (p->dtype != MIMO_BF16 || p->layer_kind != MIMO_LAYER_SWA) return 0;
-    return (size_t)p->batch * p->num_kv_heads * ((size_t)p->window + S) *
-           (p->qk_head_dim + p->v_head_dim) * 2;
-}
-
 // Decode split size: slots per workgroup.
 //  * a sliding ring of at most 1024 slots is one split;
 //  * a small grid (at most two rounds of 256-slot splits on the chip, which holds 512 resident
@@ -140,40 +132,87 @@ size_t extend_ws(const mimo_attn_params* p, int32_t S) {
 //    (half the bytes per slot) take twice the slots per split and half the grid.
 constexpr int64_t kResidentDecodeGroups = 512;
 
-int decode_chunk(const mimo_attn_params* p, int32_t max_position) {
-    const int64_t n_max = p->layer_kind == MIMO_LAYER_SWA
-                              ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
-                              : (int64_t)max_position + 1;
-    if (p->layer_kind == MIMO_LAYER_SWA && n_max <= 1024) return n_max < 1 ? 1 : (int)n_max;
-    const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
+// Split size (key rows per workgroup) for n_max key rows per query and `pairs` (query block, KV
+// head) pairs; `one_split_upto`: a key range up to this many rows is never split.
+int64_t chunk_policy(int64_t n_max, int64_t pairs, int64_t one_split_upto, bool fp8) {
+    if (n_max <= one_split_upto) return n_max < 1 ? 1 : n_max;
     if (pairs * ((n_max + 255) / 256) <= 2 * kResidentDecodeGroups) {
         int64_t ns = kResidentDecodeGroups / pairs;
         if (ns < 1) ns = 1;
         if (ns > (n_max + 127) / 128) ns = (n_max + 127) / 128;
-        const int64_t chunk = ((n_max + ns - 1) / ns + 31) / 32 * 32;
-        return (int)chunk;
+        return ((n_max + ns - 1) / ns + 31) / 32 * 32;
     }
-    const bool fp8 = fp8_cache(p);
     int64_t chunk = fp8 ? 512 : 256;
     while (pairs * ((n_max + chunk - 1) / chunk) > (fp8 ? 4096 : 8192) ||
            (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
         chunk *= 2;
-    return (int)chunk;
+    return chunk;
 }
 
-int decode_nsplit(const mimo_attn_params* p, int32_t max_position) {
-    const int64_t n_max = p->layer_kind == MIMO_LAYER_SWA
-                              ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
+struct SplitGeometry {
+    int64_t n_max;   // key rows of the longest query
+    int chunk, nsplit;
+};
+
+SplitGeometry split_geometry(int64_t n_max, int64_t pairs, int64_t one_split_upto, bool fp8) {
+    SplitGeometry g;
+    g.n_max = n_max;
+    g.chunk = (int)chunk_policy(n_max, pairs, one_split_upto, fp8);
+    g.nsplit = (int)((n_max + g.chunk - 1) / g.chunk);
+    return g;
+}
+
+// Decode: keys 0..max_position (linear) or the window's slots (ring, never split up to 1024).
+SplitGeometry decode_geometry(const mimo_attn_params* p, int32_t max_position) {
+    const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    const int64_t n_max = swa ? (int64_t)(p->window < max_position + 1 ? p->window : max_position + 1)
                               : (int64_t)max_position + 1;
-    const int chunk = decode_chunk(p, max_position);
-    return (int)((n_max + chunk - 1) / chunk);
+    return split_geometry(n_max, (int64_t)p->batch * p->num_kv_heads, swa ? 1024 : 0,
+                          fp8_cache(p));
+}
+
+size_t partials_bytes(const mimo_attn_params* p, int64_t queries, int nsplit) {
+    if (nsplit <= 1) return 0;
+    return (size_t)queries * p->num_q_heads * (size_t)nsplit * (p->v_head_dim + 2) * sizeof(float);
 }
 
 size_t decode_ws(const mimo_attn_params* p, int32_t max_position) {
     if (p->dtype != MIMO_BF16) return 0;
-    const int ns = decode_nsplit(p, max_position);
-    if (ns <= 1) return 0;
-    return (size_t)p->batch * p->num_q_heads * (size_t)ns * (p->v_head_dim + 2) * sizeof(float);
+    return partials_bytes(p, p->batch, decode_geometry(p, max_position).nsplit);
+}
+
+// Extend of at most this many new tokens per sequence runs the decode kernels in their
+// multi-token mode (one query block per token, no tile of mostly idle query rows).
+constexpr int kVerifyMaxTokens = 16;
+
+bool verify_tokens(const mimo_attn_params* p, int32_t S) {
+    return S >= 1 && S <= kVerifyMaxTokens && (int64_t)p->batch * S <= 65535;   // (grid z)
+}
+
+// Multi-token extend: key rows of the longest query — global: positions 0..max_start + S - 1
+// of the cache; sliding: the W + S rows of the workspace (never split up to 1024 rows).
+SplitGeometry verify_geometry(const mimo_attn_params* p, int32_t S, int32_t max_start) {
+    const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    const int64_t n_max = swa ? (int64_t)p->window + S : (int64_t)max_start + S;
+    return split_geometry(n_max, (int64_t)p->batch * S * p->num_kv_heads, swa ? 1024 : 0, false);
+}
+
+// bf16 extend workspace: sliding layers lay out [B, Hkv, window + S] rotated K and V rows (the
+// ring's content in position order, then the new tokens); global layers attend straight from
+// the cache.  A multi-token extend adds its split partials (256-byte aligned).
+size_t extend_rows_ws(const mimo_attn_params* p, int32_t S) {
+    if (p->dtype != MIMO_BF16 || p->layer_kind != MIMO_LAYER_SWA) return 0;
+    const size_t b = (size_t)p->batch * p->num_kv_heads * ((size_t)p->window + S) *
+                     (p->qk_head_dim + p->v_head_dim) * 2;
+    return (b + 255) / 256 * 256;
+}
+
+size_t extend_ws(const mimo_attn_params* p, int32_t S, int32_t max_start) {
+    if (p->dtype != MIMO_BF16) return 0;
+    size_t n = extend_rows_ws(p, S);
+    if (verify_tokens(p, S))
+        n += partials_bytes(p, (int64_t)p->batch * S, verify_geometry(p, S, max_start).nsplit);
+    return n;
 }
 
 }  // namespace
@@ -194,9 +233,10 @@ size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_l
     return prefill_ws(p, seq_len);
 }
 
-size_t mimo_attn_extend_workspace_size(const mimo_attn_params* p, int32_t seq_len) {
-    if (check(p) != MIMO_OK || seq_len < 0) return 0;
-    return extend_ws(p, seq_len);
+size_t mimo_attn_extend_workspace_size(const mimo_attn_params* p, int32_t seq_len,
+                                       int32_t max_start) {
+    if (check(p) != MIMO_OK || seq_len < 0 || max_start < 0) return 0;
+    return extend_ws(p, seq_len, max_start);
 }
 
 size_t mimo_attn_decode_workspace_size(const mimo_attn_params* p, int32_t max_position) {
@@ -348,7 +388,7 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
                     "q, k, v, start_pos, out, k_cache and v_cache must be non-NULL");
     if ((int64_t)seq_len * p->num_q_heads * p->batch > ((int64_t)1 << 40))
         return fail(MIMO_ERR_INVALID_ARG, "problem too large");
-    const size_t need = extend_ws(p, seq_len);
+    const size_t need = extend_ws(p, seq_len, max_start);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -440,7 +480,38 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     pa.v_sj = dv;
     rc = hip_status(mimo::launch_rope_kv_bf16(ra, st), "key rotation (bf16)");
     if (rc != MIMO_OK) return rc;
-    return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "extend (bf16)");
+    // (the decode kernels address a key-row slice through a 32-bit byte bound)
+    const int64_t key_rows = pa.k_sh / dqk;
+    if (!verify_tokens(p, seq_len) || key_rows * dqk * 2 > 0xffffffffLL)
+        return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "extend (bf16)");
+
+    // a few new tokens: the decode kernels' multi-token mode over the same key rows
+    const SplitGeometry geo = verify_geometry(p, seq_len, max_start);
+    mimo::DecodeArgs da;
+    memset(&da, 0, sizeof da);
+    da.q = (const uint16_t*)q;
+    da.positions = start_pos;
+    da.k_cache = (void*)pa.k;
+    da.v_cache = (void*)pa.v;
+    da.sinks = sinks;
+    da.out = (uint16_t*)out;
+    da.partial = (float*)((uint8_t*)workspace + extend_rows_ws(p, seq_len));
+    da.B = p->batch;
+    da.Hq = p->num_q_heads;
+    da.Hkv = p->num_kv_heads;
+    da.rope_dims = p->rope_dims;
+    da.window = p->window;
+    da.cap = (int32_t)key_rows;   // key rows per (sequence, KV head)
+    da.max_position = max_start;
+    da.chunk = geo.chunk;
+    da.nsplit = geo.nsplit;
+    da.q_per_seq = seq_len;
+    da.kpos_rel = pa.kpos_rel;
+    da.kpos_off = pa.kpos_off;
+    da.score_scale_log2 = pa.score_scale_log2;
+    da.v_scale = p->v_scale;
+    fill_omega(p, da.omega_rev);
+    return hip_status(mimo::launch_verify_bf16(da, swa, sinks != nullptr, st), "extend (bf16)");
 }
 
 int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,
@@ -518,8 +589,9 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
     da.window = p->window;
     da.cap = cache_capacity;
     da.max_position = max_position;
-    da.chunk = decode_chunk(p, max_position);
-    da.nsplit = decode_nsplit(p, max_position);
+    const SplitGeometry geo = decode_geometry(p, max_position);
+    da.chunk = geo.chunk;
+    da.nsplit = geo.nsplit;
     da.score_scale_log2 = score_scale(p) * 1.4426950408889634f;
     da.v_scale = p->v_scale;
     if (fp8_cache(p)) {

@@ -114,9 +114,16 @@ def test_workspace_sizes():
     assert ws > 0 and ws % (64 * 64 * 130 * 4) == 0
     assert mimo.decode_workspace_size(_ga(batch=64), 100) == 0
     # extend: sliding layers lay out window + S rows of K and V; global layers read the cache
-    assert mimo.extend_workspace_size(_swa(batch=2), 1000) == 2 * 8 * (128 + 1000) * (192 + 128) * 2
-    assert mimo.extend_workspace_size(_ga(batch=2), 1000) == 0
-    assert mimo.extend_workspace_size(_swa(), -1) == 0
+    assert mimo.extend_workspace_size(_swa(batch=2), 1000, 5000) == 2 * 8 * (128 + 1000) * (192 + 128) * 2
+    assert mimo.extend_workspace_size(_ga(batch=2), 1000, 5000) == 0
+    assert mimo.extend_workspace_size(_swa(), -1, 0) == 0
+    assert mimo.extend_workspace_size(_swa(), 4, -1) == 0
+    # a few new tokens: one query block per token, split partials for long global caches
+    assert mimo.extend_workspace_size(_ga(batch=2), 4, 100) == 0
+    ws = mimo.extend_workspace_size(_ga(batch=64), 4, 32768)
+    assert ws > 0 and ws % (64 * 4 * 64 * 130 * 4) == 0
+    rows = 8 * (128 + 4) * (192 + 128) * 2
+    assert mimo.extend_workspace_size(_swa(), 4, 30000) == (rows + 255) // 256 * 256
 
 
 _L = None

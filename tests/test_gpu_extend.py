@@ -63,6 +63,13 @@ CASES = [
     dict(kind=0, B=3, S=129, Hq=16, Hkv=1, sinks=False, starts=[0, 37, 700]),
     dict(kind=0, B=2, S=1, Hq=8, Hkv=2, sinks=True, starts=[5, 1234]),
     dict(kind=0, B=1, S=300, Hq=8, Hkv=2, sinks=False, starts=[64]),            # tile-aligned
+    # up to 16 new tokens: one query block per token (the decode kernels' multi-token mode)
+    dict(kind=1, B=3, S=4, Hq=16, Hkv=2, sinks=True, starts=[0, 2, 1000]),       # start < W
+    dict(kind=1, B=2, S=16, Hq=8, Hkv=1, sinks=True, starts=[126, 131], W=128),
+    dict(kind=1, B=2, S=7, Hq=8, Hkv=8, sinks=False, starts=[0, 9], W=1),
+    dict(kind=0, B=3, S=2, Hq=16, Hkv=1, sinks=False, starts=[0, 255, 4097]),
+    dict(kind=0, B=2, S=16, Hq=8, Hkv=2, sinks=True, starts=[1, 700]),
+    dict(kind=0, B=1, S=5, Hq=64, Hkv=4, sinks=False, starts=[20000]),           # split partials
 ]
 
 
@@ -97,11 +104,11 @@ def test_extend_against_synthetic_cache(ci):
         assert_close(kc1[b][:, tok[1]], krot[b, tok[0]].transpose(1, 0, 2), what=f"seq {b} K")
 
 
-@pytest.mark.parametrize("kind", [0, 1])
-def test_extend_skips_sequences_past_max_start(kind):
-    w = _wl(kind=kind, B=2, S=40, Hq=8, Hkv=2, sinks=kind == 1)
+@pytest.mark.parametrize("kind,S", [(0, 40), (1, 40), (0, 3), (1, 3)])
+def test_extend_skips_sequences_past_max_start(kind, S):
+    w = _wl(kind=kind, B=2, S=S, Hq=8, Hkv=2, sinks=kind == 1)
     starts, max_start = [10, 500], 100
-    _note(f"extend skip kind={kind}")
+    _note(f"extend skip kind={kind} S={S}")
     q, k, v, s = synth.layer_inputs(w, 5200 + kind, device=DEV)
     cap = w.window if kind == 1 else max_start + w.seq
     kc, vc = synth.cache_contents(w, 5300 + kind, w.batch, cap, device=DEV)
@@ -183,3 +190,27 @@ def test_extend_global_long_cache_sampled_rows():
     ref = oracle.extend(_oparams(w), _f32(q), _f32(k), _f32(v), np.array([start], np.int32), okc,
                         ovc, kpos, count, None, rows=rows)
     assert_close(out[:, rows], ref[:, rows], what="long cache")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_extend_four_tokens_batch64_full_size(kind):
+    """Four new tokens per sequence after the decode workload's cached lengths (batch 64, uniform
+    in [1024, 32768]): sampled sequences (global) or all of them (sliding) against the oracle."""
+    Hkv = 4 if kind == 0 else 8
+    w = _wl(kind=kind, B=synth.DECODE_BATCH, S=4, Hq=64, Hkv=Hkv, sinks=kind == 1)
+    starts = synth.decode_lengths(3 + kind).tolist()
+    B = len(starts)
+    cap = w.window if kind == 1 else max(starts) + w.seq
+    _note(f"extend 4 tokens B={B} kind={kind}")
+    q, k, v, s = synth.layer_inputs(w, 5700 + kind, device=DEV)
+    kc, vc = synth.cache_contents(w, 5800 + kind, B, cap, device=DEV)
+    sample = list(range(B)) if kind == 1 else sorted({int(np.argmin(starts)), int(np.argmax(starts)), 5, 17, 42})
+    pre = {b: (kc[b:b + 1].clone(), vc[b:b + 1].clone()) for b in sample}
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    out = mimo.extend(_params(w), q, k, v, sp, max(starts), kc, vc, sinks=s)
+    torch.cuda.synchronize()
+    for b in sample:
+        okc, ovc, kpos, count = _oracle_cache(w, pre[b][0], pre[b][1], [starts[b]])
+        ref = oracle.extend(_oparams(w, batch=1), _f32(q[b:b + 1]), _f32(k[b:b + 1]), _f32(v[b:b + 1]),
+                            np.array([starts[b]], np.int32), okc, ovc, kpos, count, _f32(s))
+        assert_close(out[b:b + 1], ref, what=f"seq {b} start {starts[b]}")
