@@ -12,9 +12,11 @@ from .oracle import (  # noqa: F401
     e4m3_decode,
     e4m3_encode,
     extend,
+    layer_prefill,
     num_threads,
     omega,
     prefill,
+    prefill_f64,
     rotate,
     scores,
 )

@@ -154,9 +154,14 @@ static double dot(const double* a, const double* b, int32_t n) {
  *   Rows not listed are left untouched.
  *   k_rot_out: optional [B,S,Hkv,dqk] double, receives the rotated keys.
  */
-int oracle_prefill(const oracle_params* p, int32_t S, const float* q, const float* k,
-                   const float* v, const int32_t* positions, const float* sinks, double* out,
-                   const int32_t* rows, int32_t nrows, double* k_rot_out) {
+/* Element i of a q/k/v input given as float (f64 = 0) or double (f64 = 1). */
+static double in_elem(const void* a, int64_t i, int f64) {
+    return f64 ? ((const double*)a)[i] : (double)((const float*)a)[i];
+}
+
+static int prefill_core(const oracle_params* p, int32_t S, const void* q, const void* k,
+                        const void* v, int f64, const int32_t* positions, const float* sinks,
+                        double* out, const int32_t* rows, int32_t nrows, double* k_rot_out) {
     if (check_params(p) != ORACLE_OK || S < 0 || !q || !k || !v || !positions || !out)
         return ORACLE_EINVAL;
     const int32_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
@@ -180,9 +185,9 @@ int oracle_prefill(const oracle_params* p, int32_t S, const float* q, const floa
     for (int64_t t = 0; t < nk; ++t) {
         const int64_t b = t / ((int64_t)S * Hkv), s = (t / Hkv) % S;
         double tmp[4096];
-        for (int32_t d = 0; d < dqk; ++d) tmp[d] = (double)k[t * dqk + d];
+        for (int32_t d = 0; d < dqk; ++d) tmp[d] = in_elem(k, t * dqk + d, f64);
         rotate_row(tmp, kr + t * dqk, dqk, r, omega, (double)positions[b * S + s]);
-        for (int32_t e = 0; e < dv; ++e) vd[t * dv + e] = (double)v[t * dv + e];
+        for (int32_t e = 0; e < dv; ++e) vd[t * dv + e] = in_elem(v, t * dv + e, f64);
     }
     if (k_rot_out) memcpy(k_rot_out, kr, sizeof(double) * (size_t)nk * dqk);
 
@@ -204,7 +209,7 @@ int oracle_prefill(const oracle_params* p, int32_t S, const float* q, const floa
                 const int32_t i = rows ? rows[w % nr] : (int32_t)(w % nr);
                 const int32_t g = h / group;
                 const int64_t qoff = (((int64_t)b * S + i) * Hq + h) * dqk;
-                for (int32_t d = 0; d < dqk; ++d) qraw[d] = (double)q[qoff + d];
+                for (int32_t d = 0; d < dqk; ++d) qraw[d] = in_elem(q, qoff + d, f64);
                 const int64_t pi = positions[(int64_t)b * S + i];
                 rotate_row(qraw, qrot, dqk, r, omega, (double)pi);
                 int64_t n = 0;
@@ -227,6 +232,19 @@ int oracle_prefill(const oracle_params* p, int32_t S, const float* q, const floa
     free(kr);
     free(vd);
     return bad ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+int oracle_prefill(const oracle_params* p, int32_t S, const float* q, const float* k,
+                   const float* v, const int32_t* positions, const float* sinks, double* out,
+                   const int32_t* rows, int32_t nrows, double* k_rot_out) {
+    return prefill_core(p, S, q, k, v, 0, positions, sinks, out, rows, nrows, k_rot_out);
+}
+
+/* Prefill with q, k, v given in double (e.g. fp64 projections of a layer input). */
+int oracle_prefill_f64(const oracle_params* p, int32_t S, const double* q, const double* k,
+                       const double* v, const int32_t* positions, const float* sinks,
+                       double* out, const int32_t* rows, int32_t nrows, double* k_rot_out) {
+    return prefill_core(p, S, q, k, v, 1, positions, sinks, out, rows, nrows, k_rot_out);
 }
 
 /*

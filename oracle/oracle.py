@@ -76,6 +76,8 @@ def _load():
                                                ctypes.c_int32, ctypes.c_double, i32]
             lib.oracle_prefill.argtypes = [P(_CParams), ctypes.c_int32, f32, f32, f32, i32, f32,
                                            f64, i32, ctypes.c_int32, f64]
+            lib.oracle_prefill_f64.argtypes = [P(_CParams), ctypes.c_int32, f64, f64, f64, i32,
+                                               f32, f64, i32, ctypes.c_int32, f64]
             lib.oracle_scores.argtypes = [P(_CParams), ctypes.c_int32, f32, f32, i32,
                                           ctypes.c_int32, ctypes.c_int32, f64]
             lib.oracle_decode.argtypes = [P(_CParams), f32, f32, f32, i32, f32, f32, i32, i32,
@@ -93,7 +95,7 @@ def _load():
             lib.oracle_num_threads.restype = ctypes.c_int
             for fn in ("oracle_rope_omega", "oracle_rope_rotate", "oracle_prefill",
                        "oracle_scores", "oracle_decode", "oracle_extend", "oracle_e4m3_encode",
-                       "oracle_e4m3_decode", "oracle_decode_fp8"):
+                       "oracle_e4m3_decode", "oracle_decode_fp8", "oracle_prefill_f64"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -313,3 +315,48 @@ def decode_fp8(p: OracleParams, q, k_new, v_new, pos, kc8=None, vc8=None, kpos=N
         _ptr(krot, ctypes.c_double), _ptr(kcode, ctypes.c_uint8), _ptr(vcode, ctypes.c_uint8),
         _ptr(br, ctypes.c_int32), 0 if br is None else len(br)), "decode_fp8")
     return out, krot, kcode, vcode
+
+
+# ----------------------------------------------------------------------------- layer
+
+
+def prefill_f64(p: OracleParams, q, k, v, positions, sinks=None, rows=None):
+    """prefill() with q, k, v taken in float64 (no rounding of the inputs)."""
+    q, k, v, sinks = _f64(q), _f64(k), _f64(v), _f32(sinks)
+    pos = _i32(positions)
+    B, S = pos.shape
+    assert q.shape == (B, S, p.num_q_heads, p.qk_head_dim), q.shape
+    assert k.shape == (B, S, p.num_kv_heads, p.qk_head_dim), k.shape
+    assert v.shape == (B, S, p.num_kv_heads, p.v_head_dim), v.shape
+    out = np.full((B, S, p.num_q_heads, p.v_head_dim), np.nan, dtype=np.float64)
+    rows_a = _i32(rows)
+    cp = p.c()
+    _check(_load().oracle_prefill_f64(
+        ctypes.byref(cp), S, _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+        _ptr(v, ctypes.c_double), _ptr(pos, ctypes.c_int32), _ptr(sinks, ctypes.c_float),
+        _ptr(out, ctypes.c_double), _ptr(rows_a, ctypes.c_int32),
+        0 if rows_a is None else len(rows_a), None), "prefill_f64")
+    return out
+
+
+def layer_prefill(p: OracleParams, x, wq, wk, wv, wo, positions, sinks=None, rows=None):
+    """The attention layer with its projections, in fp64:
+    q = x Wq, k = x Wk, v = x Wv (x [B,S,hidden]; Wq [hidden, Hq*dqk], Wk [hidden, Hkv*dqk],
+    Wv [hidden, Hkv*dv], heads contiguous in the columns), attention as prefill() (v_scale
+    included), out = attn Wo (attn [B,S,Hq*dv], Wo [Hq*dv, hidden_out]).  Matrix products are
+    numpy's fp64 matmul.  Returns out [B,S,hidden_out] (rows not listed are NaN)."""
+    x = _f64(x)
+    B, S, H = x.shape
+    wq, wk, wv, wo = _f64(wq), _f64(wk), _f64(wv), _f64(wo)
+    assert wq.shape == (H, p.num_q_heads * p.qk_head_dim), wq.shape
+    assert wk.shape == (H, p.num_kv_heads * p.qk_head_dim), wk.shape
+    assert wv.shape == (H, p.num_kv_heads * p.v_head_dim), wv.shape
+    assert wo.shape[0] == p.num_q_heads * p.v_head_dim, wo.shape
+    q = (x @ wq).reshape(B, S, p.num_q_heads, p.qk_head_dim)
+    k = (x @ wk).reshape(B, S, p.num_kv_heads, p.qk_head_dim)
+    v = (x @ wv).reshape(B, S, p.num_kv_heads, p.v_head_dim)
+    attn = prefill_f64(p, q, k, v, positions, sinks, rows).reshape(B, S, -1)
+    out = np.full((B, S, wo.shape[1]), np.nan, dtype=np.float64)
+    sel = np.arange(S) if rows is None else np.asarray(rows)
+    out[:, sel] = attn[:, sel] @ wo
+    return out

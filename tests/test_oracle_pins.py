@@ -539,6 +539,73 @@ def test_decode_fp8_quantizes_the_rotated_key(kind):
     assert np.array_equal(vcode, _e4m3_torch_codes(vn * inv_v))
 
 
+# ----------------------------------------------------------------------------- layer with projections
+
+
+def test_prefill_f64_equals_float_prefill_on_float_inputs():
+    w = _small(kind=1, W=5)
+    q, k, v, s = synth.layer_inputs(w, seed=71)
+    pos = _positions(w.batch, w.seq, [0, 3])
+    P = _params(w)
+    a = oracle.prefill(P, _np(q), _np(k), _np(v), pos, _np(s))
+    b = oracle.prefill_f64(P, _np(q).astype(np.float64), _np(k).astype(np.float64),
+                           _np(v).astype(np.float64), pos, _np(s))
+    assert np.array_equal(a, b)
+
+
+def _selection_weights(Hq, Hkv, dqk, dv):
+    """Weights that copy consecutive slices of x into q, k and v, and the identity for Wo."""
+    nq, nk, nv = Hq * dqk, Hkv * dqk, Hkv * dv
+    H = nq + nk + nv
+    eye = np.eye(H)
+    return H, eye[:, :nq], eye[:, nq:nq + nk], eye[:, nq + nk:], np.eye(Hq * dv)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_layer_with_selection_weights_is_the_attention(kind):
+    """x = [q | k | v] per token, projections that select those slices and Wo = I: the layer is
+    the (pinned) attention on q, k, v, heads contiguous in the columns."""
+    w = _small(kind=kind, W=5 if kind else 0, Hq=4, Hkv=2, dqk=16, dv=8, r=6)
+    H, wq, wk, wv, wo = _selection_weights(4, 2, 16, 8)
+    q, k, v, s = synth.layer_inputs(w, seed=72)
+    B, S = w.batch, w.seq
+    x = np.concatenate([_np(q).reshape(B, S, -1), _np(k).reshape(B, S, -1),
+                        _np(v).reshape(B, S, -1)], axis=2)
+    pos = _positions(B, S, [0, 6])
+    P = _params(w)
+    got = oracle.layer_prefill(P, x, wq, wk, wv, wo, pos, _np(s))
+    ref = oracle.prefill(P, _np(q), _np(k), _np(v), pos, _np(s)).reshape(B, S, -1)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
+    # sampled rows: the same rows, the others NaN
+    rows = np.array([0, 5, S - 1], np.int32)
+    part = oracle.layer_prefill(P, x, wq, wk, wv, wo, pos, _np(s), rows=rows)
+    np.testing.assert_allclose(part[:, rows], ref[:, rows], rtol=0, atol=1e-13)
+    assert np.isnan(np.delete(part, rows, axis=1)).all()
+
+
+def test_layer_is_linear_in_the_output_and_value_projections():
+    w = _small(kind=1, W=4, Hq=4, Hkv=2, dqk=16, dv=8, r=6)
+    B, S, H = w.batch, w.seq, 24
+    rng = np.random.default_rng(73)
+    x = rng.standard_normal((B, S, H))
+    wq = rng.standard_normal((H, 4 * 16)) / 5
+    wk = rng.standard_normal((H, 2 * 16)) / 5
+    wv = rng.standard_normal((H, 2 * 8))
+    wo = rng.standard_normal((4 * 8, 10))
+    s = rng.standard_normal(4).astype(np.float32)
+    pos = _positions(B, S, [0, 2])
+    P = _params(w)
+    base = oracle.layer_prefill(P, x, wq, wk, wv, wo, pos, s)
+    np.testing.assert_allclose(oracle.layer_prefill(P, x, wq, wk, wv, 3 * wo, pos, s), 3 * base,
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.layer_prefill(P, x, wq, wk, -2 * wv, wo, pos, s), -2 * base,
+                               rtol=1e-12, atol=1e-12)
+    # the value scale and a scale of Wo are interchangeable (folding v_scale into o_proj)
+    P2 = _params(w, v_scale=1.0)
+    np.testing.assert_allclose(oracle.layer_prefill(P2, x, wq, wk, wv, wo * P.v_scale, pos, s), base,
+                               rtol=1e-12, atol=1e-12)
+
+
 def test_oracle_rejects_invalid_arguments():
     w = _small()
     q, k, v, s = synth.layer_inputs(w, seed=1)
