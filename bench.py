@@ -27,7 +27,9 @@ and with fp8 e4m3 caches), copy
 achievable HBM rate), gemm (8192^3 bf16 matrix product: the achievable matrix-core rate),
 extend (new tokens against a cache: a 2048-token chunk after 30000 cached positions, global and
 sliding, batch 1; and 4 tokens per sequence after the decode workload's cached lengths, batch 64,
-the shape of multi-token verification).
+the shape of multi-token verification), layer (the layer entry point: hidden 4096 -> q/k/v
+projections -> attention -> output projection back to 4096, on the sliding 4096-token and the
+global 8192-token prefill shapes; the projections run on hipBLASLt).
 """
 from __future__ import annotations
 
@@ -170,8 +172,8 @@ def main():
     ap.add_argument("--eager-decode", action="store_true",
                     help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
-                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "extend", "copy",
-                             "gemm"])
+                    choices=["stack", "swa_prefill", "ga_prefill", "decode", "extend", "layer",
+                             "copy", "gemm"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -413,6 +415,27 @@ def single_layer(args, dev):
         b -= w.batch * (min(w.seq, w.window) if w.layer_kind else w.seq) * w.num_kv_heads * (DQK + DV) * 2
         res.update(ms=ms, tflops=f / ms / 1e9, GBps=b / ms / 1e6, flop=f, bytes=b,
                    frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS, frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
+    elif args.workload == "layer":
+        hidden = 4096
+        for name, w in (("sliding", synth.SWA_PREFILL), ("global", synth.GA_PREFILL)):
+            x, s = synth.layer_input(w, 13000 + w.layer_kind, hidden, device=dev)
+            wq, wk, wv, wo = synth.layer_weights(w, 13100 + w.layer_kind, hidden, hidden, device=dev)
+            p = mimo.Params(w.batch, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims,
+                            w.layer_kind, w.window, w.rope_theta, w.v_scale)
+            sp = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+            out = torch.empty((w.batch, w.seq, hidden), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mimo.layer_workspace_size(p, hidden, w.seq) + 256, dtype=torch.uint8,
+                             device=dev)
+            ms = timed(lambda: mimo.layer_prefill(p, x, wq, wk, wv, wo, sp, sinks=s, out=out,
+                                                  workspace=ws), args.steps)
+            T = w.batch * w.seq
+            f_attn, _ = prefill_counts(w.batch, w.seq, w.num_q_heads, w.num_kv_heads, w.layer_kind,
+                                       w.window)
+            f_proj = 2 * T * hidden * (w.num_q_heads * DQK + w.num_kv_heads * (DQK + DV))
+            f_out = 2 * T * w.num_q_heads * DV * hidden
+            f = f_attn + f_proj + f_out
+            res[name] = dict(ms=ms, tflops=f / ms / 1e9, flop=f, flop_projections=f_proj + f_out,
+                             flop_attention=f_attn, frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS)
     elif args.workload == "extend":
         lengths = synth.decode_lengths(3).tolist()
         cases = [("global_chunk", synth.GA_HEADS, [30000], 2048),

@@ -25,6 +25,8 @@ from .binding import (  # noqa: F401
     extend,
     extend_workspace_size,
     last_error,
+    layer_prefill,
+    layer_workspace_size,
     lib,
     prefill,
     prefill_workspace_size,

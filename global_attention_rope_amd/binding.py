@@ -23,7 +23,8 @@ CACHE_SAME, CACHE_FP8_E4M3 = 0, 2
 
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_extend",
            "mimo_attn_extend_workspace_size", "mimo_attn_decode",
-           "mimo_attn_decode_workspace_size", "mimo_attn_check_params", "mimo_attn_last_error",
+           "mimo_attn_decode_workspace_size", "mimo_attn_layer_prefill",
+           "mimo_attn_layer_workspace_size", "mimo_attn_check_params", "mimo_attn_last_error",
            "mimo_attn_abi_version")
 
 
@@ -100,6 +101,11 @@ def lib(path: str = LIB_PATH):
             L.mimo_attn_decode.restype = ctypes.c_int
             L.mimo_attn_decode_workspace_size.argtypes = [P, i32]
             L.mimo_attn_decode_workspace_size.restype = sz
+            L.mimo_attn_layer_prefill.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                                  vp, vp, i32, vp, sz, vp]
+            L.mimo_attn_layer_prefill.restype = ctypes.c_int
+            L.mimo_attn_layer_workspace_size.argtypes = [P, i32, i32]
+            L.mimo_attn_layer_workspace_size.restype = sz
             L.mimo_attn_check_params.argtypes = [P]
             L.mimo_attn_check_params.restype = ctypes.c_int
             L.mimo_attn_last_error.argtypes = []
@@ -268,4 +274,49 @@ def decode(p: Params, q, k_new, v_new, positions, max_position: int, k_cache, v_
                                   _ptr(positions), max_position, _ptr(k_cache), _ptr(v_cache), cap,
                                   _ptr(sinks), _ptr(out), _ptr(workspace), wbytes,
                                   _stream(stream)))
+    return out
+
+
+def layer_workspace_size(p: Params, hidden: int, seq_len: int) -> int:
+    cp = p.c()
+    return int(lib().mimo_attn_layer_workspace_size(ctypes.byref(cp), hidden, seq_len))
+
+
+def layer_prefill(p: Params, x, w_q, w_k, w_v, w_o, start_pos, sinks=None, out=None, k_cache=None,
+                  v_cache=None, workspace=None, stream=None):
+    """mimo_attn_layer_prefill on torch device tensors: x [B,S,hidden]; w_q [hidden, Hq*dqk],
+    w_k [hidden, Hkv*dqk], w_v [hidden, Hkv*dv], w_o [Hq*dv, out_dim] (bf16).  Returns
+    out [B,S,out_dim]."""
+    B, S, hidden = x.shape
+    dev, dt = x.device, _tdtype(p)
+    if p.batch != B:
+        raise ValueError(f"params.batch {p.batch} != x.shape[0] {B}")
+    _expect(x, "x", (B, S, hidden), dt, dev)
+    _expect(w_q, "w_q", (hidden, p.num_q_heads * p.qk_head_dim), dt, dev)
+    _expect(w_k, "w_k", (hidden, p.num_kv_heads * p.qk_head_dim), dt, dev)
+    _expect(w_v, "w_v", (hidden, p.num_kv_heads * p.v_head_dim), dt, dev)
+    if w_o is None or w_o.dim() != 2:
+        raise ValueError("w_o must be a [Hq*dv, out_dim] matrix")
+    out_dim = w_o.shape[1]
+    _expect(w_o, "w_o", (p.num_q_heads * p.v_head_dim, out_dim), dt, dev)
+    _expect(start_pos, "start_pos", (B,), torch.int32, dev)
+    if sinks is not None:
+        _expect(sinks, "sinks", (p.num_q_heads,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, S, out_dim), dtype=dt, device=dev)
+    _expect(out, "out", (B, S, out_dim), dt, dev)
+    cap = 0
+    if k_cache is not None or v_cache is not None:
+        cap = k_cache.shape[2]
+        _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), _cdtype(p), dev)
+        _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), _cdtype(p), dev)
+    need = layer_workspace_size(p, hidden, S)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cp = p.c()
+    _raise(lib().mimo_attn_layer_prefill(
+        ctypes.byref(cp), hidden, S, _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), out_dim,
+        _ptr(start_pos), _ptr(sinks), _ptr(out), _ptr(k_cache), _ptr(v_cache), cap,
+        _ptr(workspace), wbytes, _stream(stream)))
     return out

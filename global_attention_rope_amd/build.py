@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmimo_attn.so")
-SOURCES = ["abi.hip", "prefill_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip"]
+SOURCES = ["abi.hip", "prefill_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip",
+           "layer.hip"]
 ARCH = "gfx950"
 
 
@@ -30,7 +31,7 @@ def command(out: str) -> list[str]:
             # the LDS-DMA wrapper clobbers m0 on purpose (no other m0 user in these kernels)
             "-Wno-inline-asm",
             "-I", os.path.join(ROOT, "include"),
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+            *[os.path.join(CSRC, s) for s in SOURCES], "-lhipblaslt", "-o", out]
 
 
 def build(verbose: bool = False) -> str:

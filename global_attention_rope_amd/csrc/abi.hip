@@ -29,6 +29,19 @@ int ok() {
     return MIMO_OK;
 }
 
+}  // namespace
+
+// The thread-local error message, shared by every entry point of the library.
+namespace mimo {
+int set_error(int code, const char* msg) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return code;
+}
+void clear_error() { g_err[0] = '\0'; }
+}  // namespace mimo
+
+namespace {
+
 constexpr int kBf16Dqk = 192, kBf16Dv = 128, kF32MaxDim = 256, kMaxDecodeGroup = 16;
 
 // Frequencies of the rotated slice, omega_d = theta^(-2d/r) for d < r/2, in revolutions per

@@ -135,4 +135,8 @@ int prefill_bf16_block_rows(bool window);
 // Largest number of decode splits per sequence the combine kernel merges.
 int decode_max_splits();
 
+// The library's thread-local error message (mimo_attn_last_error): set it and return code.
+int set_error(int code, const char* msg);
+void clear_error();
+
 }  // namespace mimo

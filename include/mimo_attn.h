@@ -29,8 +29,9 @@
  *   - sinks is fp32 [Hq] or NULL (no sink).  Position arrays are int32 in device memory.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  Nothing is
  *     synchronised, allocated, freed or printed by the library, and it keeps no global state;
- *     calls are thread-safe.  Calls that write the same cache or workspace must be ordered by
- *     the caller (same stream or events).
+ *     calls are thread-safe.  (Exception: mimo_attn_layer_prefill keeps one hipBLASLt handle per
+ *     device, created on its first call there and kept until the process ends.)  Calls that write
+ *     the same cache or workspace must be ordered by the caller (same stream or events).
  *   - Arguments are checked on the host before anything is enqueued.  On error the function
  *     returns a negative MIMO_ERR_* code, writes nothing, and mimo_attn_last_error() returns a
  *     message (thread-local).  MIMO_ERR_HIP means a launch failed; the message holds HIP's text.
@@ -192,6 +193,32 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
 /* Workspace bytes mimo_attn_decode needs: B * Hq * splits * (dv + 2) * 4 when the cache range is
  * cut into several splits, else 0.  Returns 0 for invalid parameters. */
 size_t mimo_attn_decode_workspace_size(const mimo_attn_params* p, int32_t max_position);
+
+/*
+ * Layer prefill: the attention layer with its projections ("Add Xiaomi MiMo-V2", "Additional
+ * useful info": the value head dim is decoupled from the QK head dim and the attention output is
+ * rescaled by v_scale before the output projection; here the rescale is folded into that
+ * projection, which is the same by linearity).
+ *   x [B,S,hidden]; w_q [hidden, Hq*dqk], w_k [hidden, Hkv*dqk], w_v [hidden, Hkv*dv] (row-major,
+ *   heads contiguous in the columns); w_o [Hq*dv, out_dim]; out [B,S,out_dim].  All bf16
+ *   (MIMO_BF16 layers only; fp8 caches as for prefill).
+ *   q = x w_q, k = x w_k, v = x w_v (bf16 results of fp32-accumulated products), then exactly
+ *   mimo_attn_prefill (positions, sinks, caches as there) with v_scale 1, then
+ *   out = v_scale * attn w_o.  The products run on hipBLASLt; the attention on this library's
+ *   kernels.
+ *   workspace: at least mimo_attn_layer_workspace_size() bytes (q, k, v, attention output, 32 MiB
+ *   of GEMM scratch and the prefill workspace); its contents are not needed across calls.
+ *   Errors as for mimo_attn_prefill; MIMO_ERR_HIP also when a product fails.
+ */
+int mimo_attn_layer_prefill(const mimo_attn_params* p, int32_t hidden, int32_t seq_len,
+                            const void* x, const void* w_q, const void* w_k, const void* w_v,
+                            const void* w_o, int32_t out_dim, const int32_t* start_pos,
+                            const float* sinks, void* out, void* k_cache, void* v_cache,
+                            int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes of mimo_attn_layer_prefill (0 for invalid parameters or fp32 layers). */
+size_t mimo_attn_layer_workspace_size(const mimo_attn_params* p, int32_t hidden, int32_t seq_len);
 
 /* Host-only validation of a parameter block (no device access): MIMO_OK or a negative code. */
 int mimo_attn_check_params(const mimo_attn_params* p);

@@ -5,6 +5,13 @@ element satisfies |gpu - oracle| <= 1e-2 + 2e-2 * |oracle| (allclose form of the
 the whole tensor satisfies ||gpu - oracle||_2 / ||oracle||_2 <= 2e-2.  The bf16 output alone is
 rounded by up to 2^-9 * |x| (0.0078 at |x| = 4), so a bare max-abs bound of 1e-2 would reject
 correctly rounded large outputs.  fp32 layers: absolute 2e-5, relative 1e-5, same form.
+
+Layer with projections: the output has no fixed scale, and its error comes from bf16 roundings of
+the projected q/k/v, of the softmax weights and of the attention output, each carried through a
+dense product, so it scales with the output's RMS.  Rows that see few keys average little and
+keep the largest errors: a CPU emulation of exact arithmetic with only those bf16 roundings
+reaches 2.9% of the RMS there (the kernel path 5.2%) while the relative L2 error stays near 4e-3.
+The absolute term is therefore 6e-2 * rms(oracle) (layer_atol); the relative terms as above.
 """
 from __future__ import annotations
 
@@ -27,12 +34,15 @@ def errors(gpu: np.ndarray, ref: np.ndarray):
     return max_abs, rel
 
 
-def assert_close(gpu, ref, fp32=False, what=""):
+def assert_close(gpu, ref, fp32=False, what="", atol=None):
+    """atol overrides the absolute term (the relative terms stay)."""
     gpu = to_np64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     max_abs, rel = errors(gpu, ref)
     lim_abs, lim_rel = (F32_MAX_ABS, F32_REL_L2) if fp32 else (BF16_MAX_ABS, BF16_REL_L2)
+    if atol is not None:
+        lim_abs = atol
     excess = np.abs(gpu - ref) - (lim_abs + lim_rel * np.abs(ref))
     worst = int(np.argmax(excess)) if excess.size else 0
     ok_elem = excess.size == 0 or excess.flat[worst] <= 0
@@ -49,3 +59,10 @@ def ring_positions(pos: int, window: int) -> np.ndarray:
     recent position < pos congruent to the slot (negative: the slot is still empty)."""
     s = np.arange(window)
     return pos - 1 - ((pos - 1 - s) % window)
+
+
+def layer_atol(ref) -> float:
+    """Absolute term of the layer tolerance: 6e-2 times the RMS of the oracle output."""
+    r = np.asarray(ref, np.float64)
+    r = r[np.isfinite(r)]
+    return 6e-2 * float(np.sqrt(np.mean(r * r))) if r.size else BF16_MAX_ABS

@@ -90,6 +90,27 @@ def cache_contents(w: Workload, seed: int, batch: int, cache_capacity: int, devi
     return k_cache, v_cache
 
 
+def layer_weights(w: Workload, seed: int, hidden: int, out_dim: int, device="cpu"):
+    """Projection weights of the layer, drawn N(0, 1/fan_in) (so projected activations stay about
+    unit scale): w_q [hidden, Hq*dqk], w_k [hidden, Hkv*dqk], w_v [hidden, Hkv*dv],
+    w_o [Hq*dv, out_dim], in the workload dtype."""
+    g = _gen(seed, device)
+    mk = lambda r, c: (torch.randn((r, c), generator=g, dtype=torch.float32, device=device)
+                       / math.sqrt(r)).to(w.dtype)
+    return (mk(hidden, w.num_q_heads * w.qk_head_dim), mk(hidden, w.num_kv_heads * w.qk_head_dim),
+            mk(hidden, w.num_kv_heads * w.v_head_dim), mk(w.num_q_heads * w.v_head_dim, out_dim))
+
+
+def layer_input(w: Workload, seed: int, hidden: int, device="cpu", batch=None, seq=None):
+    """Layer input x [B,S,hidden] drawn N(0,1) and its sinks (fp32 [Hq] or None)."""
+    B = w.batch if batch is None else batch
+    S = w.seq if seq is None else seq
+    g = _gen(seed, device)
+    x = randn((B, S, hidden), g, w.dtype, device)
+    sinks = randn((w.num_q_heads,), g, torch.float32, device) if w.sinks else None
+    return x, sinks
+
+
 # fp8 cache scales of the synthetic fp8 workloads (the stored values come out about N(0,1))
 FP8_K_SCALE, FP8_V_SCALE = 1.0 / 16.0, 1.0 / 8.0
 

@@ -212,3 +212,32 @@ def test_extend_argument_errors_return_before_any_launch():
     # nothing to do: success without touching any pointer
     assert _extend(_swa(), S=0, q=None, k=None, v=None, sp=None, out=None) == mimo.MIMO_OK
     assert _extend(_ga(batch=0), q=None, cap=116) == mimo.MIMO_OK
+
+
+def _layer(p, hidden=4096, S=16, x=1, w=1, sp=1, out=1, ws=None, wsb=0, out_dim=4096):
+    cp = p.c()
+    P = ctypes.c_void_p
+    ptr = lambda v: None if v is None else P(0x1000 * v)
+    return _lib().mimo_attn_layer_prefill(ctypes.byref(cp), hidden, S, ptr(x), ptr(w), ptr(w),
+                                          ptr(w), ptr(w), out_dim, ptr(sp), None, ptr(out), None,
+                                          None, 0, ptr(ws), wsb, None)
+
+
+def test_layer_argument_errors_return_before_any_launch():
+    E = mimo.MIMO_ERR_INVALID_ARG
+    assert _layer(_swa(), hidden=0) == E
+    assert _layer(_swa(), out_dim=0) == E
+    assert _layer(_swa(), S=-1) == E
+    assert _layer(_swa(), x=None) == E
+    assert _layer(_swa(), w=None) == E
+    assert _layer(_swa(), ws=None) == mimo.MIMO_ERR_WORKSPACE
+    assert "workspace" in mimo.last_error()
+    assert _layer(_swa(rope_dims=5)) == E
+    assert _layer(_swa(dtype=mimo.F32, qk_head_dim=32, v_head_dim=16, rope_dims=10, num_q_heads=4,
+                       num_kv_heads=1, window=16)) == mimo.MIMO_ERR_UNSUPPORTED
+    assert _layer(_swa(), S=0, x=None, w=None, sp=None, out=None) == mimo.MIMO_OK
+    # q, k, v, attention output, GEMM scratch and the prefill workspace
+    T = 2 * 100
+    need = mimo.layer_workspace_size(_ga(batch=2), 4096, 100)
+    parts = T * (64 * 192 + 4 * 192 + 4 * 128 + 64 * 128) * 2 + mimo.prefill_workspace_size(_ga(batch=2), 100)
+    assert parts + (32 << 20) <= need <= parts + (32 << 20) + 5 * 256

@@ -1,0 +1,58 @@
+"""GPU parity of the layer entry point (q/k/v projections, attention, output projection with the
+value rescale folded in) against the oracle's fp64 layer.  Seeds: 12000 + case."""
+import numpy as np
+import pytest
+import torch
+
+import global_attention_rope_amd as mimo
+import oracle
+from tests import synth
+from tests.gpu_helpers import assert_close, layer_atol
+from tests.test_gpu_parity import _f32, _note, _oparams, _params, _wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(w, hidden, out_dim, starts, seed, rows=None, with_cache=False):
+    x, s = synth.layer_input(w, seed, hidden, device=DEV)
+    wq, wk, wv, wo = synth.layer_weights(w, seed + 1, hidden, out_dim, device=DEV)
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    kc = vc = None
+    if with_cache:
+        cap = w.window if w.layer_kind == 1 else max(starts) + w.seq
+        kc = torch.zeros((w.batch, w.num_kv_heads, cap, w.qk_head_dim), dtype=w.dtype, device=DEV)
+        vc = torch.zeros((w.batch, w.num_kv_heads, cap, w.v_head_dim), dtype=w.dtype, device=DEV)
+    out = mimo.layer_prefill(_params(w), x, wq, wk, wv, wo, sp, sinks=s, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    pos = np.stack([np.arange(w.seq, dtype=np.int32) + st for st in starts])
+    ref = oracle.layer_prefill(_oparams(w), _f32(x), _f32(wq), _f32(wk), _f32(wv), _f32(wo), pos,
+                               _f32(s), rows=rows)
+    return out, ref
+
+
+@pytest.mark.parametrize("case", [
+    dict(kind=1, B=2, S=100, Hq=8, Hkv=2, sinks=True, starts=[0, 40], W=32, hidden=512, out=384),
+    dict(kind=0, B=2, S=77, Hq=8, Hkv=2, sinks=False, starts=[0, 5], hidden=768, out=512),
+    dict(kind=1, B=1, S=300, Hq=16, Hkv=2, sinks=True, starts=[0], W=128, hidden=1024, out=1024),
+])
+def test_layer_prefill_small(case):
+    case = dict(case)
+    starts, hidden, out_dim = case.pop("starts"), case.pop("hidden"), case.pop("out")
+    w = _wl(**case)
+    _note(f"layer {case} hidden {hidden} out {out_dim}")
+    out, ref = _run(w, hidden, out_dim, starts, 12000 + w.seq, with_cache=True)
+    assert_close(out, ref, what=f"layer {case}", atol=layer_atol(ref))
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_layer_prefill_full_size_sampled_rows(kind):
+    """Hidden 4096 -> 64 query heads -> 4096: the sliding layer at 4096 tokens, the global one at
+    8192, sampled rows (first, last, random)."""
+    w = synth.SWA_PREFILL if kind == 1 else synth.GA_PREFILL
+    _note(f"layer full {w.name}")
+    rng = np.random.default_rng(12 + kind)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(w.seq - 8, w.seq),
+                                     rng.integers(0, w.seq, 24)])).astype(np.int32)
+    out, ref = _run(w, 4096, 4096, [0], 12100 + kind, rows=rows)
+    assert_close(out[:, rows], ref[:, rows], what=f"layer {w.name}", atol=layer_atol(ref[:, rows]))
