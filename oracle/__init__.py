@@ -6,6 +6,7 @@ with it.  See ``mimo_oracle.c`` for what is computed and where the pages state i
 """
 from .oracle import (  # noqa: F401
     OracleParams,
+    RouterParams,
     build,
     decode,
     decode_fp8,
@@ -18,5 +19,7 @@ from .oracle import (  # noqa: F401
     prefill,
     prefill_f64,
     rotate,
+    router,
+    router_sigmoid,
     scores,
 )

@@ -17,6 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mimo_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "router_oracle.c")]
 _LIB = os.path.join(_HERE, "libmimo_oracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -24,11 +25,12 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (IEEE fp64: no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB) or any(
+            os.path.getmtime(_LIB) < os.path.getmtime(f) for f in _SRCS):
         tmp = _LIB + f".tmp{os.getpid()}"
         subprocess.check_call(
             ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-             _SRC, "-o", tmp, "-lm"])
+             *_SRCS, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -64,6 +66,14 @@ class OracleParams:
                         float(self.rope_theta), float(self.v_scale), float(self.softmax_scale))
 
 
+class _CRouterParams(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_double),
+    ]
+
+
 def _load():
     global _lib
     with _lock:
@@ -91,11 +101,15 @@ def _load():
             lib.oracle_decode_fp8.argtypes = [P(_CParams), f32, f32, f32, i32, u8, u8, i32, i32,
                                               ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                                               f32, f64, f64, u8, u8, i32, ctypes.c_int32]
+            lib.oracle_router.argtypes = [P(_CRouterParams), f32, f32, i32, f64]
+            lib.oracle_router_sigmoid.argtypes = [ctypes.c_float]
+            lib.oracle_router_sigmoid.restype = ctypes.c_float
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             for fn in ("oracle_rope_omega", "oracle_rope_rotate", "oracle_prefill",
                        "oracle_scores", "oracle_decode", "oracle_extend", "oracle_e4m3_encode",
-                       "oracle_e4m3_decode", "oracle_decode_fp8", "oracle_prefill_f64"):
+                       "oracle_e4m3_decode", "oracle_decode_fp8", "oracle_prefill_f64",
+                       "oracle_router"):
                 getattr(lib, fn).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -360,3 +374,37 @@ def layer_prefill(p: OracleParams, x, wq, wk, wv, wo, positions, sinks=None, row
     sel = np.arange(S) if rows is None else np.asarray(rows)
     out[:, sel] = attn[:, sel] @ wo
     return out
+
+
+# ----------------------------------------------------------------------------- MoE router
+
+
+@dataclasses.dataclass
+class RouterParams:
+    num_experts: int = 256
+    n_group: int = 8
+    topk_group: int = 4
+    top_k: int = 8
+    norm_topk_prob: bool = True
+    routed_scaling_factor: float = 1.0
+
+
+def router(p: RouterParams, logits, bias=None):
+    """Grouped sigmoid top-k routing of logits [T, E] (float32) with an optional correction bias
+    [E].  Returns (expert indices int32 [T, top_k] in rank order, weights float64 [T, top_k])."""
+    x = _f32(logits)
+    T, E = x.shape
+    assert E == p.num_experts
+    b = _f32(bias)
+    idx = np.zeros((T, p.top_k), np.int32)
+    w = np.zeros((T, p.top_k), np.float64)
+    cp = _CRouterParams(T, E, p.n_group, p.topk_group, p.top_k, int(p.norm_topk_prob),
+                        float(p.routed_scaling_factor))
+    _check(_load().oracle_router(ctypes.byref(cp), _ptr(x, ctypes.c_float), _ptr(b, ctypes.c_float),
+                                 _ptr(idx, ctypes.c_int32), _ptr(w, ctypes.c_double)), "router")
+    return idx, w
+
+
+def router_sigmoid(x: float) -> float:
+    """The float32 score of one logit (fp64 sigmoid rounded to fp32)."""
+    return float(_load().oracle_router_sigmoid(float(x)))

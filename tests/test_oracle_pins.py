@@ -606,6 +606,85 @@ def test_layer_is_linear_in_the_output_and_value_projections():
                                rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- MoE router
+
+
+def _router_scores(x, bias):
+    """torch route: fp64 sigmoid rounded to fp32, plus the bias in fp32."""
+    s = torch.sigmoid(torch.from_numpy(np.asarray(x, np.float64))).float()
+    return s, s + torch.from_numpy(np.asarray(bias, np.float32))
+
+
+def test_router_sigmoid_is_the_rounded_fp64_sigmoid():
+    x = np.concatenate([np.linspace(-30, 30, 2001), np.random.default_rng(80).standard_normal(5000) * 4])
+    x = x.astype(np.float32)
+    mine = np.array([oracle.router_sigmoid(v) for v in x], np.float32)
+    ref = torch.sigmoid(torch.from_numpy(x.astype(np.float64))).float().numpy()
+    assert np.array_equal(mine, ref)
+
+
+@pytest.mark.parametrize("groups", [(1, 1), (8, 8)])
+def test_router_keeping_every_group_is_plain_topk(groups):
+    """One group, or every group kept: the choice is torch.topk of the selection scores, the
+    weights the chosen sigmoids normalised and scaled."""
+    G, TG = groups
+    rng = np.random.default_rng(81)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    b = (rng.standard_normal(256) * 0.1).astype(np.float32)
+    P = oracle.RouterParams(num_experts=256, n_group=G, topk_group=TG, top_k=8,
+                            norm_topk_prob=True, routed_scaling_factor=2.5)
+    idx, w = oracle.router(P, x, b)
+    s, c = _router_scores(x, b)
+    ref = torch.topk(c, 8, dim=1).indices.numpy()
+    assert np.array_equal(idx, ref)
+    sw = torch.gather(s, 1, torch.from_numpy(ref).long()).double().numpy()
+    np.testing.assert_allclose(w, 2.5 * sw / sw.sum(1, keepdims=True), rtol=1e-15, atol=0)
+    P.norm_topk_prob = False
+    _, w2 = oracle.router(P, x, b)
+    np.testing.assert_allclose(w2, 2.5 * sw, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("shape", [(8, 4, 2, 3), (12, 4, 2, 5), (16, 8, 3, 4)])
+def test_router_brute_force_subsets(shape):
+    """Tiny expert counts: the kept groups are the topk_group-subset with the largest total group
+    score (group score = sum of its two best selection scores), and the chosen experts the
+    top_k-subset of the kept groups' experts with the largest total selection score."""
+    import itertools
+    E, G, TG, K = shape
+    gs = E // G
+    rng = np.random.default_rng(82 + E)
+    x = rng.standard_normal((40, E)).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.3 - 1.5).astype(np.float32)   # negative scores: -inf masking
+    P = oracle.RouterParams(num_experts=E, n_group=G, topk_group=TG, top_k=K)
+    idx, _ = oracle.router(P, x, b)
+    _, c = _router_scores(x, b)
+    c = c.double().numpy()
+    for t in range(x.shape[0]):
+        gsc = [np.sort(c[t, g * gs:(g + 1) * gs])[-2:].sum() for g in range(G)]
+        keep = max(itertools.combinations(range(G), TG), key=lambda sub: sum(gsc[g] for g in sub))
+        pool = [e for g in keep for e in range(g * gs, (g + 1) * gs)]
+        best = max(itertools.combinations(pool, K), key=lambda sub: sum(c[t, e] for e in sub))
+        assert set(idx[t]) == set(best), (t, idx[t], best)
+        # rank order: selection scores descending
+        assert all(c[t, idx[t][i]] >= c[t, idx[t][i + 1]] for i in range(K - 1))
+        # masked with -inf: every chosen expert lies in a kept group, although scores are < 0
+        assert all(e // gs in keep for e in idx[t])
+
+
+def test_router_equal_scores_rank_lower_indices_first():
+    """Every score equal: the first groups are kept and the lowest expert indices chosen, in
+    index order (the tie rule)."""
+    P = oracle.RouterParams(num_experts=256, n_group=8, topk_group=4, top_k=8)
+    idx, w = oracle.router(P, np.zeros((3, 256), np.float32), np.zeros(256, np.float32))
+    assert np.array_equal(idx, np.tile(np.arange(8, dtype=np.int32), (3, 1)))
+    np.testing.assert_allclose(w, 1.0 / 8, rtol=1e-15)
+    # a tie inside a later group that is kept: groups with equal scores also go by index
+    x = np.zeros((1, 256), np.float32)
+    x[0, 100] = 5.0     # group 3 gets the best score; the other groups tie
+    idx, _ = oracle.router(P, x, np.zeros(256, np.float32))
+    assert idx[0, 0] == 100 and list(idx[0, 1:]) == [0, 1, 2, 3, 4, 5, 6]
+
+
 def test_oracle_rejects_invalid_arguments():
     w = _small()
     q, k, v, s = synth.layer_inputs(w, seed=1)
