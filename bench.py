@@ -29,7 +29,8 @@ extend (new tokens against a cache: a 2048-token chunk after 30000 cached positi
 sliding, batch 1; and 4 tokens per sequence after the decode workload's cached lengths, batch 64,
 the shape of multi-token verification), layer (the layer entry point: hidden 4096 -> q/k/v
 projections -> attention -> output projection back to 4096, on the sliding 4096-token and the
-global 8192-token prefill shapes; the projections run on hipBLASLt).
+global 8192-token prefill shapes; the projections run on hipBLASLt), router (the MoE router
+kernel: 32768 tokens, 256 experts in 8 groups, 4 groups kept, top 8).
 """
 from __future__ import annotations
 
@@ -173,7 +174,7 @@ def main():
                     help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
                     choices=["stack", "swa_prefill", "ga_prefill", "decode", "extend", "layer",
-                             "copy", "gemm"])
+                             "router", "copy", "gemm"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -415,6 +416,16 @@ def single_layer(args, dev):
         b -= w.batch * (min(w.seq, w.window) if w.layer_kind else w.seq) * w.num_kv_heads * (DQK + DV) * 2
         res.update(ms=ms, tflops=f / ms / 1e9, GBps=b / ms / 1e6, flop=f, bytes=b,
                    frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS, frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
+    elif args.workload == "router":
+        p = mimo.RouterParams()
+        T = synth.ROUTER_TOKENS
+        logits, bias = synth.router_inputs(14100, T, p.num_experts, device=dev)
+        idx = torch.empty((T, p.top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, p.top_k), dtype=torch.float32, device=dev)
+        ms = timed(lambda: mimo.router_topk(p, logits, bias, idx, wts), args.steps)
+        b = T * p.num_experts * 4 + p.num_experts * 4 + T * p.top_k * 8
+        res.update(ms=ms, tokens=T, experts=p.num_experts, bytes=b, GBps=b / ms / 1e6,
+                   frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)
     elif args.workload == "layer":
         hidden = 4096
         for name, w in (("sliding", synth.SWA_PREFILL), ("global", synth.GA_PREFILL)):

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     MIMO_OK,
     MimoAttnError,
     Params,
+    RouterParams,
     check_params,
     decode,
     decode_workspace_size,
@@ -30,6 +31,8 @@ from .binding import (  # noqa: F401
     lib,
     prefill,
     prefill_workspace_size,
+    router_check_params,
+    router_topk,
 )
 from .layers import (  # noqa: F401
     HybridAttentionConfig,

@@ -25,7 +25,7 @@ EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_e
            "mimo_attn_extend_workspace_size", "mimo_attn_decode",
            "mimo_attn_decode_workspace_size", "mimo_attn_layer_prefill",
            "mimo_attn_layer_workspace_size", "mimo_attn_check_params", "mimo_attn_last_error",
-           "mimo_attn_abi_version")
+           "mimo_attn_abi_version", "mimo_router_topk", "mimo_router_check_params")
 
 
 class MimoAttnError(RuntimeError):
@@ -45,6 +45,30 @@ class CParams(ctypes.Structure):
         ("cache_dtype", ctypes.c_int32), ("k_cache_scale", ctypes.c_float),
         ("v_cache_scale", ctypes.c_float),
     ]
+
+
+class CRouterParams(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+@dataclasses.dataclass
+class RouterParams:
+    num_experts: int = 256
+    n_group: int = 8
+    topk_group: int = 4
+    top_k: int = 8
+    norm_topk_prob: bool = True
+    routed_scaling_factor: float = 1.0
+
+    def c(self, num_tokens: int) -> CRouterParams:
+        return CRouterParams(num_tokens, self.num_experts, self.n_group, self.topk_group,
+                             self.top_k, int(self.norm_topk_prob),
+                             float(self.routed_scaling_factor), 0)
 
 
 @dataclasses.dataclass
@@ -106,6 +130,11 @@ def lib(path: str = LIB_PATH):
             L.mimo_attn_layer_prefill.restype = ctypes.c_int
             L.mimo_attn_layer_workspace_size.argtypes = [P, i32, i32]
             L.mimo_attn_layer_workspace_size.restype = sz
+            R = ctypes.POINTER(CRouterParams)
+            L.mimo_router_topk.argtypes = [R, vp, vp, vp, vp, vp]
+            L.mimo_router_topk.restype = ctypes.c_int
+            L.mimo_router_check_params.argtypes = [R]
+            L.mimo_router_check_params.restype = ctypes.c_int
             L.mimo_attn_check_params.argtypes = [P]
             L.mimo_attn_check_params.restype = ctypes.c_int
             L.mimo_attn_last_error.argtypes = []
@@ -320,3 +349,32 @@ def layer_prefill(p: Params, x, w_q, w_k, w_v, w_o, start_pos, sinks=None, out=N
         _ptr(start_pos), _ptr(sinks), _ptr(out), _ptr(k_cache), _ptr(v_cache), cap,
         _ptr(workspace), wbytes, _stream(stream)))
     return out
+
+
+def router_check_params(p: RouterParams, num_tokens: int = 1) -> int:
+    cp = p.c(num_tokens)
+    return lib().mimo_router_check_params(ctypes.byref(cp))
+
+
+def router_topk(p: RouterParams, logits, bias=None, expert_idx=None, weights=None, stream=None):
+    """mimo_router_topk on torch device tensors: logits fp32 [T, E], bias fp32 [E] or None.
+    Returns (expert_idx int32 [T, top_k], weights fp32 [T, top_k])."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    dev = logits.device
+    if E != p.num_experts:
+        raise ValueError(f"logits have {E} experts, params {p.num_experts}")
+    _expect(logits, "logits", (T, E), torch.float32, dev)
+    if bias is not None:
+        _expect(bias, "bias", (E,), torch.float32, dev)
+    if expert_idx is None:
+        expert_idx = torch.empty((T, p.top_k), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((T, p.top_k), dtype=torch.float32, device=dev)
+    _expect(expert_idx, "expert_idx", (T, p.top_k), torch.int32, dev)
+    _expect(weights, "weights", (T, p.top_k), torch.float32, dev)
+    cp = p.c(T)
+    _raise(lib().mimo_router_topk(ctypes.byref(cp), _ptr(logits), _ptr(bias), _ptr(expert_idx),
+                                  _ptr(weights), _stream(stream)))
+    return expert_idx, weights

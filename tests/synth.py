@@ -111,6 +111,17 @@ def layer_input(w: Workload, seed: int, hidden: int, device="cpu", batch=None, s
     return x, sinks
 
 
+ROUTER_TOKENS = 2 * 16384   # one router call per MoE layer of the stack's prefill batch
+
+
+def router_inputs(seed: int, tokens: int, experts: int = 256, device="cpu", bias_sd: float = 0.1):
+    """Gate logits [T, E] drawn N(0, 4) (fp32) and a correction bias [E] drawn N(0, bias_sd^2)."""
+    g = _gen(seed, device)
+    logits = torch.randn((tokens, experts), generator=g, dtype=torch.float32, device=device) * 2
+    bias = torch.randn((experts,), generator=g, dtype=torch.float32, device=device) * bias_sd
+    return logits, bias
+
+
 # fp8 cache scales of the synthetic fp8 workloads (the stored values come out about N(0,1))
 FP8_K_SCALE, FP8_V_SCALE = 1.0 / 16.0, 1.0 / 8.0
 

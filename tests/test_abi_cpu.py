@@ -10,13 +10,15 @@ import global_attention_rope_amd as mimo
 from global_attention_rope_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mimo_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mimo_attn.h", "mimo_router.h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mimo_attn_\w+)\s*\(", text)))
+    names = set()
+    for hdr in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mimo_(?:attn|router)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -241,3 +243,28 @@ def test_layer_argument_errors_return_before_any_launch():
     need = mimo.layer_workspace_size(_ga(batch=2), 4096, 100)
     parts = T * (64 * 192 + 4 * 192 + 4 * 128 + 64 * 128) * 2 + mimo.prefill_workspace_size(_ga(batch=2), 100)
     assert parts + (32 << 20) <= need <= parts + (32 << 20) + 5 * 256
+
+
+def test_router_params_are_checked_on_the_host():
+    ok = mimo.RouterParams()
+    assert mimo.router_check_params(ok, 100) == mimo.MIMO_OK
+    E = mimo.MIMO_ERR_INVALID_ARG
+    bad = [dict(n_group=3), dict(topk_group=0), dict(topk_group=9), dict(top_k=0),
+           dict(top_k=129), dict(routed_scaling_factor=float("inf")), dict(num_experts=256, n_group=256)]
+    for kw in bad:
+        p = mimo.RouterParams(**kw)
+        assert mimo.router_check_params(p, 10) == E, kw
+        assert mimo.last_error() != ""
+    assert mimo.router_check_params(ok, -1) == E
+    U = mimo.MIMO_ERR_UNSUPPORTED
+    assert mimo.router_check_params(mimo.RouterParams(num_experts=96, n_group=8), 4) == U
+    assert mimo.router_check_params(mimo.RouterParams(n_group=128, num_experts=512, topk_group=4), 4) == U
+    cp = ok.c(4)
+    cp.reserved = 1
+    assert _lib().mimo_router_check_params(ctypes.byref(cp)) == E
+    assert _lib().mimo_router_check_params(None) == E
+    # missing pointers are rejected before any launch; no tokens: nothing to do
+    cp = ok.c(4)
+    assert _lib().mimo_router_topk(ctypes.byref(cp), None, None, None, None, None) == E
+    cp = ok.c(0)
+    assert _lib().mimo_router_topk(ctypes.byref(cp), None, None, None, None, None) == mimo.MIMO_OK
