@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmimo_attn.so")
 SOURCES = ["abi.hip", "prefill_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip",
-           "layer.hip", "router.hip"]
+           "layer.hip", "router.hip", "verify_bf16.hip"]
 ARCH = "gfx950"
 
 

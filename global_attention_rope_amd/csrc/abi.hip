@@ -11,6 +11,7 @@
 
 #include "mimo_attn.h"
 #include "kernels.h"
+#include "verify.h"
 
 namespace {
 
@@ -194,20 +195,41 @@ size_t decode_ws(const mimo_attn_params* p, int32_t max_position) {
     return partials_bytes(p, p->batch, decode_geometry(p, max_position).nsplit);
 }
 
-// Extend of at most this many new tokens per sequence runs the decode kernels in their
-// multi-token mode (one query block per token, no tile of mostly idle query rows).
+// Extend of at most this many new tokens per sequence runs the multi-token tile kernel: the
+// (query head, token) pairs of a KV group are the query columns of one workgroup, so each key
+// tile is read once for all of them.
 constexpr int kVerifyMaxTokens = 16;
 
+int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
 bool verify_tokens(const mimo_attn_params* p, int32_t S) {
-    return S >= 1 && S <= kVerifyMaxTokens && (int64_t)p->batch * S <= 65535;   // (grid z)
+    return S >= 1 && S <= kVerifyMaxTokens &&
+           mimo::verify_tile_waves(p->num_q_heads / p->num_kv_heads, pow2_at_least(S)) > 0 &&
+           (int64_t)p->batch * S <= 65535 && p->batch <= 65535;   // (combine grid, kernel grid)
 }
 
 // Multi-token extend: key rows of the longest query — global: positions 0..max_start + S - 1
 // of the cache; sliding: the W + S rows of the workspace (never split up to 1024 rows).
+// Splits of whole 64-row tiles: enough (sequence, KV head, split) workgroups to fill the chip
+// about four times over (two resident per CU), at least 256 rows each.
 SplitGeometry verify_geometry(const mimo_attn_params* p, int32_t S, int32_t max_start) {
     const bool swa = p->layer_kind == MIMO_LAYER_SWA;
     const int64_t n_max = swa ? (int64_t)p->window + S : (int64_t)max_start + S;
-    return split_geometry(n_max, (int64_t)p->batch * S * p->num_kv_heads, swa ? 1024 : 0, false);
+    const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
+    int64_t ns = (2048 + pairs - 1) / pairs;
+    if (ns > (n_max + 255) / 256) ns = (n_max + 255) / 256;
+    if (ns > mimo::decode_max_splits()) ns = mimo::decode_max_splits();
+    if (ns < 1) ns = 1;
+    int64_t chunk = ((n_max + ns - 1) / ns + 63) / 64 * 64;
+    SplitGeometry g;
+    g.n_max = n_max;
+    g.chunk = (int)chunk;
+    g.nsplit = (int)((n_max + chunk - 1) / chunk);
+    return g;
 }
 
 // bf16 extend workspace: sliding layers lay out [B, Hkv, window + S] rotated K and V rows (the
@@ -493,38 +515,59 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     pa.v_sj = dv;
     rc = hip_status(mimo::launch_rope_kv_bf16(ra, st), "key rotation (bf16)");
     if (rc != MIMO_OK) return rc;
-    // (the decode kernels address a key-row slice through a 32-bit byte bound)
-    const int64_t key_rows = pa.k_sh / dqk;
-    if (!verify_tokens(p, seq_len) || key_rows * dqk * 2 > 0xffffffffLL)
+    if (!verify_tokens(p, seq_len))
         return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "extend (bf16)");
 
-    // a few new tokens: the decode kernels' multi-token mode over the same key rows
+    // a few new tokens: the multi-token tile kernel over the same key rows
     const SplitGeometry geo = verify_geometry(p, seq_len, max_start);
-    mimo::DecodeArgs da;
+    mimo::VerifyArgs va;
+    memset(&va, 0, sizeof va);
+    va.q = (const uint16_t*)q;
+    va.k = pa.k;
+    va.v = pa.v;
+    va.start_pos = start_pos;
+    va.sinks = sinks;
+    va.out = (uint16_t*)out;
+    va.partial = (float*)((uint8_t*)workspace + extend_rows_ws(p, seq_len));
+    va.k_sb = pa.k_sb;
+    va.k_sh = pa.k_sh;
+    va.v_sb = pa.v_sb;
+    va.v_sh = pa.v_sh;
+    va.B = p->batch;
+    va.T = seq_len;
+    va.TP = pow2_at_least(seq_len);
+    va.Hq = p->num_q_heads;
+    va.Hkv = p->num_kv_heads;
+    va.rope_dims = p->rope_dims;
+    va.window = p->window;
+    va.kpos_rel = pa.kpos_rel;
+    va.kpos_off = pa.kpos_off;
+    va.max_start = max_start;
+    va.chunk = geo.chunk;
+    va.nsplit = geo.nsplit;
+    va.score_scale_log2 = pa.score_scale_log2;
+    va.v_scale = p->v_scale;
+    fill_omega(p, va.omega_rev);
+    rc = hip_status(mimo::launch_verify_tiles_bf16(va, swa, sinks != nullptr, st), "extend (bf16)");
+    if (rc != MIMO_OK || geo.nsplit <= 1) return rc;
+    mimo::DecodeArgs da;   // the combine's view of the partials
     memset(&da, 0, sizeof da);
-    da.q = (const uint16_t*)q;
     da.positions = start_pos;
-    da.k_cache = (void*)pa.k;
-    da.v_cache = (void*)pa.v;
     da.sinks = sinks;
     da.out = (uint16_t*)out;
-    da.partial = (float*)((uint8_t*)workspace + extend_rows_ws(p, seq_len));
+    da.partial = va.partial;
     da.B = p->batch;
     da.Hq = p->num_q_heads;
     da.Hkv = p->num_kv_heads;
-    da.rope_dims = p->rope_dims;
     da.window = p->window;
-    da.cap = (int32_t)key_rows;   // key rows per (sequence, KV head)
     da.max_position = max_start;
     da.chunk = geo.chunk;
     da.nsplit = geo.nsplit;
     da.q_per_seq = seq_len;
     da.kpos_rel = pa.kpos_rel;
     da.kpos_off = pa.kpos_off;
-    da.score_scale_log2 = pa.score_scale_log2;
     da.v_scale = p->v_scale;
-    fill_omega(p, da.omega_rev);
-    return hip_status(mimo::launch_verify_bf16(da, swa, sinks != nullptr, st), "extend (bf16)");
+    return hip_status(mimo::launch_verify_combine(da, swa, sinks != nullptr, st), "extend combine");
 }
 
 int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,

@@ -19,10 +19,8 @@
 //   * the waves are merged through LDS; with one split the sink is folded in and the bf16 output
 //     written, otherwise (max, sum, O) partials go to the workspace and the combine kernel merges
 //     the splits in one pass (running maximum) and adds the sink exactly once.
-// Multi-token mode (VERIFY: a few new tokens per sequence against its cache, already stored):
-// one workgroup per (sequence, token, KV head, split) as if each token were a decode of its own
-// — the tokens of a sequence read the same cache rows at about the same time, from the XCD's L2 —
-// with no append, a linear key-row space and a lower key-row bound (window, empty rows).
+// The combine kernel also merges the split partials of the multi-token tile kernel (a few new
+// tokens per sequence: one record per (sequence, token, query head, split)).
 // fp8 caches (e4m3 codes, one scale per cache tensor): the slot loads are half as wide, codes are
 // turned into their exact bf16 values in registers (K) or on their way into the LDS tile (V), the
 // two scales are folded into the score scale and the output scale, and the new token is coded
@@ -32,6 +30,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "verify.h"
 
 namespace mimo {
 namespace {
@@ -89,11 +88,9 @@ struct LdsDecode {
 };
 
 // ROT: how many of a lane's 32-dim query chunk rows can hold rotated dims (2 when r <= 64).
-// FP8: the caches hold e4m3 codes.  VERIFY: multi-token mode (SWA then means the window mask
-// over a linear key space, not a ring).
-template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool VERIFY>
+// FP8: the caches hold e4m3 codes.
+template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
-    constexpr bool RING = SWA && !VERIFY;
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
     using elem_t = std::conditional_t<FP8, uint8_t, uint16_t>;
     constexpr int EB = sizeof(elem_t);
@@ -105,10 +102,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr int VREG = TILE * DV / VPL / 64;               // V loads per lane per tile (8 or 4)
     constexpr int VCH = DV / VPL;                            // 16-byte chunks per V row
 
-    const int s = blockIdx.x, g = blockIdx.y;
-    const int bq = blockIdx.z;                          // query row block: sequence (and token)
-    const int b = VERIFY ? bq / a.q_per_seq : bq;       // sequence: cache and position
-    const int tq = VERIFY ? bq - b * a.q_per_seq : 0;   // token of the sequence
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, gq = lane >> 4;
@@ -161,7 +155,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     //      partners, the new token, the sinks, one frequency per thread and, on sliding layers, the
     //      first slot tile.
     const int r = a.rope_dims, half = r >> 1;
-    const uint16_t* qrow = a.q + ((int64_t)bq * a.Hq + g * G + min(l16, G - 1)) * DQK;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + min(l16, G - 1)) * DQK;
     // Dims of MFMA k-chunk c held by lane group gq: 32c + 8gq.. for bf16 caches; for fp8 caches
     // 64(c/2) + 16gq + 8(c%2).., the order in which one 16-byte load of 16 key codes splits into
     // two chunks (the dot product does not depend on how its dims are ordered, as long as keys
@@ -177,15 +171,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     }
     const int64_t kv_row = (int64_t)b * a.Hkv + g;
     const int nd0 = tid < DQK / 8 ? tid * 8 : 0;   // k_new dims of this thread (tid < 24)
-    u32x4 nraw = u32x4{0u, 0u, 0u, 0u}, npar = nraw;
-    if constexpr (!VERIFY) {
-        const uint16_t* nsrc = tid >= DQK / 8 && tid < DQK / 8 + DV / 8
-                                   ? a.v_new + kv_row * DV + (tid - DQK / 8) * 8
-                                   : a.k_new + kv_row * DQK + nd0;
-        nraw = *(const u32x4*)nsrc;
-        npar = *(const u32x4*)(a.k_new + kv_row * DQK +
-                               (nd0 < half ? nd0 + half : (nd0 < r ? nd0 - half : nd0)));
-    }
+    const uint16_t* nsrc = tid >= DQK / 8 && tid < DQK / 8 + DV / 8
+                               ? a.v_new + kv_row * DV + (tid - DQK / 8) * 8
+                               : a.k_new + kv_row * DQK + nd0;
+    const u32x4 nraw = *(const u32x4*)nsrc;
+    const u32x4 npar = *(const u32x4*)(a.k_new + kv_row * DQK +
+                                       (nd0 < half ? nd0 + half : (nd0 < r ? nd0 - half : nd0)));
     const float sink_pre = (SINK && !SPLIT) ? a.sinks[g * G + min(tid & 15, G - 1)] : 0.0f;
     // (kernel arguments count as invariant memory, which the barrier below does not hold in place:
     //  read the frequencies, which sit in the argument segment, through a pointer the compiler
@@ -198,40 +189,28 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     int t0 = k_begin + wave * TILE;
     // every ring slot is in bounds; a linear cache's splits past the position would only waste
     // bandwidth, so those wait for it
-    if (RING) fetch(kA, vA, t0);
+    if (SWA) fetch(kA, vA, t0);
     // The position comes by a scalar load, counted apart from the vector loads (lgkmcnt, not
     // vmcnt): the work that needs only the position and the query (cos/sin table, query and
     // new-token rotation) runs while the slot tile is still in flight.  The load waits for its
     // own result in the same statement; the memory clobber keeps the loads above in place (the
     // compiler would otherwise sink each one next to its use, behind the position check).
-    const int32_t p_in = load_scalar_i32(a.positions + b);
-    // decode: the new token's position; multi-token mode: the sequence's first new position
-    const int32_t pos = VERIFY ? p_in + tq : p_in;
+    const int32_t pos = load_scalar_i32(a.positions + b);
 
-    const bool pos_ok = VERIFY ? (p_in >= 0 && p_in <= a.max_position)
-                               : (pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap));
+    const bool pos_ok = pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap);
     if (!pos_ok) {
         if (!SPLIT && s == 0) {  // defined result: zero output, nothing appended
             for (int e = tid; e < G * DV; e += 256)
-                a.out[((int64_t)bq * a.Hq + g * G + e / DV) * DV + e % DV] = 0;
+                a.out[((int64_t)b * a.Hq + g * G + e / DV) * DV + e % DV] = 0;
         }
         return;
     }
-    // visible key rows [k_lo, n_valid)
-    int n_valid, k_lo = 0, slot_new = -1;
-    if constexpr (VERIFY) {
-        const int32_t kpos0 = (a.kpos_rel ? p_in : 0) + a.kpos_off;
-        n_valid = pos - kpos0 + 1;
-        k_lo = max(0, -kpos0);
-        if (SWA) k_lo = max(k_lo, n_valid - a.window);
-    } else {
-        n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
-        slot_new = SWA ? pos % a.window : pos;
-    }
+    const int n_valid = SWA ? min(a.window, pos + 1) : pos + 1;
+    const int slot_new = SWA ? pos % a.window : pos;
     if (k_begin >= n_valid) return;
     const int k_end = min(n_valid, k_begin + a.chunk);
-    const bool own_new = !VERIFY && slot_new >= k_begin && slot_new < k_end;
-    if (!RING) fetch(kA, vA, t0);
+    const bool own_new = slot_new >= k_begin && slot_new < k_end;
+    if (!SWA) fetch(kA, vA, t0);
 
     // ---- cos/sin of the position per frequency, once per workgroup
     if (tid < half) {
@@ -313,7 +292,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         for (int it = 0; it < VREG; ++it) {
             const int e = lane + 64 * it;
             const int row = e / VCH;
-            const bool live = t + row < k_end && (!VERIFY || t + row >= k_lo);
+            const bool live = t + row < k_end;
             uint16_t* dst = vt + row * VT_PITCH + (e % VCH) * VPL;
             if constexpr (FP8) {
                 const u32x4 z = u32x4{0u, 0u, 0u, 0u};
@@ -349,7 +328,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = t + kb * 16 + 4 * gq + i;
-                const float v = (j < k_end && (!VERIFY || j >= k_lo)) ? Sacc[kb][i] * sc : -INFINITY;
+                const float v = j < k_end ? Sacc[kb][i] * sc : -INFINITY;
                 Sacc[kb][i] = v;
                 mx = fmaxf(mx, v);
             }
@@ -423,7 +402,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             acc += *(const f32x4*)&sm.u.red_o[w][hh][d0] * f;
         }
         if (SPLIT) {
-            float* rec = a.partial + (((int64_t)bq * a.Hq + h) * a.nsplit + s) * PSTRIDE;
+            float* rec = a.partial + (((int64_t)b * a.Hq + h) * a.nsplit + s) * PSTRIDE;
             *(float2*)(rec + d0) = make_float2(acc[0], acc[1]);
             *(float2*)(rec + d0 + 2) = make_float2(acc[2], acc[3]);
             if (d0 == 0) *(float2*)(rec + DV) = make_float2(M, L);
@@ -431,7 +410,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             const float sc_o = L > 0.0f ? a.v_scale / L : 0.0f;
             const u32x2 o2 = u32x2{pack_bf16x2(acc[0] * sc_o, acc[1] * sc_o),
                                    pack_bf16x2(acc[2] * sc_o, acc[3] * sc_o)};
-            *(u32x2*)(a.out + ((int64_t)bq * a.Hq + h) * DV + d0) = o2;
+            *(u32x2*)(a.out + ((int64_t)b * a.Hq + h) * DV + d0) = o2;
         }
     }
 }
@@ -505,18 +484,17 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
     o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
 }
 
-template <bool SWA, bool SINK, int ROT, bool FP8, bool VERIFY = false>
+template <bool SWA, bool SINK, int ROT, bool FP8>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
-    const int nq = VERIFY ? a.B * a.q_per_seq : a.B;
-    const dim3 grid(a.nsplit, a.Hkv, nq);
+    const dim3 grid(a.nsplit, a.Hkv, a.B);
     if (a.nsplit == 1) {
-        decode_bf16_kernel<SWA, SINK, false, ROT, FP8, VERIFY><<<grid, 256, 0, st>>>(a);
+        decode_bf16_kernel<SWA, SINK, false, ROT, FP8><<<grid, 256, 0, st>>>(a);
         return hipGetLastError();
     }
-    decode_bf16_kernel<SWA, SINK, true, ROT, FP8, VERIFY><<<grid, 256, 0, st>>>(a);
+    decode_bf16_kernel<SWA, SINK, true, ROT, FP8><<<grid, 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_combine_kernel<SWA, SINK, VERIFY><<<dim3(a.Hq, nq), DV, 0, st>>>(a);
+    decode_combine_kernel<SWA, SINK, false><<<dim3(a.Hq, a.B), DV, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -540,21 +518,19 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStrea
     return a.cache_fp8 ? launch_kind<true>(a, swa, sink, st) : launch_kind<false>(a, swa, sink, st);
 }
 
-hipError_t launch_verify_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st) {
-    if (a.B == 0 || a.q_per_seq == 0) return hipSuccess;
-    if (a.nsplit > decode_max_splits() || a.q_per_seq < 0 || a.cache_fp8)
-        return hipErrorInvalidConfiguration;
-    if ((int64_t)a.B * a.q_per_seq > 65535) return hipErrorInvalidConfiguration;   // grid z
-    if (a.rope_dims <= 64) {
-        if (swa) return sink ? launch_typed<true, true, 2, false, true>(a, st)
-                             : launch_typed<true, false, 2, false, true>(a, st);
-        return sink ? launch_typed<false, true, 2, false, true>(a, st)
-                    : launch_typed<false, false, 2, false, true>(a, st);
+hipError_t launch_verify_combine(const DecodeArgs& a, bool swa, bool sink, hipStream_t st) {
+    const int64_t nq = (int64_t)a.B * a.q_per_seq;
+    if (nq == 0 || a.nsplit <= 1) return hipSuccess;
+    if (nq > 65535 || a.nsplit > decode_max_splits()) return hipErrorInvalidConfiguration;
+    const dim3 grid(a.Hq, (unsigned)nq);
+    if (swa) {
+        if (sink) decode_combine_kernel<true, true, true><<<grid, DV, 0, st>>>(a);
+        else decode_combine_kernel<true, false, true><<<grid, DV, 0, st>>>(a);
+    } else {
+        if (sink) decode_combine_kernel<false, true, true><<<grid, DV, 0, st>>>(a);
+        else decode_combine_kernel<false, false, true><<<grid, DV, 0, st>>>(a);
     }
-    if (swa) return sink ? launch_typed<true, true, 6, false, true>(a, st)
-                         : launch_typed<true, false, 6, false, true>(a, st);
-    return sink ? launch_typed<false, true, 6, false, true>(a, st)
-                : launch_typed<false, false, 6, false, true>(a, st);
+    return hipGetLastError();
 }
 
 }  // namespace mimo

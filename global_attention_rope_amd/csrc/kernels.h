@@ -79,11 +79,10 @@ struct DecodeArgs {
     int32_t B, Hq, Hkv, rope_dims, window, cap, max_position, chunk, nsplit;
     int32_t cache_fp8;       // caches hold e4m3 codes: the new token is coded with k_inv/v_inv;
     float k_inv, v_inv;      // the code scales are folded into score_scale_log2 and v_scale
-    // Multi-token mode (verify kernels): q/out/partials hold q_per_seq tokens per sequence
+    // Combine of multi-token partials: out/partials hold q_per_seq tokens per sequence
     // ([B * T, Hq, d]); positions holds each sequence's first token position st; token t sits at
-    // st + t and is already stored; key row j of the (linear) key space sits at position
-    // (kpos_rel ? st : 0) + kpos_off + j; rows of negative positions hold no token; sequences with
-    // st outside [0, max_position] get a zero output.
+    // st + t and saw key rows up to its own, row j sitting at position
+    // (kpos_rel ? st : 0) + kpos_off + j; sequences with st outside [0, max_position] get zeros.
     int32_t q_per_seq, kpos_rel, kpos_off;
     float score_scale_log2;
     float v_scale;
@@ -124,8 +123,6 @@ hipError_t launch_ring_unroll_bf16(const RingUnrollArgs& a, hipStream_t st);
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool window, bool sink, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);
-// Multi-token mode of the decode kernels (see DecodeArgs): grid over B * q_per_seq queries.
-hipError_t launch_verify_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);
 hipError_t launch_prefill_f32(const F32PrefillArgs& a, hipStream_t st);
 hipError_t launch_decode_f32(const F32DecodeArgs& a, hipStream_t st);
 
