@@ -4,8 +4,8 @@
 // One wave per token: lane l holds experts [l * EPL, (l + 1) * EPL) (EPL = E / 64), so a group of
 // E / n_group experts spans 64 / n_group whole lanes.  Group top-2 sums by a reduction ladder over
 // the group's lanes, group ranks by reading every group's score by lane index, then top_k rounds
-// of a wave-wide maximum of (score, index) keys.  Every cross-lane step is a DPP permute or a
-// lane-pair swap in registers (no LDS round trips).
+// of a wave-wide maximum score whose lowest holder is found by ballots.  Every cross-lane step is
+// a DPP permute, a lane-pair swap or a ballot (no LDS round trips).
 #include <math.h>
 #include <string.h>
 
@@ -25,12 +25,11 @@ struct RouterArgs {
     float scale;
 };
 
-// Order-preserving 64-bit key of (score, expert): larger score first, then lower index, so the
-// chosen expert of a round is the maximum key.
-__device__ __forceinline__ uint64_t rank_key(float v, int i) {
+// Order-preserving 32-bit key of a score: a larger score is a larger key (0 is below every
+// score, -inf included, and marks a chosen expert).
+__device__ __forceinline__ uint32_t score_key(float v) {
     const uint32_t u = __float_as_uint(v);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // monotonic in v
-    return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - i);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // x from lane (lane ^ step partner) for the reduction ladder: step 0 pairs lanes l, l^1 and
@@ -60,13 +59,9 @@ __device__ __forceinline__ float ladder_f(float x, int step) {
     return __uint_as_float(ladder(__float_as_uint(x), step));
 }
 
-__device__ __forceinline__ uint64_t ladder_max(uint64_t k, int steps) {
+__device__ __forceinline__ uint32_t ladder_max(uint32_t k) {
 #pragma unroll
-    for (int st = 0; st < steps; ++st) {
-        const uint64_t o = ((uint64_t)ladder((uint32_t)(k >> 32), st) << 32) |
-                           ladder((uint32_t)k, st);
-        k = o > k ? o : k;
-    }
+    for (int st = 0; st < 6; ++st) k = max(k, ladder(k, st));
     return k;
 }
 
@@ -119,18 +114,24 @@ __global__ __launch_bounds__(256) void router_kernel(const RouterArgs a) {
         rank += (o > gscore || (o == gscore && j < g)) ? 1 : 0;
     }
     const bool kept = rank < a.topk_group;
-    uint64_t key[EPL];
+    uint32_t key[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) key[j] = rank_key(kept ? c[j] : -INFINITY, lane * EPL + j);
-    // ---- top_k rounds of a wave-wide maximum key
+    for (int j = 0; j < EPL; ++j) key[j] = score_key(kept ? c[j] : -INFINITY);
+    // ---- top_k rounds: the largest key over the wave, then the lowest expert index holding it
+    //      (ballots per register slot: lane-major order within a slot, slot order within a lane)
     int my_idx = -1;   // lane k keeps the k-th choice
     float my_s = 0.0f, sum = 0.0f;
     for (int k = 0; k < a.top_k; ++k) {
-        uint64_t best = key[0];
+        uint32_t best = key[0];
 #pragma unroll
-        for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-        best = ladder_max(best, 6);
-        const int bi = 0xFFFF - (int)(uint32_t)(best & 0xFFFFu);
+        for (int j = 1; j < EPL; ++j) best = max(best, key[j]);
+        const uint32_t M = __builtin_amdgcn_readfirstlane(ladder_max(best));
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const uint64_t hit = __ballot(key[j] == M);
+            if (hit) bi = min(bi, (int)__builtin_ctzll(hit) * EPL + j);
+        }
         const int owner = bi / EPL, slot = bi - owner * EPL;
         float sv = s[0];
 #pragma unroll
