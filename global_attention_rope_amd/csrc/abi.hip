@@ -215,12 +215,13 @@ bool verify_tokens(const mimo_attn_params* p, int32_t S) {
 // Multi-token extend: key rows of the longest query — global: positions 0..max_start + S - 1
 // of the cache; sliding: the W + S rows of the workspace (never split up to 1024 rows).
 // Splits of whole 64-row tiles: enough (sequence, KV head, split) workgroups to fill the chip
-// about four times over (two resident per CU), at least 256 rows each.
+// once (two resident per CU; more rounds only add partials for the combine to merge), at least
+// 256 rows each.
 SplitGeometry verify_geometry(const mimo_attn_params* p, int32_t S, int32_t max_start) {
     const bool swa = p->layer_kind == MIMO_LAYER_SWA;
     const int64_t n_max = swa ? (int64_t)p->window + S : (int64_t)max_start + S;
     const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
-    int64_t ns = (2048 + pairs - 1) / pairs;
+    int64_t ns = (512 + pairs - 1) / pairs;
     if (ns > (n_max + 255) / 256) ns = (n_max + 255) / 256;
     if (ns > mimo::decode_max_splits()) ns = mimo::decode_max_splits();
     if (ns < 1) ns = 1;
