@@ -466,28 +466,33 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     pa.v_scale = p->v_scale;
     fill_omega(p, pa.omega_rev);
 
+    // a few new tokens run the multi-token tile kernel, more the prefill kernel
+    const bool few = verify_tokens(p, seq_len);
     if (swa) {
-        // workspace rows r < W: the ring's positions start - W + r (in position order); rows
-        // W + i: the new tokens, rotated.  The ring itself is refreshed only after it is read.
+        // workspace rows r < W: the ring's positions start - W + r (in position order; the tile
+        // kernel reads those from the ring in place); rows W + i: the new tokens, rotated.  The
+        // ring itself is refreshed only after it is read.
         const int64_t rows = (int64_t)p->window + seq_len;
         uint16_t* kws = (uint16_t*)workspace;
         uint16_t* vws = kws + (int64_t)p->batch * Hkv * rows * dqk;
-        mimo::RingUnrollArgs ua;
-        memset(&ua, 0, sizeof ua);
-        ua.k_cache = (const uint16_t*)k_cache;
-        ua.v_cache = (const uint16_t*)v_cache;
-        ua.start_pos = start_pos;
-        ua.k_ws = kws;
-        ua.v_ws = vws;
-        ua.B = p->batch;
-        ua.Hkv = p->num_kv_heads;
-        ua.dqk = p->qk_head_dim;
-        ua.dv = p->v_head_dim;
-        ua.W = p->window;
-        ua.ws_rows = (int32_t)rows;
-        ua.max_start = max_start;
-        rc = hip_status(mimo::launch_ring_unroll_bf16(ua, st), "ring unroll (bf16)");
-        if (rc != MIMO_OK) return rc;
+        if (!few) {
+            mimo::RingUnrollArgs ua;
+            memset(&ua, 0, sizeof ua);
+            ua.k_cache = (const uint16_t*)k_cache;
+            ua.v_cache = (const uint16_t*)v_cache;
+            ua.start_pos = start_pos;
+            ua.k_ws = kws;
+            ua.v_ws = vws;
+            ua.B = p->batch;
+            ua.Hkv = p->num_kv_heads;
+            ua.dqk = p->qk_head_dim;
+            ua.dv = p->v_head_dim;
+            ua.W = p->window;
+            ua.ws_rows = (int32_t)rows;
+            ua.max_start = max_start;
+            rc = hip_status(mimo::launch_ring_unroll_bf16(ua, st), "ring unroll (bf16)");
+            if (rc != MIMO_OK) return rc;
+        }
         ra.k_ws = kws;
         ra.v_ws = vws;
         ra.ws_rows = (int32_t)rows;
@@ -514,9 +519,12 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     }
     pa.k_sj = dqk;
     pa.v_sj = dv;
-    rc = hip_status(mimo::launch_rope_kv_bf16(ra, st), "key rotation (bf16)");
+    // (multi-token sliding extend: the ring is stored after the attention, which reads it)
+    mimo::RopeKVArgs ra_first = ra;
+    if (few && swa) ra_first.k_dst = ra_first.v_dst = nullptr;
+    rc = hip_status(mimo::launch_rope_kv_bf16(ra_first, st), "key rotation (bf16)");
     if (rc != MIMO_OK) return rc;
-    if (!verify_tokens(p, seq_len))
+    if (!few)
         return hip_status(mimo::launch_prefill_bf16(pa, swa, sinks != nullptr, st), "extend (bf16)");
 
     // a few new tokens: the multi-token tile kernel over the same key rows
@@ -530,6 +538,11 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     va.sinks = sinks;
     va.out = (uint16_t*)out;
     va.partial = (float*)((uint8_t*)workspace + extend_rows_ws(p, seq_len));
+    if (swa) {
+        va.ring_k = (const uint16_t*)k_cache;
+        va.ring_v = (const uint16_t*)v_cache;
+        va.ring_w = p->window;
+    }
     va.k_sb = pa.k_sb;
     va.k_sh = pa.k_sh;
     va.v_sb = pa.v_sb;
@@ -550,7 +563,14 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     va.v_scale = p->v_scale;
     fill_omega(p, va.omega_rev);
     rc = hip_status(mimo::launch_verify_tiles_bf16(va, swa, sinks != nullptr, st), "extend (bf16)");
-    if (rc != MIMO_OK || geo.nsplit <= 1) return rc;
+    if (rc != MIMO_OK) return rc;
+    if (swa) {   // now store the new tokens in the ring
+        mimo::RopeKVArgs rs = ra;
+        rs.k_ws = rs.v_ws = nullptr;
+        rc = hip_status(mimo::launch_rope_kv_bf16(rs, st), "ring store (bf16)");
+        if (rc != MIMO_OK) return rc;
+    }
+    if (geo.nsplit <= 1) return rc;
     mimo::DecodeArgs da;   // the combine's view of the partials
     memset(&da, 0, sizeof da);
     da.positions = start_pos;

@@ -23,6 +23,11 @@ struct VerifyArgs {
     const float* sinks;
     uint16_t* out;
     float* partial;
+    // optional ring cache [B,Hkv,ring_w,d]: key rows j < ring_w are read from it at slot
+    // (position of row j) % ring_w instead of from k/v
+    const uint16_t* ring_k;
+    const uint16_t* ring_v;
+    int32_t ring_w;
     int64_t k_sb, k_sh, v_sb, v_sh;
     int32_t B, T, TP, Hq, Hkv, rope_dims, window, kpos_rel, kpos_off, max_start, chunk, nsplit;
     float score_scale_log2;

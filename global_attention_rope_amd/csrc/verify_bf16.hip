@@ -78,6 +78,11 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     //      chunk (P % 24) ^ swizzle; V row P / 16, chunk (P % 16) ^ swizzle)
     const uint16_t* kslice = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
     const uint16_t* vslice = a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+    // rows held by a ring cache (the earlier positions of a sliding layer), read in place
+    const int ring_w = a.ring_k ? a.ring_w : 0;
+    const int64_t ring_row0 = ((int64_t)b * a.Hkv + kvh) * (ring_w > 0 ? ring_w : 1);
+    const uint16_t* ring_k = ring_w > 0 ? a.ring_k + ring_row0 * DQK : nullptr;
+    const uint16_t* ring_v = ring_w > 0 ? a.ring_v + ring_row0 * DV : nullptr;
     int k_row[K_DMA], k_off[K_DMA], v_row[V_DMA], v_off[V_DMA];
 #pragma unroll
     for (int i = 0; i < K_DMA; ++i) {
@@ -103,12 +108,16 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
 #pragma unroll
         for (int i = 0; i < K_DMA; ++i) {
             const int j = min(max(j0 + k_row[i], jmin), nk - 1);
-            dma16(kslice + (int64_t)j * DQK + k_off[i], kst + (wave * K_DMA + i) * 1024);
+            const uint16_t* src = j < ring_w ? ring_k + (int64_t)((kpos0 + j) % ring_w) * DQK
+                                             : kslice + (int64_t)j * DQK;
+            dma16(src + k_off[i], kst + (wave * K_DMA + i) * 1024);
         }
 #pragma unroll
         for (int i = 0; i < V_DMA; ++i) {
             const int j = min(max(j0 + v_row[i], jmin), nk - 1);
-            dma16(vslice + (int64_t)j * DV + v_off[i], vst + (wave * V_DMA + i) * 1024);
+            const uint16_t* src = j < ring_w ? ring_v + (int64_t)((kpos0 + j) % ring_w) * DV
+                                             : vslice + (int64_t)j * DV;
+            dma16(src + v_off[i], vst + (wave * V_DMA + i) * 1024);
         }
     };
     if (n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
