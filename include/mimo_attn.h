@@ -161,9 +161,10 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
 /* Workspace bytes mimo_attn_extend needs for seq_len new tokens and starts up to max_start: SWA
  * bf16 layers lay the ring's content out in position order in front of the new tokens' rotated
  * keys and values (B * Hkv * (window + seq_len) * (dqk + dv) * 2 bytes, rounded up to 256);
- * GLOBAL layers read the cache in place.  Up to 16 new tokens per sequence run one query block
- * per token (the decode kernels' multi-token mode), which adds split partials
- * (B * seq_len * Hq * splits * (dv + 2) * 4 bytes) when the key range is cut into several splits.
+ * GLOBAL layers read the cache in place.  Up to 16 new tokens per sequence run a tile kernel
+ * whose query columns are the (query head, new token) pairs of a KV group, split over the key
+ * rows, which adds split partials (B * seq_len * Hq * splits * (dv + 2) * 4 bytes) when the key
+ * range is cut into several splits.
  * Returns 0 for invalid parameters. */
 size_t mimo_attn_extend_workspace_size(const mimo_attn_params* p, int32_t seq_len,
                                        int32_t max_start);

@@ -120,7 +120,7 @@ def test_workspace_sizes():
     assert mimo.extend_workspace_size(_ga(batch=2), 1000, 5000) == 0
     assert mimo.extend_workspace_size(_swa(), -1, 0) == 0
     assert mimo.extend_workspace_size(_swa(), 4, -1) == 0
-    # a few new tokens: one query block per token, split partials for long global caches
+    # a few new tokens: the multi-token tile kernel, split partials for long global caches
     assert mimo.extend_workspace_size(_ga(batch=2), 4, 100) == 0
     ws = mimo.extend_workspace_size(_ga(batch=64), 4, 32768)
     assert ws > 0 and ws % (64 * 4 * 64 * 130 * 4) == 0

@@ -63,7 +63,7 @@ CASES = [
     dict(kind=0, B=3, S=129, Hq=16, Hkv=1, sinks=False, starts=[0, 37, 700]),
     dict(kind=0, B=2, S=1, Hq=8, Hkv=2, sinks=True, starts=[5, 1234]),
     dict(kind=0, B=1, S=300, Hq=8, Hkv=2, sinks=False, starts=[64]),            # tile-aligned
-    # up to 16 new tokens: one query block per token (the decode kernels' multi-token mode)
+    # up to 16 new tokens: the multi-token tile kernel ((head, token) query columns)
     dict(kind=1, B=3, S=4, Hq=16, Hkv=2, sinks=True, starts=[0, 2, 1000]),       # start < W
     dict(kind=1, B=2, S=16, Hq=8, Hkv=1, sinks=True, starts=[126, 131], W=128),
     dict(kind=1, B=2, S=7, Hq=8, Hkv=8, sinks=False, starts=[0, 9], W=1),

@@ -83,8 +83,8 @@ def test_decode_graph_replays_match_eager(fp8):
 
 @pytest.mark.parametrize("S", [4, 40])
 def test_extend_graph_replays_match_eager(S):
-    """A captured extend step (global and sliding layer; 4 tokens run the decode kernels'
-    multi-token mode, 40 the prefill kernel) replayed on the same caches: every replay equals
+    """A captured extend step (global and sliding layer; 4 tokens run the multi-token tile
+    kernel, 40 the prefill kernel) replayed on the same caches: every replay equals
     the eager call on a copy of the state."""
     B, P0, R = 2, 500, 3
     print(f"[case] graph extend S={S}", flush=True)
