@@ -60,9 +60,15 @@ constexpr int kBufferFormat = 0x00020000;
 // 32-bit load of a workgroup-uniform address through the scalar cache, waited for in the same
 // statement (its counter is the scalar one, so vector loads issued before it stay in flight).
 // The memory clobber also keeps every earlier load ahead of it.
+// (The address goes through readfirstlane, which is free for a value already in scalar registers
+//  and keeps the operand a scalar register pair wherever the compiler is unsure of uniformity.)
 __device__ __forceinline__ int32_t load_scalar_i32(const int32_t* p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    const int32_t* ps = (const int32_t*)(uintptr_t)(lo | (hi << 32));
     int32_t v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ps) : "memory");
     return v;
 }
 

@@ -113,17 +113,48 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int qblk = WINDOW ? qrank : nqblk - 1 - qrank;   // global: heaviest blocks first
     const int h = GROUPED ? hu * NW + wave : hu;
     const int kvh = (GROUPED ? hu * NW : hu) / (Hq / a.Hkv);
-    const int32_t p0 = a.start_pos[b];
     const int r = a.rope_dims, half = r >> 1;
+    // GROUPED: the frequencies of this thread's entries of the rows' cos/sin table (entry
+    // e = row * r/2 + frequency, thread tid taking e = tid, tid + 256, ...), requested first, from
+    // the argument segment through a pointer the compiler cannot trace back to it, so that the
+    // loads stay ahead of the barrier that follows the table
+    constexpr int TAB = GROUPED ? (QPW * kMaxRopeHalfArgs + NW * 64 - 1) / (NW * 64) : 1;
+    double om_tab[TAB];
+    if constexpr (GROUPED) {
+        const char* kargs = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(kargs));
+        const __attribute__((address_space(1))) double* om_args =
+            (const __attribute__((address_space(1))) double*)(kargs + offsetof(PrefillArgs, omega_rev));
+#pragma unroll
+        for (int k = 0; k < TAB; ++k) {
+            const int e = tid + k * NW * 64;
+            om_tab[k] = e < QPW * half ? om_args[e % half] : 0.0;
+        }
+    }
+    // (the start position comes by a scalar load that waits for nothing but itself, so the vector
+    //  loads issued before it stay in flight)
+    int32_t p0 = 0;
 
     // Key rows: row j sits at position kpos0 + j.  Query row i (position p0 + i) thus meets key
     // row i + shift at its own position; rows below jmin (negative positions) hold no token, and
     // the last query row reaches key row nk - 1.  A sequence outside the accepted start range
-    // streams no tiles and gets a zero output.
-    const bool seq_ok = a.max_start < 0 || (unsigned)p0 <= (unsigned)a.max_start;
-    const int32_t kpos0 = (a.kpos_rel ? (seq_ok ? p0 : 0) : 0) + a.kpos_off;
-    const int shift = (seq_ok ? p0 : 0) - kpos0;
-    const int jmin = max(0, -kpos0);
+    // streams no tiles and gets a zero output.  When the keys are the sequence's own rows and
+    // every start is accepted, none of this depends on the start position (start_pos >= 0), so
+    // the tile loads below go out before it arrives.
+    bool seq_ok;
+    int shift, jmin;
+    const bool own_rows = a.max_start < 0 && a.kpos_rel && a.kpos_off >= 0;
+    if (own_rows) {
+        seq_ok = true;
+        shift = -a.kpos_off;
+        jmin = 0;
+    } else {
+        p0 = load_scalar_i32(a.start_pos + b);
+        seq_ok = a.max_start < 0 || (unsigned)p0 <= (unsigned)a.max_start;
+        const int32_t kpos0 = (a.kpos_rel ? (seq_ok ? p0 : 0) : 0) + a.kpos_off;
+        shift = (seq_ok ? p0 : 0) - kpos0;
+        jmin = max(0, -kpos0);
+    }
     const int nk = S + shift;
 
     const int W = a.window;
@@ -201,18 +232,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
         if constexpr (GROUPED) {
+            // rotation partners, requested with the rows themselves
+            u32x4 pw[KCH];
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int d0 = 16 * c + 8 * g;
+                if (d0 < r) pw[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : d0 - half));
+            }
+            if (own_rows) p0 = load_scalar_i32(a.start_pos + b);
             // The NW waves share the 32 rows (one head each): the cos/sin of the rows' positions
-            // per frequency are evaluated once for the workgroup into a table in stage 1, which
-            // no tile uses before the first tile step.
-            static_assert(STAGES == 2, "table lives in stage 1");   // 32 x 97 x 8 B <= K_TILE
-            // (row pitch half + 1 entries: the 32 rows' reads of one frequency hit distinct banks)
+            // per frequency are evaluated once for the workgroup into a table in K stage 1, which
+            // no tile uses before the first tile step.  Rows are padded by one entry (so that the
+            // 32 rows' reads of one frequency hit distinct banks) while 32 x (r/2 + 1) entries of
+            // 8 bytes fit the stage, i.e. up to r = 190; at r = 192 they are packed.
+            static_assert(STAGES == 2, "table lives in stage 1");
             float2* cs = (float2*)(smem + K_TILE);
-            const int pitch = half + 1;
-            for (int e = tid; e < QPW * half; e += NW * 64) {
-                const int row = e / half, f = e - row * half;
-                float c, sn;
-                rope_cos_sin_rev(p0 + min(q_first + row, S - 1), a.omega_rev[f], c, sn);
-                cs[row * pitch + f] = make_float2(c, sn);
+            const int pitch = QPW * (half + 1) * 8 <= K_TILE ? half + 1 : half;
+#pragma unroll
+            for (int k = 0; k < TAB; ++k) {
+                const int e = tid + k * NW * 64;
+                if (e < QPW * half) {
+                    const int row = e / half, f = e - row * half;
+                    float c, sn;
+                    rope_cos_sin_rev(p0 + min(q_first + row, S - 1), om_tab[k], c, sn);
+                    cs[row * pitch + f] = make_float2(c, sn);
+                }
             }
             block_sync_lds();
 #pragma unroll
@@ -220,11 +264,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 const int d0 = 16 * c + 8 * g;
                 if (d0 < r) {
                     const bool lower = d0 < half;
-                    const u32x4 pw = *(const u32x4*)(qrow + (lower ? d0 + half : d0 - half));
                     const float2* e = cs + l32 * pitch + (lower ? d0 : d0 - half);
                     float x[8], y[8];
                     unpack8(qw[c], x);
-                    unpack8(pw, y);
+                    unpack8(pw[c], y);
                     const float sgn = lower ? -1.0f : 1.0f;
 #pragma unroll
                     for (int t = 0; t < 8; ++t) {
@@ -237,6 +280,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 Qb[c] = as_bf16x8(qw[c]);
             }
         } else {
+            if (own_rows) p0 = load_scalar_i32(a.start_pos + b);
 #pragma unroll
             for (int c = 0; c < KCH; ++c) {
                 const int d0 = 16 * c + 8 * g;

@@ -91,6 +91,12 @@ def test_tiny_swa_fp32_full():
     # rotated operands (all 192 dims here) stays inside the tolerance on the first rows
     dict(kind=0, B=1, S=257, Hq=8, Hkv=2, sinks=False, starts=[0], r=192, theta=10.0,
          q_scale=0.25),
+    # sliding layers whose GQA group is a multiple of 4 run the grouped kernel, which builds a
+    # cos/sin table of the rows' positions: at the widest rotation (every dim, its rows packed)
+    # and with no rotation at all
+    dict(kind=1, B=1, S=200, Hq=8, Hkv=2, sinks=True, starts=[3], r=192, theta=10.0,
+         q_scale=0.25),
+    dict(kind=1, B=2, S=150, Hq=8, Hkv=2, sinks=True, starts=[0, 300], r=0),
 ])
 def test_prefill_bf16_small(case):
     case = dict(case)
