@@ -75,14 +75,21 @@ CASES = [
 
 @pytest.mark.parametrize("ci", range(len(CASES)))
 def test_extend_against_synthetic_cache(ci):
-    case = dict(CASES[ci])
+    run_extend_case(CASES[ci], 5000 + ci)
+
+
+def run_extend_case(case, seed, q_scale=1.0):
+    """One extend call on a synthetic cache: outputs and caches afterwards against the oracle."""
+    case = dict(case)
     starts = case.pop("starts")
     w = _wl(**case)
     S = w.seq
     _note(f"extend {case} starts {starts}")
-    q, k, v, s = synth.layer_inputs(w, 5000 + ci, device=DEV)
+    q, k, v, s = synth.layer_inputs(w, seed, device=DEV)
+    if q_scale != 1.0:
+        q = q * q_scale  # a power of two: exact in bf16
     cap = w.window if w.layer_kind == 1 else max(starts) + S + 5
-    kc, vc = synth.cache_contents(w, 5100 + ci, w.batch, cap, device=DEV)
+    kc, vc = synth.cache_contents(w, seed + 100, w.batch, cap, device=DEV)
     kc0, vc0 = to_np64(kc), to_np64(vc)
     okc, ovc, kpos, count = _oracle_cache(w, kc, vc, starts)
     sp = torch.tensor(starts, dtype=torch.int32, device=DEV)

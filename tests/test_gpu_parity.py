@@ -184,12 +184,14 @@ def test_prefill_empty_and_invalid_arguments():
 # ----------------------------------------------------------------------------- decode
 
 
-def _decode_case(w, positions, seed, cap=None):
+def _decode_case(w, positions, seed, cap=None, q_scale=1.0):
     """Random cache state + one decode step on the GPU, and the oracle on the same state."""
     B = len(positions)
     swa = w.layer_kind == 1
     cap = w.window if swa else (cap if cap else max(positions) + 1)
     q, kn, vn, s, kc, vc = synth.decode_inputs(w, seed, B, cap, device=DEV)
+    if q_scale != 1.0:
+        q = q * q_scale  # a power of two: exact in bf16
     kc0, vc0 = _f32(kc), _f32(vc)
     pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)
     out = mimo.decode(_params(w, B), q, kn, vn, pos_t, max(positions), kc, vc, sinks=s)

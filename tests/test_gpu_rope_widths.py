@@ -1,0 +1,51 @@
+"""GPU parity across rotation widths: prefill, decode, chunked extend and the multi-token extend
+with no rotated dim, with two thirds of the head rotated and with every dim rotated.
+
+The kernels find the partner of a rotated dim in different places depending on the width (the
+same 16-dim chunk, another chunk of the lane, a table row), and the decode kernel compiles a
+separate variant for widths beyond 64, so each path is run at each width.  Queries are scaled by
+1/4 (a power of two, exact in bf16) and theta is 10, so that the angles sweep many turns while the
+softmax stays flat enough for the bf16 rounding of fully rotated operands to stay inside the
+tolerance.  Seeds: 7000 + width + kind (+ path offset).
+"""
+import pytest
+
+from tests.gpu_helpers import assert_close
+from tests.test_gpu_extend import run_extend_case
+from tests.test_gpu_parity import _decode_case, _note, _run_prefill, _wl
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = [0, 128, 192]
+Q_SCALE = 0.25
+THETA = 10.0
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("r", WIDTHS)
+def test_prefill_rope_widths(kind, r):
+    # GQA group 4: the sliding kind takes its grouped kernel (cos/sin table of the rows)
+    w = _wl(kind=kind, B=2, S=150, Hq=8, Hkv=2, sinks=kind == 1, r=r, theta=THETA)
+    _note(f"prefill kind={kind} r={r}")
+    *_, out, ref, _, _, _ = _run_prefill(w, seed=7000 + r + kind, starts=[0, 517], q_scale=Q_SCALE)
+    assert_close(out, ref, what=f"prefill kind={kind} r={r}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("r", WIDTHS)
+def test_decode_rope_widths(kind, r):
+    positions = [0, 130, 3000]
+    w = _wl(kind=kind, B=len(positions), S=1, Hq=8, Hkv=2, sinks=kind == 1, r=r, theta=THETA)
+    _note(f"decode kind={kind} r={r} positions {positions}")
+    out, ref, *_ = _decode_case(w, positions, seed=7100 + r + kind, q_scale=Q_SCALE)
+    assert_close(out, ref, what=f"decode kind={kind} r={r}")
+
+
+@pytest.mark.parametrize("S", [40, 4])
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("r", WIDTHS)
+def test_extend_rope_widths(kind, r, S):
+    # S = 40: the chunked path (prefill kernel on the cache); S = 4: the multi-token tile kernel
+    case = dict(kind=kind, B=2, S=S, Hq=8, Hkv=2, sinks=kind == 1, starts=[3, 700], r=r,
+                theta=THETA)
+    run_extend_case(case, 7200 + r + kind + S, q_scale=Q_SCALE)
