@@ -1,9 +1,10 @@
 """GPU parity across rotation widths: prefill, decode, chunked extend and the multi-token extend
-with no rotated dim, with two thirds of the head rotated and with every dim rotated.
+with no rotated dim, with 16 and 48 (half-widths 8 and 24: a dim's partner sits in the other
+half of the wave), with two thirds of the head rotated and with every dim rotated.
 
-The kernels find the partner of a rotated dim in different places depending on the width (the
-same 16-dim chunk, another chunk of the lane, a table row), and the decode kernel compiles a
-separate variant for widths beyond 64, so each path is run at each width.  Queries are scaled by
+The kernels find the partner of a rotated dim in different places depending on the width (another
+lane, another chunk of the same lane, a table row), and the decode kernel compiles a separate
+variant for widths beyond 64, so each path is run at each width.  Queries are scaled by
 1/4 (a power of two, exact in bf16) and theta is 10, so that the angles sweep many turns while the
 softmax stays flat enough for the bf16 rounding of fully rotated operands to stay inside the
 tolerance.  Seeds: 7000 + width + kind (+ path offset).
@@ -16,7 +17,7 @@ from tests.test_gpu_parity import _decode_case, _note, _run_prefill, _wl
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = [0, 128, 192]
+WIDTHS = [0, 16, 48, 128, 192]
 Q_SCALE = 0.25
 THETA = 10.0
 
