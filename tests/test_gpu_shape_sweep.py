@@ -1,5 +1,6 @@
-"""GPU parity across rotation widths: prefill, decode, chunked extend and the multi-token extend
-with no rotated dim, with 16 and 48 (half-widths 8 and 24: a dim's partner sits in the other
+"""GPU parity over head shapes the configurations do not reach: rotation widths and GQA group sizes.
+
+Rotation widths, on prefill, decode, chunked extend and the multi-token extend: no rotated dim, with 16 and 48 (half-widths 8 and 24: a dim's partner sits in the other
 half of the wave), with two thirds of the head rotated and with every dim rotated.
 
 The kernels find the partner of a rotated dim in different places depending on the width (another
@@ -50,3 +51,26 @@ def test_extend_rope_widths(kind, r, S):
     case = dict(kind=kind, B=2, S=S, Hq=8, Hkv=2, sinks=kind == 1, starts=[3, 700], r=r,
                 theta=THETA)
     run_extend_case(case, 7200 + r + kind + S, q_scale=Q_SCALE)
+
+
+# ----------------------------------------------------------------------------- GQA group sizes
+# The decode kernel packs a group's query heads as the 16 columns of its products and the
+# multi-token kernel packs (head, token) pairs as columns, so group sizes from 1 to 16 (and, for
+# extend, token counts that fill a column block exactly or leave it ragged) are run on both kinds.
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 1)])
+def test_decode_group_sizes(kind, Hq, Hkv):
+    positions = [7, 129, 2500]
+    w = _wl(kind=kind, B=len(positions), S=1, Hq=Hq, Hkv=Hkv, sinks=kind == 1)
+    _note(f"decode kind={kind} Hq={Hq} Hkv={Hkv}")
+    out, ref, *_ = _decode_case(w, positions, seed=7300 + Hq + Hkv + kind)
+    assert_close(out, ref, what=f"decode kind={kind} group {Hq // Hkv}")
+
+
+@pytest.mark.parametrize("S", [1, 3, 16])
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 1)])
+def test_extend_group_sizes(kind, Hq, Hkv, S):
+    case = dict(kind=kind, B=2, S=S, Hq=Hq, Hkv=Hkv, sinks=kind == 1, starts=[0, 301])
+    run_extend_case(case, 7400 + Hq + Hkv + kind + S)
