@@ -43,21 +43,34 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     const int Hq = a.Hq, T = a.T, TP = a.TP;
     const int G = Hq / a.Hkv;
 
-    // key rows: row j sits at position kpos0 + j, token t meets row t + shift at its own position
-    const int32_t st = a.start_pos[b];
-    const bool seq_ok = (unsigned)st <= (unsigned)a.max_start;
-    const int32_t kpos0 = (a.kpos_rel ? (seq_ok ? st : 0) : 0) + a.kpos_off;
-    const int shift = (seq_ok ? st : 0) - kpos0;
-    const int jmin = max(0, -kpos0);
-    const int nk = T + shift;                        // rows the last token reaches
-    const int W = a.window;
-
     // this lane's column: query head kvh * G + hl, token t
     const int col = wave * 32 + l32;
     const int hl = col / TP, t = col - hl * TP;
     const bool col_ok = hl < G && t < T;
     const int h = kvh * G + min(hl, G - 1);
     const int tq = min(t, T - 1);
+
+    // the column's query row and the rotation partners of its rotated dims go out first: they do
+    // not depend on the start position, which then comes by a scalar load that leaves them in flight
+    const uint16_t* qrow = a.q + (((int64_t)b * T + tq) * Hq + h) * DQK;
+    const int r = a.rope_dims, half = r >> 1;
+    u32x4 qw[KCH], pw[KCH];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const int d0 = 16 * c + 8 * g;
+        if (d0 < r) pw[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : d0 - half));
+    }
+
+    // key rows: row j sits at position kpos0 + j, token t meets row t + shift at its own position
+    const int32_t st = load_scalar_i32(a.start_pos + b);
+    const bool seq_ok = (unsigned)st <= (unsigned)a.max_start;
+    const int32_t kpos0 = (a.kpos_rel ? (seq_ok ? st : 0) : 0) + a.kpos_off;
+    const int shift = (seq_ok ? st : 0) - kpos0;
+    const int jmin = max(0, -kpos0);
+    const int nk = T + shift;                        // rows the last token reaches
+    const int W = a.window;
 
     if (!seq_ok) {   // defined result: zero output (a split combine writes the zeros itself)
         if (!SPLIT && col_ok) {
@@ -125,21 +138,15 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     // ---- Q^T operands of this column, rotated at the token's position, in registers
     bf16x8 Qb[KCH];
     {
-        const uint16_t* qrow = a.q + (((int64_t)b * T + tq) * Hq + h) * DQK;
-        const int r = a.rope_dims, half = r >> 1;
         const int32_t pos = st + tq;
-        u32x4 qw[KCH];
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int d0 = 16 * c + 8 * g;
             if (d0 < r) {
                 const bool lower = d0 < half;
-                const u32x4 pw = *(const u32x4*)(qrow + (lower ? d0 + half : d0 - half));
                 float x[8], y[8];
                 unpack8(qw[c], x);
-                unpack8(pw, y);
+                unpack8(pw[c], y);
                 const int f0 = lower ? d0 : d0 - half;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
