@@ -68,11 +68,13 @@ def _check_key_codes(gpu_codes, exact_rot, what):
     return frac
 
 
-def _decode8_case(w, positions, seed):
+def _decode8_case(w, positions, seed, q_scale=1.0):
     B = len(positions)
     swa = w.layer_kind == 1
     cap = w.window if swa else max(positions) + 1
     q, kn, vn, s, _, _ = synth.decode_inputs(w, seed, B, 1, device=DEV)
+    if q_scale != 1.0:
+        q = q * q_scale  # a power of two: exact in bf16
     kc8, vc8 = synth.fp8_cache_contents(w, seed + 1, B, cap, device=DEV)
     kc0, vc0 = _np8(kc8), _np8(vc8)
     pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)

@@ -1,6 +1,7 @@
 """GPU parity over head shapes the configurations do not reach: rotation widths and GQA group sizes.
 
-Rotation widths, on prefill, decode, chunked extend and the multi-token extend: no rotated dim,
+Rotation widths, on prefill, decode (bf16 and fp8 caches), chunked extend and the multi-token
+extend: no rotated dim,
 16 and 48 (half-widths 8 and 24: a dim's partner sits in the other half of the wave), two thirds
 of the head and every dim.
 
@@ -15,6 +16,7 @@ import pytest
 
 from tests.gpu_helpers import assert_close
 from tests.test_gpu_extend import run_extend_case
+from tests.test_gpu_fp8 import _check_key_codes, _decode8_case, _np8
 from tests.test_gpu_parity import _decode_case, _note, _run_prefill, _wl
 
 pytestmark = pytest.mark.gpu
@@ -42,6 +44,24 @@ def test_decode_rope_widths(kind, r):
     _note(f"decode kind={kind} r={r} positions {positions}")
     out, ref, *_ = _decode_case(w, positions, seed=7100 + r + kind, q_scale=Q_SCALE)
     assert_close(out, ref, what=f"decode kind={kind} r={r}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("r", WIDTHS)
+def test_decode_fp8_rope_widths(kind, r):
+    # fp8 caches: the query's dims are taken in the order one 16-byte load of key codes splits
+    # into, and the appended key is coded after its rotation
+    positions = [0, 130, 3000]
+    w = _wl(kind=kind, B=len(positions), S=1, Hq=8, Hkv=2, sinks=kind == 1, r=r, theta=THETA)
+    _note(f"fp8 decode kind={kind} r={r} positions {positions}")
+    out, ref, krot, _, vcode, kc8, vc8, _, _ = _decode8_case(w, positions, 7500 + r + kind,
+                                                             q_scale=Q_SCALE)
+    assert_close(out, ref, what=f"fp8 decode kind={kind} r={r}")
+    kc1, vc1 = _np8(kc8), _np8(vc8)
+    for b, p in enumerate(positions):
+        slot = p % w.window if kind == 1 else p
+        assert (vc1[b, :, slot] == vcode[b]).all(), f"seq {b}: value codes"
+        _check_key_codes(kc1[b, :, slot], krot[b], f"seq {b} r={r}")
 
 
 @pytest.mark.parametrize("S", [40, 4])
