@@ -1,9 +1,8 @@
 """GPU parity over head shapes the configurations do not reach: rotation widths and GQA group sizes.
 
 Rotation widths, on prefill, decode (bf16 and fp8 caches), chunked extend and the multi-token
-extend: no rotated dim,
-16 and 48 (half-widths 8 and 24: a dim's partner sits in the other half of the wave), two thirds
-of the head and every dim.
+extend: no rotated dim, 16 and 48 (half-widths 8 and 24: a dim's partner sits in the other half of
+the wave), two thirds of the head and every dim.
 
 The kernels find the partner of a rotated dim in different places depending on the width (another
 lane, another chunk of the same lane, a table row), and the decode kernel compiles a separate
