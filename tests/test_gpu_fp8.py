@@ -152,10 +152,17 @@ def test_decode_fp8_full_size(kind):
 def test_prefill_writes_fp8_caches_and_decode_continues(kind):
     """Prefill storing coded caches (value codes bit for bit, key codes neighbour-valid), its
     output unchanged, then decode steps over the coded cache against the oracle's own chain."""
+    run_prefill_fp8_chain(kind, seed=11300 + kind)
+
+
+def run_prefill_fp8_chain(kind, seed, r=64, theta=None, q_scale=1.0):
+    """One prefill writing fp8 caches and one decode step over them, both against the oracle."""
     S = 300
-    w = _wl(kind=kind, B=2, S=S, Hq=16, Hkv=2, sinks=kind == 1)
-    _note(f"fp8 prefill cache kind={kind}")
-    q, k, v, s = synth.layer_inputs(w, 11300 + kind, device=DEV)
+    w = _wl(kind=kind, B=2, S=S, Hq=16, Hkv=2, sinks=kind == 1, r=r, theta=theta)
+    _note(f"fp8 prefill cache kind={kind} r={r}")
+    q, k, v, s = synth.layer_inputs(w, seed, device=DEV)
+    if q_scale != 1.0:
+        q = q * q_scale  # a power of two: exact in bf16
     starts = [0, 11]
     sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
     cap = w.window if kind == 1 else S + max(starts) + 8
@@ -177,24 +184,31 @@ def test_prefill_writes_fp8_caches_and_decode_continues(kind):
         _check_key_codes(kc1[b][:, slots], krot[b, tk].transpose(1, 0, 2), f"prefill seq {b}")
         stored[b] = (slots, st + tk)
     # decode one more token over the coded cache; the oracle's chain uses its own codes
-    qd, kd, vd, _, _, _ = synth.decode_inputs(w, 11400 + kind, 2, 1, device=DEV)
+    qd, kd, vd, _, _, _ = synth.decode_inputs(w, seed + 100, 2, 1, device=DEV)
+    if q_scale != 1.0:
+        qd = qd * q_scale
     dpos = [S + st for st in starts]
     dec = mimo.decode(_p8(w), qd, kd, vd, torch.tensor(dpos, dtype=torch.int32, device=DEV),
                       max(dpos), kc8, vc8, sinks=s)
     torch.cuda.synchronize()
     inv_k = np.float32(1) / np.float32(KS)
-    L = max(len(stored[b][0]) for b in stored)
+    # a linear cache also holds the positions before the prompt's start, which this test never
+    # wrote: their slots keep the zero codes they were allocated with (keys and values 0.0), and
+    # the decode attends to them like any earlier position
+    lead = {b: (starts[b] if kind == 0 else 0) for b in stored}
+    L = max(len(stored[b][0]) + lead[b] for b in stored)
     okc = np.zeros((2, w.num_kv_heads, L, 192), np.uint8)
     ovc = np.zeros((2, w.num_kv_heads, L, 128), np.uint8)
     kpos = np.zeros((2, L), np.int32)
     cnt = np.zeros(2, np.int32)
     for b, (slots, poss) in stored.items():
-        n = len(slots)
+        n, z = len(slots), lead[b]
         tk = poss - starts[b]
-        okc[b, :, :n] = oracle.e4m3_encode(krot[b, tk].astype(np.float32), inv_k).transpose(1, 0, 2)
-        ovc[b, :, :n] = oracle.e4m3_encode(vin[b, tk], np.float32(1) / np.float32(VS)).transpose(1, 0, 2)
-        kpos[b, :n] = poss
-        cnt[b] = n
+        kpos[b, :z] = np.arange(z)
+        okc[b, :, z:z + n] = oracle.e4m3_encode(krot[b, tk].astype(np.float32), inv_k).transpose(1, 0, 2)
+        ovc[b, :, z:z + n] = oracle.e4m3_encode(vin[b, tk], np.float32(1) / np.float32(VS)).transpose(1, 0, 2)
+        kpos[b, z:z + n] = poss
+        cnt[b] = z + n
     dref, *_ = oracle.decode_fp8(_oparams(w), _f32(qd), _f32(kd), _f32(vd), np.array(dpos, np.int32),
                                  okc, ovc, kpos, cnt, KS, VS, _f32(s))
     assert_close(dec, dref, what="decode after an fp8 prefill")

@@ -15,7 +15,7 @@ import pytest
 
 from tests.gpu_helpers import assert_close
 from tests.test_gpu_extend import run_extend_case
-from tests.test_gpu_fp8 import _check_key_codes, _decode8_case, _np8
+from tests.test_gpu_fp8 import _check_key_codes, _decode8_case, _np8, run_prefill_fp8_chain
 from tests.test_gpu_parity import _decode_case, _note, _run_prefill, _wl
 
 pytestmark = pytest.mark.gpu
@@ -61,6 +61,13 @@ def test_decode_fp8_rope_widths(kind, r):
         slot = p % w.window if kind == 1 else p
         assert (vc1[b, :, slot] == vcode[b]).all(), f"seq {b}: value codes"
         _check_key_codes(kc1[b, :, slot], krot[b], f"seq {b} r={r}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("r", [0, 192])
+def test_prefill_fp8_caches_rope_widths(kind, r):
+    # prefill coding the rotated keys it stores, then a decode step over those codes
+    run_prefill_fp8_chain(kind, seed=7600 + r + kind, r=r, theta=THETA, q_scale=Q_SCALE)
 
 
 @pytest.mark.parametrize("S", [40, 4])
