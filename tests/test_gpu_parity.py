@@ -297,6 +297,15 @@ def test_prefill_then_decode_matches_longer_prefill(kind):
     kc = torch.zeros((2, w.num_kv_heads, cap, 192), dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros((2, w.num_kv_heads, cap, 128), dtype=torch.bfloat16, device=DEV)
     wS = _wl(kind=kind, B=2, S=S, Hq=16, Hkv=2, sinks=kind == 1)
+    pre = None
+    if kind == 0:
+        # a global layer's decode attends to every earlier position, and the linear cache of
+        # sequence 1 must hold its positions 0..10 for the identity: a prefill of 11 tokens of its
+        # own writes them first (the ring of a sliding layer only holds the last window)
+        wp = _wl(kind=0, B=1, S=starts[1], Hq=16, Hkv=2, sinks=False)
+        pre = synth.layer_inputs(wp, 9100, device=DEV)
+        mimo.prefill(_params(wp), *pre[:3], torch.zeros(1, dtype=torch.int32, device=DEV),
+                     k_cache=kc[1:2], v_cache=vc[1:2])
     mimo.prefill(_params(wS), q[:, :S].contiguous(), k[:, :S].contiguous(), v[:, :S].contiguous(),
                  sp, sinks=s, k_cache=kc, v_cache=vc)
     pos = torch.tensor([S + st for st in starts], dtype=torch.int32, device=DEV)
@@ -307,8 +316,17 @@ def test_prefill_then_decode_matches_longer_prefill(kind):
     posn = np.stack([np.arange(S + 1, dtype=np.int32) + st for st in starts])
     ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), posn, _f32(s),
                          rows=np.array([S], np.int32))
-    assert_close(dec, ref[:, S], what="decode after prefill")
     assert_close(full[:, S], ref[:, S], what="longer prefill")
+    ref_dec = ref[:, S]
+    if kind == 0:
+        # sequence 1's decode == the last row of one prefill over all its positions 0..S + 11
+        n = starts[1] + S + 1
+        w1 = _wl(kind=0, B=1, S=n, Hq=16, Hkv=2, sinks=False)
+        cat = [np.concatenate([_f32(a), _f32(b[1:2])], axis=1) for a, b in zip(pre[:3], (q, k, v))]
+        ref1 = oracle.prefill(_oparams(w1), *cat, np.arange(n, dtype=np.int32)[None],
+                              rows=np.array([n - 1], np.int32))
+        ref_dec = np.concatenate([ref_dec[:1], ref1[:, n - 1]], axis=0)
+    assert_close(dec, ref_dec, what="decode after prefill")
 
 
 @pytest.mark.parametrize("layer", [0, 1])
