@@ -27,7 +27,7 @@ and with fp8 e4m3 caches), copy
 achievable HBM rate), gemm (8192^3 bf16 matrix product: the achievable matrix-core rate),
 extend (new tokens against a cache: a 2048-token chunk after 30000 cached positions, global and
 sliding, batch 1; and 4 tokens per sequence after the decode workload's cached lengths, batch 64,
-the shape of multi-token verification), layer (the layer entry point: hidden 4096 -> q/k/v
+the shape of multi-token verification; the global ones again over fp8 caches), layer (the layer entry point: hidden 4096 -> q/k/v
 projections -> attention -> output projection back to 4096, on the sliding 4096-token and the
 global 8192-token prefill shapes; the projections run on hipBLASLt), router (the MoE router
 kernel: 32768 tokens, 256 experts in 8 groups, 4 groups kept, top 8).
@@ -107,9 +107,10 @@ def decode_counts(B, Hq, Hkv, kind, W, positions, cache_bytes=2):
     return flops, bytes_
 
 
-def extend_counts(Hq, Hkv, kind, W, starts, S):
+def extend_counts(Hq, Hkv, kind, W, starts, S, cache_bytes=2):
     """flops and bytes of one extend call: visible (query, key) pairs; q, k, v read, out written,
-    the cached positions any new token sees read once, the new tokens stored (ring: the last W)."""
+    the cached positions any new token sees read once, the new tokens stored (ring: the last W),
+    cache elements of cache_bytes bytes (1 for fp8 codes)."""
     flops = bytes_ = 0
     for st in starts:
         if kind == 0:
@@ -119,8 +120,8 @@ def extend_counts(Hq, Hkv, kind, W, starts, S):
             pairs = sum(min(W, st + i + 1) for i in range(S))
             cached, stored = min(W - 1, st), min(S, W)
         flops += Hq * pairs * 2 * (DQK + DV)
-        bytes_ += (S * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV)
-                   + Hkv * (cached + stored) * (DQK + DV)) * 2
+        bytes_ += (S * (Hq * DQK + Hkv * (DQK + DV) + Hq * DV) * 2
+                   + Hkv * (cached + stored) * (DQK + DV) * cache_bytes)
     return flops, bytes_
 
 
@@ -449,19 +450,27 @@ def single_layer(args, dev):
                              flop_attention=f_attn, frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS)
     elif args.workload == "extend":
         lengths = synth.decode_lengths(3).tolist()
-        cases = [("global_chunk", synth.GA_HEADS, [30000], 2048),
-                 ("sliding_chunk", synth.SWA_HEADS, [30000], 2048),
-                 ("global_verify4", synth.GA_HEADS, lengths, 4),
-                 ("sliding_verify4", synth.SWA_HEADS, lengths, 4)]
-        for name, heads, starts, S in cases:
+        cases = [("global_chunk", synth.GA_HEADS, [30000], 2048, False),
+                 ("sliding_chunk", synth.SWA_HEADS, [30000], 2048, False),
+                 ("global_verify4", synth.GA_HEADS, lengths, 4, False),
+                 ("sliding_verify4", synth.SWA_HEADS, lengths, 4, False),
+                 ("global_chunk_fp8", synth.GA_HEADS, [30000], 2048, True),
+                 ("global_verify4_fp8", synth.GA_HEADS, lengths, 4, True)]
+        for name, heads, starts, S, fp8 in cases:
             B = len(starts)
             w = synth.Workload(name, B, S, dtype=torch.bfloat16, **heads)
             swa = w.layer_kind == 1
             cap = w.window if swa else max(starts) + S
             q, k, v, s = synth.layer_inputs(w, 8000 + w.layer_kind, device=dev)
-            kc, vc = synth.cache_contents(w, 8100 + w.layer_kind, B, cap, device=dev)
+            if fp8:
+                kc, vc = synth.fp8_cache_contents(w, 8100 + w.layer_kind, B, cap, device=dev)
+            else:
+                kc, vc = synth.cache_contents(w, 8100 + w.layer_kind, B, cap, device=dev)
             p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims, w.layer_kind,
                             w.window, w.rope_theta, w.v_scale)
+            if fp8:
+                p.cache_dtype = mimo.CACHE_FP8_E4M3
+                p.k_cache_scale, p.v_cache_scale = synth.FP8_K_SCALE, synth.FP8_V_SCALE
             sp = torch.tensor(starts, dtype=torch.int32, device=dev)
             out = torch.empty((B, S, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(mimo.extend_workspace_size(p, S, max(starts)) + 256, dtype=torch.uint8,
@@ -469,7 +478,8 @@ def single_layer(args, dev):
             # the same call repeated: the new tokens' slots are rewritten with the same values
             ms = timed(lambda: mimo.extend(p, q, k, v, sp, max(starts), kc, vc, sinks=s, out=out,
                                            workspace=ws), args.steps)
-            f, b = extend_counts(w.num_q_heads, w.num_kv_heads, w.layer_kind, w.window, starts, S)
+            f, b = extend_counts(w.num_q_heads, w.num_kv_heads, w.layer_kind, w.window, starts, S,
+                                 1 if fp8 else 2)
             res[name] = dict(ms=ms, tflops=f / ms / 1e9, GBps=b / ms / 1e6, flop=f, bytes=b,
                              frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS,
                              frac_hbm=b / ms / 1e6 / PEAK_HBM_GBPS)

@@ -233,19 +233,27 @@ SplitGeometry verify_geometry(const mimo_attn_params* p, int32_t S, int32_t max_
     return g;
 }
 
-// bf16 extend workspace: sliding layers lay out [B, Hkv, window + S] rotated K and V rows (the
-// ring's content in position order, then the new tokens); global layers attend straight from
-// the cache.  A multi-token extend adds its split partials (256-byte aligned).
-size_t extend_rows_ws(const mimo_attn_params* p, int32_t S) {
-    if (p->dtype != MIMO_BF16 || p->layer_kind != MIMO_LAYER_SWA) return 0;
-    const size_t b = (size_t)p->batch * p->num_kv_heads * ((size_t)p->window + S) *
+// Rows per (sequence, KV head) of the bf16 key/value rows an extend lays out in its workspace:
+// sliding layers window + S (the ring's content in position order, then the new tokens); global
+// layers with an fp8 cache max_start + S (row = position: the cached rows widened to bf16, then
+// the new tokens); global layers with a bf16 cache none (they attend straight from the cache).
+int64_t extend_rows(const mimo_attn_params* p, int32_t S, int32_t max_start) {
+    if (p->dtype != MIMO_BF16) return 0;
+    if (p->layer_kind == MIMO_LAYER_SWA) return (int64_t)p->window + S;
+    return fp8_cache(p) ? (int64_t)max_start + S : 0;
+}
+
+// bf16 extend workspace: those rows (K then V, 256-byte aligned), then the split partials of a
+// multi-token extend.
+size_t extend_rows_ws(const mimo_attn_params* p, int32_t S, int32_t max_start) {
+    const size_t b = (size_t)p->batch * p->num_kv_heads * (size_t)extend_rows(p, S, max_start) *
                      (p->qk_head_dim + p->v_head_dim) * 2;
     return (b + 255) / 256 * 256;
 }
 
 size_t extend_ws(const mimo_attn_params* p, int32_t S, int32_t max_start) {
     if (p->dtype != MIMO_BF16) return 0;
-    size_t n = extend_rows_ws(p, S);
+    size_t n = extend_rows_ws(p, S, max_start);
     if (verify_tokens(p, S))
         n += partials_bytes(p, (int64_t)p->batch * S, verify_geometry(p, S, max_start).nsplit);
     return n;
@@ -408,9 +416,8 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
                     max_start, seq_len);
     if (p->dtype != MIMO_BF16)
         return fail(MIMO_ERR_UNSUPPORTED, "extend is compiled for bf16 layers only");
-    if (fp8_cache(p))
-        return fail(MIMO_ERR_UNSUPPORTED, "extend does not read fp8 caches");
     const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    const bool fp8 = fp8_cache(p);
     if (swa && cache_capacity != p->window)
         return fail(MIMO_ERR_INVALID_ARG, "ring cache capacity %d must equal window %d",
                     cache_capacity, p->window);
@@ -447,6 +454,11 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     ra.cap = cache_capacity;
     ra.ring_window = swa ? p->window : 0;
     ra.max_start = max_start;
+    if (fp8) {   // the new tokens are stored as codes
+        ra.cache_fp8 = 1;
+        ra.k_inv = 1.0f / p->k_cache_scale;
+        ra.v_inv = 1.0f / p->v_cache_scale;
+    }
     fill_omega(p, ra.omega_rev);
 
     mimo::PrefillArgs pa;
@@ -468,29 +480,36 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
 
     // a few new tokens run the multi-token tile kernel, more the prefill kernel
     const bool few = verify_tokens(p, seq_len);
+    const int64_t rows = extend_rows(p, seq_len, max_start);
+    uint16_t* kws = (uint16_t*)workspace;
+    uint16_t* vws = kws + (int64_t)p->batch * Hkv * rows * dqk;
+    mimo::CacheRowsArgs ua;   // cached rows -> workspace rows by position (widened if fp8)
+    memset(&ua, 0, sizeof ua);
+    ua.k_cache = k_cache;
+    ua.v_cache = v_cache;
+    ua.start_pos = start_pos;
+    ua.k_ws = kws;
+    ua.v_ws = vws;
+    ua.B = p->batch;
+    ua.Hkv = p->num_kv_heads;
+    ua.dqk = p->qk_head_dim;
+    ua.dv = p->v_head_dim;
+    ua.cap = cache_capacity;
+    ua.ws_rows = (int32_t)rows;
+    ua.max_start = max_start;
+    if (fp8) {
+        ua.cache_fp8 = 1;
+        ua.k_scale = p->k_cache_scale;
+        ua.v_scale = p->v_cache_scale;
+    }
     if (swa) {
-        // workspace rows r < W: the ring's positions start - W + r (in position order; the tile
-        // kernel reads those from the ring in place); rows W + i: the new tokens, rotated.  The
+        // workspace rows r < W: the ring's positions start - W + r (in position order; from a bf16
+        // ring the tile kernel reads those in place); rows W + i: the new tokens, rotated.  The
         // ring itself is refreshed only after it is read.
-        const int64_t rows = (int64_t)p->window + seq_len;
-        uint16_t* kws = (uint16_t*)workspace;
-        uint16_t* vws = kws + (int64_t)p->batch * Hkv * rows * dqk;
-        if (!few) {
-            mimo::RingUnrollArgs ua;
-            memset(&ua, 0, sizeof ua);
-            ua.k_cache = (const uint16_t*)k_cache;
-            ua.v_cache = (const uint16_t*)v_cache;
-            ua.start_pos = start_pos;
-            ua.k_ws = kws;
-            ua.v_ws = vws;
-            ua.B = p->batch;
-            ua.Hkv = p->num_kv_heads;
-            ua.dqk = p->qk_head_dim;
-            ua.dv = p->v_head_dim;
+        if (!few || fp8) {
             ua.W = p->window;
-            ua.ws_rows = (int32_t)rows;
-            ua.max_start = max_start;
-            rc = hip_status(mimo::launch_ring_unroll_bf16(ua, st), "ring unroll (bf16)");
+            ua.rows = p->window;
+            rc = hip_status(mimo::launch_cache_rows_bf16(ua, st), "ring unroll (bf16)");
             if (rc != MIMO_OK) return rc;
         }
         ra.k_ws = kws;
@@ -506,6 +525,26 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
         pa.v_sh = rows * dv;
         pa.kpos_rel = 1;
         pa.kpos_off = -p->window;   // key row j sits at position start - W + j
+    } else if (fp8) {
+        // workspace row j = position j: the cached rows before each start widened to bf16, then
+        // the new tokens, rotated (which also go to the cache, as codes)
+        ua.W = 0;
+        ua.rows = max_start;
+        rc = hip_status(mimo::launch_cache_rows_bf16(ua, st), "cache widening (fp8)");
+        if (rc != MIMO_OK) return rc;
+        ra.k_ws = kws;
+        ra.v_ws = vws;
+        ra.ws_rows = (int32_t)rows;
+        ra.ws_row0 = 0;
+        ra.ws_rel = 1;
+        pa.k = kws;
+        pa.v = vws;
+        pa.k_sb = Hkv * rows * dqk;
+        pa.k_sh = rows * dqk;
+        pa.v_sb = Hkv * rows * dv;
+        pa.v_sh = rows * dv;
+        pa.kpos_rel = 0;
+        pa.kpos_off = 0;
     } else {
         // new tokens go to the linear cache first; key row j of the cache is position j
         pa.k = (const uint16_t*)k_cache;
@@ -537,8 +576,8 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     va.start_pos = start_pos;
     va.sinks = sinks;
     va.out = (uint16_t*)out;
-    va.partial = (float*)((uint8_t*)workspace + extend_rows_ws(p, seq_len));
-    if (swa) {
+    va.partial = (float*)((uint8_t*)workspace + extend_rows_ws(p, seq_len, max_start));
+    if (swa && !fp8) {
         va.ring_k = (const uint16_t*)k_cache;
         va.ring_v = (const uint16_t*)v_cache;
         va.ring_w = p->window;

@@ -9,8 +9,9 @@ constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value, in re
 
 // Rotate K (first rope_dims dims) once per token i in [i0, S) of each sequence b (position
 // start_pos[b] + i) and store it
-//   * into k_ws [B,Hkv,ws_rows,dqk] at row ws_row0 + i, when k_ws is set (rotated-K scratch of a
-//     prefill), and V likewise into v_ws [B,Hkv,ws_rows,dv] when v_ws is set;
+//   * into k_ws [B,Hkv,ws_rows,dqk] at row ws_row0 + i (ws_rel: start_pos[b] + ws_row0 + i), when
+//     k_ws is set (rotated-K scratch of a prefill), and V likewise into v_ws [B,Hkv,ws_rows,dv]
+//     when v_ws is set;
 //   * with V into the cache k_dst [B,Hkv,cap,dqk] / v_dst [B,Hkv,cap,dv], when k_dst is set and
 //     i >= cache_i0, at slot position % ring_window (ring_window > 0) or slot position (linear; a
 //     token whose slot falls outside [0, cap) is not stored).
@@ -24,23 +25,28 @@ struct RopeKVArgs {
     void* k_dst;         // [B,Hkv,cap,dqk] or null
     void* v_dst;         // [B,Hkv,cap,dv], set iff k_dst is
     int32_t B, S, Hkv, dqk, dv, rope_dims, cap, i0, cache_i0, ring_window;
-    int32_t ws_rows, ws_row0, max_start;
+    int32_t ws_rows, ws_row0, ws_rel, max_start;
     int32_t cache_fp8;   // caches hold e4m3 codes of x * k_inv / v_inv (bf16 kernel only)
     float k_inv, v_inv;
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
-// Copy the ring cache's W most recent positions before start_pos[b] into workspace rows in
-// position order: row r of [B,Hkv,ws_rows,d] holds position start_pos[b] - W + r (slot
-// position % W); rows of negative positions are left as they are.  With max_start >= 0,
-// sequences whose start_pos lies outside [0, max_start] are skipped.
-struct RingUnrollArgs {
-    const uint16_t* k_cache;   // [B,Hkv,W,dqk]
-    const uint16_t* v_cache;   // [B,Hkv,W,dv]
+// Copy the cached positions before start_pos[b] that an extend reads into bf16 workspace rows in
+// position order, row r of [B,Hkv,ws_rows,d]:
+//   * ring (W > 0; cap == W): the W most recent positions, row r holding position
+//     start_pos[b] - W + r (slot position % W); rows of negative positions are left as they are;
+//   * linear (W == 0): row j holding position j (slot j) for j < min(start_pos[b], rows).
+// fp8 caches (cache_fp8) are widened on the way: row element = bf16(e4m3(code) * scale).  With
+// max_start >= 0, sequences whose start_pos lies outside [0, max_start] are skipped.
+struct CacheRowsArgs {
+    const void* k_cache;       // [B,Hkv,cap,dqk] bf16, or e4m3 codes
+    const void* v_cache;       // [B,Hkv,cap,dv]
     const int32_t* start_pos;
     uint16_t* k_ws;            // [B,Hkv,ws_rows,dqk]
     uint16_t* v_ws;            // [B,Hkv,ws_rows,dv]
-    int32_t B, Hkv, dqk, dv, W, ws_rows, max_start;
+    int32_t B, Hkv, dqk, dv, W, cap, rows, ws_rows, max_start;
+    int32_t cache_fp8;
+    float k_scale, v_scale;
 };
 
 // bf16 prefill.  Query row i of sequence b sits at position start_pos[b] + i.  Key row j (rotated
@@ -119,7 +125,7 @@ struct F32DecodeArgs {
 };
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
-hipError_t launch_ring_unroll_bf16(const RingUnrollArgs& a, hipStream_t st);
+hipError_t launch_cache_rows_bf16(const CacheRowsArgs& a, hipStream_t st);
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool window, bool sink, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, bool swa, bool sink, hipStream_t st);

@@ -5,10 +5,11 @@
 // upstream": rotated width int(partial_rotary_factor * head_dim), per-kind theta): pair
 // (d, d + r/2), d < r/2, is turned by position * theta^(-2d/r); dims >= r are copied.
 // Destinations: the rotated-K (and V) scratch of a prefill or an extend (row = a fixed offset +
-// token index), the linear cache of global layers (slot = position) and the rotating cache of
-// sliding layers (slot = position % window; "add Xiaomi MiMo v2 (mimo_v2_flash)", "Implementation
-// plan").  The ring unroll pass lays the ring's content out by position in front of an extend's
-// new tokens.
+// token index, or + position), the linear cache of global layers (slot = position) and the
+// rotating cache of sliding layers (slot = position % window; "add Xiaomi MiMo v2
+// (mimo_v2_flash)", "Implementation plan").  The cache-rows pass lays out by position the cached
+// rows an extend reads in front of its new tokens (the ring's content; an fp8 cache's rows,
+// widened to bf16).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -45,7 +46,8 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
         const int32_t pos = start + i;
         const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
-        const int64_t ws_row = ((int64_t)b * a.Hkv + g) * a.ws_rows + a.ws_row0 + i;
+        const int64_t ws_row =
+            ((int64_t)b * a.Hkv + g) * a.ws_rows + (a.ws_rel ? start : 0) + a.ws_row0 + i;
         const int64_t slot_row = ((int64_t)b * a.Hkv + g) * a.cap + slot;
         if (c < kch) {
             const uint16_t* krow = (const uint16_t*)a.k + src_row * a.dqk;
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
         const int32_t pos = start + i;
         const int slot = cache_slot(a, i, pos);
         const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
-        const int64_t ws_row = ((int64_t)b * a.Hkv + g) * a.ws_rows + a.ws_row0 + i;
+        const int64_t ws_row =
+            ((int64_t)b * a.Hkv + g) * a.ws_rows + (a.ws_rel ? start : 0) + a.ws_row0 + i;
         if (c < a.dqk) {
             const float* krow = (const float*)a.k + src_row * a.dqk;
             float x = krow[c];
@@ -132,29 +135,38 @@ __global__ __launch_bounds__(256) void rope_kv_f32_kernel(const RopeKVArgs a) {
     }
 }
 
-// bf16 ring unroll: one thread per 16-byte chunk of a K or V row.
-__global__ __launch_bounds__(256) void ring_unroll_bf16_kernel(const RingUnrollArgs a) {
+// bf16 cache rows: one thread per 8-element chunk of a K or V row.
+__global__ __launch_bounds__(256) void cache_rows_bf16_kernel(const CacheRowsArgs a) {
     const int kch = a.dqk / 8, per_row = kch + a.dv / 8;
-    const int64_t total = (int64_t)a.B * a.Hkv * a.W * per_row;
+    const int64_t total = (int64_t)a.B * a.Hkv * a.rows * per_row;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
         const int c = (int)(e % per_row);
         const int64_t rowid = e / per_row;
-        const int r = (int)(rowid % a.W);
-        const int64_t bg = rowid / a.W;            // b * Hkv + g
+        const int r = (int)(rowid % a.rows);
+        const int64_t bg = rowid / a.rows;         // b * Hkv + g
         const int b = (int)(bg / a.Hkv);
         const int32_t start = a.start_pos[b];
         if (!start_ok(start, a.max_start)) continue;
-        const int32_t pos = start - a.W + r;
-        if (pos < 0) continue;
-        const int64_t slot_row = bg * a.W + pos % a.W;
+        const int32_t pos = a.W > 0 ? start - a.W + r : r;
+        if (pos < 0 || (a.W == 0 && pos >= start)) continue;
+        const int64_t slot_row = bg * a.cap + (a.W > 0 ? pos % a.W : pos);
         const int64_t ws_row = bg * a.ws_rows + r;
-        if (c < kch)
-            *(u32x4*)(a.k_ws + ws_row * a.dqk + 8 * c) =
-                *(const u32x4*)(a.k_cache + slot_row * a.dqk + 8 * c);
-        else
-            *(u32x4*)(a.v_ws + ws_row * a.dv + 8 * (c - kch)) =
-                *(const u32x4*)(a.v_cache + slot_row * a.dv + 8 * (c - kch));
+        const bool key = c < kch;
+        const int d = 8 * (key ? c : c - kch), dim = key ? a.dqk : a.dv;
+        uint16_t* dst = (key ? a.k_ws : a.v_ws) + ws_row * dim + d;
+        if (a.cache_fp8) {
+            const uint8_t* src = (const uint8_t*)(key ? a.k_cache : a.v_cache) + slot_row * dim + d;
+            float x[8];
+            unpack8(bf16x8_from_e4m3x8(*(const u32x2*)src), x);   // exact e4m3 values
+            const float sc = key ? a.k_scale : a.v_scale;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] *= sc;
+            *(u32x4*)dst = pack8(x);
+        } else {
+            const uint16_t* src = (const uint16_t*)(key ? a.k_cache : a.v_cache) + slot_row * dim + d;
+            *(u32x4*)dst = *(const u32x4*)src;
+        }
     }
 }
 
@@ -182,11 +194,11 @@ hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_ring_unroll_bf16(const RingUnrollArgs& a, hipStream_t st) {
-    if (a.dqk % 8 || a.dv % 8) return hipErrorInvalidValue;
-    const int64_t total = (int64_t)a.B * a.Hkv * a.W * (a.dqk / 8 + a.dv / 8);
+hipError_t launch_cache_rows_bf16(const CacheRowsArgs& a, hipStream_t st) {
+    if (a.dqk % 8 || a.dv % 8 || (a.W > 0 && a.cap != a.W)) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)a.B * a.Hkv * a.rows * (a.dqk / 8 + a.dv / 8);
     if (total <= 0) return hipSuccess;
-    ring_unroll_bf16_kernel<<<grid_for(total), 256, 0, st>>>(a);
+    cache_rows_bf16_kernel<<<grid_for(total), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -99,9 +99,10 @@ typedef struct mimo_attn_params {
  * (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals; 0x7F/0xFF NaN; largest finite
  * 448) with the shapes of the bf16 caches.  A stored element is written as the e4m3 value nearest
  * (ties to even) to clamp(x * (1 / scale), -448, 448), x the fp32 rotated key or the value, the
- * product and 1 / scale in fp32; it is read as e4m3(code) * scale.  Prefill and decode support
- * fp8 caches; extend returns MIMO_ERR_UNSUPPORTED for them.  Decode attends the new token with its
- * stored (coded) value, like every other cached token.
+ * product and 1 / scale in fp32; it is read as e4m3(code) * scale.  Prefill, decode and extend
+ * support fp8 caches.  Decode attends the new token with its stored (coded) value, like every
+ * other cached token; prefill and extend attend their new tokens at full precision (as without a
+ * cache) and the cached positions through their codes, and store the new tokens as codes.
  */
 
 /*
@@ -147,7 +148,7 @@ size_t mimo_attn_prefill_workspace_size(const mimo_attn_params* p, int32_t seq_l
  *   SWA:    ring cache [B,Hkv,window,d], cache_capacity == window; slot p % window must hold
  *           position p for the min(window, start_pos[b]) positions p before start_pos[b]; the last
  *           min(S, window) new tokens are stored at slot position % window.
- *   K is stored rotated, V as given (as prefill and decode store them).
+ *   K is stored rotated, V as given (as prefill and decode store them); fp8 caches as above.
  *   bf16 only: MIMO_F32 returns MIMO_ERR_UNSUPPORTED.
  *   workspace: at least mimo_attn_extend_workspace_size() bytes (may be NULL when that is 0).
  *   Its contents are not needed across calls.
@@ -161,7 +162,9 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
 /* Workspace bytes mimo_attn_extend needs for seq_len new tokens and starts up to max_start: SWA
  * bf16 layers lay the ring's content out in position order in front of the new tokens' rotated
  * keys and values (B * Hkv * (window + seq_len) * (dqk + dv) * 2 bytes, rounded up to 256);
- * GLOBAL layers read the cache in place.  Up to 16 new tokens per sequence run a tile kernel
+ * GLOBAL layers read a bf16 cache in place, and lay an fp8 cache's rows out widened to bf16 in
+ * front of the new tokens (B * Hkv * (max_start + seq_len) * (dqk + dv) * 2 bytes, rounded up to
+ * 256; row = position).  Up to 16 new tokens per sequence run a tile kernel
  * whose query columns are the (query head, new token) pairs of a KV group, split over the key
  * rows, which adds split partials (B * seq_len * Hq * splits * (dv + 2) * 4 bytes) when the key
  * range is cut into several splits.

@@ -96,8 +96,13 @@ def test_cache_dtype_and_scales_are_checked():
     assert mimo.check_params(_swa(dtype=mimo.F32, qk_head_dim=32, v_head_dim=16, rope_dims=10,
                                   num_q_heads=4, num_kv_heads=1, window=16, **fp8)) == \
         mimo.MIMO_ERR_UNSUPPORTED
-    # extend does not read fp8 caches
-    assert _extend(_swa(**fp8)) == mimo.MIMO_ERR_UNSUPPORTED
+    # extend over fp8 caches lays their rows out widened in its workspace (global layers too)
+    assert _extend(_swa(**fp8), ws=None) == mimo.MIMO_ERR_WORKSPACE
+    assert _extend(_ga(**fp8), ws=None, cap=200) == mimo.MIMO_ERR_WORKSPACE
+    assert mimo.extend_workspace_size(_ga(batch=2, **fp8), 1000, 5000) == \
+        2 * 4 * (5000 + 1000) * (192 + 128) * 2
+    assert mimo.extend_workspace_size(_swa(batch=2, **fp8), 1000, 5000) == \
+        mimo.extend_workspace_size(_swa(batch=2), 1000, 5000)
     # an fp8 cache slice may be twice as long as a bf16 one under the 4 GiB bound
     # (passes the bound, then stops at the missing workspace: nothing is launched)
     assert _decode(_ga(**fp8), maxp=100_000, cap=12_000_000, ws=None) == mimo.MIMO_ERR_WORKSPACE
@@ -115,7 +120,7 @@ def test_workspace_sizes():
     ws = mimo.decode_workspace_size(_ga(batch=64), 32768)
     assert ws > 0 and ws % (64 * 64 * 130 * 4) == 0
     assert mimo.decode_workspace_size(_ga(batch=64), 100) == 0
-    # extend: sliding layers lay out window + S rows of K and V; global layers read the cache
+    # extend: sliding layers lay out window + S rows of K and V; global layers read a bf16 cache
     assert mimo.extend_workspace_size(_swa(batch=2), 1000, 5000) == 2 * 8 * (128 + 1000) * (192 + 128) * 2
     assert mimo.extend_workspace_size(_ga(batch=2), 1000, 5000) == 0
     assert mimo.extend_workspace_size(_swa(), -1, 0) == 0

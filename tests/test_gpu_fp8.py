@@ -1,4 +1,4 @@
-"""GPU parity of the fp8 (e4m3) KV cache: decode over coded caches and prefill writing them.
+"""GPU parity of the fp8 (e4m3) KV cache: decode and extend over coded caches, prefill writing them.
 
 Against the fp64 oracle: decode outputs over the same coded cache (the oracle decodes the codes
 itself); the appended token's codes (values: the same fp32 product on both sides, so bit for bit;
@@ -212,3 +212,52 @@ def run_prefill_fp8_chain(kind, seed, r=64, theta=None, q_scale=1.0):
     dref, *_ = oracle.decode_fp8(_oparams(w), _f32(qd), _f32(kd), _f32(vd), np.array(dpos, np.int32),
                                  okc, ovc, kpos, cnt, KS, VS, _f32(s))
     assert_close(dec, dref, what="decode after an fp8 prefill")
+
+
+# ----------------------------------------------------------------------------- extend
+# Extend over fp8 caches: the cached positions are attended through their codes, the new tokens at
+# full precision (as prefill does), and the new tokens are stored as codes.  The oracle takes the
+# cache as the values its codes stand for (exact: e4m3 values times power-of-two scales).
+
+EXT_CASES = [
+    dict(kind=0, B=2, S=40, Hq=8, Hkv=2, sinks=False, starts=[0, 700]),        # prefill kernel
+    dict(kind=0, B=3, S=4, Hq=16, Hkv=1, sinks=True, starts=[1, 255, 4097]),   # tile kernel
+    dict(kind=1, B=2, S=300, Hq=8, Hkv=2, sinks=True, starts=[5, 4000]),       # ring, S > W
+    dict(kind=1, B=3, S=4, Hq=16, Hkv=2, sinks=True, starts=[0, 2, 1000]),     # ring, tile kernel
+]
+
+
+@pytest.mark.parametrize("ci", range(len(EXT_CASES)))
+def test_extend_fp8_caches(ci):
+    from tests.test_gpu_extend import _oracle_cache, _stored_slots
+    case = dict(EXT_CASES[ci])
+    starts = case.pop("starts")
+    w = _wl(**case)
+    S, B = w.seq, w.batch
+    _note(f"fp8 extend {case} starts {starts}")
+    q, k, v, s = synth.layer_inputs(w, 11500 + ci, device=DEV)
+    cap = w.window if w.layer_kind == 1 else max(starts) + S + 5
+    kc8, vc8 = synth.fp8_cache_contents(w, 11600 + ci, B, cap, device=DEV)
+    kc0, vc0 = _np8(kc8), _np8(vc8)
+    kf = torch.from_numpy(oracle.e4m3_decode(kc0) * KS)
+    vf = torch.from_numpy(oracle.e4m3_decode(vc0) * VS)
+    okc, ovc, kpos, count = _oracle_cache(w, kf, vf, starts)
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    out = mimo.extend(_p8(w), q, k, v, sp, max(starts), kc8, vc8, sinks=s)
+    torch.cuda.synchronize()
+    ref, krot = oracle.extend(_oparams(w), _f32(q), _f32(k), _f32(v), np.array(starts, np.int32),
+                              okc, ovc, kpos, count, _f32(s), want_k_rot=True)
+    assert_close(out, ref, what=f"fp8 extend {case}")
+    # caches: the new tokens' codes in their slots, every other slot as it was
+    kc1, vc1 = _np8(kc8), _np8(vc8)
+    vin = _f32(v)
+    inv_v = np.float32(1) / np.float32(VS)
+    for b, st in enumerate(starts):
+        slots = _stored_slots(w, st, S)
+        kept = np.setdiff1d(np.arange(cap), list(slots.values()))
+        assert np.array_equal(kc1[b][:, kept], kc0[b][:, kept]), f"seq {b}: foreign K slot changed"
+        assert np.array_equal(vc1[b][:, kept], vc0[b][:, kept]), f"seq {b}: foreign V slot changed"
+        tok = np.array(sorted(slots))
+        sl = np.array([slots[i] for i in tok])
+        assert np.array_equal(vc1[b][:, sl], oracle.e4m3_encode(vin[b, tok], inv_v).transpose(1, 0, 2))
+        _check_key_codes(kc1[b][:, sl], krot[b, tok].transpose(1, 0, 2), f"extend seq {b}")
