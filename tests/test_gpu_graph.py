@@ -81,22 +81,28 @@ def test_decode_graph_replays_match_eager(fp8):
         assert torch.equal(kc, kce) and torch.equal(vc, vce)
 
 
-@pytest.mark.parametrize("S", [4, 40])
-def test_extend_graph_replays_match_eager(S):
+@pytest.mark.parametrize("S,fp8", [(4, False), (40, False), (4, True), (40, True)])
+def test_extend_graph_replays_match_eager(S, fp8):
     """A captured extend step (global and sliding layer; 4 tokens run the multi-token tile
-    kernel, 40 the prefill kernel) replayed on the same caches: every replay equals
-    the eager call on a copy of the state."""
+    kernel, 40 the prefill kernel; bf16 or fp8 caches) replayed on the same caches: every replay
+    equals the eager call on a copy of the state."""
     B, P0, R = 2, 500, 3
-    print(f"[case] graph extend S={S}", flush=True)
+    print(f"[case] graph extend S={S} fp8={fp8}", flush=True)
     layers = []
     for kind, seed in ((0, 9200), (1, 9201)):
         heads = synth.SWA_HEADS if kind == 1 else synth.GA_HEADS
         w = synth.Workload("graph_ext", B, S, dtype=torch.bfloat16, **heads)
         cap = w.window if kind == 1 else P0 + R * S
         q, k, v, s = synth.layer_inputs(w, seed, device=DEV)
-        kc, vc = synth.cache_contents(w, seed + 1, B, cap, device=DEV)
+        if fp8:
+            kc, vc = synth.fp8_cache_contents(w, seed + 1, B, cap, device=DEV)
+        else:
+            kc, vc = synth.cache_contents(w, seed + 1, B, cap, device=DEV)
         p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, w.qk_head_dim, w.v_head_dim,
                         w.rope_dims, w.layer_kind, w.window, w.rope_theta, w.v_scale)
+        if fp8:
+            p.cache_dtype = mimo.CACHE_FP8_E4M3
+            p.k_cache_scale, p.v_cache_scale = synth.FP8_K_SCALE, synth.FP8_V_SCALE
         maxs = P0 + (R - 1) * S
         ws = torch.empty(mimo.extend_workspace_size(p, S, maxs) + 256, dtype=torch.uint8, device=DEV)
         out = torch.empty((B, S, w.num_q_heads, w.v_head_dim), dtype=torch.bfloat16, device=DEV)
