@@ -184,25 +184,28 @@ def test_prefill_empty_and_invalid_arguments():
 # ----------------------------------------------------------------------------- decode
 
 
-def _decode_case(w, positions, seed, cap=None, q_scale=1.0):
-    """Random cache state + one decode step on the GPU, and the oracle on the same state."""
+def _decode_case(w, positions, seed, cap=None, q_scale=1.0, max_position=None):
+    """Random cache state + one decode step on the GPU, and the oracle on the same state (rows of
+    sequences past max_position, which the GPU leaves at zero, are not meaningful in ref)."""
     B = len(positions)
     swa = w.layer_kind == 1
-    cap = w.window if swa else (cap if cap else max(positions) + 1)
+    maxp = max(positions) if max_position is None else max_position
+    cap = w.window if swa else (cap if cap else maxp + 1)
     q, kn, vn, s, kc, vc = synth.decode_inputs(w, seed, B, cap, device=DEV)
     if q_scale != 1.0:
         q = q * q_scale  # a power of two: exact in bf16
     kc0, vc0 = _f32(kc), _f32(vc)
     pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)
-    out = mimo.decode(_params(w, B), q, kn, vn, pos_t, max(positions), kc, vc, sinks=s)
+    out = mimo.decode(_params(w, B), q, kn, vn, pos_t, maxp, kc, vc, sinks=s)
     torch.cuda.synchronize()
+    opos = [p if p <= maxp else 0 for p in positions]
     if swa:
         # occupied ring slots only (a slot still empty holds no token), packed first
         kc_o = np.zeros_like(kc0)
         vc_o = np.zeros_like(vc0)
         kpos = np.zeros((B, w.window), np.int32)
         cnt = np.zeros(B, np.int32)
-        for b, p in enumerate(positions):
+        for b, p in enumerate(opos):
             held = ring_positions(p, w.window)
             slots = np.nonzero(held >= 0)[0]
             n = len(slots)
@@ -210,12 +213,12 @@ def _decode_case(w, positions, seed, cap=None, q_scale=1.0):
             vc_o[b, :, :n] = vc0[b, :, slots].transpose(1, 0, 2)
             kpos[b, :n] = held[slots]
             cnt[b] = n
-        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(positions),
+        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(opos),
                                   kc_o, vc_o, kpos, cnt, _f32(s), want_k_rot=True)
     else:
         kpos = np.tile(np.arange(cap, dtype=np.int32), (B, 1))
-        cnt = np.array(positions, np.int32)
-        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(positions),
+        cnt = np.array(opos, np.int32)
+        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(opos),
                                   kc0, vc0, kpos, cnt, _f32(s), want_k_rot=True)
     return out, ref, krot, kc, vc, kc0, vc0, vn
 
@@ -243,6 +246,21 @@ def test_decode_bf16_small(case):
         kc_h[b, :, slot] = kc0[b, :, slot]
         vc_h[b, :, slot] = vc0[b, :, slot]
     assert np.array_equal(kc_h, kc0) and np.array_equal(vc_h, vc0)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_decode_skips_positions_past_max_position(kind):
+    """A sequence whose position exceeds max_position gets a zero output and appends nothing;
+    the others are unaffected (global: split-K over 1001 slots; sliding: one ring pass)."""
+    positions = [100, 700, 5000]
+    w = _wl(kind=kind, B=len(positions), S=1, Hq=8, Hkv=2, sinks=kind == 1)
+    _note(f"decode past max_position kind={kind}")
+    out, ref, _, kc, vc, kc0, vc0, _ = _decode_case(w, positions, seed=9600 + kind,
+                                                    max_position=1000)
+    assert torch.count_nonzero(out[2]) == 0, "a sequence past max_position must get zeros"
+    assert np.array_equal(_f32(kc)[2], kc0[2]) and np.array_equal(_f32(vc)[2], vc0[2]), \
+        "a sequence past max_position must not append"
+    assert_close(out[:2], ref[:2], what=f"accepted sequences kind={kind}")
 
 
 def test_decode_fp32_tiny():
