@@ -28,67 +28,78 @@ __device__ __forceinline__ bool start_ok(int32_t start, int32_t max_start) {
     return max_start < 0 || (unsigned)start <= (unsigned)max_start;
 }
 
-// bf16: one thread per 8-element chunk of a K or V row.
+// bf16: one thread per 8-element chunk of a K or V row, over a group of HG KV heads of one token
+// (HG divides Hkv): the angles of a rotated chunk are evaluated once for the whole group.
+template <int HG>
 __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
     const int kch = a.dqk / 8, vch = (a.k_dst || a.v_ws) ? a.dv / 8 : 0, per_row = kch + vch;
-    const int ntok = a.S - a.i0;
-    const int64_t total = (int64_t)a.B * ntok * a.Hkv * per_row;
+    const int ntok = a.S - a.i0, ngrp = a.Hkv / HG;
+    const int64_t total = (int64_t)a.B * ntok * ngrp * per_row;
     const int r = a.rope_dims, half = r >> 1;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
         const int c = (int)(e % per_row);
-        const int64_t rowid = e / per_row;
-        const int g = (int)(rowid % a.Hkv);
-        const int i = a.i0 + (int)((rowid / a.Hkv) % ntok);
-        const int b = (int)(rowid / ((int64_t)a.Hkv * ntok));
+        const int64_t grpid = e / per_row;
+        const int g0 = (int)(grpid % ngrp) * HG;
+        const int64_t tok = grpid / ngrp;            // b * ntok + (i - i0)
+        const int i = a.i0 + (int)(tok % ntok);
+        const int b = (int)(tok / ntok);
         const int32_t start = a.start_pos[b];
         if (!start_ok(start, a.max_start)) continue;
         const int32_t pos = start + i;
         const int slot = cache_slot(a, i, pos);
-        const int64_t src_row = ((int64_t)b * a.S + i) * a.Hkv + g;
-        const int64_t ws_row =
-            ((int64_t)b * a.Hkv + g) * a.ws_rows + (a.ws_rel ? start : 0) + a.ws_row0 + i;
-        const int64_t slot_row = ((int64_t)b * a.Hkv + g) * a.cap + slot;
+        const int64_t src0 = ((int64_t)b * a.S + i) * a.Hkv + g0;     // source row of head g0
+        const int64_t bg0 = (int64_t)b * a.Hkv + g0;                  // [b, g0] of a [B, Hkv, n, d]
+        const int64_t ws_r = (a.ws_rel ? start : 0) + a.ws_row0 + i;
         if (c < kch) {
-            const uint16_t* krow = (const uint16_t*)a.k + src_row * a.dqk;
             const int d0 = c * 8;
-            u32x4 w = *(const u32x4*)(krow + d0);
-            float x[8];
-            unpack8(w, x);
-            if (d0 < r) {
-                const int pd = d0 < half ? d0 + half : d0 - half;
-                const u32x4 pw = *(const u32x4*)(krow + pd);
-                float y[8];
-                unpack8(pw, y);
-                const bool lower = d0 < half;
+            const bool rot = d0 < r, lower = d0 < half;
+            const int pd = lower ? d0 + half : d0 - half;
+            float cs[8], sn[8];
+            if (rot) {
                 const int f0 = lower ? d0 : d0 - half;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    float cs, sn;
-                    rope_cos_sin_rev(pos, a.omega_rev[f0 + t], cs, sn);
-                    x[t] = lower ? (x[t] * cs - y[t] * sn) : (x[t] * cs + y[t] * sn);
-                }
-                w = pack8(x);
+                for (int t = 0; t < 8; ++t) rope_cos_sin_rev(pos, a.omega_rev[f0 + t], cs[t], sn[t]);
             }
-            if (a.k_ws) *(u32x4*)((uint16_t*)a.k_ws + ws_row * a.dqk + d0) = w;
-            if (slot >= 0) {
-                // (an fp8 cache codes the fp32 rotated key, not its bf16 rounding)
-                if (a.cache_fp8)
-                    *(u32x2*)((uint8_t*)a.k_dst + slot_row * a.dqk + d0) = e4m3x8_from_f32(x, a.k_inv);
-                else
-                    *(u32x4*)((uint16_t*)a.k_dst + slot_row * a.dqk + d0) = w;
+#pragma unroll
+            for (int j = 0; j < HG; ++j) {
+                const uint16_t* krow = (const uint16_t*)a.k + (src0 + j) * a.dqk;
+                u32x4 w = *(const u32x4*)(krow + d0);
+                float x[8];
+                unpack8(w, x);
+                if (rot) {
+                    float y[8];
+                    unpack8(*(const u32x4*)(krow + pd), y);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        x[t] = lower ? (x[t] * cs[t] - y[t] * sn[t]) : (x[t] * cs[t] + y[t] * sn[t]);
+                    w = pack8(x);
+                }
+                if (a.k_ws) *(u32x4*)((uint16_t*)a.k_ws + ((bg0 + j) * a.ws_rows + ws_r) * a.dqk + d0) = w;
+                if (slot >= 0) {
+                    const int64_t slot_row = (bg0 + j) * a.cap + slot;
+                    // (an fp8 cache codes the fp32 rotated key, not its bf16 rounding)
+                    if (a.cache_fp8)
+                        *(u32x2*)((uint8_t*)a.k_dst + slot_row * a.dqk + d0) = e4m3x8_from_f32(x, a.k_inv);
+                    else
+                        *(u32x4*)((uint16_t*)a.k_dst + slot_row * a.dqk + d0) = w;
+                }
             }
         } else if (slot >= 0 || a.v_ws) {
             const int d0 = (c - kch) * 8;
-            const u32x4 w = *(const u32x4*)((const uint16_t*)a.v + src_row * a.dv + d0);
-            if (a.v_ws) *(u32x4*)((uint16_t*)a.v_ws + ws_row * a.dv + d0) = w;
-            if (slot >= 0) {
-                if (a.cache_fp8) {
-                    float x[8];
-                    unpack8(w, x);
-                    *(u32x2*)((uint8_t*)a.v_dst + slot_row * a.dv + d0) = e4m3x8_from_f32(x, a.v_inv);
-                } else {
-                    *(u32x4*)((uint16_t*)a.v_dst + slot_row * a.dv + d0) = w;
+#pragma unroll
+            for (int j = 0; j < HG; ++j) {
+                const u32x4 w = *(const u32x4*)((const uint16_t*)a.v + (src0 + j) * a.dv + d0);
+                if (a.v_ws) *(u32x4*)((uint16_t*)a.v_ws + ((bg0 + j) * a.ws_rows + ws_r) * a.dv + d0) = w;
+                if (slot >= 0) {
+                    const int64_t slot_row = (bg0 + j) * a.cap + slot;
+                    if (a.cache_fp8) {
+                        float x[8];
+                        unpack8(w, x);
+                        *(u32x2*)((uint8_t*)a.v_dst + slot_row * a.dv + d0) = e4m3x8_from_f32(x, a.v_inv);
+                    } else {
+                        *(u32x4*)((uint16_t*)a.v_dst + slot_row * a.dv + d0) = w;
+                    }
                 }
             }
         }
@@ -179,10 +190,21 @@ unsigned grid_for(int64_t total) {
 }  // namespace
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st) {
-    const int64_t total =
+    int64_t total =
         (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk / 8 + ((a.k_dst || a.v_ws) ? a.dv / 8 : 0));
     if (total <= 0 || (!a.k_ws && !a.k_dst && !a.v_ws)) return hipSuccess;
-    rope_kv_bf16_kernel<<<grid_for(total), 256, 0, st>>>(a);
+    // Heads per thread: the largest power of two up to 8 dividing Hkv that still leaves at least
+    // 2^18 threads (4 waves of 256 threads per CU); small calls keep one head per thread, where a
+    // smaller grid would cost more latency than the shared angles save.
+    int hg = 1;
+    while (hg < 8 && a.Hkv % (2 * hg) == 0 && total / (2 * hg) >= (int64_t{1} << 18)) hg *= 2;
+    const unsigned grid = grid_for(total / hg);
+    switch (hg) {
+        case 8: rope_kv_bf16_kernel<8><<<grid, 256, 0, st>>>(a); break;
+        case 4: rope_kv_bf16_kernel<4><<<grid, 256, 0, st>>>(a); break;
+        case 2: rope_kv_bf16_kernel<2><<<grid, 256, 0, st>>>(a); break;
+        default: rope_kv_bf16_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    }
     return hipGetLastError();
 }
 
