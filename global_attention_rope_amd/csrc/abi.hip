@@ -144,14 +144,13 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
 //  * otherwise a power of two >= 256, large enough to keep the grid (B * Hkv * splits) within 8192
 //    workgroups and the splits per sequence within what the combine kernel merges; fp8 caches
 //    (half the bytes per slot) take twice the slots per split and half the grid.
-constexpr int64_t kResidentDecodeGroups = 512;
 
 // Split size (key rows per workgroup) for n_max key rows per query and `pairs` (query block, KV
 // head) pairs; `one_split_upto`: a key range up to this many rows is never split.
 int64_t chunk_policy(int64_t n_max, int64_t pairs, int64_t one_split_upto, bool fp8) {
     if (n_max <= one_split_upto) return n_max < 1 ? 1 : n_max;
-    if (pairs * ((n_max + 255) / 256) <= 2 * kResidentDecodeGroups) {
-        int64_t ns = kResidentDecodeGroups / pairs;
+    if (pairs * ((n_max + 255) / 256) <= 2 * mimo::kResidentDecodeGroups) {
+        int64_t ns = mimo::kResidentDecodeGroups / pairs;
         if (ns < 1) ns = 1;
         if (ns > (n_max + 127) / 128) ns = (n_max + 127) / 128;
         return ((n_max + ns - 1) / ns + 31) / 32 * 32;

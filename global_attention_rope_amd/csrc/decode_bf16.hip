@@ -40,6 +40,8 @@ constexpr int DV = 128;
 constexpr int NW = 4;
 constexpr int TILE = 32;                 // slots per wave iteration
 constexpr int PSTRIDE = DV + 2;          // floats per partial record: O[128], m, l
+constexpr int kDecodeSplitShift = 2;     // 2^shift consecutive splits of one pair in the dispatch order
+constexpr int kDecodeSplitBlock = 1 << kDecodeSplitShift;
 constexpr int VT_PITCH = DV + 16;        // bf16 per V row in the per-wave LDS tile (288 bytes)
 
 constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merge buffer
@@ -102,7 +104,21 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr int VREG = TILE * DV / VPL / 64;               // V loads per lane per tile (8 or 4)
     constexpr int VCH = DV / VPL;                            // 16-byte chunks per V row
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // Work item.  A grid of more than one round of resident workgroups is laid out in blocks of
+    // kDecodeSplitBlock consecutive splits of one (sequence, KV head) pair, the pairs in turn,
+    // then the pairs' next block of splits (x = split within the block + block size * KV head,
+    // y = sequence, z = block): the splits that hold keys for every sequence go out first and
+    // the empty splits of short sequences last.  Interleaved among the long-running ones,
+    // early-exiting workgroups leave the dispatcher's round-robin over the XCDs waiting on a full
+    // XCD while others have free slots.  The blocks round the splits up; a split past the last
+    // one starts at or past every sequence's key range and leaves at the empty-split check
+    // below, having written nothing.  A grid that fits in one round keeps (split, KV head,
+    // sequence).  (Selects and shifts only, no branch: this sits in front of every load.)
+    const bool blk = a.split_blocked != 0;
+    const int s = blk ? ((int)blockIdx.z << kDecodeSplitShift) + ((int)blockIdx.x & (kDecodeSplitBlock - 1))
+                      : (int)blockIdx.x;
+    const int g = blk ? (int)blockIdx.x >> kDecodeSplitShift : (int)blockIdx.y;
+    const int b = blk ? (int)blockIdx.y : (int)blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, gq = lane >> 4;
@@ -486,12 +502,18 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
 
 template <bool SWA, bool SINK, int ROT, bool FP8>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
-    const dim3 grid(a.nsplit, a.Hkv, a.B);
+    DecodeArgs k = a;
+    k.split_blocked = a.nsplit >= kDecodeSplitBlock &&
+                      (int64_t)a.B * a.Hkv * a.nsplit > kResidentDecodeGroups;
+    const dim3 grid = k.split_blocked
+                          ? dim3(a.Hkv * kDecodeSplitBlock, a.B,
+                                 (a.nsplit + kDecodeSplitBlock - 1) / kDecodeSplitBlock)
+                          : dim3(a.nsplit, a.Hkv, a.B);
     if (a.nsplit == 1) {
-        decode_bf16_kernel<SWA, SINK, false, ROT, FP8><<<grid, 256, 0, st>>>(a);
+        decode_bf16_kernel<SWA, SINK, false, ROT, FP8><<<grid, 256, 0, st>>>(k);
         return hipGetLastError();
     }
-    decode_bf16_kernel<SWA, SINK, true, ROT, FP8><<<grid, 256, 0, st>>>(a);
+    decode_bf16_kernel<SWA, SINK, true, ROT, FP8><<<grid, 256, 0, st>>>(k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     decode_combine_kernel<SWA, SINK, false><<<dim3(a.Hq, a.B), DV, 0, st>>>(a);

@@ -6,6 +6,9 @@
 namespace mimo {
 
 constexpr int kMaxRopeHalfArgs = 128;  // r/2 frequencies passed by value, in revolutions
+// Decode workgroups resident on the chip at once: 256 CUs x two 4-wave workgroups (their registers
+// allow two per CU).
+constexpr int64_t kResidentDecodeGroups = 512;
 
 // Rotate K (first rope_dims dims) once per token i in [i0, S) of each sequence b (position
 // start_pos[b] + i) and store it
@@ -90,6 +93,9 @@ struct DecodeArgs {
     // st + t and saw key rows up to its own, row j sitting at position
     // (kpos_rel ? st : 0) + kpos_off + j; sequences with st outside [0, max_position] get zeros.
     int32_t q_per_seq, kpos_rel, kpos_off;
+    // decode grid layout (set by the launch): 0 = (split, KV head, sequence); 1 = blocks of
+    // consecutive splits of a pair, the pairs in turn, then the next block
+    int32_t split_blocked;
     float score_scale_log2;
     float v_scale;
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)

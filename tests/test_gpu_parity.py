@@ -295,6 +295,19 @@ def test_decode_full_size_global_sampled_sequences():
         assert_close(out[b:b + 1], ref, what=f"seq {b} len {L}")
 
 
+def test_decode_many_splits_mixed_lengths_all_sequences():
+    """A decode grid of more than one round of workgroups (16 sequences x 2 KV heads x 34 splits of
+    256 slots) over lengths from 300 to 8500: the splits go out in blocks per (sequence, KV head)
+    pair, the blocks round 34 up to 36, and the short sequences' splits past their positions are
+    empty.  The oracle checks every sequence."""
+    w = _wl(kind=0, B=16, S=1, Hq=16, Hkv=2, sinks=False)
+    rng = np.random.default_rng(11)
+    positions = [300, 8500, 255, 256, 257, 1023] + rng.integers(300, 8501, size=10).tolist()
+    _note(f"decode GA many splits B=16 max {max(positions)}")
+    out, ref, *_ = _decode_case(w, positions, seed=7100)
+    assert_close(out, ref, what="decode, many splits")
+
+
 def test_decode_full_size_swa_all_sequences():
     w = _wl(kind=1, B=synth.DECODE_BATCH, S=1, Hq=64, Hkv=8, sinks=True)
     positions = synth.decode_lengths(4).tolist()
