@@ -141,9 +141,11 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
 //    decode workgroups: 256 CUs x two 4-wave workgroups) is cut into as many splits as fill ONE
 //    round, at least 128 slots each (one 32-slot tile per wave), rounded up to whole tiles — a
 //    second, mostly idle round would cost as much as the first;
-//  * otherwise a power of two >= 256, large enough to keep the grid (B * Hkv * splits) within 8192
-//    workgroups and the splits per sequence within what the combine kernel merges; fp8 caches
-//    (half the bytes per slot) take twice the slots per split and half the grid.
+//  * otherwise a power of two >= 256 (fp8 caches, half the bytes per slot: >= 512), large enough
+//    to keep the grid (B * Hkv * splits) within 4096 workgroups and the splits per sequence
+//    within what the combine kernel merges (at batch 64 over lengths up to 32768: 2048-slot
+//    splits, which streamed 2-6% faster than 1024-slot ones; 4096-slot ones lost on mixed
+//    lengths).
 
 // Split size (key rows per workgroup) for n_max key rows per query and `pairs` (query block, KV
 // head) pairs; `one_split_upto`: a key range up to this many rows is never split.
@@ -156,7 +158,7 @@ int64_t chunk_policy(int64_t n_max, int64_t pairs, int64_t one_split_upto, bool 
         return ((n_max + ns - 1) / ns + 31) / 32 * 32;
     }
     int64_t chunk = fp8 ? 512 : 256;
-    while (pairs * ((n_max + chunk - 1) / chunk) > (fp8 ? 4096 : 8192) ||
+    while (pairs * ((n_max + chunk - 1) / chunk) > 4096 ||
            (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
         chunk *= 2;
     return chunk;
