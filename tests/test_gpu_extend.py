@@ -199,6 +199,29 @@ def test_extend_global_long_cache_sampled_rows():
     assert_close(out[:, rows], ref[:, rows], what="long cache")
 
 
+def test_extend_four_tokens_mixed_lengths_all_sequences():
+    """Four new tokens per sequence over 64 global-layer caches of mixed lengths (300..18000, some
+    at a split boundary): the key rows are cut into splits whose partials the combine merges, and
+    short sequences' later splits are empty.  The oracle checks every sequence."""
+    w = _wl(kind=0, B=64, S=4, Hq=16, Hkv=4, sinks=False)
+    rng = np.random.default_rng(12)
+    starts = [300, 18000, 9020, 9021, 9019] + rng.integers(300, 18001, size=59).tolist()
+    B = len(starts)
+    cap = max(starts) + w.seq
+    _note(f"extend 4 tokens many splits B={B}")
+    q, k, v, _ = synth.layer_inputs(w, 5900, device=DEV)
+    kc, vc = synth.cache_contents(w, 5901, B, cap, device=DEV)
+    pre = (kc.clone(), vc.clone())
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    out = mimo.extend(_params(w), q, k, v, sp, max(starts), kc, vc)
+    torch.cuda.synchronize()
+    for b in range(B):
+        okc, ovc, kpos, count = _oracle_cache(w, pre[0][b:b + 1], pre[1][b:b + 1], [starts[b]])
+        ref = oracle.extend(_oparams(w, batch=1), _f32(q[b:b + 1]), _f32(k[b:b + 1]), _f32(v[b:b + 1]),
+                            np.array([starts[b]], np.int32), okc, ovc, kpos, count, None)
+        assert_close(out[b:b + 1], ref, what=f"seq {b} start {starts[b]}")
+
+
 @pytest.mark.parametrize("kind", [0, 1])
 def test_extend_four_tokens_batch64_full_size(kind):
     """Four new tokens per sequence after the decode workload's cached lengths (batch 64, uniform
