@@ -148,6 +148,33 @@ def test_decode_fp8_full_size(kind):
         assert_close(out[b:b + 1], ref, what=f"fp8 global seq {b} len {L}")
 
 
+def test_decode_fp8_many_splits_mixed_lengths_all_sequences():
+    """A global-layer decode over fp8 caches whose grid takes more than one round of workgroups
+    (16 sequences x 2 KV heads x 34 splits of 512 slots, dispatched in blocks of 4 splits per
+    pair and rounded up to 36), lengths from 300 to 17000: every sequence against the oracle."""
+    w = _wl(kind=0, B=16, S=1, Hq=16, Hkv=2, sinks=False)
+    rng = np.random.default_rng(13)
+    positions = [300, 17000, 511, 512, 513, 2047] + rng.integers(300, 17001, size=10).tolist()
+    B = len(positions)
+    cap = max(positions) + 1
+    _note(f"fp8 decode many splits B={B} cap={cap}")
+    q, kn, vn, _, _, _ = synth.decode_inputs(w, 11150, B, 1, device=DEV)
+    kc8, vc8 = synth.fp8_cache_contents(w, 11250, B, cap, device=DEV)
+    pre = {b: (_np8(kc8[b:b + 1, :, :positions[b]]), _np8(vc8[b:b + 1, :, :positions[b]]))
+           for b in range(B)}
+    pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    out = mimo.decode(_p8(w, B), q, kn, vn, pos_t, max(positions), kc8, vc8)
+    torch.cuda.synchronize()
+    for b in range(B):
+        L = positions[b]
+        kcb, vcb = pre[b]
+        ref, *_ = oracle.decode_fp8(_oparams(w, 1), _f32(q[b:b + 1]), _f32(kn[b:b + 1]),
+                                    _f32(vn[b:b + 1]), np.array([L], np.int32), kcb, vcb,
+                                    np.arange(L, dtype=np.int32)[None], np.array([L], np.int32),
+                                    KS, VS, None)
+        assert_close(out[b:b + 1], ref, what=f"fp8 global seq {b} len {L}")
+
+
 @pytest.mark.parametrize("kind", [0, 1])
 def test_prefill_writes_fp8_caches_and_decode_continues(kind):
     """Prefill storing coded caches (value codes bit for bit, key codes neighbour-valid), its
