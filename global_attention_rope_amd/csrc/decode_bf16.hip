@@ -435,11 +435,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 // thread per output dim.  The position, every split's (max, sum) and the first PRE records' values
 // are requested together, before anything waits (records past the last split are read as the last
 // one again): splits the position leaves empty never wrote their records, so those values are
-// masked, never used.  Then the common maximum and the
-// weights go through LDS and each thread sums its dim.
-template <bool SWA, bool SINK, bool VERIFY>
+// masked, never used.  Then the common maximum and the weights go through LDS and each thread
+// sums its dim, in split order (PRE, the prefetch depth, is picked at launch from the split
+// count; the sum is the same for any PRE).
+template <bool SWA, bool SINK, bool VERIFY, int PRE>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a) {
-    constexpr int PRE = 96, CH = 32;
+    constexpr int CH = 32;
     __shared__ float w_s[1024], l_s[1024];
     __shared__ float red[4];
     const int h = blockIdx.x, bq = blockIdx.y, d = threadIdx.x, wave = d >> 6;
@@ -500,6 +501,16 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
     o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
 }
 
+// The combine with the smallest prefetch depth that holds every split (at most 96; more splits
+// are read in further chunks).
+template <bool SWA, bool SINK, bool VERIFY>
+void launch_combine(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+    if (a.nsplit <= 16) decode_combine_kernel<SWA, SINK, VERIFY, 16><<<grid, DV, 0, st>>>(a);
+    else if (a.nsplit <= 32) decode_combine_kernel<SWA, SINK, VERIFY, 32><<<grid, DV, 0, st>>>(a);
+    else if (a.nsplit <= 64) decode_combine_kernel<SWA, SINK, VERIFY, 64><<<grid, DV, 0, st>>>(a);
+    else decode_combine_kernel<SWA, SINK, VERIFY, 96><<<grid, DV, 0, st>>>(a);
+}
+
 template <bool SWA, bool SINK, int ROT, bool FP8>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
     DecodeArgs k = a;
@@ -516,7 +527,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
     decode_bf16_kernel<SWA, SINK, true, ROT, FP8><<<grid, 256, 0, st>>>(k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_combine_kernel<SWA, SINK, false><<<dim3(a.Hq, a.B), DV, 0, st>>>(a);
+    launch_combine<SWA, SINK, false>(a, dim3(a.Hq, a.B), st);
     return hipGetLastError();
 }
 
@@ -546,11 +557,11 @@ hipError_t launch_verify_combine(const DecodeArgs& a, bool swa, bool sink, hipSt
     if (nq > 65535 || a.nsplit > decode_max_splits()) return hipErrorInvalidConfiguration;
     const dim3 grid(a.Hq, (unsigned)nq);
     if (swa) {
-        if (sink) decode_combine_kernel<true, true, true><<<grid, DV, 0, st>>>(a);
-        else decode_combine_kernel<true, false, true><<<grid, DV, 0, st>>>(a);
+        if (sink) launch_combine<true, true, true>(a, grid, st);
+        else launch_combine<true, false, true>(a, grid, st);
     } else {
-        if (sink) decode_combine_kernel<false, true, true><<<grid, DV, 0, st>>>(a);
-        else decode_combine_kernel<false, false, true><<<grid, DV, 0, st>>>(a);
+        if (sink) launch_combine<false, true, true>(a, grid, st);
+        else launch_combine<false, false, true>(a, grid, st);
     }
     return hipGetLastError();
 }
