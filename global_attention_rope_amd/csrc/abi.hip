@@ -137,27 +137,29 @@ size_t prefill_ws(const mimo_attn_params* p, int32_t S) {
 
 // Decode split size: slots per workgroup.
 //  * a sliding ring of at most 1024 slots is one split;
-//  * a small grid (at most two rounds of 256-slot splits on the chip, which holds 512 resident
-//    decode workgroups: 256 CUs x two 4-wave workgroups) is cut into as many splits as fill ONE
-//    round, at least 128 slots each (one 32-slot tile per wave), rounded up to whole tiles — a
-//    second, mostly idle round would cost as much as the first;
-//  * otherwise a power of two >= 256 (fp8 caches, half the bytes per slot: >= 512), large enough
-//    to keep the grid (B * Hkv * splits) within 4096 workgroups and the splits per sequence
-//    within what the combine kernel merges (at batch 64 over lengths up to 32768: 2048-slot
-//    splits, which streamed 2-6% faster than 1024-slot ones; 4096-slot ones lost on mixed
-//    lengths).
+//  * a small grid (at most two rounds of 256-slot splits on the chip) is cut into as many splits
+//    as make one workgroup per CU (256), at least 128 slots each, rounded up to whole tiles;
+//  * otherwise a power of two >= 1024 (fp8 caches, half the bytes per slot: >= 2048), large
+//    enough to keep the grid (B * Hkv * splits) within 4096 workgroups and the splits per
+//    sequence within what the combine kernel merges.
+// A workgroup's fixed work (query rotation, new token, wave merge, partial record) is paid per
+// split: in graph-replayed global decodes over 32767-slot caches, 256-slot splits at batch 4-8
+// streamed 4.3-4.4 TB/s and 1024-slot ones 5.1-5.3; at batch 1-2 one round of 256 workgroups beat
+// 512 (batch 1: 3.6 -> 4.2 TB/s, mixed lengths 2.3 -> 3.1); at batch 64 over lengths up to 32768
+// 2048-slot splits streamed 2-6% faster than 1024-slot ones and 4096-slot ones lost on mixed
+// lengths.
 
 // Split size (key rows per workgroup) for n_max key rows per query and `pairs` (query block, KV
 // head) pairs; `one_split_upto`: a key range up to this many rows is never split.
 int64_t chunk_policy(int64_t n_max, int64_t pairs, int64_t one_split_upto, bool fp8) {
     if (n_max <= one_split_upto) return n_max < 1 ? 1 : n_max;
     if (pairs * ((n_max + 255) / 256) <= 2 * mimo::kResidentDecodeGroups) {
-        int64_t ns = mimo::kResidentDecodeGroups / pairs;
+        int64_t ns = mimo::kResidentDecodeGroups / 2 / pairs;   // one per CU
         if (ns < 1) ns = 1;
         if (ns > (n_max + 127) / 128) ns = (n_max + 127) / 128;
         return ((n_max + ns - 1) / ns + 31) / 32 * 32;
     }
-    int64_t chunk = fp8 ? 512 : 256;
+    int64_t chunk = fp8 ? 2048 : 1024;
     while (pairs * ((n_max + chunk - 1) / chunk) > 4096 ||
            (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
         chunk *= 2;
