@@ -133,10 +133,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     //      the scalar offset and the chunk in the immediate (no per-load address arithmetic).
     //      Slots at or past the capacity read zeros (the resource's bound); slots past the
     //      visible range and the new token's slot are fixed up when used.
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.cap * (DQK * EB), kBufferFormat);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, a.cap * (DV * EB), kBufferFormat);
+    //      (byte sizes and offsets are unsigned 32-bit: the host keeps a cache slice below 4 GiB)
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)kc, (short)0, (int)((uint32_t)a.cap * (uint32_t)(DQK * EB)), kBufferFormat);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)vc, (short)0, (int)((uint32_t)a.cap * (uint32_t)(DV * EB)), kBufferFormat);
     const int k_lane = (l16 * DQK + (FP8 ? 16 : 8) * gq) * EB;
     // (V: lane holds row (lane + 64 it) / VCH of the tile, chunk (lane + 64 it) % VCH)
     const int v_lane = ((lane / VCH) * DV + (lane % VCH) * VPL) * EB;
@@ -147,21 +148,22 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < KREG / 2; ++c)
                 kr[kb * (KREG / 2) + c] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + 64 * c,
-                                                                 (t0 + kb * 16) * (DQK * EB), 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               krs, k_lane + 64 * c,
+                               (int)((uint32_t)(t0 + kb * 16) * (uint32_t)(DQK * EB)), 0));
         }
         // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16)
 #pragma unroll
         for (int it = 0; it < VREG; ++it) {
             if constexpr (FP8)
                 vr[it] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane,
-                                                                 t0 * DV + it * (64 / VCH) * DV, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               vrs, v_lane, (int)((uint32_t)t0 * DV + it * (64 / VCH) * DV), 0));
             else
                 vr[it] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                vrs, v_lane + (it & 3) * 4 * (DV * 2),
-                               t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2), 0));
+                               (int)((uint32_t)t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2)), 0));
         }
     };
     // ---- every load that does not depend on the position goes out first, unconditionally (a
@@ -255,11 +257,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 rotate8_cs_f32(nraw, npar, nd0, half, r, sm.cs, x);
                 const u32x2 code = e4m3x8_from_f32(x, a.k_inv);
                 *(u32x2*)(Kn + nd0) = code;
-                *(u32x2*)(kc + slot_new * DQK + nd0) = code;
+                *(u32x2*)(kc + (int64_t)slot_new * DQK + nd0) = code;
             } else {
                 const u32x4 wv = rotate8_cs(nraw, npar, nd0, half, r, sm.cs);
                 *(u32x4*)(Kn + nd0) = wv;
-                *(u32x4*)(kc + slot_new * DQK + nd0) = wv;
+                *(u32x4*)(kc + (int64_t)slot_new * DQK + nd0) = wv;
             }
         } else if (tid < DQK / 8 + DV / 8) {
             const int d0 = (tid - DQK / 8) * 8;
@@ -268,10 +270,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 unpack8(nraw, x);
                 const u32x2 code = e4m3x8_from_f32(x, a.v_inv);
                 *(u32x2*)(Vn + d0) = code;
-                *(u32x2*)(vc + slot_new * DV + d0) = code;
+                *(u32x2*)(vc + (int64_t)slot_new * DV + d0) = code;
             } else {
                 *(u32x4*)(Vn + d0) = nraw;
-                *(u32x4*)(vc + slot_new * DV + d0) = nraw;
+                *(u32x4*)(vc + (int64_t)slot_new * DV + d0) = nraw;
             }
         }
         block_sync_lds();

@@ -1,0 +1,218 @@
+"""Ideal bf16 arithmetic of the attention layer: a model of rounding, for the parity tests.
+
+Test infrastructure only.  It takes the oracle's exact rotated queries and keys (oracle.rotate)
+and computes the layer the way any bf16-operand / fp32-accumulate implementation has to, with
+every value exact except for these roundings, each round-to-nearest-even to bf16 through fp32:
+  * the rotated query and the rotated key (the matrix-core operands; inputs that are bf16 already,
+    such as cache contents, are unchanged by it);
+  * the softmax weights e^{z - m} before the product with V (the sum in the denominator is taken
+    from the unrounded weights);
+  * the output v_scale * O / l.
+Nothing else is rounded (scores, maxima and sums exact).  The difference between this model and the
+fp64 oracle is the error that bf16 operands alone cause; a kernel that rounds at these points and
+accumulates in fp32 should show about the same error, element by element and in L2.  It shares no
+code with the HIP path and is not a second oracle: the oracle stays the reference the tests gate on.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def bf16(x) -> np.ndarray:
+    """Round to bf16 through fp32 (RNE at both steps), returned as float64."""
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(x, np.float64)))
+    return t.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _head(qr, kr, v, vis, sink, tau, v_scale):
+    """One query head: qr [n, dqk], kr [m, dqk], v [m, dv] (already rounded operands), vis [n, m]."""
+    z = tau * (qr @ kr.T)
+    z = np.where(vis, z, -np.inf)
+    m = z.max(axis=1) if z.shape[1] else np.full(z.shape[0], -np.inf)
+    m = np.maximum(m, sink)
+    mu = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(z - mu[:, None])
+    l = e.sum(axis=1) + (np.exp(sink - mu) if np.isfinite(sink) else 0.0)
+    o = bf16(e) @ v
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where(l[:, None] > 0, v_scale * o / l[:, None], 0.0)
+    return bf16(out)
+
+
+U = 2.0 ** -8          # unit roundoff of bf16 (8 significant bits, round to nearest)
+BOUND_SIGMAS = 5.0
+
+
+def error_bound(qr, kr, v, vis, sink, tau, v_scale, r, k_rotated):
+    """Per-element bound on |ideal bf16 arithmetic - exact| for one query head, derived from the
+    rounding points above (first order).  qr [n, dqk] and kr [m, dqk] are the exact rotated rows;
+    only their first r dims are rounded (the others are the bf16 inputs themselves), and only keys
+    with k_rotated[j] (rotated in this call; cache contents are stored bf16 values) are rounded.
+    Each rounding is an independent error of at most U relative, uniform (variance U^2/3):
+      * score z_ij = tau q'_i.k'_j moves by tau sum_d (e_d + h_jd) q'_id k'_jd (e: query rounding,
+        shared by every key of the row; h: key rounding), which moves o_i by
+        sum_j p_ij (v_j - o_i) dz_ij;
+      * a softmax weight's rounding moves o_i by p_ij rho_ij v_j;
+    so the error of an output element has a standard deviation sigma computed here exactly from
+    the exact p, o, q', k', v; the bound is BOUND_SIGMAS * sigma plus the output's own rounding
+    (U |out|).  Returns (bound [n, dv], exact output [n, dv])."""
+    n, m = vis.shape
+    z = np.where(vis, tau * (qr @ kr.T), -np.inf)
+    mx = np.maximum(z.max(axis=1) if m else np.full(n, -np.inf), sink)
+    mu = np.where(np.isfinite(mx), mx, 0.0)
+    e = np.exp(z - mu[:, None])
+    l = e.sum(axis=1) + (np.exp(sink - mu) if np.isfinite(sink) else 0.0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        pm = np.where(l[:, None] > 0, e / l[:, None], 0.0)       # [n, m]
+    o = pm @ v                                                   # [n, dv]
+    var = (U * U / 3.0) * ((pm * pm) @ (v * v))                  # softmax-weight roundings
+    if r > 0:
+        qa = qr[:, :r]
+        ka = kr[:, :r]
+        # query roundings: sum_d q'_id^2 (sum_j p_ij (v_jc - o_ic) k'_jd)^2
+        cq = np.empty_like(o)
+        for i0 in range(0, n, 32):
+            sl = slice(i0, i0 + 32)
+            a = np.matmul((pm[sl, :, None] * v[None]).transpose(0, 2, 1), ka)   # [i, dv, r]
+            a -= o[sl, :, None] * (pm[sl] @ ka)[:, None, :]
+            cq[sl] = np.einsum("id,icd->ic", qa[sl] * qa[sl], a * a)
+        var += (tau * tau * U * U / 3.0) * cq
+        # key roundings (independent per key and dim)
+        wk = (qa * qa) @ (ka * ka * k_rotated[:, None]).T        # [n, m]
+        x = pm * pm * wk
+        var += (tau * tau * U * U / 3.0) * (x @ (v * v) - 2.0 * o * (x @ v) + o * o * x.sum(1)[:, None])
+    sig = np.sqrt(np.maximum(var, 0.0))
+    out = v_scale * o
+    return v_scale * BOUND_SIGMAS * sig + U * np.abs(out) + 1e-6, out
+
+
+def prefill_bound(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows=None):
+    """error_bound over a prefill (every key rotated in the call); rows not listed are NaN."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    pos = np.asarray(positions, np.int32)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    tau = p.softmax_scale if p.softmax_scale else 1.0 / np.sqrt(D)
+    sel = np.arange(S) if rows is None else np.asarray(rows)
+    bound = np.full((B, S, Hq, v.shape[-1]), np.nan)
+    for b in range(B):
+        qr = oracle.rotate(q[b, sel], p.rope_dims, p.rope_theta, np.repeat(pos[b, sel][:, None], Hq, 1))
+        kr = oracle.rotate(k[b], p.rope_dims, p.rope_theta, np.repeat(pos[b][:, None], Hkv, 1))
+        d = pos[b, sel][:, None] - pos[b][None, :]
+        vis = d >= 0
+        if p.layer_kind == 1:
+            vis &= d < p.window
+        for h in range(Hq):
+            s = -np.inf if sinks is None else float(sinks[h])
+            bound[b, sel, h] = error_bound(qr[:, h], kr[:, h // G], v[b, :, h // G], vis, s, tau,
+                                           p.v_scale, p.rope_dims, np.ones(S, bool))[0]
+    return bound
+
+
+def extend_bound(p: "oracle.OracleParams", q, k, v, start, kc=None, vc=None, kpos=None, count=None,
+                 sinks=None):
+    """error_bound over an extend (same arguments as oracle.extend): the cached keys are stored
+    values (not rounded again), the new tokens' keys are rotated and rounded in the call."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    st = np.asarray(start, np.int32)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    tau = p.softmax_scale if p.softmax_scale else 1.0 / np.sqrt(D)
+    bound = np.zeros((B, S, Hq, v.shape[-1]))
+    for b in range(B):
+        pos = st[b] + np.arange(S, dtype=np.int32)
+        qr = oracle.rotate(q[b], p.rope_dims, p.rope_theta, np.repeat(pos[:, None], Hq, 1))
+        kr = oracle.rotate(k[b], p.rope_dims, p.rope_theta, np.repeat(pos[:, None], Hkv, 1))
+        n = 0 if kc is None else int(count[b])
+        kp = np.concatenate([np.zeros(0, np.int32) if kc is None else np.asarray(kpos[b, :n]), pos])
+        d = pos[:, None] - kp[None, :]
+        vis = d >= 0
+        if p.layer_kind == 1:
+            vis &= d < p.window
+        rot = np.concatenate([np.zeros(n, bool), np.ones(S, bool)])
+        for h in range(Hq):
+            g = h // G
+            K = np.concatenate([np.asarray(kc[b, g, :n], np.float64) if n else np.zeros((0, D)), kr[:, g]])
+            V = np.concatenate([np.asarray(vc[b, g, :n], np.float64) if n else
+                                np.zeros((0, v.shape[-1])), v[b, :, g]])
+            s = -np.inf if sinks is None else float(sinks[h])
+            bound[b, :, h] = error_bound(qr[:, h], K, V, vis, s, tau, p.v_scale, p.rope_dims, rot)[0]
+    return bound
+
+
+def prefill(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows=None, block=256):
+    """Model output of a prefill (same arguments as oracle.prefill); rows not listed are NaN."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    pos = np.asarray(positions, np.int32)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    tau = p.softmax_scale if p.softmax_scale else 1.0 / np.sqrt(D)
+    sel = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.full((B, S, Hq, v.shape[-1]), np.nan)
+    for b in range(B):
+        qr = bf16(oracle.rotate(q[b, sel], p.rope_dims, p.rope_theta,
+                                np.repeat(pos[b, sel][:, None], Hq, 1)))
+        kr = bf16(oracle.rotate(k[b], p.rope_dims, p.rope_theta,
+                                np.repeat(pos[b][:, None], Hkv, 1)))
+        vb = v[b]
+        for i0 in range(0, len(sel), block):
+            rs = sel[i0:i0 + block]
+            pi = pos[b, rs]
+            lo = 0 if p.layer_kind == 0 else max(0, int(rs.min()) - p.window + 1)
+            hi = int(rs.max()) + 1
+            d = pi[:, None] - pos[b, lo:hi][None, :]
+            vis = d >= 0
+            if p.layer_kind == 1:
+                vis &= d < p.window
+            for h in range(Hq):
+                g = h // G
+                s = -np.inf if sinks is None else float(sinks[h])
+                out[b, rs, h] = _head(qr[i0:i0 + block, h], kr[lo:hi, g], vb[lo:hi, g], vis, s,
+                                      tau, p.v_scale)
+    return out
+
+
+def decode(p: "oracle.OracleParams", q, k_new, v_new, pos, kc=None, vc=None, kpos=None,
+           count=None, sinks=None):
+    """Model output of one decode step (same arguments as oracle.decode): the cached keys are taken
+    as given (rotated, and bf16 when they come from a bf16 cache), the new token is rotated and
+    rounded like the query."""
+    q, k_new, v_new = (np.asarray(a, np.float64) for a in (q, k_new, v_new))
+    pos = np.asarray(pos, np.int32)
+    B, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    G = Hq // Hkv
+    tau = p.softmax_scale if p.softmax_scale else 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, v_new.shape[-1]))
+    for b in range(B):
+        P = int(pos[b])
+        qr = bf16(oracle.rotate(q[b], p.rope_dims, p.rope_theta, np.full(Hq, P, np.int32)))
+        kn = bf16(oracle.rotate(k_new[b], p.rope_dims, p.rope_theta, np.full(Hkv, P, np.int32)))
+        n = 0 if kc is None else int(count[b])
+        kp = np.zeros(0, np.int32) if kc is None else np.asarray(kpos[b, :n])
+        keep = kp <= P - 1
+        if p.layer_kind == 1:
+            keep &= kp > P - p.window
+        for h in range(Hq):
+            g = h // G
+            ks = [kn[g][None]]
+            vs = [v_new[b, g][None]]
+            if n:
+                ks.insert(0, np.asarray(kc[b, g, :n], np.float64)[keep])
+                vs.insert(0, np.asarray(vc[b, g, :n], np.float64)[keep])
+            K, V = np.concatenate(ks), np.concatenate(vs)
+            s = -np.inf if sinks is None else float(sinks[h])
+            out[b, h] = _head(qr[h][None], K, V, np.ones((1, len(K)), bool), s, tau,
+                              p.v_scale)[0]
+    return out
+
+
+def rel_l2(x, ref) -> float:
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))

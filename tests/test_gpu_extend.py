@@ -15,7 +15,7 @@ import torch
 
 import global_attention_rope_amd as mimo
 import oracle
-from tests import synth
+from tests import rounding_model, synth
 from tests.gpu_helpers import assert_close, ring_positions, to_np64
 from tests.test_gpu_parity import _f32, _note, _oparams, _params, _wl
 
@@ -97,7 +97,9 @@ def run_extend_case(case, seed, q_scale=1.0):
     torch.cuda.synchronize()
     ref, krot = oracle.extend(_oparams(w), _f32(q), _f32(k), _f32(v), np.array(starts, np.int32),
                               okc, ovc, kpos, count, _f32(s), want_k_rot=True)
-    assert_close(out, ref, what=f"extend out {case}")
+    bound = rounding_model.extend_bound(_oparams(w), _f32(q), _f32(k), _f32(v), starts, okc, ovc,
+                                        kpos, count, _f32(s))
+    assert_close(out, ref, what=f"extend out {case}", bound=bound)
 
     # caches: the new tokens in their slots, every other slot as it was
     kc1, vc1, v_h = to_np64(kc), to_np64(vc), to_np64(v)

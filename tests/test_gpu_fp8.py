@@ -148,10 +148,35 @@ def test_decode_fp8_full_size(kind):
         assert_close(out[b:b + 1], ref, what=f"fp8 global seq {b} len {L}")
 
 
+def test_decode_fp8_blocked_grid_padded_block_all_sequences():
+    """fp8 caches through the blocked dispatch with a padded last block: 64 sequences x 4 KV heads
+    x 10 splits of 2048 slots (blocks of 4 round 10 up to 12): every sequence against the oracle."""
+    from tests.test_gpu_parity import blocked_positions
+    w = _wl(kind=0, B=64, S=1, Hq=16, Hkv=4, sinks=False)
+    positions = blocked_positions(19)
+    B, cap = len(positions), max(positions) + 1
+    assert mimo.decode_workspace_size(_p8(w, B), max(positions)) == B * 16 * 10 * 130 * 4
+    _note(f"fp8 decode blocked grid B={B} cap={cap}")
+    q, kn, vn, _, _, _ = synth.decode_inputs(w, 11160, B, 1, device=DEV)
+    kc8, vc8 = synth.fp8_cache_contents(w, 11260, B, cap, device=DEV)
+    pre = {b: (_np8(kc8[b:b + 1, :, :positions[b]]), _np8(vc8[b:b + 1, :, :positions[b]]))
+           for b in range(B)}
+    pos_t = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    out = mimo.decode(_p8(w, B), q, kn, vn, pos_t, max(positions), kc8, vc8)
+    torch.cuda.synchronize()
+    for b in range(B):
+        L = positions[b]
+        kcb, vcb = pre[b]
+        ref, *_ = oracle.decode_fp8(_oparams(w, 1), _f32(q[b:b + 1]), _f32(kn[b:b + 1]),
+                                    _f32(vn[b:b + 1]), np.array([L], np.int32), kcb, vcb,
+                                    np.arange(L, dtype=np.int32)[None], np.array([L], np.int32),
+                                    KS, VS, None)
+        assert_close(out[b:b + 1], ref, what=f"fp8 global seq {b} len {L}")
+
+
 def test_decode_fp8_many_splits_mixed_lengths_all_sequences():
-    """A global-layer decode over fp8 caches whose grid takes more than one round of workgroups
-    (16 sequences x 2 KV heads x 34 splits of 512 slots, dispatched in blocks of 4 splits per
-    pair and rounded up to 36), lengths from 300 to 17000: every sequence against the oracle."""
+    """A global-layer decode over fp8 caches, lengths from 300 to 17000 (16 sequences x 2 KV heads
+    x 9 splits of 2048 slots, one round of workgroups): every sequence against the oracle."""
     w = _wl(kind=0, B=16, S=1, Hq=16, Hkv=2, sinks=False)
     rng = np.random.default_rng(13)
     positions = [300, 17000, 511, 512, 513, 2047] + rng.integers(300, 17001, size=10).tolist()

@@ -12,7 +12,8 @@ import global_attention_rope_amd as mimo
 import oracle
 from oracle import OracleParams
 from tests import synth
-from tests.gpu_helpers import assert_close, ring_positions, to_np64
+from tests import rounding_model
+from tests.gpu_helpers import assert_close, assert_near_model, ring_positions, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -87,32 +88,33 @@ def test_tiny_swa_fp32_full():
     dict(kind=0, B=2, S=333, Hq=16, Hkv=1, sinks=False, starts=[0, 20000]),
     dict(kind=0, B=1, S=129, Hq=8, Hkv=2, sinks=True, starts=[7]),
     dict(kind=0, B=1, S=1, Hq=4, Hkv=4, sinks=False, starts=[0]),
-    # every dim rotated: q scaled by 1/4 so the softmax is flat enough that bf16 rounding of the
-    # rotated operands (all 192 dims here) stays inside the tolerance on the first rows
-    dict(kind=0, B=1, S=257, Hq=8, Hkv=2, sinks=False, starts=[0], r=192, theta=10.0,
-         q_scale=0.25),
+    # every dim rotated (each rotated dim adds a bf16 rounding of an operand)
+    dict(kind=0, B=1, S=257, Hq=8, Hkv=2, sinks=False, starts=[0], r=192),
     # sliding layers whose GQA group is a multiple of 4 run the grouped kernel, which builds a
     # cos/sin table of the rows' positions: at the widest rotation (every dim, its rows packed)
     # and with no rotation at all
-    dict(kind=1, B=1, S=200, Hq=8, Hkv=2, sinks=True, starts=[3], r=192, theta=10.0,
-         q_scale=0.25),
+    dict(kind=1, B=1, S=200, Hq=8, Hkv=2, sinks=True, starts=[3], r=192),
     dict(kind=1, B=2, S=150, Hq=8, Hkv=2, sinks=True, starts=[0, 300], r=0),
 ])
 def test_prefill_bf16_small(case):
     case = dict(case)
     starts = case.pop("starts")
-    q_scale = case.pop("q_scale", 1.0)
     w = _wl(**case)
     _note(str(case))
-    *_, out, ref, _, _, _ = _run_prefill(w, seed=1000 + w.seq, starts=starts, q_scale=q_scale)
-    assert_close(out, ref, what=str(case))
+    q, k, v, s, out, ref, _, _, pos = _run_prefill(w, seed=1000 + w.seq, starts=starts)
+    bound = rounding_model.prefill_bound(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s))
+    assert_close(out, ref, what=str(case), bound=bound)
+    model = rounding_model.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s))
+    assert_near_model(out, ref, model, what=str(case))
 
 
 def test_prefill_swa_full_size_all_rows():
     w = synth.SWA_PREFILL
     _note(w.name)
-    *_, out, ref, _, _, _ = _run_prefill(w, seed=1000, starts=[0])
+    q, k, v, s, out, ref, _, _, pos = _run_prefill(w, seed=1000, starts=[0])
     assert_close(out, ref, what=w.name)
+    model = rounding_model.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s))
+    assert_near_model(out, ref, model, what=w.name)
 
 
 def test_prefill_global_full_size_sampled_rows():
@@ -121,8 +123,10 @@ def test_prefill_global_full_size_sampled_rows():
     rng = np.random.default_rng(2)
     rows = np.unique(np.concatenate([np.arange(64), np.arange(w.seq - 64, w.seq),
                                      rng.integers(0, w.seq, 128)])).astype(np.int32)
-    *_, out, ref, _, _, _ = _run_prefill(w, seed=2000, starts=[0], rows=rows)
+    q, k, v, s, out, ref, _, _, pos = _run_prefill(w, seed=2000, starts=[0], rows=rows)
     assert_close(out[:, rows], ref[:, rows], what=w.name)
+    model = rounding_model.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s), rows=rows)
+    assert_near_model(to_np64(out)[:, rows], ref[:, rows], model[:, rows], what=w.name)
 
 
 @pytest.mark.parametrize("kind", [0, 1])
@@ -184,9 +188,10 @@ def test_prefill_empty_and_invalid_arguments():
 # ----------------------------------------------------------------------------- decode
 
 
-def _decode_case(w, positions, seed, cap=None, q_scale=1.0, max_position=None):
+def _decode_case(w, positions, seed, cap=None, q_scale=1.0, max_position=None, with_model=False):
     """Random cache state + one decode step on the GPU, and the oracle on the same state (rows of
-    sequences past max_position, which the GPU leaves at zero, are not meaningful in ref)."""
+    sequences past max_position, which the GPU leaves at zero, are not meaningful in ref).
+    with_model: return (out, ref, rounding model's output) instead."""
     B = len(positions)
     swa = w.layer_kind == 1
     maxp = max(positions) if max_position is None else max_position
@@ -213,13 +218,17 @@ def _decode_case(w, positions, seed, cap=None, q_scale=1.0, max_position=None):
             vc_o[b, :, :n] = vc0[b, :, slots].transpose(1, 0, 2)
             kpos[b, :n] = held[slots]
             cnt[b] = n
-        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(opos),
-                                  kc_o, vc_o, kpos, cnt, _f32(s), want_k_rot=True)
+        kc_m, vc_m = kc_o, vc_o
     else:
         kpos = np.tile(np.arange(cap, dtype=np.int32), (B, 1))
         cnt = np.array(opos, np.int32)
-        ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(opos),
-                                  kc0, vc0, kpos, cnt, _f32(s), want_k_rot=True)
+        kc_m, vc_m = kc0, vc0
+    ref, krot = oracle.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn), np.array(opos),
+                              kc_m, vc_m, kpos, cnt, _f32(s), want_k_rot=True)
+    if with_model:
+        model = rounding_model.decode(_oparams(w, B), _f32(q), _f32(kn), _f32(vn),
+                                      np.array(opos), kc_m, vc_m, kpos, cnt, _f32(s))
+        return out, ref, model
     return out, ref, krot, kc, vc, kc0, vc0, vn
 
 
@@ -296,16 +305,38 @@ def test_decode_full_size_global_sampled_sequences():
 
 
 def test_decode_many_splits_mixed_lengths_all_sequences():
-    """A decode grid of more than one round of workgroups (16 sequences x 2 KV heads x 34 splits of
-    256 slots) over lengths from 300 to 8500: the splits go out in blocks per (sequence, KV head)
-    pair, the blocks round 34 up to 36, and the short sequences' splits past their positions are
-    empty.  The oracle checks every sequence."""
+    """A decode grid over lengths from 255 to 8500 (16 sequences x 2 KV heads x 9 splits of 1024
+    slots, one round of workgroups): short sequences' splits past their positions are empty, and
+    the split boundaries fall inside tiles.  The oracle checks every sequence."""
     w = _wl(kind=0, B=16, S=1, Hq=16, Hkv=2, sinks=False)
     rng = np.random.default_rng(11)
     positions = [300, 8500, 255, 256, 257, 1023] + rng.integers(300, 8501, size=10).tolist()
     _note(f"decode GA many splits B=16 max {max(positions)}")
     out, ref, *_ = _decode_case(w, positions, seed=7100)
     assert_close(out, ref, what="decode, many splits")
+
+
+# A decode whose grid takes more than one round of resident workgroups goes out in blocks of 4
+# splits per (sequence, KV head) pair.  64 sequences x 4 KV heads over lengths up to 20000 make
+# 10 splits of 2048 slots (bf16 and fp8 caches alike; tests/test_abi_cpu.py pins this geometry
+# through the workspace size), so the blocks round 10 up to 12 and the last block's two padded
+# splits start past every sequence's key range.
+BLOCKED_MAX_POSITION = 20000
+
+
+def blocked_positions(seed):
+    rng = np.random.default_rng(seed)
+    return [BLOCKED_MAX_POSITION, 300, 2047, 2048, 2049, 6143, 16385] + \
+        rng.integers(300, BLOCKED_MAX_POSITION + 1, size=57).tolist()
+
+
+def test_decode_blocked_grid_padded_block_all_sequences():
+    w = _wl(kind=0, B=64, S=1, Hq=16, Hkv=4, sinks=False)
+    positions = blocked_positions(17)
+    assert mimo.decode_workspace_size(_params(w, 64), max(positions)) == 64 * 16 * 10 * 130 * 4
+    _note(f"decode GA blocked grid B=64 max {max(positions)}")
+    out, ref, *_ = _decode_case(w, positions, seed=7150)
+    assert_close(out, ref, what="decode, blocked grid with a padded block")
 
 
 def test_decode_full_size_swa_all_sequences():
@@ -360,36 +391,74 @@ def test_prefill_then_decode_matches_longer_prefill(kind):
     assert_close(dec, ref_dec, what="decode after prefill")
 
 
-@pytest.mark.parametrize("layer", [0, 1])
+def _stack_config():
+    """The 48-layer stack's configuration as a model config carries it (hybrid_layer_pattern and
+    the per-kind fields), from which the dispatcher derives every layer's parameters."""
+    return mimo.HybridAttentionConfig(
+        hidden_size=4096, num_attention_heads=64, num_key_value_heads=4, swa_num_key_value_heads=8,
+        head_dim=192, v_head_dim=128, partial_rotary_factor=1.0 / 3.0, rope_theta=5e6,
+        swa_rope_theta=1e4, sliding_window_size=128, hybrid_layer_pattern=synth.stack_pattern(),
+        rope_dims=64)
+
+
+def _golden_layer(index):
+    """What the pages fix for stack layer `index` (tests/golden/dispatch.json, each fact cited
+    there): its kind, theta, KV heads, window, sinks and cache kind."""
+    import json
+    import os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "dispatch.json")))
+    kind = "global" if index in fx["stack"]["global_layers"] else "sliding"
+    return kind, fx["theta_selection"][kind]
+
+
+@pytest.mark.parametrize("layer", [0, 1, 5, 6])
 def test_stack_layer_full_size_prefill_then_decode_sampled(layer):
-    """A layer of the 48-layer stack at full size (batch 2, 16384 tokens; layer 0 global, layer 1
-    sliding): prefill writes the cache, then two decode steps; sampled prefill rows and every
-    decode output are checked against the oracle (whose decode cache is its own rotated keys)."""
-    pattern = synth.stack_pattern()
-    heads = synth.SWA_HEADS if pattern[layer] == 1 else synth.GA_HEADS
+    """A layer of the 48-layer stack at full size (batch 2, 16384 tokens), configured by the
+    per-layer dispatch (layer_specs of the stack's hybrid_layer_pattern config): prefill writes the
+    cache, then two decode steps.  The oracle gets the layer the pages define for that index
+    (kind, theta, KV heads, window, sinks from the golden dispatch facts), so a wrong kind, theta,
+    KV-head count, window or sink choice of the dispatcher fails here.  Sampled prefill rows and
+    every decode output are checked (the oracle's decode cache is its own rotated keys)."""
+    cfg = _stack_config()
+    spec = mimo.layer_specs(cfg)[layer]
     B, S, T = synth.STACK_BATCH, synth.STACK_SEQ, 2
-    w = synth.Workload("stack", B, S + T, dtype=torch.bfloat16, **heads)
-    _note(f"stack layer {layer} kind {w.layer_kind}")
-    q, k, v, s = synth.layer_inputs(w, 4000 + layer, device=DEV)
-    wS = synth.Workload("stack", B, S, dtype=torch.bfloat16, **heads)
+    p = spec.params(cfg, B)
+    kind_name, fact = _golden_layer(layer)
+    okind = 1 if kind_name == "sliding" else 0
+    op = OracleParams(batch=B, num_q_heads=64, num_kv_heads=fact["kv_heads"], qk_head_dim=192,
+                      v_head_dim=128, rope_dims=64, layer_kind=okind, window=fact["window"],
+                      rope_theta=fact["theta"], v_scale=float(np.sqrt(4096 / (64 * 128))))
+    _note(f"stack layer {layer}: dispatch kind {spec.kind} theta {spec.rope_theta} "
+          f"kv {spec.num_kv_heads} window {spec.window} sinks {spec.has_sinks}")
+    # inputs drawn with the pages' shapes for the index (KV heads from the golden facts)
+    w = synth.Workload("stack", B, S + T, num_q_heads=64, num_kv_heads=fact["kv_heads"],
+                       qk_head_dim=192, v_head_dim=128, rope_dims=64, rope_theta=fact["theta"],
+                       layer_kind=okind, window=fact["window"], sinks=True, hidden=4096,
+                       dtype=torch.bfloat16)
+    q, k, v, s_all = synth.layer_inputs(w, 4000 + layer, device=DEV)
+    s_gpu = s_all if spec.has_sinks else None
+    s_ref = s_all if fact["sinks"] else None
     sp = torch.zeros(B, dtype=torch.int32, device=DEV)
-    cap = w.window if w.layer_kind == 1 else S + T
-    kc = torch.zeros((B, w.num_kv_heads, cap, 192), dtype=torch.bfloat16, device=DEV)
-    vc = torch.zeros((B, w.num_kv_heads, cap, 128), dtype=torch.bfloat16, device=DEV)
-    out = mimo.prefill(_params(wS), q[:, :S].contiguous(), k[:, :S].contiguous(),
-                       v[:, :S].contiguous(), sp, sinks=s, k_cache=kc, v_cache=vc)
+    cap = spec.window if spec.cache == "ring" else S + T
+    kc = torch.zeros((B, spec.num_kv_heads, cap, 192), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros((B, spec.num_kv_heads, cap, 128), dtype=torch.bfloat16, device=DEV)
+    out = mimo.prefill(p, q[:, :S].contiguous(), k[:, :S].contiguous(), v[:, :S].contiguous(), sp,
+                       sinks=s_gpu, k_cache=kc, v_cache=vc)
     decs = []
     for t in range(T):
         pos = torch.full((B,), S + t, dtype=torch.int32, device=DEV)
-        decs.append(mimo.decode(_params(wS), q[:, S + t].contiguous(), k[:, S + t].contiguous(),
-                                v[:, S + t].contiguous(), pos, S + T - 1, kc, vc, sinks=s))
+        decs.append(mimo.decode(p, q[:, S + t].contiguous(), k[:, S + t].contiguous(),
+                                v[:, S + t].contiguous(), pos, S + T - 1, kc, vc, sinks=s_gpu))
     torch.cuda.synchronize()
     rng = np.random.default_rng(layer)
     rows = np.unique(np.concatenate([np.arange(8), np.arange(S - 8, S),
                                      rng.integers(0, S, 16)])).astype(np.int32)
     rows_all = np.concatenate([rows, np.arange(S, S + T, dtype=np.int32)])
     posn = np.stack([np.arange(S + T, dtype=np.int32)] * B)
-    ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), posn, _f32(s), rows=rows_all)
+    ref = oracle.prefill(op, _f32(q), _f32(k), _f32(v), posn, _f32(s_ref), rows=rows_all)
     assert_close(out[:, rows], ref[:, rows], what=f"stack layer {layer} prefill rows")
+    model = rounding_model.prefill(op, _f32(q), _f32(k), _f32(v), posn, _f32(s_ref), rows=rows_all)
+    assert_near_model(to_np64(out)[:, rows], ref[:, rows], model[:, rows],
+                      what=f"stack layer {layer} prefill rows")
     for t in range(T):
         assert_close(decs[t], ref[:, S + t], what=f"stack layer {layer} decode step {t}")
