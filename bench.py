@@ -175,7 +175,7 @@ def main():
                     help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
                     choices=["stack", "swa_prefill", "ga_prefill", "decode", "extend", "layer",
-                             "router", "copy", "gemm"])
+                             "router", "copy", "gemm", "decode_latency"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -367,6 +367,91 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def decode_latency(args, dev):
+    """Per-call time of the stack's decode calls (batch 2) against the latency floor, each set of
+    calls captured in one HIP graph and replayed: 40 calls that only launch (empty kernel, 16
+    workgroups), 40 one-tile dependent reads (16 workgroups, 80 KiB each, a fresh 1.3 MB region per
+    call: the bytes of one sliding layer's ring), the 40 sliding-layer decodes and the 8
+    global-layer decodes of one decode step (positions 16384).  'cold': a 512 MiB scratch buffer
+    is written before every replay, outside the timed region, so every ring comes from memory;
+    'hot': replayed back to back."""
+    import ctypes
+
+    import torch
+
+    import global_attention_rope_amd as mimo
+    from global_attention_rope_amd import build as hb
+    from tests import synth
+
+    probe = ctypes.CDLL(hb.PROBE_LIB)
+    vp = ctypes.c_void_p
+    probe.mimo_probe_empty.argtypes = [vp, ctypes.c_int32, vp]
+    probe.mimo_probe_tile_read.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
+    B, S, NSW, NGA, G = 2, synth.STACK_SEQ, 40, 8, 16
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    region = G * 80 * 1024
+    src = torch.ones(NSW * region // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty(NSW * G * 256, dtype=torch.int32, device=dev)
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def probes_empty():
+        for l in range(NSW):
+            assert probe.mimo_probe_empty(vp(dst.data_ptr() + l * G * 1024), G, cur()) == 0
+
+    def probes_read():
+        for l in range(NSW):
+            assert probe.mimo_probe_tile_read(vp(src.data_ptr() + l * region),
+                                              vp(dst.data_ptr() + l * G * 1024), G, 80, cur()) == 0
+
+    def mk_layers(heads, n, seed):
+        w = synth.Workload("dec", B, 1, dtype=torch.bfloat16, **heads)
+        cap = w.window if w.layer_kind == 1 else S + 1
+        out = []
+        for i in range(n):
+            q, kn, vn, sk, kc, vc = synth.decode_inputs(w, seed + i, B, cap, device=dev)
+            p = mimo.Params(B, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims, w.layer_kind,
+                            w.window, w.rope_theta, w.v_scale)
+            ws = torch.empty(mimo.decode_workspace_size(p, S) + 256, dtype=torch.uint8, device=dev)
+            o = torch.empty((B, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
+            out.append((p, q, kn, vn, sk, kc, vc, ws, o))
+        return out
+
+    pos = torch.full((B,), S, dtype=torch.int32, device=dev)
+    sw = mk_layers(synth.SWA_HEADS, NSW, 15000)
+    ga = mk_layers(synth.GA_HEADS, NGA, 15100)
+
+    def decodes(ls):
+        def run():
+            for (p, q, kn, vn, sk, kc, vc, ws, o) in ls:
+                mimo.decode(p, q, kn, vn, pos, S, kc, vc, sinks=sk, out=o, workspace=ws)
+        return run
+
+    cases = [("empty_kernel", probes_empty, NSW), ("tile_read_80KiB", probes_read, NSW),
+             ("sliding_decode", decodes(sw), NSW), ("global_decode", decodes(ga), NGA)]
+    res = {}
+    for name, fn, n in cases:
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        for mode in ("cold", "hot"):
+            ts = []
+            for _ in range(max(args.steps, 5)):
+                if mode == "cold":
+                    flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / n)
+            ts.sort()
+            res[f"{name}_{mode}_us_per_call"] = round(ts[len(ts) // 2], 3)
+    return res
+
+
 def single_layer(args, dev):
     """Time one layer configuration on its own (profiling aid); prints one JSON line."""
     import torch
@@ -389,7 +474,9 @@ def single_layer(args, dev):
         return e0.elapsed_time(e1) / n
 
     res = {"workload": args.workload, "steps": args.steps}
-    if args.workload == "gemm":
+    if args.workload == "decode_latency":
+        res.update(decode_latency(args, dev))
+    elif args.workload == "gemm":
         # achievable dense bf16 matrix-core rate on this part (hipBLASLt through torch), the
         # practical ceiling next to the nominal peak
         n = 8192

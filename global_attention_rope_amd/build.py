@@ -16,6 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmimo_attn.so")
+PROBE_LIB = os.path.join(PKG, "libmimo_probe.so")   # latency references (measurement aid)
+PROBE_SOURCES = ["probe.hip"]
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["abi.hip", "prefill_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip",
            "layer.hip", "router.hip", "verify_bf16.hip"]
@@ -52,17 +54,19 @@ def _run(cmd: list[str]) -> tuple[int, str]:
 
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source (always) and atomically replace the library."""
+    """Compile every source (always) and atomically replace the libraries."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     tag = f"{os.getpid()}"
-    objs = [os.path.join(OBJ_DIR, s.replace(".hip", f".{tag}.o")) for s in SOURCES]
+    every = SOURCES + PROBE_SOURCES
+    objs_all = [os.path.join(OBJ_DIR, s.replace(".hip", f".{tag}.o")) for s in every]
+    objs = objs_all[:len(SOURCES)]
     cmds = [[hipcc(), *compile_flags(), "-c", os.path.join(CSRC, s), "-o", o]
-            for s, o in zip(SOURCES, objs)]
+            for s, o in zip(every, objs_all)]
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     try:
         with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
             results = list(ex.map(_run, cmds))
-        for s, (rc, err) in zip(SOURCES, results):
+        for s, (rc, err) in zip(every, results):
             if rc != 0:
                 raise RuntimeError(f"hipcc failed on {s} ({rc}):\n{err}")
             if verbose and err.strip():
@@ -73,8 +77,14 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         if rc != 0:
             raise RuntimeError(f"link failed ({rc}):\n{err}")
         os.replace(tmp, LIB)
+        tmp = PROBE_LIB + f".tmp{tag}"
+        rc, err = _run([hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared",
+                        *objs_all[len(SOURCES):], "-o", tmp])
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{err}")
+        os.replace(tmp, PROBE_LIB)
     finally:
-        for o in objs:
+        for o in objs_all:
             if os.path.exists(o):
                 os.remove(o)
     return LIB

@@ -159,9 +159,10 @@ int64_t chunk_policy(int64_t n_max, int64_t pairs, int64_t one_split_upto, bool 
         if (ns > (n_max + 127) / 128) ns = (n_max + 127) / 128;
         return ((n_max + ns - 1) / ns + 31) / 32 * 32;
     }
+    // (more than 4096 pairs: one split each, the whole range)
     int64_t chunk = fp8 ? 2048 : 1024;
-    while (pairs * ((n_max + chunk - 1) / chunk) > 4096 ||
-           (n_max + chunk - 1) / chunk > mimo::decode_max_splits())
+    while (chunk < n_max && (pairs * ((n_max + chunk - 1) / chunk) > 4096 ||
+                             (n_max + chunk - 1) / chunk > mimo::decode_max_splits()))
         chunk *= 2;
     return chunk;
 }

@@ -31,6 +31,19 @@ def test_library_exports_every_declared_function():
     assert mimo.lib().mimo_attn_abi_version() == 2
 
 
+def test_probe_library_exports_its_declared_functions():
+    """The latency-reference library beside the layer's (a measurement aid) loads and exports what
+    include/mimo_probe.h declares."""
+    from global_attention_rope_amd import build as hb
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mimo_probe.h")).read(),
+                  flags=re.S)
+    names = set(re.findall(r"\b(mimo_probe_\w+)\s*\(", text))
+    assert names == {"mimo_probe_empty", "mimo_probe_tile_read"}
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
 def _swa(**kw):
     d = dict(batch=1, num_q_heads=64, num_kv_heads=8, qk_head_dim=192, v_head_dim=128,
              rope_dims=64, layer_kind=mimo.LAYER_SWA, window=128, rope_theta=1e4,
@@ -120,6 +133,9 @@ def test_workspace_sizes():
     ws = mimo.decode_workspace_size(_ga(batch=64), 32768)
     assert ws > 0 and ws % (64 * 64 * 130 * 4) == 0
     assert mimo.decode_workspace_size(_ga(batch=64), 100) == 0
+    # more (sequence, KV head) pairs than the split policy's grid budget: one split each
+    assert mimo.decode_workspace_size(_ga(batch=2048), 2000) == 0
+    assert mimo.decode_workspace_size(_ga(batch=1100, cache_dtype=mimo.CACHE_FP8_E4M3), 70000) == 0
     # extend: sliding layers lay out window + S rows of K and V; global layers read a bf16 cache
     assert mimo.extend_workspace_size(_swa(batch=2), 1000, 5000) == 2 * 8 * (128 + 1000) * (192 + 128) * 2
     assert mimo.extend_workspace_size(_ga(batch=2), 1000, 5000) == 0
