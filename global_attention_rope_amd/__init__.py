@@ -23,6 +23,8 @@ from .binding import (  # noqa: F401
     check_params,
     decode,
     decode_workspace_size,
+    decode_noalloc,
+    decode_noalloc_max_bytes,
     extend,
     extend_workspace_size,
     last_error,

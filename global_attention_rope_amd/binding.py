@@ -23,7 +23,8 @@ CACHE_SAME, CACHE_FP8_E4M3 = 0, 2
 
 EXPORTS = ("mimo_attn_prefill", "mimo_attn_prefill_workspace_size", "mimo_attn_extend",
            "mimo_attn_extend_workspace_size", "mimo_attn_decode",
-           "mimo_attn_decode_workspace_size", "mimo_attn_layer_prefill",
+           "mimo_attn_decode_workspace_size", "mimo_attn_decode_noalloc",
+           "mimo_attn_decode_noalloc_max_bytes", "mimo_attn_layer_prefill",
            "mimo_attn_layer_workspace_size", "mimo_attn_check_params", "mimo_attn_last_error",
            "mimo_attn_abi_version", "mimo_router_topk", "mimo_router_check_params")
 
@@ -125,6 +126,10 @@ def lib(path: str = LIB_PATH):
             L.mimo_attn_decode.restype = ctypes.c_int
             L.mimo_attn_decode_workspace_size.argtypes = [P, i32]
             L.mimo_attn_decode_workspace_size.restype = sz
+            L.mimo_attn_decode_noalloc.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp]
+            L.mimo_attn_decode_noalloc.restype = ctypes.c_int
+            L.mimo_attn_decode_noalloc_max_bytes.argtypes = []
+            L.mimo_attn_decode_noalloc_max_bytes.restype = sz
             L.mimo_attn_layer_prefill.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                                   vp, vp, i32, vp, sz, vp]
             L.mimo_attn_layer_prefill.restype = ctypes.c_int
@@ -303,6 +308,39 @@ def decode(p: Params, q, k_new, v_new, positions, max_position: int, k_cache, v_
                                   _ptr(positions), max_position, _ptr(k_cache), _ptr(v_cache), cap,
                                   _ptr(sinks), _ptr(out), _ptr(workspace), wbytes,
                                   _stream(stream)))
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(lib().mimo_attn_decode_noalloc_max_bytes())
+
+
+def decode_noalloc(p: Params, q, k_new, v_new, positions, max_position: int, k_cache, v_cache,
+                   sinks=None, out=None, stream=None):
+    """mimo_attn_decode_noalloc on torch device tensors: decode without a workspace (the library's
+    own per-device scratch array holds the split partials).  out is required to be preallocated
+    by callers that cannot allocate; when None it is allocated here."""
+    B = q.shape[0]
+    dev, dt = q.device, _tdtype(p)
+    if p.batch != B:
+        raise ValueError(f"params.batch {p.batch} != q.shape[0] {B}")
+    _expect(q, "q", (B, p.num_q_heads, p.qk_head_dim), dt, dev)
+    _expect(k_new, "k_new", (B, p.num_kv_heads, p.qk_head_dim), dt, dev)
+    _expect(v_new, "v_new", (B, p.num_kv_heads, p.v_head_dim), dt, dev)
+    _expect(positions, "positions", (B,), torch.int32, dev)
+    cap = k_cache.shape[2]
+    _expect(k_cache, "k_cache", (B, p.num_kv_heads, cap, p.qk_head_dim), _cdtype(p), dev)
+    _expect(v_cache, "v_cache", (B, p.num_kv_heads, cap, p.v_head_dim), _cdtype(p), dev)
+    if sinks is not None:
+        _expect(sinks, "sinks", (p.num_q_heads,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, p.num_q_heads, p.v_head_dim), dtype=dt, device=dev)
+    _expect(out, "out", (B, p.num_q_heads, p.v_head_dim), dt, dev)
+    cp = p.c()
+    _raise(lib().mimo_attn_decode_noalloc(ctypes.byref(cp), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                          _ptr(positions), max_position, _ptr(k_cache),
+                                          _ptr(v_cache), cap, _ptr(sinks), _ptr(out),
+                                          _stream(stream)))
     return out
 
 

@@ -6,6 +6,8 @@
 // upstream" and "Implementation plan".
 #include <math.h>
 #include <stdarg.h>
+
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -634,10 +636,46 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     return hip_status(mimo::launch_verify_combine(da, swa, sinks != nullptr, st), "extend combine");
 }
 
-int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,
-                     const void* v_new, const int32_t* positions, int32_t max_position,
-                     void* k_cache, void* v_cache, int32_t cache_capacity, const float* sinks,
-                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free decode (mimo_attn_decode_noalloc): the split partials live in
+// this file-scope device array instead of a caller workspace.  Each device that runs the library
+// holds its own copy until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it only stands in for the symbol): its device address, looked up once per device
+// with that device current, is what the kernels get.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MIMO_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MIMO_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MIMO_OK;
+}
+
+int decode_impl(const mimo_attn_params* p, const void* q, const void* k_new, const void* v_new,
+                const int32_t* positions, int32_t max_position, void* k_cache, void* v_cache,
+                int32_t cache_capacity, const float* sinks, void* out, void* workspace,
+                size_t workspace_bytes, void* stream, bool noalloc) {
     int rc = check(p);
     if (rc != MIMO_OK) return rc;
     if (max_position < 0) return fail(MIMO_ERR_INVALID_ARG, "max_position %d < 0", max_position);
@@ -688,6 +726,20 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
         return fail(MIMO_ERR_UNSUPPORTED, "bf16 decode packs at most %d query heads per KV head",
                     kMaxDecodeGroup);
     const size_t need = decode_ws(p, max_position);
+    if (noalloc) {
+        if (need > kNoAllocScratchBytes)
+            return fail(MIMO_ERR_WORKSPACE,
+                        "allocation-free decode: the split partials need %zu bytes, above its "
+                        "%zu-byte scratch (use mimo_attn_decode with a workspace)",
+                        need, kNoAllocScratchBytes);
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            rc = scratch_address(&workspace);
+            if (rc != MIMO_OK) return rc;
+            workspace_bytes = kNoAllocScratchBytes;
+        }
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -725,5 +777,27 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
     fill_omega(p, da.omega_rev);
     return hip_status(mimo::launch_decode_bf16(da, swa, sinks != nullptr, st), "decode (bf16)");
 }
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new,
+                     const void* v_new, const int32_t* positions, int32_t max_position,
+                     void* k_cache, void* v_cache, int32_t cache_capacity, const float* sinks,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(p, q, k_new, v_new, positions, max_position, k_cache, v_cache,
+                       cache_capacity, sinks, out, workspace, workspace_bytes, stream, false);
+}
+
+int mimo_attn_decode_noalloc(const mimo_attn_params* p, const void* q, const void* k_new,
+                             const void* v_new, const int32_t* positions, int32_t max_position,
+                             void* k_cache, void* v_cache, int32_t cache_capacity,
+                             const float* sinks, void* out, void* stream) {
+    return decode_impl(p, q, k_new, v_new, positions, max_position, k_cache, v_cache,
+                       cache_capacity, sinks, out, nullptr, 0, stream, true);
+}
+
+size_t mimo_attn_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 }  // extern "C"

@@ -29,9 +29,11 @@
  *   - sinks is fp32 [Hq] or NULL (no sink).  Position arrays are int32 in device memory.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  Nothing is
  *     synchronised, allocated, freed or printed by the library, and it keeps no global state;
- *     calls are thread-safe.  (Exception: mimo_attn_layer_prefill keeps one hipBLASLt handle per
- *     device, created on its first call there and kept until the process ends.)  Calls that write
- *     the same cache or workspace must be ordered by the caller (same stream or events).
+ *     calls are thread-safe.  (Exceptions: mimo_attn_layer_prefill keeps one hipBLASLt handle per
+ *     device, created on its first call there and kept until the process ends;
+ *     mimo_attn_decode_noalloc keeps its partials in a device array of the library and its address
+ *     per device.)  Calls that write the same cache or workspace must be ordered by the caller
+ *     (same stream or events).
  *   - Arguments are checked on the host before anything is enqueued.  On error the function
  *     returns a negative MIMO_ERR_* code, writes nothing, and mimo_attn_last_error() returns a
  *     message (thread-local).  MIMO_ERR_HIP means a launch failed; the message holds HIP's text.
@@ -197,6 +199,26 @@ int mimo_attn_decode(const mimo_attn_params* p, const void* q, const void* k_new
 /* Workspace bytes mimo_attn_decode needs: B * Hq * splits * (dv + 2) * 4 when the cache range is
  * cut into several splits, else 0.  Returns 0 for invalid parameters. */
 size_t mimo_attn_decode_workspace_size(const mimo_attn_params* p, int32_t max_position);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mimo_attn_decode without the
+ * workspace arguments, on the same kernels.  The split partials go to a file-scope device array
+ * of the library, mimo_attn_decode_noalloc_max_bytes() bytes (32 MiB), which each device the
+ * library runs on holds until the process ends; its address is looked up once per device.  A call
+ * whose partials (mimo_attn_decode_workspace_size) exceed it returns MIMO_ERR_WORKSPACE and
+ * writes nothing.  Nothing is allocated, and no routine that allocates is called.  Every call on
+ * one device shares that device's array, which keeps the last call's partials (nothing in it has
+ * to start at zero): calls that overlap on one device (other streams, other threads) race and
+ * must be ordered by the caller.  Arguments, results and errors otherwise as mimo_attn_decode.
+ */
+int mimo_attn_decode_noalloc(const mimo_attn_params* p, const void* q, const void* k_new,
+                             const void* v_new, const int32_t* positions, int32_t max_position,
+                             void* k_cache, void* v_cache, int32_t cache_capacity,
+                             const float* sinks, void* out, void* stream);
+
+/* Size in bytes of the array behind mimo_attn_decode_noalloc (its largest partials). */
+size_t mimo_attn_decode_noalloc_max_bytes(void);
 
 /*
  * Layer prefill: the attention layer with its projections ("Add Xiaomi MiMo-V2", "Additional

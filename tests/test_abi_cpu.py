@@ -174,6 +174,31 @@ def _decode(p, maxp=10, q=1, kn=1, vn=1, pos=1, kc=1, vc=1, cap=128, out=1, ws=N
                                    ptr(kc), ptr(vc), cap, None, ptr(out), ptr(ws), wsb, None)
 
 
+def _decode_noalloc(p, maxp=10, q=1, kn=1, vn=1, pos=1, kc=1, vc=1, cap=128, out=1):
+    cp = p.c()
+    P = ctypes.c_void_p
+    ptr = lambda x: None if x is None else P(0x1000 * x)
+    return _lib().mimo_attn_decode_noalloc(ctypes.byref(cp), ptr(q), ptr(kn), ptr(vn), ptr(pos),
+                                           maxp, ptr(kc), ptr(vc), cap, None, ptr(out), None)
+
+
+def test_decode_noalloc_limits_checked_before_any_device_call():
+    """The allocation-free decode validates like mimo_attn_decode, and rejects partials beyond its
+    fixed scratch array with a workspace error, before touching any device."""
+    E = mimo.MIMO_ERR_INVALID_ARG
+    assert mimo.decode_noalloc_max_bytes() == 32 << 20
+    assert _decode_noalloc(_swa(), maxp=-1) == E
+    assert _decode_noalloc(_swa(), kc=None) == E
+    assert _decode_noalloc(_swa(), cap=100) == E
+    assert _decode_noalloc(_ga(), maxp=500, cap=500) == E
+    assert _decode_noalloc(_swa(batch=0), q=None) == mimo.MIMO_OK
+    # 512 sequences x 4 KV heads over 4096 positions: 2 splits, 34 MB of partials > 32 MiB
+    big = _ga(batch=512)
+    assert mimo.decode_workspace_size(big, 4095) > mimo.decode_noalloc_max_bytes()
+    assert _decode_noalloc(big, maxp=4095, cap=4096) == mimo.MIMO_ERR_WORKSPACE
+    assert "scratch" in mimo.last_error()
+
+
 def _extend(p, S=16, q=1, k=1, v=1, sp=1, maxs=100, out=1, kc=1, vc=1, cap=128, ws=None, wsb=0):
     cp = p.c()
     P = ctypes.c_void_p
