@@ -20,10 +20,12 @@
 //   * LDS layouts are unpadded and XOR-swizzled at 16-byte granularity so that the MFMA operand
 //     reads are conflict-free: K chunk c of row r sits at c ^ ((r >> 1) & 7); V chunk c of row r at
 //     c ^ ((r & 3) << 2);
-//   * S^T = K * Q^T with v_mfma_f32_32x32x16_bf16 (each lane owns one query column), online
-//     softmax in the log2 domain with a lazily raised running maximum (the maximum is only moved
-//     when a tile exceeds it by more than 2^8, so the O rescale is rare; the result is exact because
-//     numerator and denominator share the reference), O^T += V^T * P^T with V^T read by
+//   * S^T = K * Q^T with v_mfma_f32_32x32x16_bf16 (each lane owns one query column); Q carries the
+//     score scale tau * log2(e) and the accumulators start at minus the running maximum, so the
+//     products hand the softmax its exponents directly (one v_exp_f32 per score, no scale or
+//     subtraction); online softmax in the log2 domain with a lazily raised running maximum (moved
+//     only when a tile exceeds it by more than 2^8, so the O rescale is rare; the result is exact
+//     because numerator and denominator share the reference); O^T += V^T * P^T with V^T read by
 //     ds_read_b64_tr_b16;
 //   * the wave index is made scalar so tile skipping and the band-edge masking are uniform
 //     branches; sliding-window workgroups only stream the tiles of their band, and each wave only
@@ -57,8 +59,10 @@ constexpr int SW_WAVES = 4, SW_STAGES = 2;
 constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyond 2^8
 
 
-__device__ __forceinline__ void rotate_pair8_kernarg(u32x4& lo, u32x4& hi, int32_t pos,
-                                                     const double* om) {
+// Rotate the pairs (lo[t], hi[t]) at pos and return the chunk this lane keeps (lo when `lower`),
+// times `scale`, rounded once to bf16.
+__device__ __forceinline__ u32x4 rotate_pair8_kernarg(const u32x4& lo, const u32x4& hi, bool lower,
+                                                      int32_t pos, const double* om, float scale) {
     float x[8], y[8];
     unpack8(lo, x);
     unpack8(hi, y);
@@ -67,11 +71,18 @@ __device__ __forceinline__ void rotate_pair8_kernarg(u32x4& lo, u32x4& hi, int32
         float c, s;
         rope_cos_sin_rev(pos, om[t], c, s);
         const float xl = x[t], xh = y[t];
-        x[t] = xl * c - xh * s;
-        y[t] = xh * c + xl * s;
+        x[t] = (lower ? xl * c - xh * s : xh * c + xl * s) * scale;
     }
-    lo = pack8(x);
-    hi = pack8(y);
+    return pack8(x);
+}
+
+// 8 bf16 times `scale`, rounded once to bf16.
+__device__ __forceinline__ u32x4 scale8(const u32x4& w, float scale) {
+    float x[8];
+    unpack8(w, x);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] *= scale;
+    return pack8(x);
 }
 
 // GROUPED: a workgroup covers NW query heads of one KV group over the same 32 rows (wave w takes
@@ -222,7 +233,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
     if (STAGES == 3 && n_tiles > 1) issue(1, std::integral_constant<int, 1 % STAGES>{});
 
-    // ---- Q^T operands, rotated, in registers
+    // ---- Q^T operands, rotated and scaled by tau * log2(e) (so that the products give the scores
+    //      in the log2 domain), rounded once to bf16, in registers
+    const float sc = a.score_scale_log2;
     bf16x8 Qb[KCH];
     {
         const int qi = q_first + l32;
@@ -272,9 +285,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
                     for (int t = 0; t < 8; ++t) {
                         const float2 cst = e[t];
-                        x[t] = __builtin_fmaf(sgn * y[t], cst.y, x[t] * cst.x);
+                        x[t] = __builtin_fmaf(sgn * y[t], cst.y, x[t] * cst.x) * sc;
                     }
                     qw[c] = pack8(x);
+                } else {
+                    qw[c] = scale8(qw[c], sc);
                 }
                 if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
                 Qb[c] = as_bf16x8(qw[c]);
@@ -286,10 +301,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 const int d0 = 16 * c + 8 * g;
                 if (d0 < r) {
                     const bool lower = d0 < half;
-                    u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
-                    u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
-                    rotate_pair8_kernarg(lo, hi, p0 + qi, a.omega_rev + (lower ? d0 : d0 - half));
-                    qw[c] = lower ? lo : hi;
+                    const u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
+                    const u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
+                    qw[c] = rotate_pair8_kernarg(lo, hi, lower, p0 + qi,
+                                                 a.omega_rev + (lower ? d0 : d0 - half), sc);
+                } else {
+                    qw[c] = scale8(qw[c], sc);
                 }
                 if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
                 Qb[c] = as_bf16x8(qw[c]);
@@ -322,7 +339,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     f32x16 O[DV / 32];
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db) O[db] = f32x16{};
-    const float sc = a.score_scale_log2;
+    // The products return sc * z - m_ref: the score accumulators start from -m_ref, kept as a
+    // 16-register copy (negm), where m_ref is the running maximum once one is known (the sink when
+    // there is one, else 0 until the first visible key).
+    f32x16 negm;
+    {
+        const float m0 = SINK ? sink_l2 : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m0;
+    }
     const int q_l = q_first + l32;
     // row q_l sees key row j iff q_l + shift - j lies in [0, lim): the window (sliding) and the
     // first key row holding a token both bound it
@@ -340,14 +365,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const uint8_t* kst = smem + ST * K_TILE;
         const uint8_t* vst = smem + ST * V_TILE;   // + v_rd, which holds the V area's base
 
-        f32x16 S0 = f32x16{}, S1 = f32x16{};
+        f32x16 S0, S1;
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const uint8_t* kp = kst + k_rd[c & 3] + (c >> 2) * 128;
             const bf16x8 A0 = *(const bf16x8*)(kp);
             const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
-            S0 = mfma32x32x16(A0, Qb[c], S0);
-            S1 = mfma32x32x16(A1, Qb[c], S1);
+            S0 = mfma32x32x16(A0, Qb[c], c == 0 ? negm : S0);
+            S1 = mfma32x32x16(A1, Qb[c], c == 0 ? negm : S1);
         }
         if (!full) {
             // (the empty asm keeps the compiler from if-converting this uniform branch, which
@@ -370,24 +395,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             ma = fmaxf(fmaxf(ma, S0[i]), S1[i]);
             mb = fmaxf(fmaxf(mb, S0[i + 8]), S1[i + 8]);
         }
-        const float mx = max_lane_pair32(fmaxf(ma, mb)) * sc;
-        // lazily raised reference maximum
-        const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
-        const float m_new = raise ? fmaxf(m_run, mx) : m_run;
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float mx = max_lane_pair32(fmaxf(ma, mb));   // relative to m_ref
+        // lazily raised reference maximum: moved to the row's maximum on its first visible key,
+        // later only when a tile exceeds it by more than 2^kRescaleLog2; the tile's scores, the
+        // sum and O follow the move
+        const bool first = m_run == -INFINITY;
+        const bool raise = mx > kRescaleLog2 || (first && mx != -INFINITY);
         if (__any(raise)) {
             asm volatile("");   // rare: keep it a branch (see above)
-            const float alpha = fast_exp2(m_run - m_use);
+            const float ref = -negm[0];
+            const float shift = raise ? mx : 0.0f;
+            const float alpha = first ? 1.0f : fast_exp2(-shift);
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                S0[i] -= shift;
+                S1[i] -= shift;
+                negm[i] = -(ref + shift);
+            }
+            if (raise) m_run = ref + shift;
         }
-        m_run = m_new;
         float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            S0[i] = fast_exp2(__builtin_fmaf(S0[i], sc, -m_use));
-            S1[i] = fast_exp2(__builtin_fmaf(S1[i], sc, -m_use));
+            S0[i] = fast_exp2(S0[i]);
+            S1[i] = fast_exp2(S1[i]);
             ps0 += S0[i];
             ps1 += S1[i];
         }

@@ -89,6 +89,26 @@ def assert_near_model(gpu, ref, model, what=""):
     return rel_g, rel_m
 
 
+def _f32np(t):
+    return None if t is None else t.to("cpu", torch.float32).numpy()
+
+
+def workload_oparams(w, batch=None):
+    """The oracle's parameter block for a synth.Workload."""
+    from oracle import OracleParams
+    return OracleParams(w.batch if batch is None else batch, w.num_q_heads, w.num_kv_heads,
+                        w.qk_head_dim, w.v_head_dim, w.rope_dims, w.layer_kind, w.window,
+                        w.rope_theta, w.v_scale)
+
+
+def prefill_bound_for(w, q, k, v, sinks, positions, rows=None):
+    """The derived per-element bound (tests/rounding_model.py) of a prefill of workload w on the
+    given torch inputs; rows not listed are NaN."""
+    from tests import rounding_model
+    return rounding_model.prefill_bound(workload_oparams(w, q.shape[0]), _f32np(q), _f32np(k),
+                                        _f32np(v), np.asarray(positions), _f32np(sinks), rows=rows)
+
+
 def ring_positions(pos: int, window: int) -> np.ndarray:
     """Position held by each ring slot just before the token at `pos` is appended: the most
     recent position < pos congruent to the slot (negative: the slot is still empty)."""

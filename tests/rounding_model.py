@@ -4,7 +4,9 @@ Test infrastructure only.  It takes the oracle's exact rotated queries and keys 
 and computes the layer the way any bf16-operand / fp32-accumulate implementation has to, with
 every value exact except for these roundings, each round-to-nearest-even to bf16 through fp32:
   * the rotated query and the rotated key (the matrix-core operands; inputs that are bf16 already,
-    such as cache contents, are unchanged by it);
+    such as cache contents, are unchanged by it).  Where the query operand carries the score
+    scale (prefill: q' times fp32(tau * log2 e), rounded once, the scores then taken in the log2
+    domain), every query dim is rounded, not only the rotated ones;
   * the softmax weights e^{z - m} before the product with V (the sum in the denominator is taken
     from the unrounded weights);
   * the output v_scale * O / l.
@@ -46,11 +48,13 @@ U = 2.0 ** -8          # unit roundoff of bf16 (8 significant bits, round to nea
 BOUND_SIGMAS = 5.0
 
 
-def error_bound(qr, kr, v, vis, sink, tau, v_scale, r, k_rotated):
+def error_bound(qr, kr, v, vis, sink, tau, v_scale, r, k_rotated, rq=None):
     """Per-element bound on |ideal bf16 arithmetic - exact| for one query head, derived from the
     rounding points above (first order).  qr [n, dqk] and kr [m, dqk] are the exact rotated rows;
-    only their first r dims are rounded (the others are the bf16 inputs themselves), and only keys
-    with k_rotated[j] (rotated in this call; cache contents are stored bf16 values) are rounded.
+    the first rq dims of the query (rq = r unless given: the query operand carries the score scale
+    when rq = dqk) and the first r dims of the keys are rounded (the others are the bf16 inputs
+    themselves), and only keys with k_rotated[j] (rotated in this call; cache contents are stored
+    bf16 values) are rounded.
     Each rounding is an independent error of at most U relative, uniform (variance U^2/3):
       * score z_ij = tau q'_i.k'_j moves by tau sum_d (e_d + h_jd) q'_id k'_jd (e: query rounding,
         shared by every key of the row; h: key rounding), which moves o_i by
@@ -69,9 +73,10 @@ def error_bound(qr, kr, v, vis, sink, tau, v_scale, r, k_rotated):
         pm = np.where(l[:, None] > 0, e / l[:, None], 0.0)       # [n, m]
     o = pm @ v                                                   # [n, dv]
     var = (U * U / 3.0) * ((pm * pm) @ (v * v))                  # softmax-weight roundings
-    if r > 0:
-        qa = qr[:, :r]
-        ka = kr[:, :r]
+    rq = r if rq is None else rq
+    if rq > 0:
+        qa = qr[:, :rq]
+        ka = kr[:, :rq]
         # query roundings: sum_d q'_id^2 (sum_j p_ij (v_jc - o_ic) k'_jd)^2
         cq = np.empty_like(o)
         for i0 in range(0, n, 32):
@@ -80,6 +85,9 @@ def error_bound(qr, kr, v, vis, sink, tau, v_scale, r, k_rotated):
             a -= o[sl, :, None] * (pm[sl] @ ka)[:, None, :]
             cq[sl] = np.einsum("id,icd->ic", qa[sl] * qa[sl], a * a)
         var += (tau * tau * U * U / 3.0) * cq
+    if r > 0:
+        qa = qr[:, :r]
+        ka = kr[:, :r]
         # key roundings (independent per key and dim)
         wk = (qa * qa) @ (ka * ka * k_rotated[:, None]).T        # [n, m]
         x = pm * pm * wk
@@ -89,8 +97,33 @@ def error_bound(qr, kr, v, vis, sink, tau, v_scale, r, k_rotated):
     return v_scale * BOUND_SIGMAS * sig + U * np.abs(out) + 1e-6, out
 
 
+# Rows that see more keys than this average their roundings away: their error stays inside the
+# fixed 1e-2 + 2e-2 |x| bound (rel L2 ~2e-3), so the derived bound is left at 0 there (no widening)
+# and the cost of computing it (rows x keys x dv x dqk) stays small.
+BOUND_MAX_KEYS = 64
+
+
+def _bound_rows(qr, K, V, vis, sink, tau, v_scale, r, k_rotated, rq, out):
+    """error_bound for the rows of vis that see at most BOUND_MAX_KEYS keys (in blocks of 32
+    rows, keys cut to the block's visible range); other rows keep out's value (0)."""
+    cnt = vis.sum(axis=1)
+    for i0 in range(0, vis.shape[0], 32):
+        rows = np.arange(i0, min(i0 + 32, vis.shape[0]))
+        rows = rows[cnt[rows] <= BOUND_MAX_KEYS]
+        if rows.size == 0:
+            continue
+        cols = np.nonzero(vis[rows].any(axis=0))[0]
+        if cols.size == 0:
+            lo, hi = 0, 0
+        else:
+            lo, hi = int(cols[0]), int(cols[-1]) + 1
+        out[rows] = error_bound(qr[rows], K[lo:hi], V[lo:hi], vis[rows][:, lo:hi], sink, tau,
+                                v_scale, r, k_rotated[lo:hi], rq=rq)[0]
+
+
 def prefill_bound(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows=None):
-    """error_bound over a prefill (every key rotated in the call); rows not listed are NaN."""
+    """error_bound over a prefill (every key rotated in the call, the query operand carrying the
+    score scale); rows not listed are NaN, rows seeing more than BOUND_MAX_KEYS keys 0."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     pos = np.asarray(positions, np.int32)
     B, S, Hq, D = q.shape
@@ -108,15 +141,20 @@ def prefill_bound(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows
             vis &= d < p.window
         for h in range(Hq):
             s = -np.inf if sinks is None else float(sinks[h])
-            bound[b, sel, h] = error_bound(qr[:, h], kr[:, h // G], v[b, :, h // G], vis, s, tau,
-                                           p.v_scale, p.rope_dims, np.ones(S, bool))[0]
+            out = np.zeros((len(sel), v.shape[-1]))
+            _bound_rows(qr[:, h], kr[:, h // G], v[b, :, h // G], vis, s, tau, p.v_scale,
+                        p.rope_dims, np.ones(S, bool), D, out)
+            bound[b, sel, h] = out
     return bound
 
 
 def extend_bound(p: "oracle.OracleParams", q, k, v, start, kc=None, vc=None, kpos=None, count=None,
-                 sinks=None):
+                 sinks=None, q_scaled=None):
     """error_bound over an extend (same arguments as oracle.extend): the cached keys are stored
-    values (not rounded again), the new tokens' keys are rotated and rounded in the call."""
+    values (not rounded again), the new tokens' keys are rotated and rounded in the call.
+    q_scaled: the query operand carries the score scale (every query dim rounded); by default
+    when more than 16 tokens are new (the library's prefill kernel takes those).  Rows seeing
+    more than BOUND_MAX_KEYS keys get 0."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     st = np.asarray(start, np.int32)
     B, S, Hq, D = q.shape
@@ -124,29 +162,38 @@ def extend_bound(p: "oracle.OracleParams", q, k, v, start, kc=None, vc=None, kpo
     G = Hq // Hkv
     tau = p.softmax_scale if p.softmax_scale else 1.0 / np.sqrt(D)
     bound = np.zeros((B, S, Hq, v.shape[-1]))
+    if q_scaled is None:
+        q_scaled = S > 16
     for b in range(B):
         pos = st[b] + np.arange(S, dtype=np.int32)
         qr = oracle.rotate(q[b], p.rope_dims, p.rope_theta, np.repeat(pos[:, None], Hq, 1))
         kr = oracle.rotate(k[b], p.rope_dims, p.rope_theta, np.repeat(pos[:, None], Hkv, 1))
         n = 0 if kc is None else int(count[b])
         kp = np.concatenate([np.zeros(0, np.int32) if kc is None else np.asarray(kpos[b, :n]), pos])
+        order = np.argsort(kp, kind="stable")   # keys by position, so visible ranges are contiguous
+        kp = kp[order]
         d = pos[:, None] - kp[None, :]
         vis = d >= 0
         if p.layer_kind == 1:
             vis &= d < p.window
-        rot = np.concatenate([np.zeros(n, bool), np.ones(S, bool)])
+        rot = np.concatenate([np.zeros(n, bool), np.ones(S, bool)])[order]
         for h in range(Hq):
             g = h // G
-            K = np.concatenate([np.asarray(kc[b, g, :n], np.float64) if n else np.zeros((0, D)), kr[:, g]])
+            K = np.concatenate([np.asarray(kc[b, g, :n], np.float64) if n else np.zeros((0, D)), kr[:, g]])[order]
             V = np.concatenate([np.asarray(vc[b, g, :n], np.float64) if n else
-                                np.zeros((0, v.shape[-1])), v[b, :, g]])
+                                np.zeros((0, v.shape[-1])), v[b, :, g]])[order]
             s = -np.inf if sinks is None else float(sinks[h])
-            bound[b, :, h] = error_bound(qr[:, h], K, V, vis, s, tau, p.v_scale, p.rope_dims, rot)[0]
+            out = np.zeros((S, v.shape[-1]))
+            _bound_rows(qr[:, h], K, V, vis, s, tau, p.v_scale, p.rope_dims, rot,
+                        D if q_scaled else None, out)
+            bound[b, :, h] = out
     return bound
 
 
 def prefill(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows=None, block=256):
-    """Model output of a prefill (same arguments as oracle.prefill); rows not listed are NaN."""
+    """Model output of a prefill (same arguments as oracle.prefill); rows not listed are NaN.
+    The query operand carries the score scale: q~ = bf16(q' * fp32(fp32(tau) * fp32(log2 e))),
+    scores z = ln 2 * <q~, bf16(k')>."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     pos = np.asarray(positions, np.int32)
     B, S, Hq, D = q.shape
@@ -156,8 +203,9 @@ def prefill(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows=None,
     sel = np.arange(S) if rows is None else np.asarray(rows)
     out = np.full((B, S, Hq, v.shape[-1]), np.nan)
     for b in range(B):
-        qr = bf16(oracle.rotate(q[b, sel], p.rope_dims, p.rope_theta,
-                                np.repeat(pos[b, sel][:, None], Hq, 1)))
+        sc = float(np.float32(np.float32(tau) * np.float32(1.4426950408889634)))
+        qr = bf16(sc * oracle.rotate(q[b, sel], p.rope_dims, p.rope_theta,
+                                     np.repeat(pos[b, sel][:, None], Hq, 1)))
         kr = bf16(oracle.rotate(k[b], p.rope_dims, p.rope_theta,
                                 np.repeat(pos[b][:, None], Hkv, 1)))
         vb = v[b]
@@ -174,7 +222,7 @@ def prefill(p: "oracle.OracleParams", q, k, v, positions, sinks=None, rows=None,
                 g = h // G
                 s = -np.inf if sinks is None else float(sinks[h])
                 out[b, rs, h] = _head(qr[i0:i0 + block, h], kr[lo:hi, g], vb[lo:hi, g], vis, s,
-                                      tau, p.v_scale)
+                                      np.log(2.0), p.v_scale)
     return out
 
 

@@ -16,7 +16,7 @@ import torch
 import global_attention_rope_amd as mimo
 import oracle
 from tests import rounding_model, synth
-from tests.gpu_helpers import assert_close, ring_positions, to_np64
+from tests.gpu_helpers import assert_close, prefill_bound_for, ring_positions, to_np64
 from tests.test_gpu_parity import _f32, _note, _oparams, _params, _wl
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +131,9 @@ def test_extend_skips_sequences_past_max_start(kind, S):
     okc, ovc, kpos, count = _oracle_cache(w, kc0[:1], vc0[:1], starts[:1])
     ref = oracle.extend(_oparams(w, batch=1), _f32(q[:1]), _f32(k[:1]), _f32(v[:1]),
                         np.array(starts[:1], np.int32), okc, ovc, kpos, count, _f32(s))
-    assert_close(out[:1], ref, what="accepted sequence")
+    bound = rounding_model.extend_bound(_oparams(w, batch=1), _f32(q[:1]), _f32(k[:1]),
+                                        _f32(v[:1]), starts[:1], okc, ovc, kpos, count, _f32(s))
+    assert_close(out[:1], ref, what="accepted sequence", bound=bound)
 
 
 def _chunked(w, q, k, v, s, chunks, cap):
@@ -162,7 +164,7 @@ def test_chunked_prefill_sliding_full_size():
     out, kc, vc = _chunked(w, q, k, v, s, chunks, w.window)
     pos = np.arange(w.seq, dtype=np.int32)[None]
     ref, krot = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s), want_k_rot=True)
-    assert_close(out, ref, what=f"{w.name} chunked")
+    assert_close(out, ref, what=f"{w.name} chunked", bound=prefill_bound_for(w, q, k, v, s, pos))
     # the ring holds the prompt's last window tokens, as a single prefill leaves it
     last = np.arange(w.seq - w.window, w.seq)
     assert np.array_equal(to_np64(vc)[0][:, last % w.window], to_np64(v)[0, last].transpose(1, 0, 2))
@@ -181,7 +183,8 @@ def test_chunked_prefill_global_full_size_sampled_rows():
                                      rng.integers(0, w.seq, 96)])).astype(np.int32)
     pos = np.arange(w.seq, dtype=np.int32)[None]
     ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s), rows=rows)
-    assert_close(out[:, rows], ref[:, rows], what=f"{w.name} chunked")
+    bound = prefill_bound_for(w, q, k, v, s, pos, rows=rows)
+    assert_close(out[:, rows], ref[:, rows], what=f"{w.name} chunked", bound=bound[:, rows])
 
 
 def test_extend_global_long_cache_sampled_rows():

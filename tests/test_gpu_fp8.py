@@ -14,7 +14,8 @@ import torch
 import global_attention_rope_amd as mimo
 import oracle
 from tests import synth
-from tests.gpu_helpers import assert_close, ring_positions
+from tests import rounding_model
+from tests.gpu_helpers import assert_close, prefill_bound_for, ring_positions
 from tests.test_gpu_parity import _f32, _note, _oparams, _params, _wl
 
 pytestmark = pytest.mark.gpu
@@ -224,7 +225,8 @@ def run_prefill_fp8_chain(kind, seed, r=64, theta=None, q_scale=1.0):
     torch.cuda.synchronize()
     pos = np.stack([np.arange(S, dtype=np.int32) + st for st in starts])
     ref, krot = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s), want_k_rot=True)
-    assert_close(out, ref, what="prefill output with an fp8 cache")
+    assert_close(out, ref, what="prefill output with an fp8 cache",
+                 bound=prefill_bound_for(w, q, k, v, s, pos))
     kc1, vc1 = _np8(kc8), _np8(vc8)
     vin = _f32(v)
     stored = {}
@@ -299,7 +301,9 @@ def test_extend_fp8_caches(ci):
     torch.cuda.synchronize()
     ref, krot = oracle.extend(_oparams(w), _f32(q), _f32(k), _f32(v), np.array(starts, np.int32),
                               okc, ovc, kpos, count, _f32(s), want_k_rot=True)
-    assert_close(out, ref, what=f"fp8 extend {case}")
+    bound = rounding_model.extend_bound(_oparams(w), _f32(q), _f32(k), _f32(v), starts, okc, ovc,
+                                        kpos, count, _f32(s))
+    assert_close(out, ref, what=f"fp8 extend {case}", bound=bound)
     # caches: the new tokens' codes in their slots, every other slot as it was
     kc1, vc1 = _np8(kc8), _np8(vc8)
     vin = _f32(v)

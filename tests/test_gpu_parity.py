@@ -13,7 +13,8 @@ import oracle
 from oracle import OracleParams
 from tests import synth
 from tests import rounding_model
-from tests.gpu_helpers import assert_close, assert_near_model, ring_positions, to_np64
+from tests.gpu_helpers import (assert_close, assert_near_model, prefill_bound_for, ring_positions,
+                               to_np64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -112,7 +113,7 @@ def test_prefill_swa_full_size_all_rows():
     w = synth.SWA_PREFILL
     _note(w.name)
     q, k, v, s, out, ref, _, _, pos = _run_prefill(w, seed=1000, starts=[0])
-    assert_close(out, ref, what=w.name)
+    assert_close(out, ref, what=w.name, bound=prefill_bound_for(w, q, k, v, s, pos))
     model = rounding_model.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s))
     assert_near_model(out, ref, model, what=w.name)
 
@@ -124,7 +125,8 @@ def test_prefill_global_full_size_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(64), np.arange(w.seq - 64, w.seq),
                                      rng.integers(0, w.seq, 128)])).astype(np.int32)
     q, k, v, s, out, ref, _, _, pos = _run_prefill(w, seed=2000, starts=[0], rows=rows)
-    assert_close(out[:, rows], ref[:, rows], what=w.name)
+    bound = prefill_bound_for(w, q, k, v, s, pos, rows=rows)
+    assert_close(out[:, rows], ref[:, rows], what=w.name, bound=bound[:, rows])
     model = rounding_model.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s), rows=rows)
     assert_near_model(to_np64(out)[:, rows], ref[:, rows], model[:, rows], what=w.name)
 
@@ -136,7 +138,7 @@ def test_prefill_writes_caches(kind):
     _note(f"cache kind={kind}")
     q, k, v, s, out, (ref, krot), kc, vc, pos = _run_prefill(w, seed=3000 + kind, starts=starts,
                                                              with_cache=True)
-    assert_close(out, ref, what="out")
+    assert_close(out, ref, what="out", bound=prefill_bound_for(w, q, k, v, s, pos))
     kc_h, vc_h = to_np64(kc), to_np64(vc)
     v_h = to_np64(v)
     cap = kc.shape[2]
@@ -456,7 +458,10 @@ def test_stack_layer_full_size_prefill_then_decode_sampled(layer):
     rows_all = np.concatenate([rows, np.arange(S, S + T, dtype=np.int32)])
     posn = np.stack([np.arange(S + T, dtype=np.int32)] * B)
     ref = oracle.prefill(op, _f32(q), _f32(k), _f32(v), posn, _f32(s_ref), rows=rows_all)
-    assert_close(out[:, rows], ref[:, rows], what=f"stack layer {layer} prefill rows")
+    bound = rounding_model.prefill_bound(op, _f32(q), _f32(k), _f32(v), posn, _f32(s_ref),
+                                         rows=rows)
+    assert_close(out[:, rows], ref[:, rows], what=f"stack layer {layer} prefill rows",
+                 bound=bound[:, rows])
     model = rounding_model.prefill(op, _f32(q), _f32(k), _f32(v), posn, _f32(s_ref), rows=rows_all)
     assert_near_model(to_np64(out)[:, rows], ref[:, rows], model[:, rows],
                       what=f"stack layer {layer} prefill rows")

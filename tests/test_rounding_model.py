@@ -37,9 +37,15 @@ def test_single_key_is_one_rounding_of_the_oracle():
     assert np.array_equal(model, rm.bf16(ref))
 
 
+@pytest.fixture
+def every_row(monkeypatch):
+    """The bound on every row (by default rows seeing more than BOUND_MAX_KEYS keys get 0)."""
+    monkeypatch.setattr(rm, "BOUND_MAX_KEYS", 1 << 30)
+
+
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("r", [0, 64, 192])
-def test_model_error_inside_derived_bound(kind, r):
+def test_model_error_inside_derived_bound(kind, r, every_row):
     op, q, k, v, pos, s = _case(kind, r)
     ref = oracle.prefill(op, q, k, v, pos, s)
     model = rm.prefill(op, q, k, v, pos, s)
@@ -50,7 +56,14 @@ def test_model_error_inside_derived_bound(kind, r):
     assert rm.rel_l2(model, ref) > 5e-4
 
 
-def test_bound_grows_with_rotated_dims_and_is_mostly_tighter_than_fixed():
+def test_default_bound_covers_only_rows_with_few_keys():
+    op, q, k, v, pos, s = _case(0, 64, S=200)
+    bound = rm.prefill_bound(op, q, k, v, pos, s)
+    assert np.all(bound[:, :rm.BOUND_MAX_KEYS] > 0)
+    assert np.all(bound[:, rm.BOUND_MAX_KEYS:] == 0)
+
+
+def test_bound_grows_with_rotated_dims_and_is_mostly_tighter_than_fixed(every_row):
     meds = []
     for r in (0, 64, 192):
         op, q, k, v, pos, s = _case(0, r)
@@ -61,7 +74,7 @@ def test_bound_grows_with_rotated_dims_and_is_mostly_tighter_than_fixed():
     assert meds[0] < meds[1] < meds[2]
 
 
-def test_extend_bound_matches_prefill_bound_on_an_empty_cache():
+def test_extend_bound_matches_prefill_bound_on_an_empty_cache(every_row):
     op, q, k, v, pos, s = _case(1, 64, B=1)
     bp = rm.prefill_bound(op, q, k, v, pos, s)
     be = rm.extend_bound(op, q, k, v, pos[:, 0], None, None, None, None, s)
