@@ -156,8 +156,16 @@ def cpu_baseline(stack_cfg, seed_base):
     dt = time.perf_counter() - t0
     flops = (prefill_counts(1, S_ga, 64, 4, 0, 0)[0] + prefill_counts(1, S_swa, 64, 8, 1, 128)[0]
              + decode_counts(1, 64, 4, 0, 128, [S_ga])[0])
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu, "kind": "oracle",
             "sample": (f"fp64 oracle, sequence 0 only: layer 0 (global) prefill of the first {S_ga} "
                        f"tokens, layer 1 (sliding) prefill of the first {S_swa} tokens, one global "
                        f"decode step at position {S_ga}; {flops:.3e} algorithmic flop in "

@@ -20,7 +20,7 @@ PROBE_LIB = os.path.join(PKG, "libmimo_probe.so")   # latency references (measur
 PROBE_SOURCES = ["probe.hip"]
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["abi.hip", "prefill_bf16.hip", "decode_bf16.hip", "rope_kv.hip", "attn_f32.hip",
-           "layer.hip", "router.hip", "verify_bf16.hip"]
+           "layer.hip", "router.hip", "verify_bf16.hip", "gemm_bf16.hip"]
 ARCH = "gfx950"
 NOISE = "is not a recognized feature for this target"
 
@@ -44,7 +44,7 @@ def compile_flags() -> list[str]:
 def command(out: str) -> list[str]:
     """One-shot command that compiles and links every source (kept for reference builds)."""
     return [hipcc(), *compile_flags(), "-shared",
-            *[os.path.join(CSRC, s) for s in SOURCES], "-lhipblaslt", "-o", out]
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 
 
 def _run(cmd: list[str]) -> tuple[int, str]:
@@ -72,8 +72,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             if verbose and err.strip():
                 print(err, file=sys.stderr)
         tmp = LIB + f".tmp{tag}"
-        rc, err = _run([hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs,
-                        "-lhipblaslt", "-o", tmp])
+        rc, err = _run([hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", tmp])
         if rc != 0:
             raise RuntimeError(f"link failed ({rc}):\n{err}")
         os.replace(tmp, LIB)

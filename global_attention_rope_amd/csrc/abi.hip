@@ -41,6 +41,12 @@ int set_error(int code, const char* msg) {
     return code;
 }
 void clear_error() { g_err[0] = '\0'; }
+
+void rope_omega_rev(double theta, int rope_dims, double* out, int n) {
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int d = 0; d < n; ++d)
+        out[d] = d < rope_dims / 2 ? pow(theta, -2.0 * (double)d / (double)rope_dims) / two_pi : 0.0;
+}
 }  // namespace mimo
 
 namespace {
@@ -50,10 +56,7 @@ constexpr int kBf16Dqk = 192, kBf16Dv = 128, kF32MaxDim = 256, kMaxDecodeGroup =
 // Frequencies of the rotated slice, omega_d = theta^(-2d/r) for d < r/2, in revolutions per
 // position (omega_d / 2pi) as the kernels take them.
 void fill_omega(const mimo_attn_params* p, double* omega_rev) {
-    const double two_pi = 6.283185307179586476925286766559;
-    for (int d = 0; d < mimo::kMaxRopeHalfArgs; ++d) omega_rev[d] = 0.0;
-    for (int d = 0; d < p->rope_dims / 2; ++d)
-        omega_rev[d] = pow(p->rope_theta, -2.0 * (double)d / (double)p->rope_dims) / two_pi;
+    mimo::rope_omega_rev(p->rope_theta, p->rope_dims, omega_rev, mimo::kMaxRopeHalfArgs);
 }
 
 bool fp8_cache(const mimo_attn_params* p) { return p->cache_dtype == MIMO_CACHE_FP8_E4M3; }

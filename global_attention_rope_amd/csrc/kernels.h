@@ -130,6 +130,45 @@ struct F32DecodeArgs {
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
+// bf16 dense products C_p = alpha * A[M, K] B_p[K, N_p] (row-major, fp32 accumulation,
+// K % 64 == 0, N_p % 8 == 0) for up to three parts p sharing A, in one launch, each with one of
+// three epilogues:
+//   kGemmPlain: C_p [M, ldc] row-major;
+//   kGemmKey:   rows are tokens (row m = b * S + s, position start_pos[b] + s), columns
+//               heads * dqk; the leading rope_dims (0 or 64) dims of each head are rotated
+//               (pairs (d, d + 32), frequencies omega_rev[d] in revolutions) and the result is
+//               stored in the attention's [B, heads, S, dqk] layout at C_p, and into the part's
+//               cache ([B, heads, cap, dqk]) when set, for tokens s >= cache_i0, at slot
+//               position % ring_window (ring_window > 0) or position (slot < cap);
+//   kGemmValue: C_p [M, ldc] row-major, columns heads * dv, plus the cache store as for keys.
+// cache_fp8: caches hold e4m3 codes of value * code_inv (keys: the fp32 rotated value; values:
+// their bf16 rounding), saturated at +-448.
+enum { kGemmPlain = 0, kGemmKey = 1, kGemmValue = 2 };
+struct GemmPart {
+    const uint16_t* B;
+    uint16_t* C;
+    void* cache;
+    int64_t ldb, ldc;
+    int32_t N, epilogue;
+    int32_t tiles;       // set by the launch
+    float code_inv;
+};
+struct GemmArgs {
+    const uint16_t* A;
+    int64_t lda;
+    int32_t M, K;
+    float alpha;
+    int32_t nparts;
+    GemmPart part[3];
+    // key / value epilogues
+    int32_t S, heads, dqk, dv;
+    const int32_t* start_pos;
+    int32_t cap, ring_window, cache_i0, cache_fp8;
+    int32_t rope_dims;
+    double omega_rev[32];   // theta^(-2d/r) / (2 pi), d < 32 (rope_dims == 64)
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st);
 hipError_t launch_cache_rows_bf16(const CacheRowsArgs& a, hipStream_t st);
 hipError_t launch_rope_kv_f32(const RopeKVArgs& a, hipStream_t st);
@@ -143,6 +182,10 @@ int prefill_bf16_block_rows(bool window);
 
 // Largest number of decode splits per sequence the combine kernel merges.
 int decode_max_splits();
+
+// Frequencies of the rotated slice in revolutions per position, theta^(-2d/r) / (2 pi) for
+// d < r/2 and 0 up to n.
+void rope_omega_rev(double theta, int rope_dims, double* out, int n);
 
 // The library's thread-local error message (mimo_attn_last_error): set it and return code.
 int set_error(int code, const char* msg);

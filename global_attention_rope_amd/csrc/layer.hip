@@ -4,13 +4,16 @@
 // Pages: "Add Xiaomi MiMo-V2", section "Additional useful info" (the value head dim is separate
 // from the QK head dim, so the output projection maps Hq * v_head_dim back to the hidden size; the
 // values are rescaled by sqrt(hidden / (heads * v_head_dim))).  By linearity the rescale of the
-// attention output equals the same scale of the output projection, so it rides on the last GEMM's
-// alpha.  The projections are plain dense products and run on hipBLASLt (bf16 operands, fp32
-// accumulation); the attention between them is this library's own kernels.
+// attention output equals the same scale of the output projection, so it rides on the last
+// product's alpha.  Every product runs on this library's bf16 MFMA kernel (csrc/gemm_bf16.hip).
+//
+// With the model's rotated width (64 of 192 dims) or none, the key projection's epilogue rotates
+// the keys in fp32 and writes them straight into the attention's rotated-key layout and into the
+// KV cache, and the value projection's epilogue stores the cache's values: no separate rotation
+// pass and no second trip of the keys through memory.  Other rotated widths take the plain
+// projection and the prefill's own key-rotation pass.
 #include <hip/hip_runtime.h>
-#include <hipblaslt/hipblaslt.h>
 #include <math.h>
-#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -19,12 +22,6 @@
 #include "kernels.h"
 
 namespace {
-
-constexpr int kMaxDevices = 64;
-constexpr size_t kGemmWorkspace = (size_t)32 << 20;   // hipBLASLt scratch inside the workspace
-
-std::mutex g_lt_mu;
-hipblasLtHandle_t g_lt[kMaxDevices];
 
 int layer_fail(int code, const char* fmt, ...) {
     char msg[512];
@@ -35,60 +32,14 @@ int layer_fail(int code, const char* fmt, ...) {
     return mimo::set_error(code, msg);
 }
 
-// One hipBLASLt handle per device, created on first use and kept until the process ends.
-hipblasLtHandle_t lt_handle() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    std::lock_guard<std::mutex> lock(g_lt_mu);
-    if (!g_lt[dev] && hipblasLtCreate(&g_lt[dev]) != HIPBLAS_STATUS_SUCCESS) g_lt[dev] = nullptr;
-    return g_lt[dev];
-}
-
-// Row-major Y[M, N] = alpha * X[M, K] * W[K, N], bf16 operands and result, fp32 accumulation.
-// (In hipBLASLt's column-major terms: Y^T = W^T * X^T, W^T being W's row-major storage.)
-hipblasStatus_t gemm_rm(hipblasLtHandle_t h, int64_t M, int64_t N, int64_t K, const void* X,
-                        const void* W, void* Y, float alpha, void* ws, size_t ws_bytes,
-                        hipStream_t st) {
-    hipblasLtMatmulDesc_t desc = nullptr;
-    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-    hipblasLtMatmulPreference_t pref = nullptr;
-    hipblasStatus_t rc = hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
-    const hipblasOperation_t op = HIPBLAS_OP_N;
-    const uint64_t wsb = ws_bytes;
-    if (rc == HIPBLAS_STATUS_SUCCESS)
-        rc = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op, sizeof op);
-    if (rc == HIPBLAS_STATUS_SUCCESS)
-        rc = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op, sizeof op);
-    if (rc == HIPBLAS_STATUS_SUCCESS) rc = hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, N, K, N);
-    if (rc == HIPBLAS_STATUS_SUCCESS) rc = hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, K, M, K);
-    if (rc == HIPBLAS_STATUS_SUCCESS) rc = hipblasLtMatrixLayoutCreate(&lc, HIP_R_16BF, N, M, N);
-    if (rc == HIPBLAS_STATUS_SUCCESS) rc = hipblasLtMatmulPreferenceCreate(&pref);
-    if (rc == HIPBLAS_STATUS_SUCCESS)
-        rc = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
-                                                   &wsb, sizeof wsb);
-    hipblasLtMatmulHeuristicResult_t res;
-    int found = 0;
-    if (rc == HIPBLAS_STATUS_SUCCESS)
-        rc = hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, &res, &found);
-    if (rc == HIPBLAS_STATUS_SUCCESS && found < 1) rc = HIPBLAS_STATUS_NOT_SUPPORTED;
-    const float beta = 0.0f;
-    if (rc == HIPBLAS_STATUS_SUCCESS)
-        rc = hipblasLtMatmul(h, desc, &alpha, W, la, X, lb, &beta, Y, lc, Y, lc, &res.algo, ws,
-                             ws_bytes, st);
-    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-    if (lc) hipblasLtMatrixLayoutDestroy(lc);
-    if (lb) hipblasLtMatrixLayoutDestroy(lb);
-    if (la) hipblasLtMatrixLayoutDestroy(la);
-    if (desc) hipblasLtMatmulDescDestroy(desc);
-    return rc;
-}
-
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct LayerBuffers {
-    size_t q, k, v, attn, gemm, attn_ws, total;   // byte offsets (total: bytes)
+    size_t q, k, v, attn, attn_ws, total;   // byte offsets (total: bytes)
 };
 
+// q [T, Hq*dqk], k [T, Hkv*dqk] (projected, before rotation), v [T, Hkv*dv], attention output
+// [T, Hq*dv], then the prefill workspace (the rotated keys, [B, Hkv, S, dqk]).
 LayerBuffers layer_buffers(const mimo_attn_params* p, int32_t S) {
     const size_t T = (size_t)p->batch * S;
     LayerBuffers L;
@@ -96,10 +47,37 @@ LayerBuffers layer_buffers(const mimo_attn_params* p, int32_t S) {
     L.k = L.q + align256(T * p->num_q_heads * p->qk_head_dim * 2);
     L.v = L.k + align256(T * p->num_kv_heads * p->qk_head_dim * 2);
     L.attn = L.v + align256(T * p->num_kv_heads * p->v_head_dim * 2);
-    L.gemm = L.attn + align256(T * p->num_q_heads * p->v_head_dim * 2);
-    L.attn_ws = L.gemm + kGemmWorkspace;
+    L.attn_ws = L.attn + align256(T * p->num_q_heads * p->v_head_dim * 2);
     L.total = L.attn_ws + align256(mimo_attn_prefill_workspace_size(p, S));
     return L;
+}
+
+// Products sharing X[M, K] (row-major): part p is Y_p[M, N_p] = alpha * X W_p[K, N_p] with the
+// plain epilogue until set otherwise.
+mimo::GemmArgs gemm_args(int64_t M, int64_t K, const void* X, float alpha) {
+    mimo::GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.A = (const uint16_t*)X;
+    g.lda = K;
+    g.M = (int32_t)M;
+    g.K = (int32_t)K;
+    g.alpha = alpha;
+    return g;
+}
+
+void add_part(mimo::GemmArgs& g, const void* W, void* Y, int64_t N, int epilogue) {
+    mimo::GemmPart& p = g.part[g.nparts++];
+    p.B = (const uint16_t*)W;
+    p.C = (uint16_t*)Y;
+    p.ldb = p.ldc = N;
+    p.N = (int32_t)N;
+    p.epilogue = epilogue;
+    p.code_inv = 1.0f;
+}
+
+int gemm_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MIMO_OK;
+    return layer_fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 }  // namespace
@@ -132,42 +110,108 @@ int mimo_attn_layer_prefill(const mimo_attn_params* p, int32_t hidden, int32_t s
     }
     if (!x || !w_q || !w_k || !w_v || !w_o || !start_pos || !out)
         return layer_fail(MIMO_ERR_INVALID_ARG, "x, weights, start_pos and out must be non-NULL");
-    const LayerBuffers L = layer_buffers(p, seq_len);
-    if (!workspace || workspace_bytes < L.total)
-        return layer_fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
-                          workspace ? workspace_bytes : (size_t)0);
-    hipblasLtHandle_t h = lt_handle();
-    if (!h) return layer_fail(MIMO_ERR_HIP, "hipBLASLt handle could not be created");
-    hipStream_t st = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)workspace;
-    void *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *attn = ws + L.attn;
-    void* gws = ws + L.gemm;
-    const int64_t T = (int64_t)p->batch * seq_len;
+    // every argument check comes before the first launch, so an error enqueues nothing
+    if ((k_cache == nullptr) != (v_cache == nullptr))
+        return layer_fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both be NULL");
+    const bool swa = p->layer_kind == MIMO_LAYER_SWA;
+    if (k_cache) {
+        if (cache_capacity < 1)
+            return layer_fail(MIMO_ERR_INVALID_ARG, "cache_capacity must be >= 1");
+        if (swa && cache_capacity != p->window)
+            return layer_fail(MIMO_ERR_INVALID_ARG, "ring cache capacity %d must equal window %d",
+                              cache_capacity, p->window);
+    }
     const int64_t nq = (int64_t)p->num_q_heads * p->qk_head_dim;
     const int64_t nk = (int64_t)p->num_kv_heads * p->qk_head_dim;
     const int64_t nv = (int64_t)p->num_kv_heads * p->v_head_dim;
     const int64_t na = (int64_t)p->num_q_heads * p->v_head_dim;
-    const struct {
-        const void* w;
-        void* y;
-        int64_t n;
-    } proj[3] = {{w_q, q, nq}, {w_k, k, nk}, {w_v, v, nv}};
-    for (const auto& pr : proj) {
-        const hipblasStatus_t s = gemm_rm(h, T, pr.n, hidden, x, pr.w, pr.y, 1.0f, gws,
-                                          kGemmWorkspace, st);
-        if (s != HIPBLAS_STATUS_SUCCESS)
-            return layer_fail(MIMO_ERR_HIP, "projection GEMM failed (hipBLASLt status %d)", (int)s);
-    }
-    // attention without the value rescale, which the output projection applies
+    if (hidden % 64 || out_dim % 8)
+        return layer_fail(MIMO_ERR_UNSUPPORTED,
+                          "the projection kernel needs hidden %% 64 == 0 and out_dim %% 8 == 0 "
+                          "(hidden %d, out_dim %d)", hidden, out_dim);
+    const int64_t T = (int64_t)p->batch * seq_len;
+    if (T > 0x7fffffffLL || (int64_t)seq_len * p->num_q_heads * p->batch > ((int64_t)1 << 40))
+        return layer_fail(MIMO_ERR_INVALID_ARG, "problem too large");
+    const LayerBuffers L = layer_buffers(p, seq_len);
+    if (!workspace || workspace_bytes < L.total)
+        return layer_fail(MIMO_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                          workspace ? workspace_bytes : (size_t)0);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    void *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *attn = ws + L.attn;
+    void* kws = ws + L.attn_ws;   // rotated keys [B, Hkv, S, dqk]
+    const bool fp8 = p->cache_dtype == MIMO_CACHE_FP8_E4M3;
+
     mimo_attn_params pa = *p;
-    pa.v_scale = 1.0f;
-    rc = mimo_attn_prefill(&pa, seq_len, q, k, v, start_pos, sinks, attn, k_cache, v_cache,
-                           cache_capacity, ws + L.attn_ws, L.total - L.attn_ws, stream);
-    if (rc != MIMO_OK) return rc;   // (message already set)
-    const hipblasStatus_t s =
-        gemm_rm(h, T, out_dim, na, attn, w_o, out, p->v_scale, gws, kGemmWorkspace, st);
-    if (s != HIPBLAS_STATUS_SUCCESS)
-        return layer_fail(MIMO_ERR_HIP, "output GEMM failed (hipBLASLt status %d)", (int)s);
+    pa.v_scale = 1.0f;   // the output projection applies it
+    mimo::GemmArgs g = gemm_args(T, hidden, x, 1.0f);
+    add_part(g, w_q, q, nq, mimo::kGemmPlain);
+    if (p->rope_dims != 0 && p->rope_dims != 64) {
+        // other rotated widths: plain projections, then the prefill's own key-rotation pass
+        add_part(g, w_k, k, nk, mimo::kGemmPlain);
+        add_part(g, w_v, v, nv, mimo::kGemmPlain);
+        rc = gemm_status(mimo::launch_gemm_bf16(g, st), "q/k/v projections");
+        if (rc != MIMO_OK) return rc;
+        rc = mimo_attn_prefill(&pa, seq_len, q, k, v, start_pos, sinks, attn, k_cache, v_cache,
+                               cache_capacity, kws, L.total - L.attn_ws, stream);
+        if (rc != MIMO_OK) return rc;   // (message already set)
+    } else {
+        // one launch for the three products; the key part's epilogue rotates the keys and writes
+        // them in the attention's layout and the cache, the value part's the cache's values
+        add_part(g, w_k, kws, nk, mimo::kGemmKey);
+        add_part(g, w_v, v, nv, mimo::kGemmValue);
+        g.part[1].cache = k_cache;
+        g.part[2].cache = v_cache;
+        g.part[1].code_inv = fp8 ? 1.0f / p->k_cache_scale : 1.0f;
+        g.part[2].code_inv = fp8 ? 1.0f / p->v_cache_scale : 1.0f;
+        g.S = seq_len;
+        g.heads = p->num_kv_heads;
+        g.dqk = p->qk_head_dim;
+        g.dv = p->v_head_dim;
+        g.start_pos = start_pos;
+        g.cap = cache_capacity;
+        g.ring_window = swa ? p->window : 0;
+        g.cache_i0 = (swa && seq_len > p->window) ? seq_len - p->window : 0;   // ring: last W
+        g.cache_fp8 = fp8;
+        g.rope_dims = p->rope_dims;
+        mimo::rope_omega_rev(p->rope_theta, p->rope_dims, g.omega_rev, 32);
+        rc = gemm_status(mimo::launch_gemm_bf16(g, st), "q/k/v projections");
+        if (rc != MIMO_OK) return rc;
+        // the attention over the rotated keys (the prefill kernel rotates the queries itself)
+        mimo::PrefillArgs a;
+        memset(&a, 0, sizeof a);
+        a.q = (const uint16_t*)q;
+        a.k = (const uint16_t*)kws;
+        a.v = (const uint16_t*)v;
+        a.start_pos = start_pos;
+        a.sinks = sinks;
+        a.out = (uint16_t*)attn;
+        a.k_sb = (int64_t)p->num_kv_heads * seq_len * p->qk_head_dim;
+        a.k_sh = (int64_t)seq_len * p->qk_head_dim;
+        a.k_sj = p->qk_head_dim;
+        a.v_sb = (int64_t)seq_len * nv;
+        a.v_sh = p->v_head_dim;
+        a.v_sj = nv;
+        a.kpos_rel = 1;
+        a.max_start = -1;
+        a.B = p->batch;
+        a.S = seq_len;
+        a.Hq = p->num_q_heads;
+        a.Hkv = p->num_kv_heads;
+        a.rope_dims = p->rope_dims;
+        a.window = p->window;
+        const float tau = p->softmax_scale != 0.0f ? p->softmax_scale
+                                                   : (float)(1.0 / sqrt((double)p->qk_head_dim));
+        a.score_scale_log2 = tau * 1.4426950408889634f;
+        a.v_scale = 1.0f;
+        mimo::rope_omega_rev(p->rope_theta, p->rope_dims, a.omega_rev, mimo::kMaxRopeHalfArgs);
+        rc = gemm_status(mimo::launch_prefill_bf16(a, swa, sinks != nullptr, st), "prefill (bf16)");
+        if (rc != MIMO_OK) return rc;
+    }
+    mimo::GemmArgs go = gemm_args(T, na, attn, p->v_scale);
+    add_part(go, w_o, out, out_dim, mimo::kGemmPlain);
+    rc = gemm_status(mimo::launch_gemm_bf16(go, st), "output projection");
+    if (rc != MIMO_OK) return rc;
     mimo::clear_error();
     return MIMO_OK;
 }

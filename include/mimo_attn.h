@@ -29,11 +29,9 @@
  *   - sinks is fp32 [Hq] or NULL (no sink).  Position arrays are int32 in device memory.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  Nothing is
  *     synchronised, allocated, freed or printed by the library, and it keeps no global state;
- *     calls are thread-safe.  (Exceptions: mimo_attn_layer_prefill keeps one hipBLASLt handle per
- *     device, created on its first call there and kept until the process ends;
- *     mimo_attn_decode_noalloc keeps its partials in a device array of the library and its address
- *     per device.)  Calls that write the same cache or workspace must be ordered by the caller
- *     (same stream or events).
+ *     calls are thread-safe.  (Exception: mimo_attn_decode_noalloc keeps its partials in a device
+ *     array of the library and that array's address per device.)  Calls that write the same cache
+ *     or workspace must be ordered by the caller (same stream or events).
  *   - Arguments are checked on the host before anything is enqueued.  On error the function
  *     returns a negative MIMO_ERR_* code, writes nothing, and mimo_attn_last_error() returns a
  *     message (thread-local).  MIMO_ERR_HIP means a launch failed; the message holds HIP's text.
@@ -227,14 +225,16 @@ size_t mimo_attn_decode_noalloc_max_bytes(void);
  * projection, which is the same by linearity).
  *   x [B,S,hidden]; w_q [hidden, Hq*dqk], w_k [hidden, Hkv*dqk], w_v [hidden, Hkv*dv] (row-major,
  *   heads contiguous in the columns); w_o [Hq*dv, out_dim]; out [B,S,out_dim].  All bf16
- *   (MIMO_BF16 layers only; fp8 caches as for prefill).
- *   q = x w_q, k = x w_k, v = x w_v (bf16 results of fp32-accumulated products), then exactly
+ *   (MIMO_BF16 layers only; fp8 caches as for prefill).  hidden % 64 == 0 and out_dim % 8 == 0,
+ *   else MIMO_ERR_UNSUPPORTED.
+ *   q = x w_q, v = x w_v (bf16 results of fp32-accumulated products); k = x w_k rotated in fp32
+ *   from the products' fp32 results before its one rounding to bf16 (rope_dims 0 or 64; other
+ *   widths round k first and rotate it as mimo_attn_prefill does); then the attention of
  *   mimo_attn_prefill (positions, sinks, caches as there) with v_scale 1, then
- *   out = v_scale * attn w_o.  The products run on hipBLASLt; the attention on this library's
- *   kernels.
- *   workspace: at least mimo_attn_layer_workspace_size() bytes (q, k, v, attention output, 32 MiB
- *   of GEMM scratch and the prefill workspace); its contents are not needed across calls.
- *   Errors as for mimo_attn_prefill; MIMO_ERR_HIP also when a product fails.
+ *   out = v_scale * attn w_o.  Every product runs on this library's own bf16 matrix-core kernel.
+ *   workspace: at least mimo_attn_layer_workspace_size() bytes (q, k, v, attention output and the
+ *   prefill workspace); its contents are not needed across calls.
+ *   Errors as for mimo_attn_prefill; every argument is checked before anything is enqueued.
  */
 int mimo_attn_layer_prefill(const mimo_attn_params* p, int32_t hidden, int32_t seq_len,
                             const void* x, const void* w_q, const void* w_k, const void* w_v,

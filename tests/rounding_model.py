@@ -264,3 +264,48 @@ def decode(p: "oracle.OracleParams", q, k_new, v_new, pos, kc=None, vc=None, kpo
 def rel_l2(x, ref) -> float:
     x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
     return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
+
+
+def layer_prefill(p: "oracle.OracleParams", x, wq, wk, wv, wo, positions, sinks=None, rows=None):
+    """Model output of the layer with its projections (same arguments as oracle.layer_prefill),
+    with the roundings of the library's path: q = bf16(x Wq) and v = bf16(x Wv) (products exact,
+    rounded once); keys rotated from the exact product x Wk and rounded once; then the prefill's
+    own roundings (the rotated query scaled and rounded, softmax weights, output) over those q, k,
+    v with v_scale 1; out = bf16(v_scale * attn Wo).  Rows not listed are NaN."""
+    x = np.asarray(x, np.float64)
+    B, S, H = x.shape
+    wq, wk, wv, wo = (np.asarray(a, np.float64) for a in (wq, wk, wv, wo))
+    pos = np.asarray(positions, np.int32)
+    Hq, Hkv, D, DVv = p.num_q_heads, p.num_kv_heads, p.qk_head_dim, p.v_head_dim
+    G = Hq // Hkv
+    sel = np.arange(S) if rows is None else np.asarray(rows)
+    q = np.zeros((B, S, Hq, D))
+    q[:, sel] = bf16(x[:, sel] @ wq).reshape(B, len(sel), Hq, D)
+    k = (x @ wk).reshape(B, S, Hkv, D)
+    v = bf16(x @ wv).reshape(B, S, Hkv, DVv)
+    tau = p.softmax_scale if p.softmax_scale else 1.0 / np.sqrt(D)
+    sc = float(np.float32(np.float32(tau) * np.float32(1.4426950408889634)))
+    attn = np.full((B, S, Hq, DVv), np.nan)
+    for b in range(B):
+        qr = bf16(sc * oracle.rotate(q[b, sel], p.rope_dims, p.rope_theta,
+                                     np.repeat(pos[b, sel][:, None], Hq, 1)))
+        kr = bf16(oracle.rotate(k[b], p.rope_dims, p.rope_theta, np.repeat(pos[b][:, None], Hkv, 1)))
+        d = pos[b, sel][:, None] - pos[b][None, :]
+        vis = d >= 0
+        if p.layer_kind == 1:
+            vis &= d < p.window
+        for h in range(Hq):
+            s = -np.inf if sinks is None else float(sinks[h])
+            attn[b, sel, h] = _head(qr[:, h], kr[:, h // G], v[b, :, h // G], vis, s, np.log(2.0), 1.0)
+    out = np.full((B, S, wo.shape[1]), np.nan)
+    out[:, sel] = bf16(p.v_scale * (attn[:, sel].reshape(B, len(sel), -1) @ wo))
+    return out
+
+
+def layer_row_tolerance(model, ref, sigmas=6.0):
+    """Per-element tolerance of the layer output derived from the model: sigmas times the RMS of
+    the model's own error over the element's row (rows that see few keys keep larger errors, and
+    each row has out_dim elements to estimate it from), plus two roundings of the output."""
+    e = np.asarray(model, np.float64) - np.asarray(ref, np.float64)
+    rms_row = np.sqrt(np.nanmean(e * e, axis=-1, keepdims=True))
+    return sigmas * rms_row + 2 * U * np.abs(ref)
