@@ -244,12 +244,14 @@ SplitGeometry verify_geometry(const mimo_attn_params* p, int32_t S, int32_t max_
 
 // Rows per (sequence, KV head) of the bf16 key/value rows an extend lays out in its workspace:
 // sliding layers window + S (the ring's content in position order, then the new tokens); global
-// layers with an fp8 cache max_start + S (row = position: the cached rows widened to bf16, then
-// the new tokens); global layers with a bf16 cache none (they attend straight from the cache).
+// layers with an fp8 cache: a few new tokens S (the multi-token kernel reads the cached codes in
+// place), more max_start + S (row = position: the cached rows widened to bf16, then the new
+// tokens); global layers with a bf16 cache none (they attend straight from the cache).
 int64_t extend_rows(const mimo_attn_params* p, int32_t S, int32_t max_start) {
     if (p->dtype != MIMO_BF16) return 0;
     if (p->layer_kind == MIMO_LAYER_SWA) return (int64_t)p->window + S;
-    return fp8_cache(p) ? (int64_t)max_start + S : 0;
+    if (!fp8_cache(p)) return 0;
+    return verify_tokens(p, S) ? (int64_t)S : (int64_t)max_start + S;
 }
 
 // bf16 extend workspace: those rows (K then V, 256-byte aligned), then the split partials of a
@@ -534,6 +536,21 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
         pa.v_sh = rows * dv;
         pa.kpos_rel = 1;
         pa.kpos_off = -p->window;   // key row j sits at position start - W + j
+    } else if (fp8 && few) {
+        // workspace row t = new token t, rotated (the tokens also go to the cache, as codes); the
+        // multi-token kernel reads the cached positions' codes in place
+        ra.k_ws = kws;
+        ra.v_ws = vws;
+        ra.ws_rows = (int32_t)rows;
+        ra.ws_row0 = 0;
+        pa.k = kws;
+        pa.v = vws;
+        pa.k_sb = Hkv * rows * dqk;
+        pa.k_sh = rows * dqk;
+        pa.v_sb = Hkv * rows * dv;
+        pa.v_sh = rows * dv;
+        pa.kpos_rel = 0;
+        pa.kpos_off = 0;
     } else if (fp8) {
         // workspace row j = position j: the cached rows before each start widened to bf16, then
         // the new tokens, rotated (which also go to the cache, as codes)
@@ -591,6 +608,14 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
         va.ring_v = (const uint16_t*)v_cache;
         va.ring_w = p->window;
     }
+    if (!swa && fp8) {
+        // cached positions read as codes, in place: the scales ride on the score and output scales
+        va.code_k = (const uint8_t*)k_cache;
+        va.code_v = (const uint8_t*)v_cache;
+        va.code_cap = cache_capacity;
+        va.code_k_scale = p->k_cache_scale;
+        va.code_v_scale = p->v_cache_scale;
+    }
     va.k_sb = pa.k_sb;
     va.k_sh = pa.k_sh;
     va.v_sb = pa.v_sb;
@@ -609,6 +634,10 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     va.nsplit = geo.nsplit;
     va.score_scale_log2 = pa.score_scale_log2;
     va.v_scale = p->v_scale;
+    if (va.code_k) {   // (the cache scales of codes read in place)
+        va.score_scale_log2 *= p->k_cache_scale;
+        va.v_scale *= p->v_cache_scale;
+    }
     fill_omega(p, va.omega_rev);
     rc = hip_status(mimo::launch_verify_tiles_bf16(va, swa, sinks != nullptr, st), "extend (bf16)");
     if (rc != MIMO_OK) return rc;
@@ -635,7 +664,7 @@ int mimo_attn_extend(const mimo_attn_params* p, int32_t seq_len, const void* q, 
     da.q_per_seq = seq_len;
     da.kpos_rel = pa.kpos_rel;
     da.kpos_off = pa.kpos_off;
-    da.v_scale = p->v_scale;
+    da.v_scale = va.v_scale;
     return hip_status(mimo::launch_verify_combine(da, swa, sinks != nullptr, st), "extend combine");
 }
 

@@ -29,6 +29,13 @@ struct VerifyArgs {
     const uint16_t* ring_v;
     int32_t ring_w;
     int64_t k_sb, k_sh, v_sb, v_sh;
+    // fp8 caches read in place (global layers, key rows = positions): rows j < start_pos[b] are
+    // e4m3 codes at slot j of code_k [B,Hkv,code_cap,192] / code_v [B,Hkv,code_cap,128], taken
+    // as bf16(e4m3(code) * scale); rows start_pos[b] + t are the new tokens, row t of k / v
+    const uint8_t* code_k;
+    const uint8_t* code_v;
+    int32_t code_cap;
+    float code_k_scale, code_v_scale;
     int32_t B, T, TP, Hq, Hkv, rope_dims, window, kpos_rel, kpos_off, max_start, chunk, nsplit;
     float score_scale_log2;
     float v_scale;

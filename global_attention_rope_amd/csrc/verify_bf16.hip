@@ -11,6 +11,12 @@
 // Tiles: 64 keys, staged through a 2-stage LDS ring by global_load_lds_dwordx4, XOR-swizzled as
 // in the prefill kernel; per-column online softmax in the log2 domain with a lazily raised
 // running maximum.
+// fp8 caches (global layers): the cached rows' e4m3 codes go memory -> registers (half the bytes
+// of a bf16 tile, two tiles ahead), and each tile is widened into the bf16 LDS tile before its
+// products as the codes' exact values; the two cache scales ride on the score scale and the output
+// scale, and the new tokens' rows (at most 16, full precision, staged once per workgroup and copied
+// into the tiles that hold them) have their scores and softmax weights divided by them instead.
+// No pass over the whole cache.
 #include <type_traits>
 
 #include "device_common.h"
@@ -28,12 +34,17 @@ constexpr int KCH = DQK / 16;
 constexpr int STAGES = 2;
 constexpr int PSTRIDE = DV + 2;              // floats per partial record: O[128], m, l
 constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyond 2^8
+// fp8: one bf16 tile and the new rows
+constexpr int NEW_ROWS = 16;
+constexpr int NEW_BYTES = NEW_ROWS * (DQK + DV) * 2;
 
-template <int NW, bool WINDOW, bool SINK, bool SPLIT>
+template <int NW, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
 __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs a) {
     constexpr int K_DMA = K_TILE / 1024 / NW;      // 1-KiB DMA instructions per wave per tile
     constexpr int V_DMA = V_TILE / 1024 / NW;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * (K_TILE + V_TILE)];
+    constexpr int NST = FP8 ? 1 : STAGES;          // bf16 tile stages
+    constexpr int SMEM = FP8 ? K_TILE + V_TILE + NEW_BYTES : STAGES * (K_TILE + V_TILE);
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -133,7 +144,75 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
             dma16(src + v_off[i], vst + (wave * V_DMA + i) * 1024);
         }
     };
-    if (n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
+    if (!FP8 && n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
+
+    // fp8: the new tokens' rows (bf16, [T, 192] and [T, 128] of this sequence and KV head) into
+    // LDS once; rows past T as zeros
+    uint8_t* const newk = smem + K_TILE + V_TILE;
+    uint8_t* const newv = newk + NEW_ROWS * DQK * 2;
+    if constexpr (FP8) {
+        constexpr int UNITS = NEW_ROWS * (DQK + DV) / 8;
+        for (int u = tid; u < UNITS; u += NW * 64) {
+            const bool key = u < NEW_ROWS * DQK / 8;
+            const int uu = key ? u : u - NEW_ROWS * DQK / 8, cpr = key ? DQK / 8 : DV / 8;
+            const int row = uu / cpr, c8 = uu - row * cpr;
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (row < T)
+                w = key ? *(const u32x4*)(kslice + (int64_t)row * DQK + 8 * c8)
+                        : *(const u32x4*)(vslice + (int64_t)row * DV + 8 * c8);
+            *(u32x4*)((key ? newk + row * DQK * 2 : newv + row * DV * 2) + 16 * c8) = w;
+        }
+    }
+    // fp8: the cached rows' codes of a tile go memory -> registers (units of 16 codes: K rows of
+    // 12 units, then V rows of 8), two tiles ahead of the products; widening writes the bf16 tile:
+    // the codes' exact values for positions before the start, the staged new rows after it, zeros
+    // past the last token.  Code rows at or past the start are loaded clamped in bounds, unused.
+    constexpr int NT = NW * 64;
+    constexpr int KU = BN * (DQK / 16) / NT, VU = BN * (DV / 16) / NT;
+    const int64_t code_row0 = ((int64_t)b * a.Hkv + kvh) * (FP8 ? a.code_cap : 1);
+    auto load_codes = [&](u32x4 (&c)[KU + VU], int tt) {
+        const int j0 = (kt_lo + tt) * BN, jlast = max(st - 1, 0);
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int u = tid + k * NT, row = u / (DQK / 16), c16 = u % (DQK / 16);
+            c[k] = *(const u32x4*)(a.code_k + (code_row0 + min(j0 + row, jlast)) * DQK + 16 * c16);
+        }
+#pragma unroll
+        for (int k = 0; k < VU; ++k) {
+            const int u = tid + k * NT, row = u / (DV / 16), c16 = u % (DV / 16);
+            c[KU + k] = *(const u32x4*)(a.code_v + (code_row0 + min(j0 + row, jlast)) * DV + 16 * c16);
+        }
+    };
+    auto widen = [&](const u32x4 (&c)[KU + VU], int tt) {
+        const int j0 = (kt_lo + tt) * BN;
+#pragma unroll
+        for (int k = 0; k < KU + VU; ++k) {
+            const bool key = k < KU;
+            const int u = tid + (key ? k : k - KU) * NT;
+            const int cpr = key ? DQK / 16 : DV / 16;
+            const int row = u / cpr, c16 = u % cpr;
+            const int j = j0 + row;
+            u32x4 w[2];
+            if (j < st) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    w[hh] = bf16x8_from_e4m3x8(u32x2{c[k][2 * hh], c[k][2 * hh + 1]});
+            } else if (j < st + T) {
+                const uint8_t* nr = key ? newk + (j - st) * DQK * 2 : newv + (j - st) * DV * 2;
+                w[0] = *(const u32x4*)(nr + 32 * c16);
+                w[1] = *(const u32x4*)(nr + 32 * c16 + 16);
+            } else {
+                w[0] = w[1] = u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c8 = 2 * c16 + hh;
+                uint8_t* dst = key ? smem + row * (DQK * 2) + 16 * (c8 ^ ((row >> 1) & 7))
+                                   : smem + K_TILE + row * (DV * 2) + 16 * (c8 ^ ((row & 3) << 2));
+                *(u32x4*)dst = w[hh];
+            }
+        }
+    };
 
     // ---- Q^T operands of this column, rotated at the token's position, in registers
     bf16x8 Qb[KCH];
@@ -171,7 +250,7 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     int v_rd[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        v_rd[db] = STAGES * K_TILE + vrow * (DV * 2) +
+        v_rd[db] = NST * K_TILE + vrow * (DV * 2) +
                    16 * (4 * (db ^ ((jsel >> 2) & 3)) + 2 * (qsel & 1) + ((jsel & 3) >> 1)) +
                    8 * (jsel & 1);
         asm volatile("" : "+v"(v_rd[db]));
@@ -189,16 +268,10 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     const unsigned lim = (unsigned)max(0, min(WINDOW ? W : 0x7fffffff, tc - jmin + 1));
     const int tc_first = shift, tc_last = T - 1 + shift;   // over the valid tokens
 
-    for (int tt = 0; tt < n_tiles; ++tt) {
-        const int ST = tt & 1;
-        wait_vmcnt<0>();
-        block_sync_lds();   // tile tt in LDS for every wave; the other stage is free
-        if (tt + 1 < n_tiles) {
-            if (ST == 0) issue(tt + 1, std::integral_constant<int, 1>{});
-            else issue(tt + 1, std::integral_constant<int, 0>{});
-        }
+    // products of tile tt, in bf16 stage ST of the LDS ring
+    auto tile_products = [&](int tt, int ST) {
         const int j0 = (kt_lo + tt) * BN;
-        if (j0 > tc_last || (WINDOW && j0 + BN - 1 <= tc_first - W)) continue;
+        if (j0 > tc_last || (WINDOW && j0 + BN - 1 <= tc_first - W)) return;
         const bool full = j0 >= jmin && j0 + BN - 1 <= tc_first && (!WINDOW || tc_last - j0 < W);
         const uint8_t* kst = smem + ST * K_TILE;
         const uint8_t* vst = smem + ST * V_TILE;   // + v_rd, which holds the V area's base
@@ -211,6 +284,21 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
             const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
             S0 = mfma32x32x16(A0, Qb[c], S0);
             S1 = mfma32x32x16(A1, Qb[c], S1);
+        }
+        if constexpr (FP8) {
+            // the score scale carries the key cache's scale: the new tokens' rows (positions at
+            // or past the start, full-precision keys) are divided by it
+            if (j0 + BN > st) {
+                asm volatile("");
+                const float ik = 1.0f / a.code_k_scale;
+                const int rr = j0 + 4 * g - st;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i >> 2) + (i & 3);
+                    S0[i] *= rr + off >= 0 ? ik : 1.0f;
+                    S1[i] *= rr + off + 32 >= 0 ? ik : 1.0f;
+                }
+            }
         }
         if (!full) {
             asm volatile("");
@@ -249,6 +337,21 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
             ps1 += S1[i];
         }
         l_run += ps0 + ps1;
+        if constexpr (FP8) {
+            // the output scale carries the value cache's scale: the new tokens' weights are
+            // divided by it (after the sum, which takes them as they are)
+            if (j0 + BN > st) {
+                asm volatile("");
+                const float iv = 1.0f / a.code_v_scale;
+                const int rr = j0 + 4 * g - st;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i >> 2) + (i & 3);
+                    S0[i] *= rr + off >= 0 ? iv : 1.0f;
+                    S1[i] *= rr + off + 32 >= 0 ? iv : 1.0f;
+                }
+            }
+        }
         bf16x8 Pb[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -268,6 +371,41 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
                 O[db] = mfma32x32x16(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), Pb[c],
                                      O[db]);
             }
+        }
+    };
+
+    if constexpr (FP8) {
+        // two tiles of codes in flight (one for a single-wave workgroup, whose registers would
+        // not hold two)
+        constexpr int DEPTH = NW == 1 ? 1 : 2;
+        u32x4 cA[KU + VU], cB[KU + VU];
+        if (n_tiles > 0) load_codes(cA, 0);
+        if (DEPTH > 1 && n_tiles > 1) load_codes(cB, 1);
+        auto step = [&](u32x4 (&c)[KU + VU], int tt) {
+            block_sync_lds();   // the previous tile's products are done with the bf16 tile
+            widen(c, tt);       // (waits for this tile's codes; the next tile's stay in flight)
+            block_sync_lds();
+            if (tt + DEPTH < n_tiles) load_codes(c, tt + DEPTH);
+            tile_products(tt, 0);
+        };
+        if constexpr (DEPTH == 1) {
+            for (int tt = 0; tt < n_tiles; ++tt) step(cA, tt);
+        } else {
+            for (int tt = 0; tt < n_tiles; tt += 2) {
+                step(cA, tt);
+                if (tt + 1 < n_tiles) step(cB, tt + 1);
+            }
+        }
+    } else {
+        for (int tt = 0; tt < n_tiles; ++tt) {
+            const int ST = tt & 1;
+            wait_vmcnt<0>();
+            block_sync_lds();   // tile tt in LDS for every wave; the other stage is free
+            if (tt + 1 < n_tiles) {
+                if (ST == 0) issue(tt + 1, std::integral_constant<int, 1>{});
+                else issue(tt + 1, std::integral_constant<int, 0>{});
+            }
+            tile_products(tt, ST);
         }
     }
 
@@ -305,8 +443,15 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
 template <int NW, bool WINDOW, bool SINK>
 hipError_t launch_nw(const VerifyArgs& a, hipStream_t st) {
     const dim3 grid(a.nsplit, a.Hkv, a.B), block(NW * 64);
-    if (a.nsplit > 1) verify_tiles_kernel<NW, WINDOW, SINK, true><<<grid, block, 0, st>>>(a);
-    else verify_tiles_kernel<NW, WINDOW, SINK, false><<<grid, block, 0, st>>>(a);
+    if constexpr (!WINDOW) {
+        if (a.code_k) {
+            if (a.nsplit > 1) verify_tiles_kernel<NW, false, SINK, true, true><<<grid, block, 0, st>>>(a);
+            else verify_tiles_kernel<NW, false, SINK, false, true><<<grid, block, 0, st>>>(a);
+            return hipGetLastError();
+        }
+    }
+    if (a.nsplit > 1) verify_tiles_kernel<NW, WINDOW, SINK, true, false><<<grid, block, 0, st>>>(a);
+    else verify_tiles_kernel<NW, WINDOW, SINK, false, false><<<grid, block, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -332,6 +477,9 @@ hipError_t launch_verify_tiles_bf16(const VerifyArgs& a, bool window, bool sink,
     const int nw = verify_tile_waves(a.Hq / a.Hkv, a.TP);
     if (nw == 0 || a.TP < a.T || (a.TP & (a.TP - 1)) || a.chunk % BN || a.nsplit < 1 ||
         a.nsplit > decode_max_splits())
+        return hipErrorInvalidConfiguration;
+    // codes read in place: global layers, key row = position, at most NEW_ROWS new tokens
+    if (a.code_k && (window || a.ring_k || a.kpos_rel || a.kpos_off || a.T > NEW_ROWS || !a.code_v))
         return hipErrorInvalidConfiguration;
     if (window) return sink ? launch_ws<true, true>(a, nw, st) : launch_ws<true, false>(a, nw, st);
     return sink ? launch_ws<false, true>(a, nw, st) : launch_ws<false, false>(a, nw, st);
