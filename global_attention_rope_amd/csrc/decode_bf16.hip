@@ -13,6 +13,9 @@
 //   * the split that owns the new token's slot rotates k_new, stores it and v_new into the cache
 //     (linear: slot = position; ring: slot = position % window) and substitutes them for that
 //     slot, so no workgroup reads a slot another one is writing;
+//   * nothing before the slot loop waits for the other waves: each wave evaluates the cos/sin of
+//     the position into its own LDS table, and only the wave whose tiles hold the new token's slot
+//     prepares the new token, in its own LDS area (wave-level ordering only);
 //   * per tile: S^T = K * Q^T, online softmax per head in the log2 domain, V staged in a per-wave
 //     LDS tile and read transposed with ds_read_b64_tr_b16, O^T += V^T * P^T; the next tile's
 //     loads are in flight meanwhile (two waves per SIMD keep ~160 KB per CU in flight);
@@ -78,9 +81,10 @@ __device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int
 }
 
 struct LdsDecode {
-    float2 cs[kMaxRopeHalf + 8];              // cos/sin of the position per frequency, identity
-    uint16_t Kn[DQK];                         // the new token (bf16, or e4m3 codes in the first half)
-    uint16_t Vn[DV];
+    float2 cs[NW][kMaxRopeHalf + 8];          // per wave: cos/sin of the position per frequency,
+                                              // then the identity entries
+    uint16_t Kn[NW][DQK];                     // per wave: the new token (bf16, or e4m3 codes in
+    uint16_t Vn[NW][DV];                      // the first half), in the wave that owns its slot
     float red_m[NW][16], red_l[NW][16];
     float sink[16];
     union {
@@ -188,9 +192,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         qpar[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : (d0 < r ? d0 - half : d0)));
     }
     const int64_t kv_row = (int64_t)b * a.Hkv + g;
-    const int nd0 = tid < DQK / 8 ? tid * 8 : 0;   // k_new dims of this thread (tid < 24)
-    const uint16_t* nsrc = tid >= DQK / 8 && tid < DQK / 8 + DV / 8
-                               ? a.v_new + kv_row * DV + (tid - DQK / 8) * 8
+    const int nd0 = lane < DQK / 8 ? lane * 8 : 0;   // k_new dims of this lane (lane < 24)
+    const uint16_t* nsrc = lane >= DQK / 8 && lane < DQK / 8 + DV / 8
+                               ? a.v_new + kv_row * DV + (lane - DQK / 8) * 8
                                : a.k_new + kv_row * DQK + nd0;
     const u32x4 nraw = *(const u32x4*)nsrc;
     const u32x4 npar = *(const u32x4*)(a.k_new + kv_row * DQK +
@@ -201,8 +205,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     //  cannot trace back to it)
     const char* kargs = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(kargs));
-    const double om = ((const __attribute__((address_space(1))) double*)(
-        kargs + offsetof(DecodeArgs, omega_rev)))[min(tid, kMaxRopeHalf - 1)];
+    const __attribute__((address_space(1))) double* om_args =
+        (const __attribute__((address_space(1))) double*)(kargs + offsetof(DecodeArgs, omega_rev));
+    const double om0 = om_args[lane], om1 = om_args[lane + 64];   // frequencies lane, lane + 64
     const int stride = NW * TILE;
     int t0 = k_begin + wave * TILE;
     // every ring slot is in bounds; a linear cache's splits past the position would only waste
@@ -230,41 +235,48 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     const bool own_new = slot_new >= k_begin && slot_new < k_end;
     if (!SWA) fetch(kA, vA, t0);
 
-    // ---- cos/sin of the position per frequency, once per workgroup
-    if (tid < half) {
+    // ---- cos/sin of the position per frequency, in this wave's table (read by this wave only)
+    float2* const cs = sm.cs[wave];
+    if (lane < half) {
         float c, sn;
-        rope_cos_sin_rev(pos, om, c, sn);
-        sm.cs[tid] = make_float2(c, sn);
+        rope_cos_sin_rev(pos, om0, c, sn);
+        cs[lane] = make_float2(c, sn);
     }
-    if (tid >= 256 - 8) sm.cs[kIdentity + tid - (256 - 8)] = make_float2(1.0f, 0.0f);
-    if (SINK && !SPLIT && tid < 16) sm.sink[tid] = sink_pre * kLog2e;
-    block_sync_lds();
+    if (lane + 64 < half) {
+        float c, sn;
+        rope_cos_sin_rev(pos, om1, c, sn);
+        cs[lane + 64] = make_float2(c, sn);
+    }
+    if (lane < 8) cs[kIdentity + lane] = make_float2(1.0f, 0.0f);
+    if (SINK && !SPLIT && tid < 16) sm.sink[tid] = sink_pre * kLog2e;   // (read after the merge barriers)
+    __builtin_amdgcn_wave_barrier();
 
     // ---- this lane's rotated query chunks: the B operand of v_mfma_f32_16x16x32_bf16
     bf16x8 Qb[DQK / 32];
 #pragma unroll
     for (int c = 0; c < DQK / 32; ++c)
-        Qb[c] = as_bf16x8(c < ROT ? rotate8_cs(qraw[c], qpar[c], qdim(c), half, r, sm.cs)
-                                  : qraw[c]);
-    // ---- the new token: rotate, keep in LDS, append to the cache (the owning split only).
-    //      An fp8 cache stores (and the tile loop reads) its codes.
-    elem_t* const Kn = (elem_t*)sm.Kn;
-    elem_t* const Vn = (elem_t*)sm.Vn;
-    if (own_new) {
-        if (tid < DQK / 8) {
+        Qb[c] = as_bf16x8(c < ROT ? rotate8_cs(qraw[c], qpar[c], qdim(c), half, r, cs) : qraw[c]);
+    // ---- the new token: rotate, keep in LDS, append to the cache, in the wave whose tiles hold
+    //      its slot (wave w computes the tiles at k_begin + 32 w + 128 i).  An fp8 cache stores
+    //      (and the tile loop reads) its codes.
+    const bool own_new_w = own_new && wave == (((slot_new - k_begin) >> 5) & (NW - 1));
+    elem_t* const Kn = (elem_t*)sm.Kn[wave];
+    elem_t* const Vn = (elem_t*)sm.Vn[wave];
+    if (own_new_w) {
+        if (lane < DQK / 8) {
             if constexpr (FP8) {
                 float x[8];
-                rotate8_cs_f32(nraw, npar, nd0, half, r, sm.cs, x);
+                rotate8_cs_f32(nraw, npar, nd0, half, r, cs, x);
                 const u32x2 code = e4m3x8_from_f32(x, a.k_inv);
                 *(u32x2*)(Kn + nd0) = code;
                 *(u32x2*)(kc + (int64_t)slot_new * DQK + nd0) = code;
             } else {
-                const u32x4 wv = rotate8_cs(nraw, npar, nd0, half, r, sm.cs);
+                const u32x4 wv = rotate8_cs(nraw, npar, nd0, half, r, cs);
                 *(u32x4*)(Kn + nd0) = wv;
                 *(u32x4*)(kc + (int64_t)slot_new * DQK + nd0) = wv;
             }
-        } else if (tid < DQK / 8 + DV / 8) {
-            const int d0 = (tid - DQK / 8) * 8;
+        } else if (lane < DQK / 8 + DV / 8) {
+            const int d0 = (lane - DQK / 8) * 8;
             if constexpr (FP8) {
                 float x[8];
                 unpack8(nraw, x);
@@ -276,7 +288,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 *(u32x4*)(vc + (int64_t)slot_new * DV + d0) = nraw;
             }
         }
-        block_sync_lds();
+        __builtin_amdgcn_wave_barrier();
     }
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -289,7 +301,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // consume the tile held in (kr, vr) at slot t, refilling the registers with the next tile as
     // soon as the scores are formed
     auto consume = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
-        if (own_new && slot_new >= t && slot_new < t + TILE) {
+        if (own_new_w && slot_new >= t && slot_new < t + TILE) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (t + kb * 16 + l16 == slot_new) {
