@@ -41,6 +41,17 @@ def compile_flags() -> list[str]:
             "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source code generation options.  The decode kernels are short, latency-bound launches whose
+# code is fetched cold on every call: accumulating the matrix products in ordinary vector
+# registers (not the accumulation registers, which the rescale and merge code would otherwise copy
+# in and out) keeps their code about 12% smaller.
+SOURCE_FLAGS = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def flags_for(source: str) -> list[str]:
+    return compile_flags() + SOURCE_FLAGS.get(source, [])
+
+
 def command(out: str) -> list[str]:
     """One-shot command that compiles and links every source (kept for reference builds)."""
     return [hipcc(), *compile_flags(), "-shared",
@@ -60,7 +71,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     every = SOURCES + PROBE_SOURCES
     objs_all = [os.path.join(OBJ_DIR, s.replace(".hip", f".{tag}.o")) for s in every]
     objs = objs_all[:len(SOURCES)]
-    cmds = [[hipcc(), *compile_flags(), "-c", os.path.join(CSRC, s), "-o", o]
+    cmds = [[hipcc(), *flags_for(s), "-c", os.path.join(CSRC, s), "-o", o]
             for s, o in zip(every, objs_all)]
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     try:

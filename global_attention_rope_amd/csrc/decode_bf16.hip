@@ -48,6 +48,7 @@ constexpr int kDecodeSplitBlock = 1 << kDecodeSplitShift;
 constexpr int VT_PITCH = DV + 16;        // bf16 per V row in the per-wave LDS tile (288 bytes)
 
 constexpr int RO_PITCH = DV + 4;         // floats per head row of the wave-merge buffer
+constexpr float kRescaleLog2 = 8.0f;     // raise a head's reference maximum only beyond 2^8
 
 // Rotate 8 consecutive dims d0.. of a row (w) against their partners (pw) with the cos/sin of the
 // row's position per frequency (cs, in LDS).  Dims at or past r read the identity entries
@@ -98,6 +99,13 @@ struct LdsDecode {
 template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
+    // Every argument the kernel reads is requested here, in one batch of scalar loads waited for
+    // once: the compiler would otherwise fetch them in several dependent rounds as they come up.
+    asm volatile("" ::"s"(a.q), "s"(a.k_new), "s"(a.v_new), "s"(a.positions), "s"(a.k_cache),
+                 "s"(a.v_cache), "s"(a.sinks), "s"(a.out), "s"(a.partial));
+    asm volatile("" ::"s"(a.Hq), "s"(a.Hkv), "s"(a.rope_dims), "s"(a.window), "s"(a.cap),
+                 "s"(a.max_position), "s"(a.chunk), "s"(a.nsplit), "s"(a.k_inv), "s"(a.v_inv),
+                 "s"(a.split_blocked), "s"(a.score_scale_log2), "s"(a.v_scale));
     using elem_t = std::conditional_t<FP8, uint8_t, uint16_t>;
     constexpr int EB = sizeof(elem_t);
     // K: 16-byte loads per lane per tile (two 16-slot blocks x 6 bf16 chunks of 8 dims, or
@@ -364,10 +372,23 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             }
         }
         mx = max_lane_pair32(max_lane_pair16(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
+        // lazily raised reference maximum (per head): set by the head's first visible key, later
+        // moved only when a tile exceeds it by more than 2^kRescaleLog2, so O is rarely rescaled
+        // (the weights stay below 2^kRescaleLog2; numerator and denominator share the reference)
+        const bool first = m_run == -INFINITY;
+        const bool raise = first ? mx != -INFINITY : mx > m_run + kRescaleLog2;
+        if (__any(raise)) {
+            asm volatile("");   // (keep it a branch: rare after a wave's first tile)
+            const float m_new = raise ? mx : m_run;
+            if (__any(raise && !first)) {
+                const float alpha = (raise && !first) ? fast_exp2(m_run - m_new) : 1.0f;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DV / 16; ++db) O[db] *= alpha;
+            }
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
         float psum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -378,9 +399,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 psum += p;
             }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < DV / 16; ++db) O[db] *= alpha;
+        l_run += psum;
         // P^T: k-slot t' of lane group gq is slot 4gq + t' (t' < 4) or 16 + 4gq + (t' - 4).
         const bf16x8 Pb = as_bf16x8(u32x4{pack_bf16x2(Sacc[0][0], Sacc[0][1]),
                                           pack_bf16x2(Sacc[0][2], Sacc[0][3]),
@@ -457,6 +476,10 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
     constexpr int CH = 32;
     __shared__ float w_s[1024], l_s[1024];
     __shared__ float red[4];
+    // (every argument read, requested in one batch of scalar loads)
+    asm volatile("" ::"s"(a.partial), "s"(a.sinks), "s"(a.positions), "s"(a.out), "s"(a.Hq),
+                 "s"(a.nsplit), "s"(a.q_per_seq), "s"(a.max_position), "s"(a.cap), "s"(a.window),
+                 "s"(a.kpos_rel), "s"(a.kpos_off), "s"(a.chunk), "s"(a.v_scale));
     const int h = blockIdx.x, bq = blockIdx.y, d = threadIdx.x, wave = d >> 6;
     const int b = VERIFY ? bq / a.q_per_seq : bq;
     const int nsp = a.nsplit;

@@ -54,6 +54,14 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// The same from a workgroup-uniform base plus a per-lane 32-bit byte offset (the base in scalar
+// registers, so that per-tile address arithmetic stays scalar).
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t offset, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base),
+                 "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferFormat = 0x00020000;
 

@@ -178,33 +178,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     // ---- DMA source mapping: LDS 16-byte slot P of this wave's instruction i holds
     //      K row P / 24, logical chunk (P % 24) ^ swizzle; V row P / 16, chunk (P % 16) ^ swizzle.
+    //      A tile whose rows all lie in [jmin, nk) is read from a scalar base (its first row) plus
+    //      per-lane byte offsets that are the same for every tile; a tile that reaches past those
+    //      rows has them clamped into the range (they are masked anyway, and clamping keeps
+    //      unwritten rows out of the products), its addresses formed on the spot.
     const uint16_t* kslice = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
     const uint16_t* vslice = a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
     const int64_t v_sj = a.v_sj;
-    int k_row[K_DMA], k_off[K_DMA], v_row[V_DMA], v_off[V_DMA];
+    auto k_slot = [&](int i, int ln, int& row, int& col) __attribute__((always_inline)) {
+        const int P = (wave * K_DMA + i) * 64 + ln;
+        row = P / (DQK / 8);
+        col = ((P % (DQK / 8)) ^ ((row >> 1) & 7)) * 8;
+    };
+    auto v_slot = [&](int i, int ln, int& row, int& col) __attribute__((always_inline)) {
+        const int P = (wave * V_DMA + i) * 64 + ln;
+        row = P / (DV / 8);
+        col = ((P % (DV / 8)) ^ ((row & 3) << 2)) * 8;
+    };
+    uint32_t k_lo[K_DMA], v_lo[V_DMA];   // byte offsets within a tile
 #pragma unroll
     for (int i = 0; i < K_DMA; ++i) {
-        const int P = (wave * K_DMA + i) * 64 + lane;
-        const int row = P / (DQK / 8), phys = P % (DQK / 8);
-        k_row[i] = row;
-        k_off[i] = (phys ^ ((row >> 1) & 7)) * 8;
+        int row, col;
+        k_slot(i, lane, row, col);
+        k_lo[i] = (uint32_t)(row * DQK + col) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < V_DMA; ++i) {
-        const int P = (wave * V_DMA + i) * 64 + lane;
-        const int row = P / (DV / 8), phys = P % (DV / 8);
-        v_row[i] = row;
-        v_off[i] = (phys ^ ((row & 3) << 2)) * 8;
+        int row, col;
+        v_slot(i, lane, row, col);
+        v_lo[i] = (uint32_t)((int64_t)row * v_sj + col) * 2u;
     }
-    // per-lane source pointers of tile 0; tile t adds t * BN rows (a scalar offset) except on a
-    // tile that reaches past the key rows [jmin, nk): its rows are clamped into that range (they
-    // are masked anyway, and clamping keeps unwritten rows out of the products)
-    const uint16_t* kp[K_DMA];
-    const uint16_t* vp[V_DMA];
-#pragma unroll
-    for (int i = 0; i < K_DMA; ++i) kp[i] = kslice + (int64_t)(kt_lo * BN + k_row[i]) * DQK + k_off[i];
-#pragma unroll
-    for (int i = 0; i < V_DMA; ++i) vp[i] = vslice + (int64_t)(kt_lo * BN + v_row[i]) * v_sj + v_off[i];
     const uint32_t lds0 = (uint32_t)(size_t)(lds_u8_t*)smem;
     auto issue = [&](int t, auto stage_c) {
         constexpr int ST = decltype(stage_c)::value;
@@ -212,21 +215,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const uint32_t kst = lds0 + ST * K_TILE;
         const uint32_t vst = lds0 + STAGES * K_TILE + ST * V_TILE;
         if (j0 >= jmin && j0 + BN <= nk) {
-            const int64_t dk = (int64_t)t * BN * DQK, dv = (int64_t)t * BN * v_sj;
+            const uint16_t* kb = kslice + (int64_t)j0 * DQK;
+            const uint16_t* vb = vslice + (int64_t)j0 * v_sj;
 #pragma unroll
-            for (int i = 0; i < K_DMA; ++i) dma16(kp[i] + dk, kst + (wave * K_DMA + i) * 1024);
+            for (int i = 0; i < K_DMA; ++i) dma16_sbase(kb, k_lo[i], kst + (wave * K_DMA + i) * 1024);
 #pragma unroll
-            for (int i = 0; i < V_DMA; ++i) dma16(vp[i] + dv, vst + (wave * V_DMA + i) * 1024);
+            for (int i = 0; i < V_DMA; ++i) dma16_sbase(vb, v_lo[i], vst + (wave * V_DMA + i) * 1024);
         } else {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));   // (kept here, not hoisted out of the tile loop)
 #pragma unroll
             for (int i = 0; i < K_DMA; ++i) {
-                const int j = min(max(j0 + k_row[i], jmin), nk - 1);
-                dma16(kslice + (int64_t)j * DQK + k_off[i], kst + (wave * K_DMA + i) * 1024);
+                int row, col;
+                k_slot(i, ln, row, col);
+                const int j = min(max(j0 + row, jmin), nk - 1);
+                dma16(kslice + (int64_t)j * DQK + col, kst + (wave * K_DMA + i) * 1024);
             }
 #pragma unroll
             for (int i = 0; i < V_DMA; ++i) {
-                const int j = min(max(j0 + v_row[i], jmin), nk - 1);
-                dma16(vslice + (int64_t)j * v_sj + v_off[i], vst + (wave * V_DMA + i) * 1024);
+                int row, col;
+                v_slot(i, ln, row, col);
+                const int j = min(max(j0 + row, jmin), nk - 1);
+                dma16(vslice + (int64_t)j * v_sj + col, vst + (wave * V_DMA + i) * 1024);
             }
         }
     };
