@@ -29,7 +29,7 @@ extend (new tokens against a cache: a 2048-token chunk after 30000 cached positi
 sliding, batch 1; and 4 tokens per sequence after the decode workload's cached lengths, batch 64,
 the shape of multi-token verification; the global ones again over fp8 caches), layer (the layer entry point: hidden 4096 -> q/k/v
 projections -> attention -> output projection back to 4096, on the sliding 4096-token and the
-global 8192-token prefill shapes; the projections run on hipBLASLt), router (the MoE router
+global 8192-token prefill shapes; the projections run on this library's bf16 MFMA kernel), router (the MoE router
 kernel: 32768 tokens, 256 experts in 8 groups, 4 groups kept, top 8).
 """
 from __future__ import annotations
@@ -380,9 +380,10 @@ def decode_latency(args, dev):
     calls captured in one HIP graph and replayed: 40 calls that only launch (empty kernel, 16
     workgroups), 40 one-tile dependent reads (16 workgroups, 80 KiB each, a fresh 1.3 MB region per
     call: the bytes of one sliding layer's ring), the 40 sliding-layer decodes and the 8
-    global-layer decodes of one decode step (positions 16384).  'cold': a 512 MiB scratch buffer
-    is written before every replay, outside the timed region, so every ring comes from memory;
-    'hot': replayed back to back."""
+    global-layer decodes of one decode step (positions 16384); then one decode call of each kind
+    at the decode workload's batch of 64.  'cold': a 512 MiB scratch buffer is written before
+    every replay, outside the timed region, so every ring comes from memory (the write-back of
+    that buffer's dirty lines can still overlap the replay); 'hot': replayed back to back."""
     import ctypes
 
     import torch
@@ -434,8 +435,28 @@ def decode_latency(args, dev):
                 mimo.decode(p, q, kn, vn, pos, S, kc, vc, sinks=sk, out=o, workspace=ws)
         return run
 
+    # the decode workload's batch of 64 (cached lengths uniform in [1024, 32768]; full 128-slot
+    # rings), one layer of each kind per replay
+    lengths = synth.decode_lengths(3).tolist()
+    B64 = len(lengths)
+    pos64 = torch.tensor(lengths, dtype=torch.int32, device=dev)
+
+    def mk_b64(heads, seed):
+        w = synth.Workload("dec64", B64, 1, dtype=torch.bfloat16, **heads)
+        cap = w.window if w.layer_kind == 1 else max(lengths) + 1
+        q, kn, vn, sk, kc, vc = synth.decode_inputs(w, seed, B64, cap, device=dev)
+        p = mimo.Params(B64, w.num_q_heads, w.num_kv_heads, DQK, DV, w.rope_dims, w.layer_kind,
+                        w.window, w.rope_theta, w.v_scale)
+        ws = torch.empty(mimo.decode_workspace_size(p, max(lengths)) + 256, dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty((B64, w.num_q_heads, DV), dtype=torch.bfloat16, device=dev)
+        return lambda: mimo.decode(p, q, kn, vn, pos64, max(lengths), kc, vc, sinks=sk, out=o,
+                                   workspace=ws)
+
     cases = [("empty_kernel", probes_empty, NSW), ("tile_read_80KiB", probes_read, NSW),
-             ("sliding_decode", decodes(sw), NSW), ("global_decode", decodes(ga), NGA)]
+             ("sliding_decode", decodes(sw), NSW), ("global_decode", decodes(ga), NGA),
+             ("sliding_decode_b64", mk_b64(synth.SWA_HEADS, 15200), 1),
+             ("global_decode_b64", mk_b64(synth.GA_HEADS, 15300), 1)]
     res = {}
     for name, fn, n in cases:
         fn()

@@ -147,6 +147,9 @@ def test_workspace_sizes():
     assert ws > 0 and ws % (64 * 4 * 64 * 130 * 4) == 0
     rows = 8 * (128 + 4) * (192 + 128) * 2
     assert mimo.extend_workspace_size(_swa(), 4, 30000) == (rows + 255) // 256 * 256
+    # one sequence, 4 KV heads, 4 tokens after 30000 positions: 30004 key rows in 256-row splits,
+    # 118 of them (more than one combine prefetch block of 96 holds)
+    assert mimo.extend_workspace_size(_ga(), 4, 30000) == 1 * 4 * 64 * 118 * 130 * 4
 
 
 _L = None

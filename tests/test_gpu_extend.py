@@ -70,6 +70,8 @@ CASES = [
     dict(kind=0, B=3, S=2, Hq=16, Hkv=1, sinks=False, starts=[0, 255, 4097]),
     dict(kind=0, B=2, S=16, Hq=8, Hkv=2, sinks=True, starts=[1, 700]),
     dict(kind=0, B=1, S=5, Hq=64, Hkv=4, sinks=False, starts=[20000]),           # split partials
+    # 118 splits: the combine reads past its first prefetch block of 96 (with a sink)
+    dict(kind=0, B=1, S=4, Hq=64, Hkv=4, sinks=True, starts=[30000]),
 ]
 
 
