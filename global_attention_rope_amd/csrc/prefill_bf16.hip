@@ -9,11 +9,13 @@
 //   h -> KV head h / (Hq / Hkv), optional sink s_h (sliding layers in the model).
 //
 // Shape of the computation (qk head dim 192, v head dim 128):
-//   * each wave owns 32 query rows of one query head and keeps their rotated Q^T (bf16) in
-//     registers; global layers: 8 waves on 8 consecutive row blocks of one head, one workgroup per
-//     CU; sliding layers: 4 waves, two workgroups per CU, and when the GQA group is a multiple of 4
-//     the 4 waves take 4 heads of one KV group over the same 32 rows, so every wave computes every
-//     tile of the ~3-tile band and each K/V tile feeds 4 heads;
+//   * prefill_kernel: each wave owns 32 query rows of one query head and keeps their rotated Q^T
+//     (bf16) in registers; global layers: 8 waves on 8 consecutive row blocks of one head, one
+//     workgroup per CU; sliding layers whose GQA group is not a multiple of 4: 4 waves, two
+//     workgroups per CU;
+//   * prefill_sw16_kernel (sliding layers, GQA group a multiple of 4): 4 waves take 4 heads of one
+//     KV group over the same 16 rows on 16x16x32 products and 32-key tiles, so each K/V tile feeds
+//     4 heads and four workgroups share a CU (details at the kernel);
 //   * K (64 x 192) and V (64 x 128) tiles stream through a 3-stage (global) or 2-stage (sliding)
 //     LDS ring filled by global_load_lds_dwordx4 (memory -> LDS without registers) one or two
 //     tiles ahead of the one being computed; one barrier per tile;
@@ -85,12 +87,11 @@ __device__ __forceinline__ u32x4 scale8(const u32x4& w, float scale) {
     return pack8(x);
 }
 
-// GROUPED: a workgroup covers NW query heads of one KV group over the same 32 rows (wave w takes
-// head base + w); otherwise it covers NW consecutive 32-row blocks of one query head.
-template <int NW, int STAGES, bool WINDOW, bool SINK, bool GROUPED>
+// A workgroup covers NW consecutive 32-row blocks of one query head.
+template <int NW, int STAGES, bool WINDOW, bool SINK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const PrefillArgs a) {
-    constexpr int BM = GROUPED ? QPW : NW * QPW;   // query rows per workgroup
+    constexpr int BM = NW * QPW;                   // query rows per workgroup
     constexpr int K_DMA = K_TILE / 1024 / NW;      // 1-KiB DMA instructions per wave per tile
     constexpr int V_DMA = V_TILE / 1024 / NW;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * (K_TILE + V_TILE)];
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int l32 = lane & 31, g = lane >> 5;
     const int S = a.S, Hq = a.Hq;
     const int nqblk = (S + BM - 1) / BM;
-    const int hunits = GROUPED ? Hq / NW : Hq;     // head units per (row block, sequence)
+    const int hunits = Hq;                         // heads per (row block, sequence)
     const int total = a.B * hunits * nqblk;
 
     // ---- work item (XCD-aware order; heavy-first on global layers)
@@ -122,26 +123,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int b = (w / hunits) % a.B;
     const int qrank = w / (hunits * a.B);
     const int qblk = WINDOW ? qrank : nqblk - 1 - qrank;   // global: heaviest blocks first
-    const int h = GROUPED ? hu * NW + wave : hu;
-    const int kvh = (GROUPED ? hu * NW : hu) / (Hq / a.Hkv);
+    const int h = hu;
+    const int kvh = hu / (Hq / a.Hkv);
     const int r = a.rope_dims, half = r >> 1;
-    // GROUPED: the frequencies of this thread's entries of the rows' cos/sin table (entry
-    // e = row * r/2 + frequency, thread tid taking e = tid, tid + 256, ...), requested first, from
-    // the argument segment through a pointer the compiler cannot trace back to it, so that the
-    // loads stay ahead of the barrier that follows the table
-    constexpr int TAB = GROUPED ? (QPW * kMaxRopeHalfArgs + NW * 64 - 1) / (NW * 64) : 1;
-    double om_tab[TAB];
-    if constexpr (GROUPED) {
-        const char* kargs = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
-        asm volatile("" : "+s"(kargs));
-        const __attribute__((address_space(1))) double* om_args =
-            (const __attribute__((address_space(1))) double*)(kargs + offsetof(PrefillArgs, omega_rev));
-#pragma unroll
-        for (int k = 0; k < TAB; ++k) {
-            const int e = tid + k * NW * 64;
-            om_tab[k] = e < QPW * half ? om_args[e % half] : 0.0;
-        }
-    }
     // (the start position comes by a scalar load that waits for nothing but itself, so the vector
     //  loads issued before it stay in flight)
     int32_t p0 = 0;
@@ -169,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int nk = S + shift;
 
     const int W = a.window;
-    const int q_first = qblk * BM + (GROUPED ? 0 : wave * QPW);   // this wave's first row (scalar)
+    const int q_first = qblk * BM + wave * QPW;   // this wave's first row (scalar)
     const int q_last = min(q_first + QPW, S) - 1;                 // its last valid row
     const int blk_first = qblk * BM;
     const int blk_last = min(blk_first + BM, S) - 1;
@@ -254,73 +238,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         u32x4 qw[KCH];
 #pragma unroll
         for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
-        if constexpr (GROUPED) {
-            // rotation partners, requested with the rows themselves
-            u32x4 pw[KCH];
+        if (own_rows) p0 = load_scalar_i32(a.start_pos + b);
 #pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const int d0 = 16 * c + 8 * g;
-                if (d0 < r) pw[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : d0 - half));
+        for (int c = 0; c < KCH; ++c) {
+            const int d0 = 16 * c + 8 * g;
+            if (d0 < r) {
+                const bool lower = d0 < half;
+                const u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
+                const u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
+                qw[c] = rotate_pair8_kernarg(lo, hi, lower, p0 + qi,
+                                             a.omega_rev + (lower ? d0 : d0 - half), sc);
+            } else {
+                qw[c] = scale8(qw[c], sc);
             }
-            if (own_rows) p0 = load_scalar_i32(a.start_pos + b);
-            // The NW waves share the 32 rows (one head each): the cos/sin of the rows' positions
-            // per frequency are evaluated once for the workgroup into a table in K stage 1, which
-            // no tile uses before the first tile step.  Rows are padded by one entry (so that the
-            // 32 rows' reads of one frequency hit distinct banks) while 32 x (r/2 + 1) entries of
-            // 8 bytes fit the stage, i.e. up to r = 190; at r = 192 they are packed.
-            static_assert(STAGES == 2, "table lives in stage 1");
-            float2* cs = (float2*)(smem + K_TILE);
-            const int pitch = QPW * (half + 1) * 8 <= K_TILE ? half + 1 : half;
-#pragma unroll
-            for (int k = 0; k < TAB; ++k) {
-                const int e = tid + k * NW * 64;
-                if (e < QPW * half) {
-                    const int row = e / half, f = e - row * half;
-                    float c, sn;
-                    rope_cos_sin_rev(p0 + min(q_first + row, S - 1), om_tab[k], c, sn);
-                    cs[row * pitch + f] = make_float2(c, sn);
-                }
-            }
-            block_sync_lds();
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const int d0 = 16 * c + 8 * g;
-                if (d0 < r) {
-                    const bool lower = d0 < half;
-                    const float2* e = cs + l32 * pitch + (lower ? d0 : d0 - half);
-                    float x[8], y[8];
-                    unpack8(qw[c], x);
-                    unpack8(pw[c], y);
-                    const float sgn = lower ? -1.0f : 1.0f;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float2 cst = e[t];
-                        x[t] = __builtin_fmaf(sgn * y[t], cst.y, x[t] * cst.x) * sc;
-                    }
-                    qw[c] = pack8(x);
-                } else {
-                    qw[c] = scale8(qw[c], sc);
-                }
-                if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
-                Qb[c] = as_bf16x8(qw[c]);
-            }
-        } else {
-            if (own_rows) p0 = load_scalar_i32(a.start_pos + b);
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const int d0 = 16 * c + 8 * g;
-                if (d0 < r) {
-                    const bool lower = d0 < half;
-                    const u32x4 lo = lower ? qw[c] : *(const u32x4*)(qrow + d0 - half);
-                    const u32x4 hi = lower ? *(const u32x4*)(qrow + d0 + half) : qw[c];
-                    qw[c] = rotate_pair8_kernarg(lo, hi, lower, p0 + qi,
-                                                 a.omega_rev + (lower ? d0 : d0 - half), sc);
-                } else {
-                    qw[c] = scale8(qw[c], sc);
-                }
-                if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
-                Qb[c] = as_bf16x8(qw[c]);
-            }
+            if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
+            Qb[c] = as_bf16x8(qw[c]);
         }
     }
 
@@ -498,33 +430,357 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
+
+// Sliding layers, GQA group a multiple of 4: a workgroup of 4 waves takes 4 query heads of one KV
+// group over 16 rows (wave w: head 4 * unit + w), on v_mfma_f32_16x16x32_bf16, with 32-key tiles
+// through a 2-stage LDS ring (40 KiB): about 100 registers and 40 KiB per workgroup, so that four
+// workgroups share a CU and their memory phases (query rows in, outputs out) overlap the others'
+// products.  Layouts in LDS as in prefill_kernel (K chunk c of row r at c ^ ((r >> 1) & 7), V
+// chunk c at c ^ ((r & 3) << 2)); the scores and the weighted sum follow the decode kernel's
+// operand layout:
+//   S^T (16 keys x 16 rows) = K * Q^T: A = K, lane l holds key l % 16, dims 32c + 8(l / 16) + [0, 8);
+//     B = Q^T, lane l holds row l % 16, the same dims; C: lane l holds row l % 16, keys 4(l / 16) + i;
+//   O^T (16 dims x 16 rows) += V^T * P^T: k-slot t of lane group gq is key 4gq + t (t < 4) or
+//     16 + 4gq + (t - 4) of the 32-key tile, on both operands.
+constexpr int SW16_ROWS = 16;
+constexpr int SW16_BN = 32;
+constexpr int SW16_K_TILE = SW16_BN * DQK * 2;   // 12 KiB
+constexpr int SW16_V_TILE = SW16_BN * DV * 2;    // 8 KiB
+constexpr int SW16_WAVES = 4;
+
+template <bool SINK>
+__global__ __launch_bounds__(SW16_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void
+prefill_sw16_kernel(const PrefillArgs a) {
+    constexpr int NW = SW16_WAVES, BN = SW16_BN, QR = SW16_ROWS;
+    constexpr int K_DMA = SW16_K_TILE / 1024 / NW;   // 3
+    constexpr int V_DMA = SW16_V_TILE / 1024 / NW;   // 2
+    constexpr int KC = DQK / 32;                     // 32-dim k-chunks of the scores
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (SW16_K_TILE + SW16_V_TILE)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int S = a.S, Hq = a.Hq;
+    const int nqblk = (S + QR - 1) / QR;
+    const int hunits = Hq / NW;
+
+    // work item: workgroup ids go round-robin to the 8 XCDs; each XCD walks the row blocks of its
+    // own (sequence, head unit) pairs in order, so the K/V band stays in that XCD's L2
+    const int id = blockIdx.x;
+    int w = id;
+    const int pairs = a.B * hunits;
+    if (pairs % 8 == 0) {
+        const int P = pairs / 8, xcd = id & 7, k = id >> 3;
+        w = (k / P) * pairs + xcd * P + k % P;
+    }
+    const int hu = w % hunits;
+    const int b = (w / hunits) % a.B;
+    const int qblk = w / (hunits * a.B);
+    const int h = hu * NW + wave;
+    const int kvh = hu * NW / (Hq / a.Hkv);
+    const int r = a.rope_dims, half = r >> 1;
+
+    // the frequencies of this thread's entries of the rows' cos/sin table (entry e = row * r/2 + f,
+    // thread tid taking e = tid, tid + 256, ...), from the argument segment through a pointer the
+    // compiler cannot trace back to it, so that the loads stay ahead of the table's barrier
+    constexpr int TAB = (QR * kMaxRopeHalfArgs + NW * 64 - 1) / (NW * 64);
+    double om_tab[TAB];
+    {
+        const char* kargs = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(kargs));
+        const __attribute__((address_space(1))) double* om_args =
+            (const __attribute__((address_space(1))) double*)(kargs + offsetof(PrefillArgs, omega_rev));
+#pragma unroll
+        for (int k = 0; k < TAB; ++k) {
+            const int e = tid + k * NW * 64;
+            om_tab[k] = e < QR * half ? om_args[e % half] : 0.0;
+        }
+    }
+
+    // key rows (as in prefill_kernel): row j at position kpos0 + j; query row i meets key row
+    // i + shift at its own position; rows below jmin hold no token
+    int32_t p0 = 0;
+    bool seq_ok;
+    int shift, jmin;
+    const bool own_rows = a.max_start < 0 && a.kpos_rel && a.kpos_off >= 0;
+    if (own_rows) {
+        seq_ok = true;
+        shift = -a.kpos_off;
+        jmin = 0;
+    } else {
+        p0 = load_scalar_i32(a.start_pos + b);
+        seq_ok = a.max_start < 0 || (unsigned)p0 <= (unsigned)a.max_start;
+        const int32_t kpos0 = (a.kpos_rel ? (seq_ok ? p0 : 0) : 0) + a.kpos_off;
+        shift = (seq_ok ? p0 : 0) - kpos0;
+        jmin = max(0, -kpos0);
+    }
+    const int nk = S + shift;
+    const int W = a.window;
+    const int q_first = qblk * QR;
+    const int q_last = min(q_first + QR, S) - 1;
+    const int kt_lo = max(jmin, q_first + shift - W + 1) / BN;
+    const int n_tiles = seq_ok ? (q_last + shift) / BN + 1 - kt_lo : 0;
+
+    // DMA: LDS 16-byte slot P of this wave's instruction i holds K row P / 24, chunk
+    // (P % 24) ^ ((row >> 1) & 7); V row P / 16, chunk (P % 16) ^ ((row & 3) << 2)
+    const uint16_t* kslice = a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+    const uint16_t* vslice = a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+    const int64_t v_sj = a.v_sj;
+    auto k_slot = [&](int i, int ln, int& row, int& col) __attribute__((always_inline)) {
+        const int P = (wave * K_DMA + i) * 64 + ln;
+        row = P / (DQK / 8);
+        col = ((P % (DQK / 8)) ^ ((row >> 1) & 7)) * 8;
+    };
+    auto v_slot = [&](int i, int ln, int& row, int& col) __attribute__((always_inline)) {
+        const int P = (wave * V_DMA + i) * 64 + ln;
+        row = P / (DV / 8);
+        col = ((P % (DV / 8)) ^ ((row & 3) << 2)) * 8;
+    };
+    uint32_t k_lo[K_DMA], v_lo[V_DMA];
+#pragma unroll
+    for (int i = 0; i < K_DMA; ++i) {
+        int row, col;
+        k_slot(i, lane, row, col);
+        k_lo[i] = (uint32_t)(row * DQK + col) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < V_DMA; ++i) {
+        int row, col;
+        v_slot(i, lane, row, col);
+        v_lo[i] = (uint32_t)((int64_t)row * v_sj + col) * 2u;
+    }
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_u8_t*)smem;
+    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+        const int j0 = (kt_lo + t) * BN;
+        const uint32_t kst = lds0 + st * SW16_K_TILE;
+        const uint32_t vst = lds0 + 2 * SW16_K_TILE + st * SW16_V_TILE;
+        if (j0 >= jmin && j0 + BN <= nk) {
+            const uint16_t* kb = kslice + (int64_t)j0 * DQK;
+            const uint16_t* vb = vslice + (int64_t)j0 * v_sj;
+#pragma unroll
+            for (int i = 0; i < K_DMA; ++i) dma16_sbase(kb, k_lo[i], kst + (wave * K_DMA + i) * 1024);
+#pragma unroll
+            for (int i = 0; i < V_DMA; ++i) dma16_sbase(vb, v_lo[i], vst + (wave * V_DMA + i) * 1024);
+        } else {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int i = 0; i < K_DMA; ++i) {
+                int row, col;
+                k_slot(i, ln, row, col);
+                const int j = min(max(j0 + row, jmin), nk - 1);
+                dma16(kslice + (int64_t)j * DQK + col, kst + (wave * K_DMA + i) * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < V_DMA; ++i) {
+                int row, col;
+                v_slot(i, ln, row, col);
+                const int j = min(max(j0 + row, jmin), nk - 1);
+                dma16(vslice + (int64_t)j * v_sj + col, vst + (wave * V_DMA + i) * 1024);
+            }
+        }
+    };
+    if (n_tiles > 0) issue(0, 0);
+
+    // ---- Q^T operands (rows q_first + l16, dims 32c + 8gq..), rotated and scaled by
+    //      tau * log2(e), rounded once to bf16; the rows' cos/sin table lives in K stage 1 until
+    //      the first tile step
+    const float sc = a.score_scale_log2;
+    bf16x8 Qb[KC];
+    {
+        const int qi = q_first + l16;
+        const bool qok = qi < S;
+        const uint16_t* qrow = a.q + (((int64_t)b * S + (qok ? qi : S - 1)) * Hq + h) * DQK;
+        u32x4 qw[KC], pw[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qw[c] = *(const u32x4*)(qrow + 32 * c + 8 * gq);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int d0 = 32 * c + 8 * gq;
+            if (d0 < r) pw[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : d0 - half));
+        }
+        if (own_rows) p0 = load_scalar_i32(a.start_pos + b);
+        float2* cs = (float2*)(smem + SW16_K_TILE);
+        const int pitch = QR * (half + 1) * 8 <= SW16_K_TILE ? half + 1 : half;
+#pragma unroll
+        for (int k = 0; k < TAB; ++k) {
+            const int e = tid + k * NW * 64;
+            if (e < QR * half) {
+                const int row = e / half, f = e - row * half;
+                float c, sn;
+                rope_cos_sin_rev(p0 + min(q_first + row, S - 1), om_tab[k], c, sn);
+                cs[row * pitch + f] = make_float2(c, sn);
+            }
+        }
+        block_sync_lds();
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int d0 = 32 * c + 8 * gq;
+            if (d0 < r) {
+                const bool lower = d0 < half;
+                const float2* e = cs + l16 * pitch + (lower ? d0 : d0 - half);
+                float x[8], y[8];
+                unpack8(qw[c], x);
+                unpack8(pw[c], y);
+                const float sgn = lower ? -1.0f : 1.0f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float2 cst = e[t];
+                    x[t] = __builtin_fmaf(sgn * y[t], cst.y, x[t] * cst.x) * sc;
+                }
+                qw[c] = pack8(x);
+            } else {
+                qw[c] = scale8(qw[c], sc);
+            }
+            if (!qok) qw[c] = u32x4{0u, 0u, 0u, 0u};
+            Qb[c] = as_bf16x8(qw[c]);
+        }
+    }
+
+    // ---- per-lane LDS read offsets within a stage: K (key l16 of block kb, chunk 4c + gq),
+    //      V^T (rows 4gq + l16 / 4 and + 16, dims 16db + 4(l16 % 4))
+    int k_rd[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) k_rd[c] = l16 * (DQK * 2) + 16 * ((4 * c + gq) ^ ((l16 >> 1) & 7));
+    int v_rd[DV / 16];
+    {
+        const int vrow = 4 * gq + (l16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DV / 16; ++db) {
+            const int byte = (db * 16 + 4 * (l16 & 3)) * 2;
+            v_rd[db] = 2 * SW16_K_TILE + vrow * (DV * 2) + 16 * ((byte >> 4) ^ ((vrow & 3) << 2)) +
+                       (byte & 15);
+            asm volatile("" : "+v"(v_rd[db]));
+        }
+    }
+
+    const float sink_l2 = SINK ? a.sinks[h] * kLog2e : -INFINITY;
+    float m_run = SINK ? sink_l2 : -INFINITY;      // reference maximum (lazily raised)
+    float l_run = (SINK && gq == 0) ? 1.0f : 0.0f;
+    float m_ref = SINK ? sink_l2 : 0.0f;
+    f32x4 O[DV / 16];
+#pragma unroll
+    for (int db = 0; db < DV / 16; ++db) O[db] = f32x4{};
+    const int q_l = q_first + l16;
+    const unsigned lim = (unsigned)max(0, min(W, q_l + shift - jmin + 1));
+
+    auto compute = [&](int t, int st) __attribute__((always_inline)) {
+        const int j0 = (kt_lo + t) * BN;
+        if (j0 > q_last + shift || j0 + BN - 1 <= q_first + shift - W) return;   // uniform
+        const bool full = j0 >= jmin && j0 + BN - 1 <= q_first + shift && q_last + shift - j0 < W;
+        const uint8_t* kst = smem + st * SW16_K_TILE;
+        const uint8_t* vst = smem + st * SW16_V_TILE;   // + v_rd, which holds the V area's base
+        f32x4 Sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bf16x8 A = *(const bf16x8*)(kst + k_rd[c] + kb * 16 * (DQK * 2));
+                acc = mfma16x16x32(A, Qb[c], acc);
+            }
+            Sacc[kb] = acc;
+        }
+        if (!full) {
+            asm volatile("");
+            // key j0 + 16kb + 4gq + i against row q_l
+            const int d = q_l + shift - j0 - 4 * gq;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Sacc[kb][i] = (unsigned)(d - 16 * kb - i) < lim ? Sacc[kb][i] : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(Sacc[0][0], Sacc[0][1]), fmaxf(Sacc[0][2], Sacc[0][3])),
+                         fmaxf(fmaxf(Sacc[1][0], Sacc[1][1]), fmaxf(Sacc[1][2], Sacc[1][3])));
+        mx = max_lane_pair32(max_lane_pair16(mx));
+        const bool first = m_run == -INFINITY;
+        const bool raise = first ? mx != -INFINITY : mx > m_ref + kRescaleLog2;
+        if (__any(raise)) {
+            asm volatile("");
+            const float m_new = raise ? mx : m_ref;
+            const float alpha = (raise && !first) ? fast_exp2(m_ref - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DV / 16; ++db) O[db] *= alpha;
+            m_ref = m_new;
+            if (raise) m_run = m_new;
+        }
+        float ps = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Sacc[kb][i] = fast_exp2(Sacc[kb][i] - m_ref);
+                ps += Sacc[kb][i];
+            }
+        l_run += ps;
+        const bf16x8 Pb = as_bf16x8(u32x4{pack_bf16x2(Sacc[0][0], Sacc[0][1]),
+                                          pack_bf16x2(Sacc[0][2], Sacc[0][3]),
+                                          pack_bf16x2(Sacc[1][0], Sacc[1][1]),
+                                          pack_bf16x2(Sacc[1][2], Sacc[1][3])});
+#pragma unroll
+        for (int db = 0; db < DV / 16; ++db) {
+            const uint8_t* vp = vst + v_rd[db];
+            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+            const bf16x4 v1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 16 * DV * 2));
+            O[db] = mfma16x16x32(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), Pb, O[db]);
+        }
+    };
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int st = t & 1;
+        wait_vmcnt<0>();
+        block_sync_lds();   // tile t in LDS for every wave; the other stage (and the table) free
+        if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
+        compute(t, st);
+    }
+
+    // ---- epilogue: out = v_scale * O / l (bf16); lane l writes row q_l, dims 16db + 4gq..
+    const float lt = sum_lane_pair32(sum_lane_pair16(l_run));
+    const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+    if (q_l < S) {
+        uint16_t* orow = a.out + (((int64_t)b * S + q_l) * Hq + h) * DV;
+#pragma unroll
+        for (int db = 0; db < DV / 16; ++db)
+            *(u32x2*)(orow + 16 * db + 4 * gq) =
+                u32x2{pack_bf16x2(O[db][0] * inv, O[db][1] * inv),
+                      pack_bf16x2(O[db][2] * inv, O[db][3] * inv)};
+    }
+}
+
 }  // namespace
 
 int prefill_bf16_block_rows(bool window) { return (window ? SW_WAVES : GA_WAVES) * QPW; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, bool window, bool sink, hipStream_t st) {
     if (a.k_sj != DQK) return hipErrorInvalidValue;   // keys must be contiguous rotated rows
-    const int group = a.Hq / a.Hkv;
-    const bool grouped = window && group % SW_WAVES == 0;
-    const int bm = grouped ? QPW : prefill_bf16_block_rows(window);
+    if (window && (a.Hq / a.Hkv) % SW16_WAVES == 0 && a.v_sj < (1 << 24)) {
+        // sliding layers with whole groups of 4 query heads per KV head: 16-row workgroups of 4
+        // heads, four per CU
+        const int64_t nwg = (int64_t)a.B * (a.Hq / SW16_WAVES) * ((a.S + SW16_ROWS - 1) / SW16_ROWS);
+        if (nwg == 0) return hipSuccess;
+        if (nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+        if (sink) prefill_sw16_kernel<true><<<dim3((unsigned)nwg), dim3(SW16_WAVES * 64), 0, st>>>(a);
+        else prefill_sw16_kernel<false><<<dim3((unsigned)nwg), dim3(SW16_WAVES * 64), 0, st>>>(a);
+        return hipGetLastError();
+    }
+    const int bm = prefill_bf16_block_rows(window);
     const int nqblk = (a.S + bm - 1) / bm;
-    const int64_t total = (int64_t)a.B * (grouped ? a.Hq / SW_WAVES : a.Hq) * nqblk;
+    const int64_t total = (int64_t)a.B * a.Hq * nqblk;
     if (total == 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)total);
     if (window) {
         const dim3 block(SW_WAVES * 64);
-        if (grouped) {
-            if (sink) prefill_kernel<SW_WAVES, SW_STAGES, true, true, true><<<grid, block, 0, st>>>(a);
-            else prefill_kernel<SW_WAVES, SW_STAGES, true, false, true><<<grid, block, 0, st>>>(a);
-        } else {
-            if (sink) prefill_kernel<SW_WAVES, SW_STAGES, true, true, false><<<grid, block, 0, st>>>(a);
-            else prefill_kernel<SW_WAVES, SW_STAGES, true, false, false><<<grid, block, 0, st>>>(a);
-        }
+        if (sink) prefill_kernel<SW_WAVES, SW_STAGES, true, true><<<grid, block, 0, st>>>(a);
+        else prefill_kernel<SW_WAVES, SW_STAGES, true, false><<<grid, block, 0, st>>>(a);
     } else {
         const dim3 block(GA_WAVES * 64);
-        if (sink) prefill_kernel<GA_WAVES, GA_STAGES, false, true, false><<<grid, block, 0, st>>>(a);
-        else prefill_kernel<GA_WAVES, GA_STAGES, false, false, false><<<grid, block, 0, st>>>(a);
+        if (sink) prefill_kernel<GA_WAVES, GA_STAGES, false, true><<<grid, block, 0, st>>>(a);
+        else prefill_kernel<GA_WAVES, GA_STAGES, false, false><<<grid, block, 0, st>>>(a);
     }
     return hipGetLastError();
 }
