@@ -6,7 +6,8 @@
 //
 // Per (sequence b, KV head g, split s) one workgroup of 4 waves:
 //   * each wave issues the loads of its first 32-slot tile (K straight into MFMA operand layout,
-//     V as coalesced 16-byte rows) early — on sliding layers before the position is even read —
+//     V as coalesced 16-byte rows) early — before the position is even read on sliding layers
+//     and on small global-layer grids —
 //     so their latency overlaps the query rotation;
 //   * the query heads of group g (<= 16) are rotated at the new token's position and kept as the
 //     B operand of v_mfma_f32_16x16x32_bf16 (heads are the 16-wide N dimension);
@@ -96,7 +97,11 @@ struct LdsDecode {
 
 // ROT: how many of a lane's 32-dim query chunk rows can hold rotated dims (2 when r <= 64).
 // FP8: the caches hold e4m3 codes.
-template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8>
+// EARLY: the first slot tile is requested before the position is known (always on sliding layers,
+// whose ring slots are all in bounds; on global layers when the grid fits one round of resident
+// workgroups, where every call is latency-bound: a split past a short sequence's position then
+// fetches one tile it does not use, which a larger grid would pay for in bandwidth).
+template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool EARLY>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) LdsDecode sm;
     // Every argument the kernel reads is requested here, in one batch of scalar loads waited for
@@ -218,9 +223,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     const double om0 = om_args[lane], om1 = om_args[lane + 64];   // frequencies lane, lane + 64
     const int stride = NW * TILE;
     int t0 = k_begin + wave * TILE;
-    // every ring slot is in bounds; a linear cache's splits past the position would only waste
-    // bandwidth, so those wait for it
-    if (SWA) fetch(kA, vA, t0);
+    if (EARLY) fetch(kA, vA, t0);
     // The position comes by a scalar load, counted apart from the vector loads (lgkmcnt, not
     // vmcnt): the work that needs only the position and the query (cos/sin table, query and
     // new-token rotation) runs while the slot tile is still in flight.  The load waits for its
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     if (k_begin >= n_valid) return;
     const int k_end = min(n_valid, k_begin + a.chunk);
     const bool own_new = slot_new >= k_begin && slot_new < k_end;
-    if (!SWA) fetch(kA, vA, t0);
+    if (!EARLY) fetch(kA, vA, t0);
 
     // ---- cos/sin of the position per frequency, in this wave's table (read by this wave only)
     float2* const cs = sm.cs[wave];
@@ -557,11 +560,14 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
                           ? dim3(a.Hkv * kDecodeSplitBlock, a.B,
                                  (a.nsplit + kDecodeSplitBlock - 1) / kDecodeSplitBlock)
                           : dim3(a.nsplit, a.Hkv, a.B);
+    const bool early = SWA || (int64_t)a.B * a.Hkv * a.nsplit <= kResidentDecodeGroups;
     if (a.nsplit == 1) {
-        decode_bf16_kernel<SWA, SINK, false, ROT, FP8><<<grid, 256, 0, st>>>(k);
+        if (early) decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true><<<grid, 256, 0, st>>>(k);
+        else decode_bf16_kernel<SWA, SINK, false, ROT, FP8, false><<<grid, 256, 0, st>>>(k);
         return hipGetLastError();
     }
-    decode_bf16_kernel<SWA, SINK, true, ROT, FP8><<<grid, 256, 0, st>>>(k);
+    if (early) decode_bf16_kernel<SWA, SINK, true, ROT, FP8, true><<<grid, 256, 0, st>>>(k);
+    else decode_bf16_kernel<SWA, SINK, true, ROT, FP8, false><<<grid, 256, 0, st>>>(k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch_combine<SWA, SINK, false>(a, dim3(a.Hq, a.B), st);
