@@ -37,6 +37,9 @@ constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyon
 // fp8: one bf16 tile and the new rows
 constexpr int NEW_ROWS = 16;
 constexpr int NEW_BYTES = NEW_ROWS * (DQK + DV) * 2;
+#ifndef FP8_DEPTH
+#define FP8_DEPTH 2
+#endif
 
 template <int NW, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
 __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs a) {
@@ -164,22 +167,32 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
         }
     }
     // fp8: the cached rows' codes of a tile go memory -> registers (units of 16 codes: K rows of
-    // 12 units, then V rows of 8), two tiles ahead of the products; widening writes the bf16 tile:
-    // the codes' exact values for positions before the start, the staged new rows after it, zeros
-    // past the last token.  Code rows at or past the start are loaded clamped in bounds, unused.
+    // 12 units, then V rows of 8), DEPTH tiles ahead of the products; widening writes the bf16
+    // tile: the codes' exact values for positions before the start, the staged new rows after it,
+    // zeros past the last token.  Every load is issued unconditionally, with its code row clamped
+    // in bounds (rows at or past the start, tiles past the last are loaded and not used): the
+    // compiler then counts exactly which loads a widening has to wait for, instead of waiting for
+    // all of them on the paths where a later load might have been skipped.
     constexpr int NT = NW * 64;
-    constexpr int KU = BN * (DQK / 16) / NT, VU = BN * (DV / 16) / NT;
+    constexpr int K_UNITS = BN * (DQK / 16), V_UNITS = BN * (DV / 16);
+    constexpr int KU = (K_UNITS + NT - 1) / NT, VU = (V_UNITS + NT - 1) / NT;   // per thread
+    // (a unit past the tile's occurs only where NT does not divide the units, 8 waves: it loads
+    //  the last unit again and widens nothing)
+    auto unit_ok = [&](int k) {
+        if (k < KU) return K_UNITS % NT == 0 || tid + k * NT < K_UNITS;
+        return V_UNITS % NT == 0 || tid + (k - KU) * NT < V_UNITS;
+    };
     const int64_t code_row0 = ((int64_t)b * a.Hkv + kvh) * (FP8 ? a.code_cap : 1);
     auto load_codes = [&](u32x4 (&c)[KU + VU], int tt) {
         const int j0 = (kt_lo + tt) * BN, jlast = max(st - 1, 0);
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
-            const int u = tid + k * NT, row = u / (DQK / 16), c16 = u % (DQK / 16);
+            const int u = min(tid + k * NT, K_UNITS - 1), row = u / (DQK / 16), c16 = u % (DQK / 16);
             c[k] = *(const u32x4*)(a.code_k + (code_row0 + min(j0 + row, jlast)) * DQK + 16 * c16);
         }
 #pragma unroll
         for (int k = 0; k < VU; ++k) {
-            const int u = tid + k * NT, row = u / (DV / 16), c16 = u % (DV / 16);
+            const int u = min(tid + k * NT, V_UNITS - 1), row = u / (DV / 16), c16 = u % (DV / 16);
             c[KU + k] = *(const u32x4*)(a.code_v + (code_row0 + min(j0 + row, jlast)) * DV + 16 * c16);
         }
     };
@@ -187,6 +200,7 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
         const int j0 = (kt_lo + tt) * BN;
 #pragma unroll
         for (int k = 0; k < KU + VU; ++k) {
+            if (!unit_ok(k)) continue;
             const bool key = k < KU;
             const int u = tid + (key ? k : k - KU) * NT;
             const int cpr = key ? DQK / 16 : DV / 16;
@@ -375,25 +389,28 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     };
 
     if constexpr (FP8) {
-        // two tiles of codes in flight (one for a single-wave workgroup, whose registers would
-        // not hold two)
-        constexpr int DEPTH = NW == 1 ? 1 : 2;
-        u32x4 cA[KU + VU], cB[KU + VU];
-        if (n_tiles > 0) load_codes(cA, 0);
-        if (DEPTH > 1 && n_tiles > 1) load_codes(cB, 1);
+        // DEPTH tiles of codes in flight (one where the registers would not hold more: a single
+        // wave, or 8 waves two to a SIMD); register set d holds tiles d, d + DEPTH, ...
+        constexpr int DEPTH = (NW == 1 || NW == 8) ? 1 : FP8_DEPTH;
+        u32x4 cs[DEPTH][KU + VU];
+        // Round r runs DEPTH steps: step d widens tile DEPTH * r + d from register set d (a
+        // uniform branch skips it in round -1, which only loads) and loads the tile DEPTH later
+        // into the same set.  Every round runs all DEPTH steps, past the last tile too, and the
+        // first loads come from the same instructions as the later ones, so that every path into
+        // the loop head has issued the sets' loads in the same order.
         auto step = [&](u32x4 (&c)[KU + VU], int tt) {
-            block_sync_lds();   // the previous tile's products are done with the bf16 tile
-            widen(c, tt);       // (waits for this tile's codes; the next tile's stay in flight)
-            block_sync_lds();
-            if (tt + DEPTH < n_tiles) load_codes(c, tt + DEPTH);
-            tile_products(tt, 0);
+            if (tt >= 0) {
+                block_sync_lds();   // the previous tile's products are done with the bf16 tile
+                widen(c, tt);       // (waits for this tile's codes; later tiles' stay in flight)
+                block_sync_lds();
+            }
+            load_codes(c, min(tt + DEPTH, n_tiles - 1));   // (past the last: that tile again)
+            if (tt >= 0 && tt < n_tiles) tile_products(tt, 0);
         };
-        if constexpr (DEPTH == 1) {
-            for (int tt = 0; tt < n_tiles; ++tt) step(cA, tt);
-        } else {
-            for (int tt = 0; tt < n_tiles; tt += 2) {
-                step(cA, tt);
-                if (tt + 1 < n_tiles) step(cB, tt + 1);
+        if (n_tiles > 0) {
+            for (int tt = -DEPTH; tt < n_tiles; tt += DEPTH) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) step(cs[d], tt + d);
             }
         }
     } else {

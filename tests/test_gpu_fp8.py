@@ -276,6 +276,11 @@ def run_prefill_fp8_chain(kind, seed, r=64, theta=None, q_scale=1.0):
 EXT_CASES = [
     dict(kind=0, B=2, S=40, Hq=8, Hkv=2, sinks=False, starts=[0, 700]),        # prefill kernel
     dict(kind=0, B=3, S=4, Hq=16, Hkv=1, sinks=True, starts=[1, 255, 4097]),   # tile kernel
+    # the tile kernel's other workgroup sizes (16 heads x 16 / 8 token columns: 8 / 4 waves, whose
+    # threads split a tile's 1280 code units unevenly / evenly; 4 columns: one wave)
+    dict(kind=0, B=2, S=12, Hq=32, Hkv=2, sinks=False, starts=[3, 2500]),
+    dict(kind=0, B=2, S=7, Hq=32, Hkv=2, sinks=True, starts=[0, 1300]),
+    dict(kind=0, B=2, S=1, Hq=8, Hkv=2, sinks=False, starts=[64, 333]),
     dict(kind=1, B=2, S=300, Hq=8, Hkv=2, sinks=True, starts=[5, 4000]),       # ring, S > W
     dict(kind=1, B=3, S=4, Hq=16, Hkv=2, sinks=True, starts=[0, 2, 1000]),     # ring, tile kernel
 ]
