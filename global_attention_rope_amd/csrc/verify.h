@@ -42,7 +42,8 @@ struct VerifyArgs {
     double omega_rev[kMaxRopeHalfArgs];  // theta^(-2d/r) / (2 pi)
 };
 
-// Waves per workgroup of the tile kernel for G query heads per KV head and TP token columns.
+// Column waves (32 query columns each) of the tile kernel for G query heads per KV head and TP
+// token columns; 0 beyond 256 columns.
 int verify_tile_waves(int G, int TP);
 
 hipError_t launch_verify_tiles_bf16(const VerifyArgs& a, bool window, bool sink, hipStream_t st);

@@ -6,7 +6,10 @@
 // "Implementation plan"), shaped for T <= 16 queries per sequence: the query columns of the
 // S^T = K * Q^T products are (query head, token) pairs of one KV group — 16 heads x 4 tokens fill
 // two 32-column waves — so every K/V tile is read from memory once per (sequence, KV head) and
-// feeds all heads and tokens.  The key rows are split across workgroups (split-K); each split
+// feeds all heads and tokens.  Up to 128 columns, each column wave is doubled: one wave takes the
+// first 32 keys of every tile, its twin the last 32, each with a softmax state of its own, merged
+// through LDS at the end — half the score registers per wave, so that two waves share a SIMD and
+// cover each other's operand-read and product latencies.  The key rows are split across workgroups (split-K); each split
 // writes (O, max, sum) partials for the decode combine kernel, or the output when there is one.
 // Tiles: 64 keys, staged through a 2-stage LDS ring by global_load_lds_dwordx4, XOR-swizzled as
 // in the prefill kernel; per-column online softmax in the log2 domain with a lazily raised
@@ -41,8 +44,15 @@ constexpr int NEW_BYTES = NEW_ROWS * (DQK + DV) * 2;
 #define FP8_DEPTH 2
 #endif
 
-template <int NW, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
-__global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs a) {
+// CW column waves (32 query columns each) times KS key halves: with KS = 2 the waves of half kh
+// take keys 32 kh .. 32 kh + 31 of every tile with a softmax state of their own, merged at the end;
+// every wave then keeps half the score registers, and two waves share each SIMD.
+template <int CW, int KS, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
+__global__ __launch_bounds__(CW * KS * 64) __attribute__((amdgpu_waves_per_eu(KS))) void
+verify_tiles_kernel(const VerifyArgs a) {
+    constexpr int NW = CW * KS;
+    constexpr int KH_ROWS = BN / KS;               // keys of a tile per wave
+    constexpr int NB = KH_ROWS / 32;               // 32-key score blocks per wave
     constexpr int K_DMA = K_TILE / 1024 / NW;      // 1-KiB DMA instructions per wave per tile
     constexpr int V_DMA = V_TILE / 1024 / NW;
     constexpr int NST = FP8 ? 1 : STAGES;          // bf16 tile stages
@@ -52,13 +62,14 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cw = wave % CW, kh = wave / CW;      // column wave, key half (scalar)
     const int l32 = lane & 31, g = lane >> 5;
     const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int Hq = a.Hq, T = a.T, TP = a.TP;
     const int G = Hq / a.Hkv;
 
     // this lane's column: query head kvh * G + hl, token t
-    const int col = wave * 32 + l32;
+    const int col = cw * 32 + l32;
     const int hl = col / TP, t = col - hl * TP;
     const bool col_ok = hl < G && t < T;
     const int h = kvh * G + min(hl, G - 1);
@@ -87,7 +98,7 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     const int W = a.window;
 
     if (!seq_ok) {   // defined result: zero output (a split combine writes the zeros itself)
-        if (!SPLIT && col_ok) {
+        if (!SPLIT && col_ok && kh == 0) {
             uint16_t* orow = a.out + (((int64_t)b * T + t) * Hq + h) * DV;
             for (int d = 4 * g; d < DV; d += 8) *(u32x2*)(orow + d) = u32x2{0u, 0u};
         }
@@ -270,9 +281,10 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
         asm volatile("" : "+v"(v_rd[db]));
     }
 
-    const float sink_l2 = (SINK && !SPLIT) ? a.sinks[h] * kLog2e : -INFINITY;
+    // (the sink joins the first key half's state)
+    const float sink_l2 = (SINK && !SPLIT && kh == 0) ? a.sinks[h] * kLog2e : -INFINITY;
     float m_run = sink_l2;
-    float l_run = (SINK && !SPLIT && g == 0) ? 1.0f : 0.0f;
+    float l_run = (SINK && !SPLIT && kh == 0 && g == 0) ? 1.0f : 0.0f;
     f32x16 O[DV / 32];
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db) O[db] = f32x16{};
@@ -282,54 +294,62 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     const unsigned lim = (unsigned)max(0, min(WINDOW ? W : 0x7fffffff, tc - jmin + 1));
     const int tc_first = shift, tc_last = T - 1 + shift;   // over the valid tokens
 
-    // products of tile tt, in bf16 stage ST of the LDS ring
+    // products of this wave's keys of tile tt, in bf16 stage ST of the LDS ring (the swizzles
+    // repeat every 16 rows, so a key half starts on the same pattern)
     auto tile_products = [&](int tt, int ST) {
-        const int j0 = (kt_lo + tt) * BN;
-        if (j0 > tc_last || (WINDOW && j0 + BN - 1 <= tc_first - W)) return;
-        const bool full = j0 >= jmin && j0 + BN - 1 <= tc_first && (!WINDOW || tc_last - j0 < W);
-        const uint8_t* kst = smem + ST * K_TILE;
-        const uint8_t* vst = smem + ST * V_TILE;   // + v_rd, which holds the V area's base
+        const int j0 = (kt_lo + tt) * BN + kh * KH_ROWS;   // this wave's first key row
+        if (j0 > tc_last || (WINDOW && j0 + KH_ROWS - 1 <= tc_first - W)) return;
+        const bool full =
+            j0 >= jmin && j0 + KH_ROWS - 1 <= tc_first && (!WINDOW || tc_last - j0 < W);
+        const uint8_t* kst = smem + ST * K_TILE + kh * KH_ROWS * DQK * 2;
+        // (+ v_rd, which holds the V area's base)
+        const uint8_t* vst = smem + ST * V_TILE + kh * KH_ROWS * DV * 2;
 
-        f32x16 S0 = f32x16{}, S1 = f32x16{};
+        f32x16 Sb[NB];
+#pragma unroll
+        for (int x = 0; x < NB; ++x) Sb[x] = f32x16{};
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const uint8_t* kp = kst + k_rd[c & 3] + (c >> 2) * 128;
-            const bf16x8 A0 = *(const bf16x8*)(kp);
-            const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
-            S0 = mfma32x32x16(A0, Qb[c], S0);
-            S1 = mfma32x32x16(A1, Qb[c], S1);
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+                Sb[x] = mfma32x32x16(*(const bf16x8*)(kp + x * 32 * DQK * 2), Qb[c], Sb[x]);
         }
         if constexpr (FP8) {
             // the score scale carries the key cache's scale: the new tokens' rows (positions at
             // or past the start, full-precision keys) are divided by it
-            if (j0 + BN > st) {
+            if (j0 + KH_ROWS > st) {
                 asm volatile("");
                 const float ik = 1.0f / a.code_k_scale;
                 const int rr = j0 + 4 * g - st;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = 8 * (i >> 2) + (i & 3);
-                    S0[i] *= rr + off >= 0 ? ik : 1.0f;
-                    S1[i] *= rr + off + 32 >= 0 ? ik : 1.0f;
-                }
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 8 * (i >> 2) + (i & 3) + 32 * x;
+                        Sb[x][i] *= rr + off >= 0 ? ik : 1.0f;
+                    }
             }
         }
         if (!full) {
             asm volatile("");
             const int d = tc - j0 - 4 * g;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                S0[i] = (unsigned)(d - off) < lim ? S0[i] : -INFINITY;
-                S1[i] = (unsigned)(d - off - 32) < lim ? S1[i] : -INFINITY;
-            }
-        }
-        float ma = fmaxf(S0[0], S1[0]), mb = fmaxf(S0[8], S1[8]);
+            for (int x = 0; x < NB; ++x)
 #pragma unroll
-        for (int i = 1; i < 8; ++i) {
-            ma = fmaxf(fmaxf(ma, S0[i]), S1[i]);
-            mb = fmaxf(fmaxf(mb, S0[i + 8]), S1[i + 8]);
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i >> 2) + (i & 3) + 32 * x;
+                    Sb[x][i] = (unsigned)(d - off) < lim ? Sb[x][i] : -INFINITY;
+                }
         }
+        float ma = Sb[0][0], mb = Sb[0][8];
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+#pragma unroll
+            for (int i = x == 0 ? 1 : 0; i < 8; ++i) {
+                ma = fmaxf(ma, Sb[x][i]);
+                mb = fmaxf(mb, Sb[x][i + 8]);
+            }
         const float mx = max_lane_pair32(fmaxf(ma, mb)) * sc;
         const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
         const float m_new = raise ? fmaxf(m_run, mx) : m_run;
@@ -342,40 +362,44 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
             for (int db = 0; db < DV / 32; ++db) O[db] *= alpha;
         }
         m_run = m_new;
-        float ps0 = 0.0f, ps1 = 0.0f;
+        float ps[NB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            S0[i] = fast_exp2(__builtin_fmaf(S0[i], sc, -m_use));
-            S1[i] = fast_exp2(__builtin_fmaf(S1[i], sc, -m_use));
-            ps0 += S0[i];
-            ps1 += S1[i];
+        for (int x = 0; x < NB; ++x) {
+            ps[x] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                Sb[x][i] = fast_exp2(__builtin_fmaf(Sb[x][i], sc, -m_use));
+                ps[x] += Sb[x][i];
+            }
         }
-        l_run += ps0 + ps1;
+#pragma unroll
+        for (int x = 0; x < NB; ++x) l_run += ps[x];
         if constexpr (FP8) {
             // the output scale carries the value cache's scale: the new tokens' weights are
             // divided by it (after the sum, which takes them as they are)
-            if (j0 + BN > st) {
+            if (j0 + KH_ROWS > st) {
                 asm volatile("");
                 const float iv = 1.0f / a.code_v_scale;
                 const int rr = j0 + 4 * g - st;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = 8 * (i >> 2) + (i & 3);
-                    S0[i] *= rr + off >= 0 ? iv : 1.0f;
-                    S1[i] *= rr + off + 32 >= 0 ? iv : 1.0f;
-                }
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 8 * (i >> 2) + (i & 3) + 32 * x;
+                        Sb[x][i] *= rr + off >= 0 ? iv : 1.0f;
+                    }
             }
         }
-        bf16x8 Pb[4];
+        bf16x8 Pb[2 * NB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const f32x16& Sx = (c >> 1) ? S1 : S0;
+        for (int c = 0; c < 2 * NB; ++c) {
+            const f32x16& Sx = Sb[c >> 1];
             const int o = 8 * (c & 1);
             Pb[c] = as_bf16x8(u32x4{pack_bf16x2(Sx[o], Sx[o + 1]), pack_bf16x2(Sx[o + 2], Sx[o + 3]),
                                     pack_bf16x2(Sx[o + 4], Sx[o + 5]), pack_bf16x2(Sx[o + 6], Sx[o + 7])});
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2 * NB; ++c) {
 #pragma unroll
             for (int db = 0; db < DV / 32; ++db) {
                 const uint8_t* vp = vst + v_rd[db] + 16 * c * (DV * 2);
@@ -391,7 +415,7 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     if constexpr (FP8) {
         // DEPTH tiles of codes in flight (one where the registers would not hold more: a single
         // wave, or 8 waves two to a SIMD); register set d holds tiles d, d + DEPTH, ...
-        constexpr int DEPTH = (NW == 1 || NW == 8) ? 1 : FP8_DEPTH;
+        constexpr int DEPTH = (NW <= 2 || (NW == 8 && KS == 1)) ? 1 : FP8_DEPTH;
         u32x4 cs[DEPTH][KU + VU];
         // Round r runs DEPTH steps: step d widens tile DEPTH * r + d from register set d (a
         // uniform branch skips it in round -1, which only loads) and loads the tile DEPTH later
@@ -426,9 +450,52 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
         }
     }
 
-    // ---- epilogue: partial record (split) or out = v_scale * O / l (bf16)
+    // ---- the key halves' states merged into the first half's waves, through LDS in two rounds
+    //      of two O blocks (lane-for-lane: the partner lane holds the same column and dims)
+    if constexpr (KS == 2) {
+        constexpr int XS = 36;   // floats per lane and round: 32 of O, then m and l
+        float* const xch = (float*)smem + (cw * 64 + lane) * XS;
+        float a0 = 1.0f, a1 = 0.0f;
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            block_sync_lds();   // every wave done with the tiles (round 1: with round 0's data)
+            if (kh == 1) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        *(f32x4*)(xch + 16 * q + 4 * v4) =
+                            f32x4{O[2 * rd + q][4 * v4], O[2 * rd + q][4 * v4 + 1],
+                                  O[2 * rd + q][4 * v4 + 2], O[2 * rd + q][4 * v4 + 3]};
+                if (rd == 0) *(float2*)(xch + 32) = make_float2(m_run, l_run);
+            }
+            block_sync_lds();
+            if (kh == 0) {
+                if (rd == 0) {
+                    const float2 ml = *(const float2*)(xch + 32);
+                    const float m = fmaxf(m_run, ml.x);
+                    const float ref = m == -INFINITY ? 0.0f : m;
+                    a0 = fast_exp2(m_run - ref);
+                    a1 = fast_exp2(ml.x - ref);
+                    l_run = l_run * a0 + ml.y * a1;
+                    m_run = m;
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        const f32x4 o1 = *(const f32x4*)(xch + 16 * q + 4 * v4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            O[2 * rd + q][4 * v4 + e] = O[2 * rd + q][4 * v4 + e] * a0 + o1[e] * a1;
+                    }
+            }
+        }
+    }
+
+    // ---- epilogue (first key half): partial record (split) or out = v_scale * O / l (bf16)
     const float lt = sum_lane_pair32(l_run);
-    if (!col_ok) return;
+    if (!col_ok || kh != 0) return;
     if (SPLIT) {
         float* rec = a.partial + ((((int64_t)b * T + t) * Hq + h) * a.nsplit + s) * PSTRIDE;
 #pragma unroll
@@ -457,28 +524,31 @@ __global__ __launch_bounds__(NW * 64) void verify_tiles_kernel(const VerifyArgs 
     }
 }
 
-template <int NW, bool WINDOW, bool SINK>
-hipError_t launch_nw(const VerifyArgs& a, hipStream_t st) {
-    const dim3 grid(a.nsplit, a.Hkv, a.B), block(NW * 64);
+template <int CW, bool WINDOW, bool SINK>
+hipError_t launch_cw(const VerifyArgs& a, hipStream_t st) {
+    constexpr int KS = CW <= 4 ? 2 : 1;   // (8 column waves take whole tiles: 1024 threads at most)
+    const dim3 grid(a.nsplit, a.Hkv, a.B), block(CW * KS * 64);
     if constexpr (!WINDOW) {
         if (a.code_k) {
-            if (a.nsplit > 1) verify_tiles_kernel<NW, false, SINK, true, true><<<grid, block, 0, st>>>(a);
-            else verify_tiles_kernel<NW, false, SINK, false, true><<<grid, block, 0, st>>>(a);
+            if (a.nsplit > 1)
+                verify_tiles_kernel<CW, KS, false, SINK, true, true><<<grid, block, 0, st>>>(a);
+            else
+                verify_tiles_kernel<CW, KS, false, SINK, false, true><<<grid, block, 0, st>>>(a);
             return hipGetLastError();
         }
     }
-    if (a.nsplit > 1) verify_tiles_kernel<NW, WINDOW, SINK, true, false><<<grid, block, 0, st>>>(a);
-    else verify_tiles_kernel<NW, WINDOW, SINK, false, false><<<grid, block, 0, st>>>(a);
+    if (a.nsplit > 1) verify_tiles_kernel<CW, KS, WINDOW, SINK, true, false><<<grid, block, 0, st>>>(a);
+    else verify_tiles_kernel<CW, KS, WINDOW, SINK, false, false><<<grid, block, 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <bool WINDOW, bool SINK>
 hipError_t launch_ws(const VerifyArgs& a, int nw, hipStream_t st) {
     switch (nw) {
-        case 1: return launch_nw<1, WINDOW, SINK>(a, st);
-        case 2: return launch_nw<2, WINDOW, SINK>(a, st);
-        case 4: return launch_nw<4, WINDOW, SINK>(a, st);
-        default: return launch_nw<8, WINDOW, SINK>(a, st);
+        case 1: return launch_cw<1, WINDOW, SINK>(a, st);
+        case 2: return launch_cw<2, WINDOW, SINK>(a, st);
+        case 4: return launch_cw<4, WINDOW, SINK>(a, st);
+        default: return launch_cw<8, WINDOW, SINK>(a, st);
     }
 }
 
