@@ -44,12 +44,17 @@ constexpr int NEW_BYTES = NEW_ROWS * (DQK + DV) * 2;
 #define FP8_DEPTH 2
 #endif
 
-// CW column waves (32 query columns each) times KS key halves: with KS = 2 the waves of half kh
-// take keys 32 kh .. 32 kh + 31 of every tile with a softmax state of their own, merged at the end;
-// every wave then keeps half the score registers, and two waves share each SIMD.
-template <int CW, int KS, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
-__global__ __launch_bounds__(CW * KS * 64) __attribute__((amdgpu_waves_per_eu(KS))) void
+// CW column waves of CWD query columns each, times KS key halves: with KS = 2 the waves of half
+// kh take keys 32 kh .. 32 kh + 31 of every tile with a softmax state of their own, merged at the
+// end.  CWD = 32: 32x32x16 products (a wave's scores are one 32-key x 32-column block per half);
+// CWD = 16: 16x16x32 products on the operand layout of the 16-row sliding prefill kernel (two
+// 16-key blocks x 16 columns per half), about half the registers and twice the waves.
+template <int CWD, int CW, int KS, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
+__global__ __launch_bounds__(CW * KS * 64) __attribute__((amdgpu_waves_per_eu(CWD == 16 ? 2 : KS))) void
 verify_tiles_kernel(const VerifyArgs a) {
+    constexpr bool M16 = CWD == 16;
+    constexpr int QC = M16 ? DQK / 32 : KCH;       // Q^T operand chunks of QSTEP dims
+    constexpr int QSTEP = M16 ? 32 : 16;
     constexpr int NW = CW * KS;
     constexpr int KH_ROWS = BN / KS;               // keys of a tile per wave
     constexpr int NB = KH_ROWS / 32;               // 32-key score blocks per wave
@@ -64,12 +69,15 @@ verify_tiles_kernel(const VerifyArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cw = wave % CW, kh = wave / CW;      // column wave, key half (scalar)
     const int l32 = lane & 31, g = lane >> 5;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int lc = M16 ? l16 : l32;                // this lane's column within its wave
+    const int lsub = M16 ? gq : g;                 // its 8-dim slot of a Q^T chunk
     const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int Hq = a.Hq, T = a.T, TP = a.TP;
     const int G = Hq / a.Hkv;
 
     // this lane's column: query head kvh * G + hl, token t
-    const int col = cw * 32 + l32;
+    const int col = cw * CWD + lc;
     const int hl = col / TP, t = col - hl * TP;
     const bool col_ok = hl < G && t < T;
     const int h = kvh * G + min(hl, G - 1);
@@ -79,12 +87,12 @@ verify_tiles_kernel(const VerifyArgs a) {
     // not depend on the start position, which then comes by a scalar load that leaves them in flight
     const uint16_t* qrow = a.q + (((int64_t)b * T + tq) * Hq + h) * DQK;
     const int r = a.rope_dims, half = r >> 1;
-    u32x4 qw[KCH], pw[KCH];
+    u32x4 qw[QC], pw[QC];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) qw[c] = *(const u32x4*)(qrow + 16 * c + 8 * g);
+    for (int c = 0; c < QC; ++c) qw[c] = *(const u32x4*)(qrow + QSTEP * c + 8 * lsub);
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-        const int d0 = 16 * c + 8 * g;
+    for (int c = 0; c < QC; ++c) {
+        const int d0 = QSTEP * c + 8 * lsub;
         if (d0 < r) pw[c] = *(const u32x4*)(qrow + (d0 < half ? d0 + half : d0 - half));
     }
 
@@ -100,7 +108,7 @@ verify_tiles_kernel(const VerifyArgs a) {
     if (!seq_ok) {   // defined result: zero output (a split combine writes the zeros itself)
         if (!SPLIT && col_ok && kh == 0) {
             uint16_t* orow = a.out + (((int64_t)b * T + t) * Hq + h) * DV;
-            for (int d = 4 * g; d < DV; d += 8) *(u32x2*)(orow + d) = u32x2{0u, 0u};
+            for (int d = 4 * lsub; d < DV; d += 4 * (64 / CWD)) *(u32x2*)(orow + d) = u32x2{0u, 0u};
         }
         return;
     }
@@ -240,12 +248,12 @@ verify_tiles_kernel(const VerifyArgs a) {
     };
 
     // ---- Q^T operands of this column, rotated at the token's position, in registers
-    bf16x8 Qb[KCH];
+    bf16x8 Qb[QC];
     {
         const int32_t pos = st + tq;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int d0 = 16 * c + 8 * g;
+        for (int c = 0; c < QC; ++c) {
+            const int d0 = QSTEP * c + 8 * lsub;
             if (d0 < r) {
                 const bool lower = d0 < half;
                 float x[8], y[8];
@@ -265,29 +273,47 @@ verify_tiles_kernel(const VerifyArgs a) {
         }
     }
 
-    // ---- per-lane LDS read offsets (bytes, within a stage), as in the prefill kernel
-    const int swz = (l32 >> 1) & 7;
-    int k_rd[4];
+    // ---- per-lane LDS read offsets (bytes, within a stage), as in the prefill kernels
+    int k_rd[M16 ? QC : 4], v_rd[M16 ? DV / 16 : 4];
+    if constexpr (M16) {
+        // K: key l16 of a 16-key block, chunk 4c + gq; V^T: rows 4gq + l16 / 4 (and + 16), dims
+        // 16db + 4(l16 % 4)
 #pragma unroll
-    for (int x = 0; x < 4; ++x) k_rd[x] = l32 * (DQK * 2) + 16 * ((2 * x + g) ^ swz);
-    const int qsel = lane >> 4, jsel = lane & 15;
-    const int vrow = 4 * (qsel >> 1) + (jsel >> 2);
-    int v_rd[4];
+        for (int c = 0; c < QC; ++c)
+            k_rd[c] = l16 * (DQK * 2) + 16 * ((4 * c + gq) ^ ((l16 >> 1) & 7));
+        const int vrow = 4 * gq + (l16 >> 2);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        v_rd[db] = NST * K_TILE + vrow * (DV * 2) +
-                   16 * (4 * (db ^ ((jsel >> 2) & 3)) + 2 * (qsel & 1) + ((jsel & 3) >> 1)) +
-                   8 * (jsel & 1);
-        asm volatile("" : "+v"(v_rd[db]));
+        for (int db = 0; db < DV / 16; ++db) {
+            const int byte = (db * 16 + 4 * (l16 & 3)) * 2;
+            v_rd[db] = NST * K_TILE + vrow * (DV * 2) + 16 * ((byte >> 4) ^ ((vrow & 3) << 2)) +
+                       (byte & 15);
+            asm volatile("" : "+v"(v_rd[db]));
+        }
+    } else {
+        const int swz = (l32 >> 1) & 7;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) k_rd[x] = l32 * (DQK * 2) + 16 * ((2 * x + g) ^ swz);
+        const int qsel = lane >> 4, jsel = lane & 15;
+        const int vrow = 4 * (qsel >> 1) + (jsel >> 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            v_rd[db] = NST * K_TILE + vrow * (DV * 2) +
+                       16 * (4 * (db ^ ((jsel >> 2) & 3)) + 2 * (qsel & 1) + ((jsel & 3) >> 1)) +
+                       8 * (jsel & 1);
+            asm volatile("" : "+v"(v_rd[db]));
+        }
     }
 
     // (the sink joins the first key half's state)
     const float sink_l2 = (SINK && !SPLIT && kh == 0) ? a.sinks[h] * kLog2e : -INFINITY;
     float m_run = sink_l2;
-    float l_run = (SINK && !SPLIT && kh == 0 && g == 0) ? 1.0f : 0.0f;
-    f32x16 O[DV / 32];
+    float l_run = (SINK && !SPLIT && kh == 0 && lsub == 0) ? 1.0f : 0.0f;
+    f32x16 O[DV / 32];     // CWD = 32: lane (column l32, half g) holds dims 32db + 8(i / 4) + 4g + i % 4
+    f32x4 O16[DV / 16];    // CWD = 16: lane (column l16, group gq) holds dims 16db + 4gq + i
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db) O[db] = f32x16{};
+#pragma unroll
+    for (int db = 0; db < DV / 16; ++db) O16[db] = f32x4{};
     const float sc = a.score_scale_log2;
     // column (token tc = t + shift in row coordinates) sees row j iff tc - j lies in [0, lim)
     const int tc = t + shift;
@@ -304,6 +330,88 @@ verify_tiles_kernel(const VerifyArgs a) {
         const uint8_t* kst = smem + ST * K_TILE + kh * KH_ROWS * DQK * 2;
         // (+ v_rd, which holds the V area's base)
         const uint8_t* vst = smem + ST * V_TILE + kh * KH_ROWS * DV * 2;
+
+        if constexpr (M16) {
+            // S^T blocks kb (keys j0 + 16kb + 4gq + i against column l16)
+            f32x4 Sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x4 acc = f32x4{};
+#pragma unroll
+                for (int c = 0; c < QC; ++c)
+                    acc = mfma16x16x32(*(const bf16x8*)(kst + k_rd[c] + kb * 16 * (DQK * 2)), Qb[c], acc);
+                Sacc[kb] = acc;
+            }
+            const int rr = j0 + 4 * gq - st;   // (fp8: key offsets at or past the start are new rows)
+            if constexpr (FP8) {
+                if (j0 + KH_ROWS > st) {
+                    asm volatile("");
+                    const float ik = 1.0f / a.code_k_scale;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Sacc[kb][i] *= rr + 16 * kb + i >= 0 ? ik : 1.0f;
+                }
+            }
+            if (!full) {
+                asm volatile("");
+                const int d = tc - j0 - 4 * gq;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Sacc[kb][i] = (unsigned)(d - 16 * kb - i) < lim ? Sacc[kb][i] : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(Sacc[0][0], Sacc[0][1]), fmaxf(Sacc[0][2], Sacc[0][3])),
+                             fmaxf(fmaxf(Sacc[1][0], Sacc[1][1]), fmaxf(Sacc[1][2], Sacc[1][3])));
+            mx = max_lane_pair32(max_lane_pair16(mx)) * sc;
+            const bool raise = mx > m_run + kRescaleLog2 || m_run == -INFINITY;
+            const float m_new = raise ? fmaxf(m_run, mx) : m_run;
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+            if (__any(raise)) {
+                asm volatile("");
+                const float alpha = fast_exp2(m_run - m_use);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DV / 16; ++db) O16[db] *= alpha;
+            }
+            m_run = m_new;
+            float ps = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Sacc[kb][i] = fast_exp2(__builtin_fmaf(Sacc[kb][i], sc, -m_use));
+                    ps += Sacc[kb][i];
+                }
+            l_run += ps;
+            if constexpr (FP8) {
+                if (j0 + KH_ROWS > st) {
+                    asm volatile("");
+                    const float iv = 1.0f / a.code_v_scale;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Sacc[kb][i] *= rr + 16 * kb + i >= 0 ? iv : 1.0f;
+                }
+            }
+            // P^T: k-slot i of group gq is key 4gq + i (i < 4) or 16 + 4gq + (i - 4), as the
+            // transposed V reads below hand out V's rows
+            const bf16x8 Pb = as_bf16x8(u32x4{pack_bf16x2(Sacc[0][0], Sacc[0][1]),
+                                              pack_bf16x2(Sacc[0][2], Sacc[0][3]),
+                                              pack_bf16x2(Sacc[1][0], Sacc[1][1]),
+                                              pack_bf16x2(Sacc[1][2], Sacc[1][3])});
+#pragma unroll
+            for (int db = 0; db < DV / 16; ++db) {
+                const uint8_t* vp = vst + v_rd[db];
+                const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+                const bf16x4 v1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 16 * DV * 2));
+                O16[db] = mfma16x16x32(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), Pb,
+                                       O16[db]);
+            }
+            return;
+        }
 
         f32x16 Sb[NB];
 #pragma unroll
@@ -454,19 +562,37 @@ verify_tiles_kernel(const VerifyArgs a) {
     //      of two O blocks (lane-for-lane: the partner lane holds the same column and dims)
     if constexpr (KS == 2) {
         constexpr int XS = 36;   // floats per lane and round: 32 of O, then m and l
+        constexpr int ROUNDS = M16 ? 1 : 2;
         float* const xch = (float*)smem + (cw * 64 + lane) * XS;
         float a0 = 1.0f, a1 = 0.0f;
+        // the 32 floats of O that round rd moves: f32x4 number q4 (0..7)
+        auto get4 = [&](int rd, int q4) -> f32x4 {
+            if constexpr (M16) {
+                return O16[q4];
+            } else {
+                const f32x16& o = O[2 * rd + (q4 >> 2)];
+                const int e = 4 * (q4 & 3);
+                return f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+            }
+        };
+        auto set4 = [&](int rd, int q4, const f32x4& v) {
+            if constexpr (M16) {
+                O16[q4] = v;
+            } else {
+                f32x16& o = O[2 * rd + (q4 >> 2)];
+                const int e = 4 * (q4 & 3);
+                o[e] = v[0];
+                o[e + 1] = v[1];
+                o[e + 2] = v[2];
+                o[e + 3] = v[3];
+            }
+        };
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
+        for (int rd = 0; rd < ROUNDS; ++rd) {
             block_sync_lds();   // every wave done with the tiles (round 1: with round 0's data)
             if (kh == 1) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4)
-                        *(f32x4*)(xch + 16 * q + 4 * v4) =
-                            f32x4{O[2 * rd + q][4 * v4], O[2 * rd + q][4 * v4 + 1],
-                                  O[2 * rd + q][4 * v4 + 2], O[2 * rd + q][4 * v4 + 3]};
+                for (int q4 = 0; q4 < 8; ++q4) *(f32x4*)(xch + 4 * q4) = get4(rd, q4);
                 if (rd == 0) *(float2*)(xch + 32) = make_float2(m_run, l_run);
             }
             block_sync_lds();
@@ -481,21 +607,36 @@ verify_tiles_kernel(const VerifyArgs a) {
                     m_run = m;
                 }
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4) {
-                        const f32x4 o1 = *(const f32x4*)(xch + 16 * q + 4 * v4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            O[2 * rd + q][4 * v4 + e] = O[2 * rd + q][4 * v4 + e] * a0 + o1[e] * a1;
-                    }
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    const f32x4 o1 = *(const f32x4*)(xch + 4 * q4);
+                    const f32x4 o0 = get4(rd, q4);
+                    set4(rd, q4, f32x4{o0[0] * a0 + o1[0] * a1, o0[1] * a0 + o1[1] * a1,
+                                       o0[2] * a0 + o1[2] * a1, o0[3] * a0 + o1[3] * a1});
+                }
             }
         }
     }
 
     // ---- epilogue (first key half): partial record (split) or out = v_scale * O / l (bf16)
-    const float lt = sum_lane_pair32(l_run);
+    const float lt = M16 ? sum_lane_pair32(sum_lane_pair16(l_run)) : sum_lane_pair32(l_run);
     if (!col_ok || kh != 0) return;
+    if constexpr (M16) {
+        if (SPLIT) {
+            float* rec = a.partial + ((((int64_t)b * T + t) * Hq + h) * a.nsplit + s) * PSTRIDE;
+#pragma unroll
+            for (int db = 0; db < DV / 16; ++db) *(f32x4*)(rec + 16 * db + 4 * gq) = O16[db];
+            if (gq == 0) *(float2*)(rec + DV) = make_float2(m_run, lt);
+        } else {
+            const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+            uint16_t* orow = a.out + (((int64_t)b * T + t) * Hq + h) * DV;
+#pragma unroll
+            for (int db = 0; db < DV / 16; ++db)
+                *(u32x2*)(orow + 16 * db + 4 * gq) =
+                    u32x2{pack_bf16x2(O16[db][0] * inv, O16[db][1] * inv),
+                          pack_bf16x2(O16[db][2] * inv, O16[db][3] * inv)};
+        }
+        return;
+    }
     if (SPLIT) {
         float* rec = a.partial + ((((int64_t)b * T + t) * Hq + h) * a.nsplit + s) * PSTRIDE;
 #pragma unroll
@@ -524,31 +665,39 @@ verify_tiles_kernel(const VerifyArgs a) {
     }
 }
 
-template <int CW, bool WINDOW, bool SINK>
+template <int CWD, int CW, bool WINDOW, bool SINK>
 hipError_t launch_cw(const VerifyArgs& a, hipStream_t st) {
-    constexpr int KS = CW <= 4 ? 2 : 1;   // (8 column waves take whole tiles: 1024 threads at most)
+    // (32-column waves: 8 column waves take whole tiles, 1024 threads at most)
+    constexpr int KS = (CWD == 16 || CW <= 4) ? 2 : 1;
     const dim3 grid(a.nsplit, a.Hkv, a.B), block(CW * KS * 64);
     if constexpr (!WINDOW) {
         if (a.code_k) {
             if (a.nsplit > 1)
-                verify_tiles_kernel<CW, KS, false, SINK, true, true><<<grid, block, 0, st>>>(a);
+                verify_tiles_kernel<CWD, CW, KS, false, SINK, true, true><<<grid, block, 0, st>>>(a);
             else
-                verify_tiles_kernel<CW, KS, false, SINK, false, true><<<grid, block, 0, st>>>(a);
+                verify_tiles_kernel<CWD, CW, KS, false, SINK, false, true><<<grid, block, 0, st>>>(a);
             return hipGetLastError();
         }
     }
-    if (a.nsplit > 1) verify_tiles_kernel<CW, KS, WINDOW, SINK, true, false><<<grid, block, 0, st>>>(a);
-    else verify_tiles_kernel<CW, KS, WINDOW, SINK, false, false><<<grid, block, 0, st>>>(a);
+    if (a.nsplit > 1)
+        verify_tiles_kernel<CWD, CW, KS, WINDOW, SINK, true, false><<<grid, block, 0, st>>>(a);
+    else
+        verify_tiles_kernel<CWD, CW, KS, WINDOW, SINK, false, false><<<grid, block, 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <bool WINDOW, bool SINK>
 hipError_t launch_ws(const VerifyArgs& a, int nw, hipStream_t st) {
     switch (nw) {
-        case 1: return launch_cw<1, WINDOW, SINK>(a, st);
-        case 2: return launch_cw<2, WINDOW, SINK>(a, st);
-        case 4: return launch_cw<4, WINDOW, SINK>(a, st);
-        default: return launch_cw<8, WINDOW, SINK>(a, st);
+        // up to 16 columns one twinned 16-column wave pair (B64, one token per sequence after
+        // 1024-32768 fp8 positions: 0.50 ms against 0.73 on 32-column waves; at 64 columns the
+        // 16-column layout was slower over fp8 caches, its 160 registers leaving one workgroup
+        // per CU, and no faster over bf16 ones)
+        case 1: return (a.Hq / a.Hkv) * a.TP <= 16 ? launch_cw<16, 1, WINDOW, SINK>(a, st)
+                                                   : launch_cw<32, 1, WINDOW, SINK>(a, st);
+        case 2: return launch_cw<32, 2, WINDOW, SINK>(a, st);
+        case 4: return launch_cw<32, 4, WINDOW, SINK>(a, st);
+        default: return launch_cw<32, 8, WINDOW, SINK>(a, st);
     }
 }
 
