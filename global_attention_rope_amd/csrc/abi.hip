@@ -224,13 +224,20 @@ bool verify_tokens(const mimo_attn_params* p, int32_t S) {
 // Multi-token extend: key rows of the longest query — global: positions 0..max_start + S - 1
 // of the cache; sliding: the W + S rows of the workspace (never split up to 1024 rows).
 // Splits of whole 64-row tiles: enough (sequence, KV head, split) workgroups to fill the chip
-// once (two resident per CU; more rounds only add partials for the combine to merge), at least
-// 256 rows each.
+// once (two resident per CU), at least 256 rows each, and at most kVerifyMaxSplitRows rows each:
+// the tile kernel's grid is split-major, so with mixed lengths the workgroups that start last
+// are the longest sequences' last splits, and no workgroup runs much longer than the others (B64,
+// 4 tokens after 1024-32768 positions, fp8 cache: 0.54 ms with two splits of 16384 rows, 0.455
+// with splits of 4096; 2048- and 8192-row splits lost at this batch).
+constexpr int64_t kVerifyMaxSplitRows = 4096;
+
 SplitGeometry verify_geometry(const mimo_attn_params* p, int32_t S, int32_t max_start) {
     const bool swa = p->layer_kind == MIMO_LAYER_SWA;
     const int64_t n_max = swa ? (int64_t)p->window + S : (int64_t)max_start + S;
     const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
     int64_t ns = (512 + pairs - 1) / pairs;
+    if (ns < (n_max + kVerifyMaxSplitRows - 1) / kVerifyMaxSplitRows)
+        ns = (n_max + kVerifyMaxSplitRows - 1) / kVerifyMaxSplitRows;
     if (ns > (n_max + 255) / 256) ns = (n_max + 255) / 256;
     if (ns > mimo::decode_max_splits()) ns = mimo::decode_max_splits();
     if (ns < 1) ns = 1;

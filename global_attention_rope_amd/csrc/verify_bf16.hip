@@ -72,7 +72,9 @@ verify_tiles_kernel(const VerifyArgs a) {
     const int l16 = lane & 15, gq = lane >> 4;
     const int lc = M16 ? l16 : l32;                // this lane's column within its wave
     const int lsub = M16 ? gq : g;                 // its 8-dim slot of a Q^T chunk
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    // (split-major grid: the dispatcher hands out every sequence's first split before any second
+    //  one, so the last workgroups to start are the longest sequences' last splits)
+    const int kvh = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
     const int Hq = a.Hq, T = a.T, TP = a.TP;
     const int G = Hq / a.Hkv;
 
@@ -669,7 +671,7 @@ template <int CWD, int CW, bool WINDOW, bool SINK>
 hipError_t launch_cw(const VerifyArgs& a, hipStream_t st) {
     // (32-column waves: 8 column waves take whole tiles, 1024 threads at most)
     constexpr int KS = (CWD == 16 || CW <= 4) ? 2 : 1;
-    const dim3 grid(a.nsplit, a.Hkv, a.B), block(CW * KS * 64);
+    const dim3 grid(a.Hkv, a.B, a.nsplit), block(CW * KS * 64);
     if constexpr (!WINDOW) {
         if (a.code_k) {
             if (a.nsplit > 1)

@@ -143,8 +143,10 @@ def test_workspace_sizes():
     assert mimo.extend_workspace_size(_swa(), 4, -1) == 0
     # a few new tokens: the multi-token tile kernel, split partials for long global caches
     assert mimo.extend_workspace_size(_ga(batch=2), 4, 100) == 0
-    ws = mimo.extend_workspace_size(_ga(batch=64), 4, 32768)
-    assert ws > 0 and ws % (64 * 4 * 64 * 130 * 4) == 0
+    # 64 sequences x 4 KV heads fill the chip's two workgroups per CU at 2 splits; splits are at
+    # most 4096 rows, so 32772 key rows take 9 (of 3648 rows)
+    assert mimo.extend_workspace_size(_ga(batch=64), 4, 32768) == 64 * 4 * 64 * 9 * 130 * 4
+    assert mimo.extend_workspace_size(_ga(batch=64), 4, 4092) == 64 * 4 * 64 * 2 * 130 * 4
     rows = 8 * (128 + 4) * (192 + 128) * 2
     assert mimo.extend_workspace_size(_swa(), 4, 30000) == (rows + 255) // 256 * 256
     # one sequence, 4 KV heads, 4 tokens after 30000 positions: 30004 key rows in 256-row splits,
