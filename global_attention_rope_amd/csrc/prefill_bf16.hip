@@ -60,6 +60,9 @@ constexpr int KCH = DQK / 16;
 constexpr int GA_WAVES = 8, GA_STAGES = 3;
 constexpr int SW_WAVES = 4, SW_STAGES = 2;
 constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyond 2^8
+// a lane's 32 weights of a tile summing past this (or overflowing) move its row's reference; below
+// it every weight is at most 2^16, so O (f32) holds any row length a tile count reaches
+constexpr float kSumLimit = 65536.0f;
 
 
 // Rotate the pairs (lo[t], hi[t]) at pos and return the chunk this lane keeps (lo when `lower`),
@@ -322,43 +325,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const uint8_t* vst = smem + ST * V_TILE;   // + v_rd, which holds the V area's base
 
         f32x16 S0, S1;
+        // the tile's scores minus the rows' references, masked outside each row's visible keys
+        auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const uint8_t* kp = kst + k_rd[c & 3] + (c >> 2) * 128;
-            const bf16x8 A0 = *(const bf16x8*)(kp);
-            const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
-            S0 = mfma32x32x16(A0, Qb[c], c == 0 ? negm : S0);
-            S1 = mfma32x32x16(A1, Qb[c], c == 0 ? negm : S1);
-        }
-        if (!full) {
-            // (the empty asm keeps the compiler from if-converting this uniform branch, which
-            //  would run the masking on every tile)
-            asm volatile("");
-            // key j0 + 8(i/4) + 4g + i%4 (+32 in block 1) against row q_l: visible iff the
-            // unsigned difference d - off is below the row's limit
-            const int d = q_l + shift - j0 - 4 * g;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                S0[i] = (unsigned)(d - off) < lim ? S0[i] : -INFINITY;
-                S1[i] = (unsigned)(d - off - 32) < lim ? S1[i] : -INFINITY;
+            for (int c = 0; c < KCH; ++c) {
+                const uint8_t* kp = kst + k_rd[c & 3] + (c >> 2) * 128;
+                const bf16x8 A0 = *(const bf16x8*)(kp);
+                const bf16x8 A1 = *(const bf16x8*)(kp + 32 * DQK * 2);
+                S0 = mfma32x32x16(A0, Qb[c], c == 0 ? negm : S0);
+                S1 = mfma32x32x16(A1, Qb[c], c == 0 ? negm : S1);
             }
-        }
-        // row maximum: two chains of 3-input maxima
-        float ma = fmaxf(S0[0], S1[0]), mb = fmaxf(S0[8], S1[8]);
+            if (!full) {
+                // (the empty asm keeps the compiler from if-converting this uniform branch, which
+                //  would run the masking on every tile)
+                asm volatile("");
+                // key j0 + 8(i/4) + 4g + i%4 (+32 in block 1) against row q_l: visible iff the
+                // unsigned difference d - off is below the row's limit
+                const int d = q_l + shift - j0 - 4 * g;
 #pragma unroll
-        for (int i = 1; i < 8; ++i) {
-            ma = fmaxf(fmaxf(ma, S0[i]), S1[i]);
-            mb = fmaxf(fmaxf(mb, S0[i + 8]), S1[i + 8]);
-        }
-        const float mx = max_lane_pair32(fmaxf(ma, mb));   // relative to m_ref
-        // lazily raised reference maximum: moved to the row's maximum on its first visible key,
-        // later only when a tile exceeds it by more than 2^kRescaleLog2; the tile's scores, the
-        // sum and O follow the move
-        const bool first = m_run == -INFINITY;
-        const bool raise = mx > kRescaleLog2 || (first && mx != -INFINITY);
-        if (__any(raise)) {
-            asm volatile("");   // rare: keep it a branch (see above)
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i >> 2) + (i & 3);
+                    S0[i] = (unsigned)(d - off) < lim ? S0[i] : -INFINITY;
+                    S1[i] = (unsigned)(d - off - 32) < lim ? S1[i] : -INFINITY;
+                }
+            }
+        };
+        // the reference moves to the row's maximum on its first visible key, later when a tile
+        // exceeds it by more than 2^kRescaleLog2; the tile's scores, the sum and O follow the move
+        auto rebase = [&]() __attribute__((always_inline)) {
+            float ma = fmaxf(S0[0], S1[0]), mb = fmaxf(S0[8], S1[8]);
+#pragma unroll
+            for (int i = 1; i < 8; ++i) {
+                ma = fmaxf(fmaxf(ma, S0[i]), S1[i]);
+                mb = fmaxf(fmaxf(mb, S0[i + 8]), S1[i + 8]);
+            }
+            const float mx = max_lane_pair32(fmaxf(ma, mb));   // relative to the reference
+            const bool first = m_run == -INFINITY;
+            const bool raise = mx > kRescaleLog2 || (first && mx != -INFINITY);
             const float ref = -negm[0];
             const float shift = raise ? mx : 0.0f;
             const float alpha = first ? 1.0f : fast_exp2(-shift);
@@ -372,14 +375,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                 negm[i] = -(ref + shift);
             }
             if (raise) m_run = ref + shift;
-        }
-        float ps0 = 0.0f, ps1 = 0.0f;
+        };
+        float ps0, ps1;
+        auto weights = [&]() __attribute__((always_inline)) {
+            ps0 = ps1 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            S0[i] = fast_exp2(S0[i]);
-            S1[i] = fast_exp2(S1[i]);
-            ps0 += S0[i];
-            ps1 += S1[i];
+            for (int i = 0; i < 16; ++i) {
+                S0[i] = fast_exp2(S0[i]);
+                S1[i] = fast_exp2(S1[i]);
+                ps0 += S0[i];
+                ps1 += S1[i];
+            }
+        };
+        // No row maximum on the common path: the weights come straight from the scores, and a
+        // row whose scores outgrew its reference shows in its lanes' sums of weights (above
+        // 2^kSumLog2, or infinite).  Only then (and on a row's first visible keys) are the tile's
+        // scores computed again, still in LDS, and the reference moved to the maximum.
+        scores();
+        if (__any(m_run == -INFINITY)) {
+            asm volatile("");   // a row's first keys (uniform branch)
+            rebase();
+        }
+        weights();
+        if (__any(ps0 + ps1 > kSumLimit)) {
+            asm volatile("");   // rare (uniform branch)
+            scores();
+            rebase();
+            weights();
         }
         l_run += ps0 + ps1;
 
