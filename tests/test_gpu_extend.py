@@ -67,6 +67,7 @@ CASES = [
     dict(kind=1, B=3, S=4, Hq=16, Hkv=2, sinks=True, starts=[0, 2, 1000]),       # start < W
     dict(kind=1, B=2, S=16, Hq=8, Hkv=1, sinks=True, starts=[126, 131], W=128),
     dict(kind=1, B=2, S=7, Hq=8, Hkv=8, sinks=False, starts=[0, 9], W=1),
+    dict(kind=1, B=2, S=3, Hq=8, Hkv=2, sinks=True, starts=[0, 500]),          # 16 columns, 1 split
     dict(kind=0, B=3, S=2, Hq=16, Hkv=1, sinks=False, starts=[0, 255, 4097]),
     dict(kind=0, B=2, S=16, Hq=8, Hkv=2, sinks=True, starts=[1, 700]),
     dict(kind=0, B=1, S=5, Hq=64, Hkv=4, sinks=False, starts=[20000]),           # split partials

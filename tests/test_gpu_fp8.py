@@ -281,6 +281,7 @@ EXT_CASES = [
     dict(kind=0, B=2, S=12, Hq=32, Hkv=2, sinks=False, starts=[3, 2500]),
     dict(kind=0, B=2, S=7, Hq=32, Hkv=2, sinks=True, starts=[0, 1300]),
     dict(kind=0, B=2, S=1, Hq=8, Hkv=2, sinks=False, starts=[64, 333]),
+    dict(kind=0, B=2, S=2, Hq=8, Hkv=2, sinks=True, starts=[100, 3000]),       # 8 columns, 12 splits
     dict(kind=1, B=2, S=300, Hq=8, Hkv=2, sinks=True, starts=[5, 4000]),       # ring, S > W
     dict(kind=1, B=3, S=4, Hq=16, Hkv=2, sinks=True, starts=[0, 2, 1000]),     # ring, tile kernel
 ]

@@ -159,6 +159,32 @@ def test_prefill_writes_caches(kind):
         assert all((kc_h[b, :, sl] == 7.0).all() and (vc_h[b, :, sl] == 7.0).all() for sl in untouched)
 
 
+@pytest.mark.parametrize("kind,Hq,Hkv", [(0, 16, 2), (1, 8, 8), (1, 16, 2)])
+def test_prefill_late_keys_outgrow_the_reference(kind, Hq, Hkv, monkeypatch):
+    """Keys past the first 64-key tile scaled by 16 (exact in bf16): a row's later scores exceed
+    its first tile's maximum by tens of binary orders, so the reference each row took on its first
+    keys must move mid-row (the global kernel and the sliding one for GQA groups that are not a
+    multiple of 4 find this from the weights' sums and compute the tile's scores again; the
+    16-row sliding kernel from its row maxima).  Scores this large and this peaked turn the bf16
+    rounding of the operands into output errors of ~0.2 (ideal bf16 arithmetic, the rounding
+    model, lands on the same values), past the fixed 1e-2 bound: every row gets the derived bound."""
+    monkeypatch.setattr(rounding_model, "BOUND_MAX_KEYS", 512)
+    w = _wl(kind=kind, B=1, S=300, Hq=Hq, Hkv=Hkv, sinks=kind == 1, W=200)
+    _note(f"late keys x16 kind={kind} Hq={Hq} Hkv={Hkv}")
+    q, k, v, s = synth.layer_inputs(w, 4100 + kind, device=DEV)
+    k = k.clone()
+    k[:, 64:] *= 16.0
+    sp = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = mimo.prefill(_params(w), q, k, v, sp, sinks=s)
+    torch.cuda.synchronize()
+    pos = np.arange(w.seq, dtype=np.int32)[None]
+    ref = oracle.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s))
+    assert np.isfinite(to_np64(out)).all()
+    assert_close(out, ref, what="late keys", bound=prefill_bound_for(w, q, k, v, s, pos))
+    model = rounding_model.prefill(_oparams(w), _f32(q), _f32(k), _f32(v), pos, _f32(s))
+    assert_near_model(out, ref, model, what="late keys")
+
+
 def test_prefill_deterministic():
     w = _wl(kind=0, B=1, S=500, Hq=16, Hkv=1, sinks=False)
     q, k, v, s = synth.layer_inputs(w, 4000, device=DEV)
