@@ -9,8 +9,9 @@
 // feeds all heads and tokens.  Up to 128 columns, each column wave is doubled: one wave takes the
 // first 32 keys of every tile, its twin the last 32, each with a softmax state of its own, merged
 // through LDS at the end — half the score registers per wave, so that two waves share a SIMD and
-// cover each other's operand-read and product latencies.  The key rows are split across workgroups (split-K); each split
-// writes (O, max, sum) partials for the decode combine kernel, or the output when there is one.
+// cover each other's operand-read and product latencies.  The key rows are split across
+// workgroups (split-K, at most 4096 rows each, the grid split-major); each split writes
+// (O, max, sum) partials for the decode combine kernel, or the output when there is one.
 // Tiles: 64 keys, staged through a 2-stage LDS ring by global_load_lds_dwordx4, XOR-swizzled as
 // in the prefill kernel; per-column online softmax in the log2 domain with a lazily raised
 // running maximum.
@@ -40,9 +41,7 @@ constexpr float kRescaleLog2 = 8.0f;         // raise the running max only beyon
 // fp8: one bf16 tile and the new rows
 constexpr int NEW_ROWS = 16;
 constexpr int NEW_BYTES = NEW_ROWS * (DQK + DV) * 2;
-#ifndef FP8_DEPTH
-#define FP8_DEPTH 2
-#endif
+constexpr int kFp8Depth = 2;                 // fp8: tiles of codes in flight (register sets)
 
 // CW column waves of CWD query columns each, times KS key halves: with KS = 2 the waves of half
 // kh take keys 32 kh .. 32 kh + 31 of every tile with a softmax state of their own, merged at the
@@ -50,8 +49,8 @@ constexpr int NEW_BYTES = NEW_ROWS * (DQK + DV) * 2;
 // CWD = 16: 16x16x32 products on the operand layout of the 16-row sliding prefill kernel (two
 // 16-key blocks x 16 columns per half), about half the registers and twice the waves.
 template <int CWD, int CW, int KS, bool WINDOW, bool SINK, bool SPLIT, bool FP8>
-__global__ __launch_bounds__(CW * KS * 64) __attribute__((amdgpu_waves_per_eu(CWD == 16 ? 2 : KS))) void
-verify_tiles_kernel(const VerifyArgs a) {
+__global__ __launch_bounds__(CW * KS * 64)
+__attribute__((amdgpu_waves_per_eu(CWD == 16 ? 2 : KS))) void verify_tiles_kernel(const VerifyArgs a) {
     constexpr bool M16 = CWD == 16;
     constexpr int QC = M16 ? DQK / 32 : KCH;       // Q^T operand chunks of QSTEP dims
     constexpr int QSTEP = M16 ? 32 : 16;
@@ -110,7 +109,8 @@ verify_tiles_kernel(const VerifyArgs a) {
     if (!seq_ok) {   // defined result: zero output (a split combine writes the zeros itself)
         if (!SPLIT && col_ok && kh == 0) {
             uint16_t* orow = a.out + (((int64_t)b * T + t) * Hq + h) * DV;
-            for (int d = 4 * lsub; d < DV; d += 4 * (64 / CWD)) *(u32x2*)(orow + d) = u32x2{0u, 0u};
+            for (int d = 4 * lsub; d < DV; d += 4 * (64 / CWD))
+                *(u32x2*)(orow + d) = u32x2{0u, 0u};
         }
         return;
     }
@@ -525,7 +525,7 @@ verify_tiles_kernel(const VerifyArgs a) {
     if constexpr (FP8) {
         // DEPTH tiles of codes in flight (one where the registers would not hold more: a single
         // wave, or 8 waves two to a SIMD); register set d holds tiles d, d + DEPTH, ...
-        constexpr int DEPTH = (NW <= 2 || (NW == 8 && KS == 1)) ? 1 : FP8_DEPTH;
+        constexpr int DEPTH = (NW <= 2 || (NW == 8 && KS == 1)) ? 1 : kFp8Depth;
         u32x4 cs[DEPTH][KU + VU];
         // Round r runs DEPTH steps: step d widens tile DEPTH * r + d from register set d (a
         // uniform branch skips it in round -1, which only loads) and loads the tile DEPTH later
