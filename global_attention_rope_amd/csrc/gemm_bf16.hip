@@ -17,10 +17,11 @@
 //     read transposed from the LDS B tile by ds_read_b64_tr_b16) and A^T as the B operand (32 rows
 //     of C, 8 consecutive k per lane, read straight from the LDS A tile), so that each lane ends
 //     with one row of C and, per block, four groups of four consecutive columns (8-byte stores);
-//   * A (256 x 64) and B (64 x 256) tiles stream through a 2-stage LDS ring (128 KiB) filled by
-//     global_load_lds_dwordx4, one tile ahead of the one being computed; A rows are swizzled at
-//     16-byte granularity (chunk c of row r at c ^ (r & 7)), B rows as chunk c at c ^ 4 (r & 3),
-//     so that both operand reads are conflict-free;
+//   * A (256 x 32) and B (32 x 256) tiles stream through a 4-stage LDS ring (128 KiB) filled by
+//     global_load_lds_dwordx4, three tiles ahead of the one being computed (with 64-deep tiles
+//     and two stages, one tile ahead, each tile's copy latency sat on the products' path); A rows
+//     (64 bytes) are swizzled at 16-byte granularity (chunk c of row r at c ^ ((r >> 2) & 3)),
+//     B rows as chunk c at c ^ 4 (r & 3), so that both operand reads are conflict-free;
 //   * epilogues: plain (C = alpha * acc); key projection (the rotation of the leading 64 dims of
 //     each key head applied to the fp32 accumulators, the rotated key stored in the attention's
 //     [B, Hkv, S, dqk] layout and into the KV cache: linear slot = position, ring slot =
@@ -34,7 +35,7 @@
 namespace mimo {
 namespace {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64, GSTAGES = 2, GW = 8;
+constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4, GW = 8;
 constexpr int A_TILE = GBM * GBK * 2;   // bytes
 constexpr int B_TILE = GBK * GBN * 2;
 constexpr int A_DMA = A_TILE / 1024 / GW;   // 1-KiB DMA instructions per wave per tile
@@ -68,16 +69,17 @@ __global__ __launch_bounds__(GW * 64) void gemm_bf16_kernel(const GemmArgs a) {
     const int wm = wave & 3, wn = wave >> 2;   // wave's 64-row and 128-column slice
     const int nk = a.K / GBK;
 
-    // ---- DMA sources: LDS 16-byte slot P of this wave's instruction i holds
-    //      A row P / 8, logical chunk (P % 8) ^ (row & 7); B row P / 16, chunk (P % 16) ^ 4 (row & 3).
+    // ---- DMA sources: LDS 16-byte slot P of this wave's instruction i holds A row P / 4, logical
+    //      chunk (P % 4) ^ ((row >> 2) & 3); B row P / 32, chunk (P % 32) ^ 4 (row & 3).
+    constexpr int ACH = GBK / 8;   // 16-byte chunks per A row
     const uint16_t* ap[A_DMA];
     const uint16_t* bp[B_DMA];
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
         const int P = (wave * A_DMA + i) * 64 + lane;
-        const int row = P / 8, phys = P % 8;
+        const int row = P / ACH, phys = P % ACH;
         const int m = min(m0 + row, a.M - 1);
-        ap[i] = a.A + (int64_t)m * a.lda + ((phys ^ (row & 7)) * 8);
+        ap[i] = a.A + (int64_t)m * a.lda + ((phys ^ ((row >> 2) & 3)) * 8);
     }
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
@@ -96,14 +98,16 @@ __global__ __launch_bounds__(GW * 64) void gemm_bf16_kernel(const GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i) dma16(bp[i] + dk * ldb, bst + (wave * B_DMA + i) * 1024);
     };
-    if (nk > 0) issue(0, 0);
+#pragma unroll
+    for (int t = 0; t < GSTAGES - 1; ++t)
+        if (t < nk) issue(t, t);
 
     // ---- per-lane LDS read offsets (bytes within a stage)
     // A^T operand, row block mb: row r = 64 wave + 32 mb + l32, logical chunk 2 kk + g
     int a_rd[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) a_rd[mb] = (64 * wm + 32 * mb + l32) * (GBK * 2);
-    const int aswz = l32 & 7;   // (row & 7) of every row this lane reads
+    const int aswz = (l32 >> 2) & 3;   // ((row >> 2) & 3) of every row this lane reads
     // B^T operand, column block nb: ds_read_b64_tr_b16 hands lane j of a 16-lane group
     // B[k0 + t][n0 + j] (t < 4) when it points at B[k0 + j/4][n0 + 4 (j % 4)]; lane group g takes
     // k rows 8g .. 8g + 3 and, in a second read, 8g + 4 .. 8g + 7 (the 8 consecutive k that the
@@ -127,9 +131,13 @@ __global__ __launch_bounds__(GW * 64) void gemm_bf16_kernel(const GemmArgs a) {
 
     for (int t = 0; t < nk; ++t) {
         const int st = t % GSTAGES;
-        wait_vmcnt<0>();
-        block_sync_lds();   // tile t is in LDS for every wave; stage (t - 1) % 2 is free
-        if (t + 1 < nk) issue(t + 1, (t + 1) % GSTAGES);
+        // tile t has landed once at most the later tiles' copies are outstanding (this wave's
+        // copies complete in order)
+        if (t + 2 < nk) wait_vmcnt<2 * (A_DMA + B_DMA)>();
+        else if (t + 1 < nk) wait_vmcnt<A_DMA + B_DMA>();
+        else wait_vmcnt<0>();
+        block_sync_lds();   // tile t is in LDS for every wave; stage (t - 1) % 4 is free
+        if (t + GSTAGES - 1 < nk) issue(t + GSTAGES - 1, (t + GSTAGES - 1) % GSTAGES);
         const uint8_t* as = smem + st * A_TILE;
         const uint8_t* bs = smem + st * B_TILE;   // + b_rd, which holds the B area's base
 #pragma unroll
