@@ -344,6 +344,19 @@ def test_decode_many_splits_mixed_lengths_all_sequences():
     assert_close(out, ref, what="decode, many splits")
 
 
+def test_decode_full_round_grid_without_splits():
+    """512 (sequence, KV head) pairs over short caches: one split each, so the grid is exactly one
+    round of resident workgroups (two per CU), with a sink on a global layer and no combine.  The
+    oracle checks every sequence."""
+    w = _wl(kind=0, B=64, S=1, Hq=16, Hkv=8, sinks=True)
+    rng = np.random.default_rng(23)
+    positions = [0, 1, 31, 32, 100, 127] + rng.integers(0, 128, size=58).tolist()
+    assert mimo.decode_workspace_size(_params(w, 64), max(positions)) == 0   # one split
+    _note("decode GA one-round grid, B=64 Hkv=8, no splits")
+    out, ref, *_ = _decode_case(w, positions, seed=7120)
+    assert_close(out, ref, what="decode, full-round grid without splits")
+
+
 # A decode whose grid takes more than one round of resident workgroups goes out in blocks of 4
 # splits per (sequence, KV head) pair.  64 sequences x 4 KV heads over lengths up to 20000 make
 # 10 splits of 2048 slots (bf16 and fp8 caches alike; tests/test_abi_cpu.py pins this geometry
