@@ -183,7 +183,7 @@ def main():
                     help="launch every decode call from Python instead of replaying a HIP graph")
     ap.add_argument("--workload", default="stack",
                     choices=["stack", "swa_prefill", "ga_prefill", "decode", "extend", "layer",
-                             "router", "copy", "gemm", "decode_latency"])
+                             "router", "copy", "gemm", "decode_latency", "ceilings"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hybrid attention hot path runs on a single device "
@@ -513,6 +513,37 @@ def single_layer(args, dev):
         y = torch.randn((n, n), device=dev).to(torch.bfloat16)
         ms = timed(lambda: torch.mm(x, y), args.steps)
         res.update(ms=ms, tflops=2 * n ** 3 / ms / 1e9)
+    elif args.workload == "ceilings":
+        # attainable read bandwidth and dense bf16 matrix rate of this part, measured by the probe
+        # library's stream-read and MFMA-loop kernels (the practical ceilings beside the nominal
+        # 8 TB/s and 2.5 PFLOP/s)
+        import ctypes
+
+        from global_attention_rope_amd import build as hb
+        probe = ctypes.CDLL(hb.PROBE_LIB)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        probe.mimo_probe_stream_read.argtypes = [vp, i64, i32, vp, i32, vp]
+        probe.mimo_probe_mfma.argtypes = [vp, i32, i32, vp]
+        cur = lambda: vp(torch.cuda.current_stream().cuda_stream)
+        nbytes, G = 2 << 30, 2048
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty(G * 512, dtype=torch.int32, device=dev)
+        for flags, name in ((0, "stream_read"), (1, "stream_read_nontemporal"),
+                            (2, "stream_read_slices"), (3, "stream_read_slices_nontemporal")):
+            fn = lambda: probe.mimo_probe_stream_read(vp(src.data_ptr()), nbytes, flags,
+                                                      vp(dst.data_ptr()), G, cur())
+            assert fn() == 0
+            ms = timed(fn, args.steps)
+            res[name] = dict(ms=ms, bytes=nbytes, GBps=nbytes / ms / 1e6,
+                             frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBPS)
+        iters = 20000
+        for groups, name in ((256, "mfma_loop_2_waves_per_simd"), (512, "mfma_loop_4_waves_per_simd")):
+            fn = lambda: probe.mimo_probe_mfma(vp(dst.data_ptr()), groups, iters, cur())
+            assert fn() == 0
+            ms = timed(fn, args.steps)
+            f = groups * 8 * iters * 4 * 32768
+            res[name] = dict(ms=ms, flop=f, tflops=f / ms / 1e9,
+                             frac_mfma=f / ms / 1e9 / PEAK_BF16_TFLOPS)
     elif args.workload == "copy":
         nbytes = 2 << 30
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)

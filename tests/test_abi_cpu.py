@@ -38,10 +38,31 @@ def test_probe_library_exports_its_declared_functions():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mimo_probe.h")).read(),
                   flags=re.S)
     names = set(re.findall(r"\b(mimo_probe_\w+)\s*\(", text))
-    assert names == {"mimo_probe_empty", "mimo_probe_tile_read"}
+    assert names == {"mimo_probe_empty", "mimo_probe_tile_read", "mimo_probe_stream_read",
+                     "mimo_probe_mfma"}
     lib = ctypes.CDLL(hb.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_arguments_checked_before_any_launch():
+    """The ceiling probes reject NULL buffers, empty grids and bad sizes on the host (no device call
+    is made, so this runs without a GPU)."""
+    from global_attention_rope_amd import build as hb
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.mimo_probe_stream_read.argtypes = [vp, i64, i32, vp, i32, vp]
+    lib.mimo_probe_mfma.argtypes = [vp, i32, i32, vp]
+    fake = vp(0x1000)
+    assert lib.mimo_probe_stream_read(None, 1 << 20, 0, fake, 8, None) == -1
+    assert lib.mimo_probe_stream_read(fake, 1 << 20, 0, None, 8, None) == -1
+    assert lib.mimo_probe_stream_read(fake, 1 << 20, 1, fake, 0, None) == -1
+    for bad in (0, 8, (1 << 20) + 4):
+        assert lib.mimo_probe_stream_read(fake, bad, 0, fake, 8, None) == -2
+    assert lib.mimo_probe_stream_read(fake, 3 * 4096, 2, fake, 2, None) == -2   # uneven slices
+    assert lib.mimo_probe_mfma(None, 8, 10, None) == -1
+    assert lib.mimo_probe_mfma(fake, 0, 10, None) == -1
+    assert lib.mimo_probe_mfma(fake, 8, 0, None) == -2
 
 
 def _swa(**kw):
