@@ -169,18 +169,20 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                                krs, k_lane + 64 * c,
                                (int)((uint32_t)(t0 + kb * 16) * (uint32_t)(DQK * EB)), 0));
         }
-        // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16)
+        // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16;
+        //  global layers read V non-temporally: whole rows per instruction, streamed once)
+        constexpr int VPOL = SWA ? 0 : 2;
 #pragma unroll
         for (int it = 0; it < VREG; ++it) {
             if constexpr (FP8)
                 vr[it] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               vrs, v_lane, (int)((uint32_t)t0 * DV + it * (64 / VCH) * DV), 0));
+                               vrs, v_lane, (int)((uint32_t)t0 * DV + it * (64 / VCH) * DV), VPOL));
             else
                 vr[it] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                vrs, v_lane + (it & 3) * 4 * (DV * 2),
-                               (int)((uint32_t)t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2)), 0));
+                               (int)((uint32_t)t0 * (DV * 2) + (it >> 2) * 16 * (DV * 2)), VPOL));
         }
     };
     // ---- every load that does not depend on the position goes out first, unconditionally (a
