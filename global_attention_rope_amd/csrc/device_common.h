@@ -54,6 +54,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// The same with a non-temporal load, for rows streamed once (a whole 1-KiB span per instruction).
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // The same from a workgroup-uniform base plus a per-lane 32-bit byte offset (the base in scalar
 // registers, so that per-tile address arithmetic stays scalar).
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t offset, uint32_t lds_base) {

@@ -14,7 +14,8 @@
 // (O, max, sum) partials for the decode combine kernel, or the output when there is one.
 // Tiles: 64 keys, staged through a 2-stage LDS ring by global_load_lds_dwordx4, XOR-swizzled as
 // in the prefill kernel; per-column online softmax in the log2 domain with a lazily raised
-// running maximum.
+// running maximum.  Global layers read a bf16 cache non-temporally: every row is streamed once,
+// by one split, in whole 1-KiB spans per instruction.
 // fp8 caches (global layers): the cached rows' e4m3 codes go memory -> registers (half the bytes
 // of a bf16 tile, two tiles ahead), and each tile is widened into the bf16 LDS tile before its
 // products as the codes' exact values; the two cache scales ride on the score scale and the output
@@ -158,14 +159,16 @@ __attribute__((amdgpu_waves_per_eu(CWD == 16 ? 2 : KS))) void verify_tiles_kerne
             const int j = min(max(j0 + k_row[i], jmin), nk - 1);
             const uint16_t* src = j < ring_w ? ring_k + (int64_t)((kpos0 + j) % ring_w) * DQK
                                              : kslice + (int64_t)j * DQK;
-            dma16(src + k_off[i], kst + (wave * K_DMA + i) * 1024);
+            if constexpr (WINDOW) dma16(src + k_off[i], kst + (wave * K_DMA + i) * 1024);
+            else dma16_nt(src + k_off[i], kst + (wave * K_DMA + i) * 1024);
         }
 #pragma unroll
         for (int i = 0; i < V_DMA; ++i) {
             const int j = min(max(j0 + v_row[i], jmin), nk - 1);
             const uint16_t* src = j < ring_w ? ring_v + (int64_t)((kpos0 + j) % ring_w) * DV
                                              : vslice + (int64_t)j * DV;
-            dma16(src + v_off[i], vst + (wave * V_DMA + i) * 1024);
+            if constexpr (WINDOW) dma16(src + v_off[i], vst + (wave * V_DMA + i) * 1024);
+            else dma16_nt(src + v_off[i], vst + (wave * V_DMA + i) * 1024);
         }
     };
     if (!FP8 && n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
