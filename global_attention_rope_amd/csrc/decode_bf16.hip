@@ -159,6 +159,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // (V: lane holds row (lane + 64 it) / VCH of the tile, chunk (lane + 64 it) % VCH)
     const int v_lane = ((lane / VCH) * DV + (lane % VCH) * VPL) * EB;
     u32x4 kA[KREG], vA[VREG];
+    // Keys of global layers are read non-temporally on grids of one round of workgroups (the
+    // latency-bound small batches, whose caches come from memory, not from a cache level); larger
+    // grids keep ordinary key loads, whose second half line per row, requested by the next
+    // instruction, then hits in L2.
+    constexpr int KPOL = (!SWA && EARLY) ? 2 : 0;
     auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 kr[kb * (KREG / 2) + c] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                krs, k_lane + 64 * c,
-                               (int)((uint32_t)(t0 + kb * 16) * (uint32_t)(DQK * EB)), 0));
+                               (int)((uint32_t)(t0 + kb * 16) * (uint32_t)(DQK * EB)), KPOL));
         }
         // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16;
         //  global layers read V non-temporally: whole rows per instruction, streamed once)
