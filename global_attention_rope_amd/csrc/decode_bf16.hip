@@ -90,7 +90,8 @@ struct LdsDecode {
     float red_m[NW][16], red_l[NW][16];
     float sink[16];
     union {
-        uint16_t vt[NW][TILE * VT_PITCH];     // per-wave V tiles
+        uint16_t kv[NW][TILE * DQK];          // per-wave tile area: the V tile (rows of VT_PITCH),
+                                              // before it the K tile on large global grids
         float red_o[NW][16][RO_PITCH];        // wave merge, after the slot loop
     } u;
 };
@@ -163,16 +164,28 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // latency-bound small batches, whose caches come from memory, not from a cache level); larger
     // grids keep ordinary key loads, whose second half line per row, requested by the next
     // instruction, then hits in L2.
-    constexpr int KPOL = (!SWA && EARLY) ? 2 : 0;
+    // Larger bf16 grids read each key tile as whole 1-KiB spans instead (load i of lane l holds
+    // 16-byte chunk 64 i + l of the tile: row (64 i + l) / 24, chunk (64 i + l) % 24), also
+    // non-temporally, and pass it through the wave's LDS tile into operand layout (KLDS).
+    constexpr bool KLDS = !SWA && !EARLY && !FP8;
+    constexpr int KPOL = (!SWA && (EARLY || KLDS)) ? 2 : 0;
     auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
+        if constexpr (KLDS) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int c = 0; c < KREG / 2; ++c)
-                kr[kb * (KREG / 2) + c] = __builtin_bit_cast(
+            for (int i = 0; i < KREG; ++i)
+                kr[i] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               krs, k_lane + 64 * c,
-                               (int)((uint32_t)(t0 + kb * 16) * (uint32_t)(DQK * EB)), KPOL));
+                               krs, lane * 16, (int)((uint32_t)t0 * (DQK * 2) + i * 1024), KPOL));
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int c = 0; c < KREG / 2; ++c)
+                    kr[kb * (KREG / 2) + c] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   krs, k_lane + 64 * c,
+                                   (int)((uint32_t)(t0 + kb * 16) * (uint32_t)(DQK * EB)), KPOL));
+            }
         }
         // (64 / VCH rows per instruction: it % 4 picks the row group within 16 rows on bf16;
         //  global layers read V non-temporally: whole rows per instruction, streamed once)
@@ -313,21 +326,30 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     f32x4 O[DV / 16];
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db) O[db] = f32x4{};
-    uint16_t* vt = sm.u.vt[wave];
+    uint16_t* vt = sm.u.kv[wave];
     const float sc = a.score_scale_log2;
 
     // consume the tile held in (kr, vr) at slot t, refilling the registers with the next tile as
     // soon as the scores are formed
     auto consume = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t) {
         if (own_new_w && slot_new >= t && slot_new < t + TILE) {
+            if constexpr (KLDS) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (t + kb * 16 + l16 == slot_new) {
-#pragma unroll
-                    for (int c = 0; c < KREG / 2; ++c)
-                        kr[kb * (KREG / 2) + c] =
-                            *(const u32x4*)(Kn + (FP8 ? 16 : 8) * gq + (64 / EB) * c);
+                for (int i = 0; i < KREG; ++i) {
+                    const int P = 64 * i + lane;
+                    if (t + P / (DQK / 8) == slot_new)
+                        kr[i] = *(const u32x4*)(Kn + (P % (DQK / 8)) * 8);
                 }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (t + kb * 16 + l16 == slot_new) {
+#pragma unroll
+                        for (int c = 0; c < KREG / 2; ++c)
+                            kr[kb * (KREG / 2) + c] =
+                                *(const u32x4*)(Kn + (FP8 ? 16 : 8) * gq + (64 / EB) * c);
+                    }
+            }
 #pragma unroll
             for (int it = 0; it < VREG; ++it) {
                 const int e = lane + 64 * it;
@@ -335,38 +357,65 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             }
         }
         // V rows -> this wave's LDS tile as bf16 (rows past the visible range as zeros)
-        __builtin_amdgcn_wave_barrier();
+        auto stage_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < VREG; ++it) {
-            const int e = lane + 64 * it;
-            const int row = e / VCH;
-            const bool live = t + row < k_end;
-            uint16_t* dst = vt + row * VT_PITCH + (e % VCH) * VPL;
-            if constexpr (FP8) {
-                const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-                *(u32x4*)dst = live ? bf16x8_from_e4m3x8(u32x2{vr[it][0], vr[it][1]}) : z;
-                *(u32x4*)(dst + 8) = live ? bf16x8_from_e4m3x8(u32x2{vr[it][2], vr[it][3]}) : z;
-            } else {
-                *(u32x4*)dst = live ? vr[it] : u32x4{0u, 0u, 0u, 0u};
+            for (int it = 0; it < VREG; ++it) {
+                const int e = lane + 64 * it;
+                const int row = e / VCH;
+                const bool live = t + row < k_end;
+                uint16_t* dst = vt + row * VT_PITCH + (e % VCH) * VPL;
+                if constexpr (FP8) {
+                    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+                    *(u32x4*)dst = live ? bf16x8_from_e4m3x8(u32x2{vr[it][0], vr[it][1]}) : z;
+                    *(u32x4*)(dst + 8) = live ? bf16x8_from_e4m3x8(u32x2{vr[it][2], vr[it][3]}) : z;
+                } else {
+                    *(u32x4*)dst = live ? vr[it] : u32x4{0u, 0u, 0u, 0u};
+                }
             }
-        }
+        };
         // S^T (16 slots x 16 heads) for the two 16-slot blocks of the tile
         f32x4 Sacc[2];
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (KLDS) {
+            // K chunks -> the wave's tile area (rows of 384 bytes, 16-byte chunk c of row r at
+            // c ^ (r % 8)), then read back in operand layout: the same 24 chunks of every row
+            // cross lanes; the area then takes the V tile (LDS operations of a wave run in order)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x4 acc = f32x4{};
-#pragma unroll
-            for (int c = 0; c < DQK / 32; ++c) {
-                u32x4 kw;
-                if constexpr (FP8) {
-                    const u32x4& w = kr[kb * (KREG / 2) + (c >> 1)];
-                    kw = bf16x8_from_e4m3x8((c & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
-                } else {
-                    kw = kr[kb * (KREG / 2) + c];
-                }
-                acc = mfma16x16x32(as_bf16x8(kw), Qb[c], acc);
+            for (int i = 0; i < KREG; ++i) {
+                const int P = 64 * i + lane, row = P / (DQK / 8), ch = P % (DQK / 8);
+                *(u32x4*)(vt + row * DQK + (ch ^ (row & 7)) * 8) = kr[i];
             }
-            Sacc[kb] = acc;
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x4 acc = f32x4{};
+                const uint16_t* krow = vt + (kb * 16 + l16) * DQK;
+#pragma unroll
+                for (int c = 0; c < DQK / 32; ++c)
+                    acc = mfma16x16x32(*(const bf16x8*)(krow + ((4 * c + gq) ^ (l16 & 7)) * 8),
+                                       Qb[c], acc);
+                Sacc[kb] = acc;
+            }
+            __builtin_amdgcn_wave_barrier();
+            stage_v();
+        } else {
+            stage_v();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x4 acc = f32x4{};
+#pragma unroll
+                for (int c = 0; c < DQK / 32; ++c) {
+                    u32x4 kw;
+                    if constexpr (FP8) {
+                        const u32x4& w = kr[kb * (KREG / 2) + (c >> 1)];
+                        kw = bf16x8_from_e4m3x8((c & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+                    } else {
+                        kw = kr[kb * (KREG / 2) + c];
+                    }
+                    acc = mfma16x16x32(as_bf16x8(kw), Qb[c], acc);
+                }
+                Sacc[kb] = acc;
+            }
         }
         if (t + stride < k_end) fetch(kr, vr, t + stride);
 
