@@ -82,6 +82,9 @@ __device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int
     return pack8(x);
 }
 
+// KVE: bf16 elements of a wave's tile area (the V tile, or on large bf16 global grids the larger
+// K tile that passes through it first).
+template <int KVE>
 struct LdsDecode {
     float2 cs[NW][kMaxRopeHalf + 8];          // per wave: cos/sin of the position per frequency,
                                               // then the identity entries
@@ -90,7 +93,7 @@ struct LdsDecode {
     float red_m[NW][16], red_l[NW][16];
     float sink[16];
     union {
-        uint16_t kv[NW][TILE * DQK];          // per-wave tile area: the V tile (rows of VT_PITCH),
+        uint16_t kv[NW][KVE];                 // per-wave tile area: the V tile (rows of VT_PITCH),
                                               // before it the K tile on large global grids
         float red_o[NW][16][RO_PITCH];        // wave merge, after the slot loop
     } u;
@@ -104,7 +107,9 @@ struct LdsDecode {
 // fetches one tile it does not use, which a larger grid would pay for in bandwidth).
 template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool EARLY>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) LdsDecode sm;
+    constexpr bool KLDS = !SWA && !EARLY;   // (large global grids: keys through LDS, below)
+    constexpr int KVE = (KLDS && !FP8) ? TILE * DQK : TILE * VT_PITCH;
+    __shared__ __attribute__((aligned(16))) LdsDecode<KVE> sm;
     // Every argument the kernel reads is requested here, in one batch of scalar loads waited for
     // once: the compiler would otherwise fetch them in several dependent rounds as they come up.
     asm volatile("" ::"s"(a.q), "s"(a.k_new), "s"(a.v_new), "s"(a.positions), "s"(a.k_cache),
@@ -164,18 +169,22 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // latency-bound small batches, whose caches come from memory, not from a cache level); larger
     // grids keep ordinary key loads, whose second half line per row, requested by the next
     // instruction, then hits in L2.
-    // Larger bf16 grids read each key tile as whole 1-KiB spans instead (load i of lane l holds
-    // 16-byte chunk 64 i + l of the tile: row (64 i + l) / 24, chunk (64 i + l) % 24), also
+    // Larger grids read each key tile as whole 1-KiB spans instead (load i of lane l holds
+    // 16-byte chunk 64 i + l of the tile: row (64 i + l) / KCPR, chunk (64 i + l) % KCPR), also
     // non-temporally, and pass it through the wave's LDS tile into operand layout (KLDS).
-    constexpr bool KLDS = !SWA && !EARLY && !FP8;
     constexpr int KPOL = (!SWA && (EARLY || KLDS)) ? 2 : 0;
+    constexpr int KCPR = DQK * EB / 16;                      // 16-byte chunks per key row
+    // LDS position of chunk c of key row r: c ^ kswz(r), which keeps it within its row (bf16: 24
+    // chunks, any 3-bit mask; fp8: 12 chunks, 2-bit masks) and spreads the operand reads of the
+    // 16 rows over the banks
+    auto kswz = [](int r) { return FP8 ? ((r >> 1) ^ (r >> 3)) & 3 : r & 7; };
     auto fetch = [&](u32x4 (&kr)[KREG], u32x4 (&vr)[VREG], int t0) {
         if constexpr (KLDS) {
 #pragma unroll
             for (int i = 0; i < KREG; ++i)
                 kr[i] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               krs, lane * 16, (int)((uint32_t)t0 * (DQK * 2) + i * 1024), KPOL));
+                               krs, lane * 16, (int)((uint32_t)t0 * (DQK * EB) + i * 1024), KPOL));
         } else {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -337,8 +346,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < KREG; ++i) {
                     const int P = 64 * i + lane;
-                    if (t + P / (DQK / 8) == slot_new)
-                        kr[i] = *(const u32x4*)(Kn + (P % (DQK / 8)) * 8);
+                    if (t + P / KCPR == slot_new)
+                        kr[i] = *(const u32x4*)((const uint8_t*)Kn + (P % KCPR) * 16);
                 }
             } else {
 #pragma unroll
@@ -377,23 +386,37 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
         f32x4 Sacc[2];
         __builtin_amdgcn_wave_barrier();
         if constexpr (KLDS) {
-            // K chunks -> the wave's tile area (rows of 384 bytes, 16-byte chunk c of row r at
-            // c ^ (r % 8)), then read back in operand layout: the same 24 chunks of every row
-            // cross lanes; the area then takes the V tile (LDS operations of a wave run in order)
+            // K chunks -> the wave's tile area (rows of DQK * EB bytes, chunk c of row r at
+            // c ^ kswz(r)), then read back in operand layout (the chunks of every row cross
+            // lanes); the area then takes the V tile (LDS operations of a wave run in order)
+            uint8_t* const kt = (uint8_t*)vt;
 #pragma unroll
             for (int i = 0; i < KREG; ++i) {
-                const int P = 64 * i + lane, row = P / (DQK / 8), ch = P % (DQK / 8);
-                *(u32x4*)(vt + row * DQK + (ch ^ (row & 7)) * 8) = kr[i];
+                const int P = 64 * i + lane, row = P / KCPR, ch = P % KCPR;
+                *(u32x4*)(kt + row * (DQK * EB) + (ch ^ kswz(row)) * 16) = kr[i];
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x4 acc = f32x4{};
-                const uint16_t* krow = vt + (kb * 16 + l16) * DQK;
+                const int row = kb * 16 + l16;
+                const uint8_t* krow = kt + row * (DQK * EB);
+                if constexpr (FP8) {
+                    // chunk 4 c2 + gq of the codes holds dims 64 c2 + 16 gq.. (two k-chunks)
 #pragma unroll
-                for (int c = 0; c < DQK / 32; ++c)
-                    acc = mfma16x16x32(*(const bf16x8*)(krow + ((4 * c + gq) ^ (l16 & 7)) * 8),
-                                       Qb[c], acc);
+                    for (int c2 = 0; c2 < DQK / 64; ++c2) {
+                        const u32x4 w = *(const u32x4*)(krow + ((4 * c2 + gq) ^ kswz(row)) * 16);
+                        acc = mfma16x16x32(as_bf16x8(bf16x8_from_e4m3x8(u32x2{w[0], w[1]})),
+                                           Qb[2 * c2], acc);
+                        acc = mfma16x16x32(as_bf16x8(bf16x8_from_e4m3x8(u32x2{w[2], w[3]})),
+                                           Qb[2 * c2 + 1], acc);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < DQK / 32; ++c)
+                        acc = mfma16x16x32(*(const bf16x8*)(krow + ((4 * c + gq) ^ kswz(row)) * 16),
+                                           Qb[c], acc);
+                }
                 Sacc[kb] = acc;
             }
             __builtin_amdgcn_wave_barrier();
