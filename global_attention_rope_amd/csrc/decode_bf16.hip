@@ -5,10 +5,12 @@
 // "Implementation plan" (sliding layers keep a rotating cache of the window).
 //
 // Per (sequence b, KV head g, split s) one workgroup of 4 waves:
-//   * each wave issues the loads of its first 32-slot tile (K straight into MFMA operand layout,
-//     V as coalesced 16-byte rows) early — before the position is even read on sliding layers
-//     and on small global-layer grids —
-//     so their latency overlaps the query rotation;
+//   * each wave issues the loads of its first 32-slot tile early — before the position is even
+//     read on sliding layers and on small global-layer grids — so their latency overlaps the
+//     query rotation.  Sliding layers load K straight into MFMA operand layout; global layers
+//     load it as whole 1-KiB spans, non-temporally (each slot is read once), and pass it through
+//     the wave's LDS tile area into operand layout; V comes as coalesced 16-byte rows
+//     (non-temporal on global layers);
 //   * the query heads of group g (<= 16) are rotated at the new token's position and kept as the
 //     B operand of v_mfma_f32_16x16x32_bf16 (heads are the 16-wide N dimension);
 //   * the split that owns the new token's slot rotates k_new, stores it and v_new into the cache
@@ -82,8 +84,8 @@ __device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int
     return pack8(x);
 }
 
-// KVE: bf16 elements of a wave's tile area (the V tile, or on large bf16 global grids the larger
-// K tile that passes through it first).
+// KVE: bf16 elements of a wave's tile area (the V tile, or on bf16 global layers the larger K
+// tile that passes through it first).
 template <int KVE>
 struct LdsDecode {
     float2 cs[NW][kMaxRopeHalf + 8];          // per wave: cos/sin of the position per frequency,
@@ -94,7 +96,7 @@ struct LdsDecode {
     float sink[16];
     union {
         uint16_t kv[NW][KVE];                 // per-wave tile area: the V tile (rows of VT_PITCH),
-                                              // before it the K tile on large global grids
+                                              // before it the K tile on global layers
         float red_o[NW][16][RO_PITCH];        // wave merge, after the slot loop
     } u;
 };
@@ -107,7 +109,7 @@ struct LdsDecode {
 // fetches one tile it does not use, which a larger grid would pay for in bandwidth).
 template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool EARLY>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
-    constexpr bool KLDS = !SWA && !EARLY;   // (large global grids: keys through LDS, below)
+    constexpr bool KLDS = !SWA;   // (global layers: keys through LDS, below)
     constexpr int KVE = (KLDS && !FP8) ? TILE * DQK : TILE * VT_PITCH;
     __shared__ __attribute__((aligned(16))) LdsDecode<KVE> sm;
     // Every argument the kernel reads is requested here, in one batch of scalar loads waited for
@@ -165,14 +167,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     // (V: lane holds row (lane + 64 it) / VCH of the tile, chunk (lane + 64 it) % VCH)
     const int v_lane = ((lane / VCH) * DV + (lane % VCH) * VPL) * EB;
     u32x4 kA[KREG], vA[VREG];
-    // Keys of global layers are read non-temporally on grids of one round of workgroups (the
-    // latency-bound small batches, whose caches come from memory, not from a cache level); larger
-    // grids keep ordinary key loads, whose second half line per row, requested by the next
-    // instruction, then hits in L2.
-    // Larger grids read each key tile as whole 1-KiB spans instead (load i of lane l holds
-    // 16-byte chunk 64 i + l of the tile: row (64 i + l) / KCPR, chunk (64 i + l) % KCPR), also
-    // non-temporally, and pass it through the wave's LDS tile into operand layout (KLDS).
-    constexpr int KPOL = (!SWA && (EARLY || KLDS)) ? 2 : 0;
+    // Global layers read each key tile as whole 1-KiB spans, non-temporally (every slot is read
+    // once): load i of lane l holds 16-byte chunk 64 i + l of the tile (row (64 i + l) / KCPR,
+    // chunk (64 i + l) % KCPR), and the tile passes through the wave's LDS tile area into operand
+    // layout (KLDS).  Sliding layers load the operand layout straight from the ring (16 rows x
+    // 64 bytes per instruction, ordinary loads: the ring is read again at the next step).
+    constexpr int KPOL = SWA ? 0 : 2;
     constexpr int KCPR = DQK * EB / 16;                      // 16-byte chunks per key row
     // LDS position of chunk c of key row r: c ^ kswz(r), which keeps it within its row (bf16: 24
     // chunks, any 3-bit mask; fp8: 12 chunks, 2-bit masks) and spreads the operand reads of the
