@@ -547,32 +547,34 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
 }
 
 // Merge the splits of one (sequence, query head); the sink joins the denominator once, here.  One
-// thread per output dim.  The position, every split's (max, sum) and the first PRE records' values
-// are requested together, before anything waits (records past the last split are read as the last
-// one again): splits the position leaves empty never wrote their records, so those values are
-// masked, never used.  Then the common maximum and the weights go through LDS and each thread
-// sums its dim, in split order (PRE, the prefetch depth, is picked at launch from the split
-// count; the sum is the same for any PRE).
+// wave per (sequence, head), two output dims per lane (d and d + 64).  The position, the first
+// 64 splits' (max, sum) and the first PRE records' values are requested together, before
+// anything waits (records past the last split are read as the last one again): splits the
+// position leaves empty never wrote their records, so those values are masked, never used.  The
+// common maximum and the denominator are wave reductions; the weights go through LDS within the
+// wave (no workgroup barrier) and each lane sums its dims in split order (PRE, the prefetch depth,
+// is picked at launch from the split count; the sum is the same for any PRE).
 template <bool SWA, bool SINK, bool VERIFY, int PRE>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a) {
-    constexpr int CH = 32;
-    __shared__ float w_s[1024], l_s[1024];
-    __shared__ float red[4];
+__global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
+    constexpr int CH = 16;
+    __shared__ float w_s[1024];
     // (every argument read, requested in one batch of scalar loads)
     asm volatile("" ::"s"(a.partial), "s"(a.sinks), "s"(a.positions), "s"(a.out), "s"(a.Hq),
                  "s"(a.nsplit), "s"(a.q_per_seq), "s"(a.max_position), "s"(a.cap), "s"(a.window),
                  "s"(a.kpos_rel), "s"(a.kpos_off), "s"(a.chunk), "s"(a.v_scale));
-    const int h = blockIdx.x, bq = blockIdx.y, d = threadIdx.x, wave = d >> 6;
+    const int h = blockIdx.x, bq = blockIdx.y, lane = threadIdx.x;
     const int b = VERIFY ? bq / a.q_per_seq : bq;
     const int nsp = a.nsplit;
     const float* rec = a.partial + ((int64_t)bq * a.Hq + h) * nsp * PSTRIDE;
-    float x[PRE];
+    float x0[PRE], x1[PRE];
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) x[i] = rec[(int64_t)min(i, nsp - 1) * PSTRIDE + d];
-    for (int i = d; i < nsp; i += 128) {
-        w_s[i] = rec[(int64_t)i * PSTRIDE + DV];
-        l_s[i] = rec[(int64_t)i * PSTRIDE + DV + 1];
+    for (int i = 0; i < PRE; ++i) {
+        const float* r = rec + (int64_t)min(i, nsp - 1) * PSTRIDE;
+        x0[i] = r[lane];
+        x1[i] = r[lane + 64];
     }
+    const float* r0 = rec + (int64_t)min(lane, nsp - 1) * PSTRIDE;
+    const float m0 = r0[DV], l0 = r0[DV + 1];
     const float sk = SINK ? a.sinks[h] * kLog2e : -INFINITY;
     const int32_t p_in = load_scalar_i32(a.positions + b);   // (also keeps the loads above first)
     uint16_t* o = a.out + ((int64_t)bq * a.Hq + h) * DV;
@@ -580,54 +582,69 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a)
     const bool pos_ok = VERIFY ? (p_in >= 0 && p_in <= a.max_position)
                                : (pos >= 0 && pos <= a.max_position && (SWA || pos < a.cap));
     if (!pos_ok) {
-        o[d] = 0;
+        o[lane] = 0;
+        o[lane + 64] = 0;
         return;
     }
     // key rows the decode kernel's splits covered (the same count it used)
     const int n_valid = VERIFY ? pos - ((a.kpos_rel ? p_in : 0) + a.kpos_off) + 1
                                : (SWA ? min(a.window, pos + 1) : pos + 1);
     const int ns = min(nsp, (n_valid + a.chunk - 1) / a.chunk);   // splits that wrote a record
-    block_sync_lds();
-    float mx = -INFINITY;
-    for (int i = d; i < ns; i += 128) mx = fmaxf(mx, w_s[i]);
+    float mx = lane < ns ? m0 : -INFINITY;
+    for (int i = lane + 64; i < ns; i += 64) mx = fmaxf(mx, rec[(int64_t)i * PSTRIDE + DV]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((d & 63) == 0) red[wave] = mx;
-    block_sync_lds();
-    const float M = fmaxf(fmaxf(red[0], red[1]), sk);
+    const float M = fmaxf(mx, sk);
     const float Mu = (M == -INFINITY) ? 0.0f : M;
     float ls = 0.0f;
-    for (int i = d; i < ns; i += 128) {
-        const float w = fast_exp2(w_s[i] - Mu);
+    if (lane < ns) {
+        const float w = fast_exp2(m0 - Mu);
+        w_s[lane] = w;
+        ls = w * l0;
+    }
+    for (int i = lane + 64; i < ns; i += 64) {
+        const float w = fast_exp2(rec[(int64_t)i * PSTRIDE + DV] - Mu);
         w_s[i] = w;
-        ls += w * l_s[i];
+        ls += w * rec[(int64_t)i * PSTRIDE + DV + 1];
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off);
-    if ((d & 63) == 0) red[2 + wave] = ls;
-    block_sync_lds();
-    const float L = red[2] + red[3] + (SINK ? fast_exp2(sk - Mu) : 0.0f);
-    float acc = 0.0f;
+    const float L = ls + (SINK ? fast_exp2(sk - Mu) : 0.0f);
+    __builtin_amdgcn_wave_barrier();   // (the weights in LDS: written and read by this wave only)
+    float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) acc += i < ns ? w_s[i] * x[i] : 0.0f;
-    for (int s0 = PRE; s0 < ns; s0 += CH) {
-        float y[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) y[i] = rec[(int64_t)min(s0 + i, ns - 1) * PSTRIDE + d];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) acc += s0 + i < ns ? w_s[s0 + i] * y[i] : 0.0f;
+    for (int i = 0; i < PRE; ++i) {
+        const float w = i < ns ? w_s[i] : 0.0f;
+        acc0 += w * x0[i];
+        acc1 += w * x1[i];
     }
-    o[d] = f32_to_bf16_bits(L > 0.0f ? a.v_scale * acc / L : 0.0f);
+    for (int s0 = PRE; s0 < ns; s0 += CH) {
+        float y0[CH], y1[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float* r = rec + (int64_t)min(s0 + i, ns - 1) * PSTRIDE;
+            y0[i] = r[lane];
+            y1[i] = r[lane + 64];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float w = s0 + i < ns ? w_s[s0 + i] : 0.0f;
+            acc0 += w * y0[i];
+            acc1 += w * y1[i];
+        }
+    }
+    const float f = L > 0.0f ? a.v_scale / L : 0.0f;
+    o[lane] = f32_to_bf16_bits(acc0 * f);
+    o[lane + 64] = f32_to_bf16_bits(acc1 * f);
 }
 
-// The combine with the smallest prefetch depth that holds every split (at most 96; more splits
-// are read in further chunks).
+// The combine with the smallest prefetch depth that holds every split (at most 64; more splits
+// are read in further chunks of 16).
 template <bool SWA, bool SINK, bool VERIFY>
 void launch_combine(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-    if (a.nsplit <= 16) decode_combine_kernel<SWA, SINK, VERIFY, 16><<<grid, DV, 0, st>>>(a);
-    else if (a.nsplit <= 32) decode_combine_kernel<SWA, SINK, VERIFY, 32><<<grid, DV, 0, st>>>(a);
-    else if (a.nsplit <= 64) decode_combine_kernel<SWA, SINK, VERIFY, 64><<<grid, DV, 0, st>>>(a);
-    else decode_combine_kernel<SWA, SINK, VERIFY, 96><<<grid, DV, 0, st>>>(a);
+    if (a.nsplit <= 16) decode_combine_kernel<SWA, SINK, VERIFY, 16><<<grid, 64, 0, st>>>(a);
+    else if (a.nsplit <= 32) decode_combine_kernel<SWA, SINK, VERIFY, 32><<<grid, 64, 0, st>>>(a);
+    else decode_combine_kernel<SWA, SINK, VERIFY, 64><<<grid, 64, 0, st>>>(a);
 }
 
 template <bool SWA, bool SINK, int ROT, bool FP8>
