@@ -84,9 +84,24 @@ __device__ __forceinline__ u32x4 rotate8_cs(const u32x4& w, const u32x4& pw, int
     return pack8(x);
 }
 
+// The per-wave tile areas and the wave-merge buffer: overlapping (the merge waits for every wave
+// to leave its tile) or apart (SEP: the merge writes at once).
+template <int KVE, bool SEP>
+struct TileAreas {
+    union {
+        uint16_t kv[NW][KVE];
+        float red_o[NW][16][RO_PITCH];
+    };
+};
+template <int KVE>
+struct TileAreas<KVE, true> {
+    uint16_t kv[NW][KVE];
+    float red_o[NW][16][RO_PITCH];
+};
+
 // KVE: bf16 elements of a wave's tile area (the V tile, or on bf16 global layers the larger K
 // tile that passes through it first).
-template <int KVE>
+template <int KVE, bool SEP>
 struct LdsDecode {
     float2 cs[NW][kMaxRopeHalf + 8];          // per wave: cos/sin of the position per frequency,
                                               // then the identity entries
@@ -94,11 +109,9 @@ struct LdsDecode {
     uint16_t Vn[NW][DV];                      // the first half), in the wave that owns its slot
     float red_m[NW][16], red_l[NW][16];
     float sink[16];
-    union {
-        uint16_t kv[NW][KVE];                 // per-wave tile area: the V tile (rows of VT_PITCH),
-                                              // before it the K tile on global layers
-        float red_o[NW][16][RO_PITCH];        // wave merge, after the slot loop
-    } u;
+    TileAreas<KVE, SEP> u;                    // per-wave tile areas (the V tile in rows of
+                                              // VT_PITCH, before it the K tile on global
+                                              // layers) and the wave merge after the slot loop
 };
 
 // ROT: how many of a lane's 32-dim query chunk rows can hold rotated dims (2 when r <= 64).
@@ -111,7 +124,9 @@ template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool EARLY>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr bool KLDS = !SWA;   // (global layers: keys through LDS, below)
     constexpr int KVE = (KLDS && !FP8) ? TILE * DQK : TILE * VT_PITCH;
-    __shared__ __attribute__((aligned(16))) LdsDecode<KVE> sm;
+    // sliding layers (latency-bound, few workgroups): the merge buffer apart from the tiles
+    constexpr bool SEP = SWA;
+    __shared__ __attribute__((aligned(16))) LdsDecode<KVE, SEP> sm;
     // Every argument the kernel reads is requested here, in one batch of scalar loads waited for
     // once: the compiler would otherwise fetch them in several dependent rounds as they come up.
     asm volatile("" ::"s"(a.q), "s"(a.k_new), "s"(a.v_new), "s"(a.positions), "s"(a.k_cache),
@@ -504,9 +519,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     };
     for (; t0 < k_end; t0 += stride) consume(kA, vA, t0);
 
-    // ---- merge the waves of the workgroup (the V tiles are dead now; red_o reuses them).
+    // ---- merge the waves of the workgroup (red_o overlays the dead V tiles, or sits apart).
     l_run = sum_lane_pair32(sum_lane_pair16(l_run));
-    block_sync_lds();
+    if constexpr (!SEP) block_sync_lds();   // (every wave out of its tile before red_o overlays it)
     if (gq == 0) {
         sm.red_m[wave][l16] = m_run;
         sm.red_l[wave][l16] = l_run;
