@@ -120,7 +120,9 @@ struct LdsDecode {
 // whose ring slots are all in bounds; on global layers when the grid fits one round of resident
 // workgroups, where every call is latency-bound: a split past a short sequence's position then
 // fetches one tile it does not use, which a larger grid would pay for in bandwidth).
-template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool EARLY>
+// ONE: a split holds at most one tile per wave (a sliding ring of up to 128 slots), so there is no
+// slot loop and no refill: the kernel, fetched cold on every launch, is that much shorter.
+template <bool SWA, bool SINK, bool SPLIT, int ROT, bool FP8, bool EARLY, bool ONE>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr bool KLDS = !SWA;   // (global layers: keys through LDS, below)
     constexpr int KVE = (KLDS && !FP8) ? TILE * DQK : TILE * VT_PITCH;
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
                 Sacc[kb] = acc;
             }
         }
-        if (t + stride < k_end) fetch(kr, vr, t + stride);
+        if (!ONE && t + stride < k_end) fetch(kr, vr, t + stride);
 
         float mx = -INFINITY;
 #pragma unroll
@@ -517,7 +519,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs a) {
             O[db] = mfma16x16x32(A, Pb, O[db]);
         }
     };
-    for (; t0 < k_end; t0 += stride) consume(kA, vA, t0);
+    if constexpr (ONE) {
+        if (t0 < k_end) consume(kA, vA, t0);
+    } else {
+        for (; t0 < k_end; t0 += stride) consume(kA, vA, t0);
+    }
 
     // ---- merge the waves of the workgroup (red_o overlays the dead V tiles, or sits apart).
     l_run = sum_lane_pair32(sum_lane_pair16(l_run));
@@ -673,12 +679,14 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
                           : dim3(a.nsplit, a.Hkv, a.B);
     const bool early = SWA || (int64_t)a.B * a.Hkv * a.nsplit <= kResidentDecodeGroups;
     if (a.nsplit == 1) {
-        if (early) decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true><<<grid, 256, 0, st>>>(k);
-        else decode_bf16_kernel<SWA, SINK, false, ROT, FP8, false><<<grid, 256, 0, st>>>(k);
+        if (SWA && a.chunk <= NW * TILE)
+            decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true, true><<<grid, 256, 0, st>>>(k);
+        else if (early) decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true, false><<<grid, 256, 0, st>>>(k);
+        else decode_bf16_kernel<SWA, SINK, false, ROT, FP8, false, false><<<grid, 256, 0, st>>>(k);
         return hipGetLastError();
     }
-    if (early) decode_bf16_kernel<SWA, SINK, true, ROT, FP8, true><<<grid, 256, 0, st>>>(k);
-    else decode_bf16_kernel<SWA, SINK, true, ROT, FP8, false><<<grid, 256, 0, st>>>(k);
+    if (early) decode_bf16_kernel<SWA, SINK, true, ROT, FP8, true, false><<<grid, 256, 0, st>>>(k);
+    else decode_bf16_kernel<SWA, SINK, true, ROT, FP8, false, false><<<grid, 256, 0, st>>>(k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch_combine<SWA, SINK, false>(a, dim3(a.Hq, a.B), st);
