@@ -93,6 +93,9 @@ def _decode8_case(w, positions, seed, q_scale=1.0):
     dict(kind=0, Hq=8, Hkv=2, sinks=True, positions=[31, 32, 33]),
     dict(kind=1, Hq=8, Hkv=1, sinks=True, positions=[0, 5, 126, 127, 128, 129, 300, 5000]),
     dict(kind=1, Hq=16, Hkv=2, sinks=False, positions=[1, 200]),
+    # rings wider than one 32-slot tile per wave (the slot loop with refills): 200 and 1024 slots
+    dict(kind=1, Hq=8, Hkv=2, sinks=True, W=200, positions=[0, 150, 199, 200, 201, 1000]),
+    dict(kind=1, Hq=16, Hkv=1, sinks=False, W=1024, positions=[5, 1023, 1024, 3000]),
 ])
 def test_decode_fp8_small(case):
     case = dict(case)
