@@ -28,22 +28,41 @@ __device__ __forceinline__ bool start_ok(int32_t start, int32_t max_start) {
     return max_start < 0 || (unsigned)start <= (unsigned)max_start;
 }
 
+// First token whose values are written: every token when a value workspace is given, else the
+// tokens that get a cache slot (a ring keeps the last W), else none.
+__host__ __device__ inline int rope_v_first(const RopeKVArgs& a) {
+    if (a.v_ws) return a.i0;
+    if (a.k_dst) {
+        const int f = a.i0 > a.cache_i0 ? a.i0 : a.cache_i0;
+        return f < a.S ? f : a.S;
+    }
+    return a.S;
+}
+
 // bf16: one thread per 8-element chunk of a K or V row, over a group of HG KV heads of one token
-// (HG divides Hkv): the angles of a rotated chunk are evaluated once for the whole group.
+// (HG divides Hkv): the angles of a rotated chunk are evaluated once for the whole group.  The
+// K chunks of every token come first, then the V chunks of the tokens whose values are written
+// (on a sliding layer's prefill only the last W tokens), so that no thread idles on a value row
+// nobody stores.
 template <int HG>
 __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(const RopeKVArgs a) {
-    const int kch = a.dqk / 8, vch = (a.k_dst || a.v_ws) ? a.dv / 8 : 0, per_row = kch + vch;
+    const int kch = a.dqk / 8, vch = a.dv / 8;
     const int ntok = a.S - a.i0, ngrp = a.Hkv / HG;
-    const int64_t total = (int64_t)a.B * ntok * ngrp * per_row;
+    const int iv0 = rope_v_first(a), ntv = a.S - iv0;
+    const int64_t total_k = (int64_t)a.B * ntok * ngrp * kch;
+    const int64_t total = total_k + (int64_t)a.B * ntv * ngrp * vch;
     const int r = a.rope_dims, half = r >> 1;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
-        const int c = (int)(e % per_row);
-        const int64_t grpid = e / per_row;
+        const bool isk = e < total_k;
+        const int64_t ev = isk ? e : e - total_k;
+        const int per = isk ? kch : vch, nt = isk ? ntok : ntv;
+        const int c = (int)(ev % per) + (isk ? 0 : kch);
+        const int64_t grpid = ev / per;
         const int g0 = (int)(grpid % ngrp) * HG;
-        const int64_t tok = grpid / ngrp;            // b * ntok + (i - i0)
-        const int i = a.i0 + (int)(tok % ntok);
-        const int b = (int)(tok / ntok);
+        const int64_t tok = grpid / ngrp;            // b * nt + (i - first token)
+        const int i = (isk ? a.i0 : iv0) + (int)(tok % nt);
+        const int b = (int)(tok / nt);
         const int32_t start = a.start_pos[b];
         if (!start_ok(start, a.max_start)) continue;
         const int32_t pos = start + i;
@@ -190,8 +209,8 @@ unsigned grid_for(int64_t total) {
 }  // namespace
 
 hipError_t launch_rope_kv_bf16(const RopeKVArgs& a, hipStream_t st) {
-    int64_t total =
-        (int64_t)a.B * (a.S - a.i0) * a.Hkv * (a.dqk / 8 + ((a.k_dst || a.v_ws) ? a.dv / 8 : 0));
+    int64_t total = (int64_t)a.B * a.Hkv *
+                    ((int64_t)(a.S - a.i0) * (a.dqk / 8) + (int64_t)(a.S - rope_v_first(a)) * (a.dv / 8));
     if (total <= 0 || (!a.k_ws && !a.k_dst && !a.v_ws)) return hipSuccess;
     // Heads per thread: the largest power of two up to 8 dividing Hkv that still leaves at least
     // 2^18 threads (4 waves of 256 threads per CU); small calls keep one head per thread, where a
