@@ -774,16 +774,31 @@ prefill_sw16_kernel(const PrefillArgs a) {
         compute(t, st);
     }
 
-    // ---- epilogue: out = v_scale * O / l (bf16); lane l writes row q_l, dims 16db + 4gq..
+    // ---- epilogue: out = v_scale * O / l (bf16).  Lane l holds row q_l, dims 16db + 4gq..; the
+    //      wave's 16 rows (4 KiB) pass through LDS so that the stores write whole 256-byte rows
+    //      (16 lanes x 16 bytes, non-temporally) instead of 32 bytes of a row per instruction.  The
+    //      staging area is the ring stage the last tile does not use (free since that tile's
+    //      barrier): waves 0-2 in its K part, wave 3 in its V part; 32-byte blocks of row r sit at
+    //      block ^ (r % 8).
     const float lt = sum_lane_pair32(sum_lane_pair16(l_run));
     const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-    if (q_l < S) {
-        uint16_t* orow = a.out + (((int64_t)b * S + q_l) * Hq + h) * DV;
+    const int st_free = n_tiles & 1;
+    uint8_t* const stg = wave < 3 ? smem + st_free * SW16_K_TILE + wave * 4096
+                                  : smem + 2 * SW16_K_TILE + st_free * SW16_V_TILE;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int db = 0; db < DV / 16; ++db)
-            *(u32x2*)(orow + 16 * db + 4 * gq) =
-                u32x2{pack_bf16x2(O[db][0] * inv, O[db][1] * inv),
-                      pack_bf16x2(O[db][2] * inv, O[db][3] * inv)};
+    for (int db = 0; db < DV / 16; ++db)
+        *(u32x2*)(stg + l16 * 256 + 32 * (db ^ (l16 & 7)) + 8 * gq) =
+            u32x2{pack_bf16x2(O[db][0] * inv, O[db][1] * inv),
+                  pack_bf16x2(O[db][2] * inv, O[db][3] * inv)};
+    __builtin_amdgcn_wave_barrier();
+    const int c16 = lane & 15;   // 16-byte column of the row
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = (lane >> 4) + 4 * k, q = q_first + row;
+        const u32x4 ov = *(const u32x4*)(stg + row * 256 + 32 * ((c16 >> 1) ^ (row & 7)) + 16 * (c16 & 1));
+        if (q < S)   // (written once: non-temporal)
+            __builtin_nontemporal_store(ov, (u32x4*)(a.out + (((int64_t)b * S + q) * Hq + h) * DV + 8 * c16));
     }
 }
 
