@@ -448,10 +448,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (STAGES == 3 && t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2 % STAGES>{});
     }
 
-    // ---- epilogue: out = v_scale * O / l, bf16
+    // ---- epilogue: out = v_scale * O / l, bf16.  Lane (l32, g) holds row q_l, dims
+    //      32 db + 8 ii + 4 g..; on global layers the wave's 32 rows (8 KiB) pass through LDS so
+    //      that the stores write whole 256-byte rows (16 lanes x 16 bytes, non-temporally).  The
+    //      staging areas are the two ring stages the last tile does not use (free since that
+    //      tile's barrier: no copy is issued after it): waves 0-5 in their K parts, 6-7 in the V
+    //      part of the first; 32-byte blocks of row r sit at block ^ (r % 8).
     const float lt = sum_lane_pair32(l_run);
     const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-    if (q_l < S) {
+    if constexpr (!WINDOW && STAGES == 3 && NW == 8) {
+        const int s_last = (n_tiles + STAGES - 1) % STAGES;   // stage of the last tile (if any)
+        const int f0 = s_last == 0 ? 1 : 0, f1 = s_last == 2 ? 1 : 2;   // the other two
+        uint8_t* const stg = wave < 6 ? smem + (wave < 3 ? f0 : f1) * K_TILE + (wave % 3) * 8192
+                                      : smem + STAGES * K_TILE + f0 * V_TILE + (wave - 6) * 8192;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                // row l32, bytes 64 db + 16 ii + 8 g: 32-byte block 2 db + ii / 2
+                const int blk = 2 * db + (ii >> 1);
+                *(u32x2*)(stg + l32 * 256 + 32 * (blk ^ (l32 & 7)) + 16 * (ii & 1) + 8 * g) =
+                    u32x2{pack_bf16x2(O[db][4 * ii] * inv, O[db][4 * ii + 1] * inv),
+                          pack_bf16x2(O[db][4 * ii + 2] * inv, O[db][4 * ii + 3] * inv)};
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int c16 = lane & 15;   // 16-byte column of the row
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int row = (lane >> 4) + 4 * k, q = q_first + row;
+            const u32x4 ov =
+                *(const u32x4*)(stg + row * 256 + 32 * ((c16 >> 1) ^ (row & 7)) + 16 * (c16 & 1));
+            if (q < S)   // (written once: non-temporal)
+                __builtin_nontemporal_store(
+                    ov, (u32x4*)(a.out + (((int64_t)b * S + q) * Hq + h) * DV + 8 * c16));
+        }
+    } else if (q_l < S) {
         uint16_t* orow = a.out + (((int64_t)b * S + q_l) * Hq + h) * DV;
 #pragma unroll
         for (int db = 0; db < DV / 32; ++db) {
