@@ -679,9 +679,13 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t st) {
                           : dim3(a.nsplit, a.Hkv, a.B);
     const bool early = SWA || (int64_t)a.B * a.Hkv * a.nsplit <= kResidentDecodeGroups;
     if (a.nsplit == 1) {
-        if (SWA && a.chunk <= NW * TILE)
-            decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true, true><<<grid, 256, 0, st>>>(k);
-        else if (early) decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true, false><<<grid, 256, 0, st>>>(k);
+        if constexpr (SWA) {   // (rings of at most one tile per wave)
+            if (a.chunk <= NW * TILE) {
+                decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true, true><<<grid, 256, 0, st>>>(k);
+                return hipGetLastError();
+            }
+        }
+        if (early) decode_bf16_kernel<SWA, SINK, false, ROT, FP8, true, false><<<grid, 256, 0, st>>>(k);
         else decode_bf16_kernel<SWA, SINK, false, ROT, FP8, false, false><<<grid, 256, 0, st>>>(k);
         return hipGetLastError();
     }
